@@ -1,0 +1,368 @@
+/*
+ * Oracle for jagged GDPA / JFA — TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, fp64 loop nests of what the jagged attention path computes.
+ * Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this file's library; the product path never does.
+ * It shares no code, header or constant with the GPU library.
+ *
+ * What is computed (the pages never write the formula out; the formula below
+ * is the plain reading of their words):
+ *   - "GEM Training: How Meta Doubled the Efficiency..." (globalainews.in),
+ *     section "What to watch": the attention-like modules are two matrix
+ *     products with an element-wise activation between them, GELU or SiLU
+ *     taking the place of softmax (GDPA).
+ *   - same page, section "What happened": JFA is FlashAttention run directly
+ *     on variable-length jagged tensors, with custom attention biases,
+ *     asymmetric query / key-value lengths and a backward pass.
+ *
+ * For sample b with Lq query rows and Lk key rows, head h, sample-local
+ * indices i (query) and j (key):
+ *   X[i][j]  = scale * <q_i, k_j> + bias(h, i, j)
+ *   valid    = (j < Lk) and (not causal or j <= i + Lk - Lq)
+ *   GDPA:  O_i = sum_{valid j} act(X_ij) v_j                 (no normalisation)
+ *   JFA:   O_i = sum_{valid j} softmax_j(X_i.) v_j,  LSE_i = log sum_j exp X_ij
+ *          (a row with no valid key: O_i = 0, LSE_i = -inf)
+ * Bias kinds: REL    table[h][clamp(i - j, lo, hi) - lo]
+ *             KEYPOS table[h][clamp(j, lo, hi) - lo]
+ *
+ * Backward, with upstream gradient dO and L = <O, dO>:
+ *   dP_ij = <dO_i, v_j>
+ *   GDPA:  dX_ij = dP_ij act'(X_ij),   dV_j = sum_i act(X_ij) dO_i
+ *   JFA:   dX_ij = P_ij (dP_ij - sum_k P_ik dP_ik),  dV_j = sum_i P_ij dO_i
+ *   dQ_i = scale sum_j dX_ij k_j,   dK_j = scale sum_i dX_ij q_i
+ *
+ * Inputs are float32 arrays (bf16 values are exactly representable in
+ * float32); all arithmetic is double.  Layout is token-major [T, H, D] with
+ * int32 offsets [B+1]; a NULL q_off means one block of lq_fixed query rows
+ * shared by every sample ([lq_fixed, H, D]) whose forward output still has one
+ * row block per sample ([B * lq_fixed, H, D]).  Outputs are double arrays;
+ * every element is written.
+ *
+ * Pinned by the CPU test suite against padded dense attention with an explicit
+ * mask, per-sample library attention, central finite differences of the
+ * forward pass and hand-derived closed forms.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ACT_SILU = 0, ACT_GELU_TANH = 1, ACT_GELU_ERF = 2 };
+enum { BIAS_NONE = 0, BIAS_REL = 1, BIAS_KEYPOS = 2 };
+
+/* SiLU(x) = x * sigmoid(x); derivative sigma (1 + x (1 - sigma)). */
+static double silu(double x) { return x / (1.0 + exp(-x)); }
+static double silu_grad(double x) {
+    double s = 1.0 / (1.0 + exp(-x));
+    return s * (1.0 + x * (1.0 - s));
+}
+
+/* GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). */
+static const double GELU_C = 0.7978845608028654; /* sqrt(2/pi) */
+static double gelu_tanh(double x) {
+    double t = tanh(GELU_C * (x + 0.044715 * x * x * x));
+    return 0.5 * x * (1.0 + t);
+}
+static double gelu_tanh_grad(double x) {
+    double t = tanh(GELU_C * (x + 0.044715 * x * x * x));
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * GELU_C * (1.0 + 3.0 * 0.044715 * x * x);
+}
+
+/* GELU, exact form: x Phi(x), Phi the standard normal CDF; derivative Phi + x phi. */
+static double gelu_erf(double x) { return 0.5 * x * (1.0 + erf(x / sqrt(2.0))); }
+static double gelu_erf_grad(double x) {
+    double cdf = 0.5 * (1.0 + erf(x / sqrt(2.0)));
+    double pdf = exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+    return cdf + x * pdf;
+}
+
+static double act_f(int act, double x) {
+    switch (act) {
+    case ACT_SILU: return silu(x);
+    case ACT_GELU_TANH: return gelu_tanh(x);
+    default: return gelu_erf(x);
+    }
+}
+static double act_grad(int act, double x) {
+    switch (act) {
+    case ACT_SILU: return silu_grad(x);
+    case ACT_GELU_TANH: return gelu_tanh_grad(x);
+    default: return gelu_erf_grad(x);
+    }
+}
+
+typedef struct {
+    const float *q, *k, *v;
+    const int32_t *q_off, *kv_off;
+    int32_t lq_fixed;
+    int B, H, D;
+    double scale;
+    int act;
+    int causal;
+    int bias_kind;
+    const float *bias_table;
+    int bias_lo, bias_hi;
+} problem;
+
+static int64_t clampi(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+static double bias_at(const problem *p, int h, int64_t i, int64_t j) {
+    int64_t width = (int64_t)p->bias_hi - p->bias_lo + 1;
+    const float *row = p->bias_table + (int64_t)h * width;
+    switch (p->bias_kind) {
+    case BIAS_REL: return row[clampi(i - j, p->bias_lo, p->bias_hi) - p->bias_lo];
+    case BIAS_KEYPOS: return row[clampi(j, p->bias_lo, p->bias_hi) - p->bias_lo];
+    default: return 0.0;
+    }
+}
+
+static int is_valid(const problem *p, int64_t i, int64_t j, int64_t lq, int64_t lk) {
+    if (j < 0 || j >= lk) return 0;
+    return !p->causal || j <= i + lk - lq;
+}
+
+typedef struct { int64_t qs, lq, ks, lk, o0; } sample;
+
+/* Rows of sample b: query rows start at global row qs (lq of them), key rows
+ * at ks (lk of them); output rows start at o0. */
+static sample sample_rows(const problem *p, int b) {
+    sample s;
+    if (p->q_off) { s.qs = p->q_off[b]; s.lq = (int64_t)p->q_off[b + 1] - p->q_off[b]; s.o0 = s.qs; }
+    else { s.qs = 0; s.lq = p->lq_fixed; s.o0 = (int64_t)b * p->lq_fixed; }
+    s.ks = p->kv_off[b];
+    s.lk = (int64_t)p->kv_off[b + 1] - p->kv_off[b];
+    return s;
+}
+
+static const float *row_of(const problem *p, const float *base, int64_t row, int h) {
+    return base + (row * p->H + h) * (int64_t)p->D;
+}
+
+static double score(const problem *p, int h, const sample *s, int64_t i, int64_t j) {
+    const float *qi = row_of(p, p->q, s->qs + i, h);
+    const float *kj = row_of(p, p->k, s->ks + j, h);
+    double dot = 0.0;
+    for (int d = 0; d < p->D; ++d) dot += (double)qi[d] * (double)kj[d];
+    return p->scale * dot + bias_at(p, h, i, j);
+}
+
+static double *orow(const problem *p, double *base, int64_t row, int h) {
+    return base + (row * p->H + h) * (int64_t)p->D;
+}
+
+/* Per-row softmax statistics of JFA over the valid keys: m = max, l = sum exp(X - m). */
+static int row_stats(const problem *p, int h, const sample *s, int64_t i, double *m_out, double *l_out) {
+    double m = -INFINITY;
+    int any = 0;
+    for (int64_t j = 0; j < s->lk; ++j) {
+        if (!is_valid(p, i, j, s->lq, s->lk)) continue;
+        double x = score(p, h, s, i, j);
+        if (x > m) m = x;
+        any = 1;
+    }
+    double l = 0.0;
+    if (any)
+        for (int64_t j = 0; j < s->lk; ++j)
+            if (is_valid(p, i, j, s->lq, s->lk)) l += exp(score(p, h, s, i, j) - m);
+    *m_out = m;
+    *l_out = l;
+    return any;
+}
+
+/* Forward over one (sample, head) slice.  softmax = 0: GDPA, 1: JFA. */
+static void fwd_slice(const problem *p, int softmax, int b, int h, double *o, double *lse) {
+    sample s = sample_rows(p, b);
+    const int D = p->D;
+    for (int64_t i = 0; i < s.lq; ++i) {
+        double *oi = orow(p, o, s.o0 + i, h);
+        for (int d = 0; d < D; ++d) oi[d] = 0.0;
+        double m = 0.0, l = 1.0;
+        if (softmax) {
+            int any = row_stats(p, h, &s, i, &m, &l);
+            if (lse) lse[(s.o0 + i) * p->H + h] = any ? m + log(l) : -INFINITY;
+            if (!any) continue;
+        }
+        for (int64_t j = 0; j < s.lk; ++j) {
+            if (!is_valid(p, i, j, s.lq, s.lk)) continue;
+            double x = score(p, h, &s, i, j);
+            double w = softmax ? exp(x - m) / l : act_f(p->act, x);
+            const float *vj = row_of(p, p->v, s.ks + j, h);
+            for (int d = 0; d < D; ++d) oi[d] += w * (double)vj[d];
+        }
+    }
+}
+
+/* Backward over one (sample, head) slice.  dQ rows of the sample and dK / dV
+ * rows of the sample belong to this slice alone, so no reduction across
+ * slices is needed (shared query blocks are not supported in backward). */
+static void bwd_slice(const problem *p, int softmax, int b, int h, const float *dout,
+                      double *dq, double *dk, double *dv, double *xrow, double *dprow) {
+    sample s = sample_rows(p, b);
+    const int D = p->D;
+    for (int64_t j = 0; j < s.lk; ++j) {
+        double *dkj = orow(p, dk, s.ks + j, h), *dvj = orow(p, dv, s.ks + j, h);
+        for (int d = 0; d < D; ++d) { dkj[d] = 0.0; dvj[d] = 0.0; }
+    }
+    for (int64_t i = 0; i < s.lq; ++i) {
+        double *dqi = orow(p, dq, s.qs + i, h);
+        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+        const float *doi = row_of(p, dout, s.o0 + i, h);
+        const float *qi = row_of(p, p->q, s.qs + i, h);
+        double m = 0.0, l = 1.0;
+        if (softmax && !row_stats(p, h, &s, i, &m, &l)) continue;
+        /* weights W_ij (act(X) or softmax P) and dP_ij for this row */
+        double delta = 0.0;
+        for (int64_t j = 0; j < s.lk; ++j) {
+            if (!is_valid(p, i, j, s.lq, s.lk)) continue;
+            xrow[j] = score(p, h, &s, i, j);
+            const float *vj = row_of(p, p->v, s.ks + j, h);
+            double dp = 0.0;
+            for (int d = 0; d < D; ++d) dp += (double)doi[d] * (double)vj[d];
+            dprow[j] = dp;
+            if (softmax) delta += exp(xrow[j] - m) / l * dp;
+        }
+        for (int64_t j = 0; j < s.lk; ++j) {
+            if (!is_valid(p, i, j, s.lq, s.lk)) continue;
+            double w, dx;
+            if (softmax) {
+                w = exp(xrow[j] - m) / l;
+                dx = w * (dprow[j] - delta);
+            } else {
+                w = act_f(p->act, xrow[j]);
+                dx = dprow[j] * act_grad(p->act, xrow[j]);
+            }
+            const float *kj = row_of(p, p->k, s.ks + j, h);
+            double *dkj = orow(p, dk, s.ks + j, h), *dvj = orow(p, dv, s.ks + j, h);
+            for (int d = 0; d < D; ++d) {
+                dqi[d] += p->scale * dx * (double)kj[d];
+                dkj[d] += p->scale * dx * (double)qi[d];
+                dvj[d] += w * (double)doi[d];
+            }
+        }
+    }
+}
+
+static int nthreads_or_default(int nthreads) {
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+static int max_lk(const problem *p) {
+    int64_t mx = 0;
+    for (int b = 0; b < p->B; ++b) {
+        int64_t lk = (int64_t)p->kv_off[b + 1] - p->kv_off[b];
+        if (lk > mx) mx = lk;
+    }
+    return (int)mx;
+}
+
+static problem make_problem(const float *q, const float *k, const float *v, const int32_t *q_off,
+                            int32_t lq_fixed, const int32_t *kv_off, int B, int H, int D, double scale,
+                            int act, int causal, int bias_kind, const float *bias_table, int bias_lo,
+                            int bias_hi) {
+    problem p;
+    p.q = q; p.k = k; p.v = v; p.q_off = q_off; p.kv_off = kv_off; p.lq_fixed = lq_fixed;
+    p.B = B; p.H = H; p.D = D; p.scale = scale; p.act = act; p.causal = causal;
+    p.bias_kind = bias_table ? bias_kind : BIAS_NONE; p.bias_table = bias_table;
+    p.bias_lo = bias_lo; p.bias_hi = bias_hi;
+    return p;
+}
+
+static void run_fwd(const problem *p, int softmax, double *o, double *lse, int nthreads) {
+    const int64_t n = (int64_t)p->B * p->H;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads_or_default(nthreads))
+    for (int64_t u = 0; u < n; ++u) fwd_slice(p, softmax, (int)(u / p->H), (int)(u % p->H), o, lse);
+}
+
+static int run_bwd(const problem *p, int softmax, const float *dout, double *dq, double *dk,
+                   double *dv, int nthreads) {
+    if (!p->q_off) return 1;
+    const int64_t n = (int64_t)p->B * p->H;
+    const int lkmax = max_lk(p) + 1;
+    int rc = 0;
+#pragma omp parallel num_threads(nthreads_or_default(nthreads))
+    {
+        double *xrow = (double *)malloc(sizeof(double) * lkmax);
+        double *dprow = (double *)malloc(sizeof(double) * lkmax);
+        if (!xrow || !dprow) {
+#pragma omp atomic write
+            rc = 2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < n; ++u)
+                bwd_slice(p, softmax, (int)(u / p->H), (int)(u % p->H), dout, dq, dk, dv, xrow, dprow);
+        }
+        free(xrow);
+        free(dprow);
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------ exported API */
+/* act: 0 SiLU, 1 GELU (tanh form), 2 GELU (erf form).
+ * bias_kind: 0 none, 1 REL (query minus key), 2 KEYPOS (key position).
+ * nthreads <= 0: OpenMP default.  Return 0 on success. */
+
+int ref_gdpa_fwd(const float *q, const float *k, const float *v, double *o, const int32_t *q_off,
+                 int32_t lq_fixed, const int32_t *kv_off, int B, int H, int D, double scale, int act,
+                 int causal, int bias_kind, const float *bias_table, int bias_lo, int bias_hi,
+                 int nthreads) {
+    problem p = make_problem(q, k, v, q_off, lq_fixed, kv_off, B, H, D, scale, act, causal, bias_kind,
+                             bias_table, bias_lo, bias_hi);
+    run_fwd(&p, 0, o, NULL, nthreads);
+    return 0;
+}
+
+/* lse: [total_q_out, H] (token-major, like the outputs). */
+int ref_attn_fwd(const float *q, const float *k, const float *v, double *o, double *lse,
+                 const int32_t *q_off, int32_t lq_fixed, const int32_t *kv_off, int B, int H, int D,
+                 double scale, int causal, int bias_kind, const float *bias_table, int bias_lo,
+                 int bias_hi, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, lq_fixed, kv_off, B, H, D, scale, ACT_SILU, causal,
+                             bias_kind, bias_table, bias_lo, bias_hi);
+    run_fwd(&p, 1, o, lse, nthreads);
+    return 0;
+}
+
+int ref_gdpa_bwd(const float *q, const float *k, const float *v, const float *dout, double *dq,
+                 double *dk, double *dv, const int32_t *q_off, const int32_t *kv_off, int B, int H,
+                 int D, double scale, int act, int causal, int bias_kind, const float *bias_table,
+                 int bias_lo, int bias_hi, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, bias_kind,
+                             bias_table, bias_lo, bias_hi);
+    return run_bwd(&p, 0, dout, dq, dk, dv, nthreads);
+}
+
+int ref_attn_bwd(const float *q, const float *k, const float *v, const float *dout, double *dq,
+                 double *dk, double *dv, const int32_t *q_off, const int32_t *kv_off, int B, int H,
+                 int D, double scale, int causal, int bias_kind, const float *bias_table, int bias_lo,
+                 int bias_hi, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, bias_kind,
+                             bias_table, bias_lo, bias_hi);
+    return run_bwd(&p, 1, dout, dq, dk, dv, nthreads);
+}
+
+/* Element-wise activation and derivative, exported so the tests can pin them
+ * against library implementations. */
+void ref_act(int act, const double *x, double *y, double *dy, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) {
+        y[i] = act_f(act, x[i]);
+        dy[i] = act_grad(act, x[i]);
+    }
+}
+
+int ref_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,278 @@
+"""Pin the fp64 oracle with identities, closed forms and finite differences.
+
+Each check below is fixed by mathematics rather than by re-typing the oracle:
+  * activations against torch's library SiLU / GELU and textbook normal-CDF values;
+  * per-sample identity: a jagged batch equals each sample run alone, and equals
+    torch's scaled_dot_product_attention (JFA) per sample;
+  * central finite differences of L = <O, dO> against the oracle's gradients;
+  * closed forms: one key, zero queries, all-ones values, constant bias, empty samples,
+    a hand-worked two-key example;
+  * JFA gradient identities: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import ref
+from recsys_jagged_attention_gdpa_amd import synth
+from tests.helpers import max_rel, oracle_bwd, oracle_fwd
+
+
+# ------------------------------------------------------------------ activations
+@pytest.mark.parametrize("name", ["silu", "gelu_tanh", "gelu_erf"])
+def test_activation_matches_torch_library(name):
+    x = np.linspace(-12, 12, 4001)
+    y, dy = ref.act(name, x)
+    xt = torch.from_numpy(x).requires_grad_(True)
+    fn = {"silu": F.silu, "gelu_tanh": lambda t: F.gelu(t, approximate="tanh"),
+          "gelu_erf": lambda t: F.gelu(t, approximate="none")}[name]
+    yt = fn(xt)
+    yt.sum().backward()
+    assert np.abs(y - yt.detach().numpy()).max() <= 1e-14
+    assert np.abs(dy - xt.grad.numpy()).max() <= 1e-13
+
+
+def test_activation_textbook_values():
+    # Standard normal CDF and density at 1 (printed in every normal table).
+    phi1, pdf1 = 0.8413447460685429, 0.24197072451914337
+    y, dy = ref.act("gelu_erf", [1.0, 0.0, -1.0])
+    assert abs(y[0] - phi1) < 1e-15 and y[1] == 0.0 and abs(y[2] + (1 - phi1)) < 1e-15
+    assert abs(dy[0] - (phi1 + pdf1)) < 1e-15 and abs(dy[1] - 0.5) < 1e-15
+    # SiLU(ln 3) = ln 3 * sigmoid(ln 3) = 0.75 ln 3; SiLU'(0) = 1/2.
+    y, dy = ref.act("silu", [math.log(3.0), 0.0])
+    assert abs(y[0] - 0.75 * math.log(3.0)) < 1e-15 and y[1] == 0.0 and dy[1] == 0.5
+    y, dy = ref.act("gelu_tanh", [0.0])
+    assert y[0] == 0.0 and dy[0] == 0.5
+
+
+# --------------------------------------------------------- per-sample identities
+def _w(mode, seed, **kw):
+    base = dict(lq=[9, 0, 23, 1, 17], lk=[9, 5, 23, 1, 0], H=2, D=16, dtype=torch.float32,
+                seed=seed, mode=mode)
+    base.update(kw)
+    return synth.custom(**base)
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_batch_equals_samples_alone_bitwise(mode, causal):
+    w = _w(mode, 1, causal=causal, bias_kind="rel", bias_lo=-4, bias_hi=6, act="gelu_erf")
+    full = oracle_fwd(w)
+    full.update(oracle_bwd(w))
+    for b in range(w.B):
+        s = w.subset([b])
+        one = oracle_fwd(s)
+        one.update(oracle_bwd(s))
+        q0, q1 = int(w.q_off[b]), int(w.q_off[b + 1])
+        k0, k1 = int(w.kv_off[b]), int(w.kv_off[b + 1])
+        assert np.array_equal(one["o"], full["o"][q0:q1])
+        assert np.array_equal(one["dq"], full["dq"][q0:q1])
+        assert np.array_equal(one["dk"], full["dk"][k0:k1])
+        assert np.array_equal(one["dv"], full["dv"][k0:k1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_jfa_per_sample_matches_torch_sdpa(causal):
+    w = _w("jfa", 2, causal=causal, bias_kind="keypos", bias_lo=0, bias_hi=12)
+    got = oracle_fwd(w)
+    got.update(oracle_bwd(w))
+    for b in range(w.B):
+        lq, lk = int(w.lq[b]), int(w.lk[b])
+        if lq == 0 or lk == 0:
+            continue
+        q0, k0 = int(w.q_off[b]), int(w.kv_off[b])
+        q = w.q[q0:q0 + lq].double().permute(1, 0, 2).clone().requires_grad_(True)
+        k = w.k[k0:k0 + lk].double().permute(1, 0, 2).clone().requires_grad_(True)
+        v = w.v[k0:k0 + lk].double().permute(1, 0, 2).clone().requires_grad_(True)
+        i = torch.arange(lq).view(-1, 1)
+        j = torch.arange(lk).view(1, -1)
+        allowed = (j <= i + lk - lq) if causal else torch.ones(lq, lk, dtype=torch.bool)
+        bias = w.bias_table.double()[:, j.clamp(0, 12).expand(lq, lk)]
+        mask = bias.masked_fill(~allowed, float("-inf"))
+        rows = allowed.any(-1)
+        o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=w.scale)
+        o = torch.where(rows.view(1, -1, 1), o, torch.zeros_like(o))
+        do = w.dout[q0:q0 + lq].double().permute(1, 0, 2)
+        (o * do).sum().backward()
+        o_ref = o.detach().permute(1, 0, 2).numpy()
+        r = rows.numpy()
+        assert max_rel(got["o"][q0:q0 + lq][r], o_ref[r]) <= 1e-12
+        assert max_rel(got["dq"][q0:q0 + lq][r], q.grad.permute(1, 0, 2).numpy()[r]) <= 1e-11
+        assert max_rel(got["dk"][k0:k0 + lk], k.grad.permute(1, 0, 2).numpy()) <= 1e-11
+        assert max_rel(got["dv"][k0:k0 + lk], v.grad.permute(1, 0, 2).numpy()) <= 1e-11
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+def test_shared_query_block_equals_materialised(mode):
+    ws = synth.custom(mode=mode, lq=None, lk=[7, 0, 30, 2], H=2, D=16, dtype=torch.float32,
+                      seed=4, shared_q=6, bias_kind="keypos", bias_lo=0, bias_hi=15,
+                      with_dout=False)
+    qm = ws.q.repeat(ws.B, 1, 1)
+    wm = synth.Workload(**{**ws.__dict__, "q": qm, "lq_fixed": 0,
+                           "q_off": (np.arange(ws.B + 1) * 6).astype(np.int32)})
+    a, b = oracle_fwd(ws), oracle_fwd(wm)
+    assert np.array_equal(a["o"], b["o"])
+    if mode == "jfa":
+        assert np.array_equal(a["lse"], b["lse"])
+
+
+# ---------------------------------------------------------- finite differences
+def _loss(w, q, k, v):
+    w2 = synth.Workload(**{**w.__dict__, "q": q, "k": k, "v": v})
+    return float((oracle_fwd(w2)["o"] * w.dout.double().numpy()).sum())
+
+
+@pytest.mark.parametrize("mode,act,causal,bias", [
+    ("gdpa", "silu", False, "none"), ("gdpa", "gelu_tanh", True, "rel"),
+    ("gdpa", "gelu_erf", False, "keypos"), ("jfa", "silu", True, "rel"),
+    ("jfa", "silu", False, "keypos")])
+def test_gradients_match_central_differences(mode, act, causal, bias):
+    w = _w(mode, 7, act=act, causal=causal, bias_kind=bias, bias_lo=-3 if bias == "rel" else 0,
+           bias_hi=5, dtype=torch.bfloat16)
+    # bf16-valued inputs held in float32, so x +- 2^-14 is exact in float32.
+    q, k, v = (t.float() for t in (w.q, w.k, w.v))
+    w = synth.Workload(**{**w.__dict__, "q": q, "k": k, "v": v, "dout": w.dout.float()})
+    g = oracle_bwd(w)
+    rng = np.random.default_rng(99)
+    h = 2.0 ** -14
+    for name, base in (("dq", q), ("dk", k), ("dv", v)):
+        for _ in range(2):
+            d = torch.from_numpy(rng.integers(-1, 2, size=tuple(base.shape)).astype(np.float32) * h)
+            plus, minus = base + d, base - d
+            assert torch.equal((plus.double() - base.double()), d.double())
+            assert torch.equal((base.double() - minus.double()), d.double())
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name[1]] = plus
+            args_m[name[1]] = minus
+            fd = (_loss(w, **args_p) - _loss(w, **args_m)) / 2.0
+            an = float((g[name] * d.double().numpy()).sum())
+            assert abs(fd - an) <= 1e-7 * max(abs(an), 1e-3), (name, fd, an)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_hand_worked_two_key_example():
+    # One sample, one query, two keys, D = 2, scale 1.  q = (1, 0), k0 = (0, 0),
+    # k1 = (ln 3, 0) give scores 0 and ln 3; softmax weights 1/4, 3/4.
+    # v0 = (4, 0), v1 = (0, 8): JFA O = (1, 6), LSE = ln 4.
+    # GDPA-SiLU: weights SiLU(0) = 0 and SiLU(ln 3) = 0.75 ln 3: O = (0, 6 ln 3).
+    q = torch.tensor([[[1.0, 0.0]]])
+    k = torch.tensor([[[0.0, 0.0]], [[math.log(3.0), 0.0]]])
+    v = torch.tensor([[[4.0, 0.0]], [[0.0, 8.0]]])
+    qo, ko = np.array([0, 1], np.int32), np.array([0, 2], np.int32)
+    o, lse = ref.attn_fwd(q, k, v, qo, ko, scale=1.0)
+    k32 = np.float32(math.log(3.0))  # the score is the float32 ln 3 the input holds
+    assert np.allclose(o[0, 0], [1.0, 6.0], rtol=0, atol=1e-6)
+    e = math.exp(float(k32))
+    assert abs(o[0, 0, 0] - 4.0 / (1 + e)) < 1e-15 and abs(o[0, 0, 1] - 8.0 * e / (1 + e)) < 1e-14
+    assert abs(lse[0, 0] - math.log(1 + e)) < 1e-15
+    o = ref.gdpa_fwd(q, k, v, qo, ko, scale=1.0, act="silu")
+    x = float(k32)
+    assert o[0, 0, 0] == 0.0 and abs(o[0, 0, 1] - 8.0 * x / (1 + math.exp(-x))) < 1e-14
+
+
+def test_single_key_closed_forms():
+    w = _w("jfa", 11, lq=[5, 3], lk=[1, 1], bias_kind="rel", bias_lo=-2, bias_hi=2)
+    o = oracle_fwd(w)
+    for b in range(2):
+        q0, q1 = int(w.q_off[b]), int(w.q_off[b + 1])
+        k0 = int(w.kv_off[b])
+        # softmax over one key is 1: O = v_0 exactly; LSE = the score itself
+        assert np.array_equal(o["o"][q0:q1], np.broadcast_to(w.v[k0].double().numpy(), (q1 - q0, 2, 16)))
+        for i in range(q1 - q0):
+            for h in range(2):
+                x = w.scale * float((w.q[q0 + i, h].double() * w.k[k0, h].double()).sum())
+                x += float(w.bias_table[h, min(max(i, -2), 2) + 2])
+                assert abs(o["lse"][q0 + i, h] - x) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_closed_forms(causal):
+    for mode in ("gdpa", "jfa"):
+        w = _w(mode, 12, causal=causal, act="gelu_tanh")
+        w = synth.Workload(**{**w.__dict__, "q": torch.zeros_like(w.q)})
+        o = oracle_fwd(w)
+        if mode == "gdpa":
+            assert np.all(o["o"] == 0.0)  # act(0) = 0 for SiLU and both GELUs
+            continue
+        for b in range(w.B):
+            lq, lk = int(w.lq[b]), int(w.lk[b])
+            q0, k0 = int(w.q_off[b]), int(w.kv_off[b])
+            for i in range(lq):
+                n = lk if not causal else max(0, min(lk, i + lk - lq + 1))
+                if n == 0:
+                    assert np.all(o["o"][q0 + i] == 0) and np.all(np.isneginf(o["lse"][q0 + i]))
+                    continue
+                mean = w.v[k0:k0 + n].double().mean(0).numpy()
+                assert np.abs(o["o"][q0 + i] - mean).max() < 1e-13
+                assert np.abs(o["lse"][q0 + i] - math.log(n)).max() < 1e-13
+
+
+def test_gdpa_all_ones_values_gives_activation_sums():
+    w = _w("gdpa", 13, act="gelu_erf", bias_kind="rel", bias_lo=-3, bias_hi=3)
+    w = synth.Workload(**{**w.__dict__, "v": torch.ones_like(w.v)})
+    o = oracle_fwd(w)["o"]
+    # every feature of a row carries the same sum of activations
+    assert np.all(o == o[..., :1])
+
+
+def test_jfa_constant_bias_shifts_lse_only():
+    w = _w("jfa", 14, causal=True)
+    c = 0.625
+    wc = synth.Workload(**{**w.__dict__, "bias_kind": "keypos", "bias_lo": 0, "bias_hi": 3,
+                           "bias_table": torch.full((2, 4), c)})
+    a, b = oracle_fwd(w), oracle_fwd(wc)
+    assert max_rel(b["o"], a["o"]) < 1e-13
+    fin = np.isfinite(a["lse"])
+    assert np.abs(b["lse"][fin] - a["lse"][fin] - c).max() < 1e-13
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+def test_empty_samples_and_rows(mode):
+    w = _w(mode, 15, lq=[0, 4, 0, 3], lk=[0, 0, 6, 2])
+    o = oracle_fwd(w)
+    g = oracle_bwd(w)
+    # sample 1 has queries but no keys: zero output, -inf LSE, zero dQ
+    assert np.all(o["o"][0:4] == 0) and np.all(g["dq"][0:4] == 0)
+    if mode == "jfa":
+        assert np.all(np.isneginf(o["lse"][0:4]))
+    # sample 2 has keys but no queries: zero dK, dV
+    assert np.all(g["dk"][0:6] == 0) and np.all(g["dv"][0:6] == 0)
+
+
+def test_gdpa_is_linear_in_values_and_gradients_linear_in_dout():
+    w = _w("gdpa", 16, act="silu")
+    # bf16-valued operands so that 2 v + v2 is exact in float32
+    w = synth.Workload(**{**w.__dict__, "v": w.v.bfloat16().float(),
+                          "dout": w.dout.bfloat16().float()})
+    v2 = torch.randn(w.v.shape, generator=torch.Generator().manual_seed(3)).bfloat16().float()
+    assert torch.equal((2.0 * w.v + v2).double(), 2.0 * w.v.double() + v2.double())
+    a = oracle_fwd(w)["o"]
+    b = oracle_fwd(synth.Workload(**{**w.__dict__, "v": v2}))["o"]
+    c = oracle_fwd(synth.Workload(**{**w.__dict__, "v": 2.0 * w.v + v2}))["o"]
+    assert max_rel(c, 2.0 * a + b) < 1e-13
+    g1 = oracle_bwd(w)
+    g3 = oracle_bwd(synth.Workload(**{**w.__dict__, "dout": 3.0 * w.dout}))
+    for n in ("dq", "dk", "dv"):
+        assert max_rel(g3[n], 3.0 * g1[n]) < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_jfa_gradient_sum_identities(causal):
+    w = _w("jfa", 17, causal=causal, bias_kind="rel", bias_lo=-5, bias_hi=5)
+    g = oracle_bwd(w)
+    o = oracle_fwd(w)
+    for b in range(w.B):
+        lq, lk = int(w.lq[b]), int(w.lk[b])
+        q0, k0 = int(w.q_off[b]), int(w.kv_off[b])
+        if lk == 0:
+            continue
+        dk = g["dk"][k0:k0 + lk].sum(0)
+        scale_ref = max(np.abs(g["dk"][k0:k0 + lk]).max(), 1e-300)
+        assert np.abs(dk).max() <= 1e-12 * scale_ref * lk
+        rows = np.isfinite(o["lse"][q0:q0 + lq])  # [lq, H]
+        do = w.dout[q0:q0 + lq].double().numpy() * rows[..., None]
+        assert np.abs(g["dv"][k0:k0 + lk].sum(0) - do.sum(0)).max() < 1e-12 * max(lq, 1)

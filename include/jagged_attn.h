@@ -1,0 +1,151 @@
+/*
+ * jagged_attn.h — C ABI of the MI355X (gfx950) jagged attention library.
+ *
+ * Two attention forms over jagged (variable-length, unpadded) batches, with
+ * forward and backward passes:
+ *
+ *   GDPA (generalized dot-product attention):
+ *       O_i = sum_{valid j} act(scale * <q_i, k_j> + bias_ij) v_j
+ *     act is SiLU or GELU and there is no row normalisation.  The pages
+ *     describe the attention-like modules as two matrix products with an
+ *     element-wise activation in between, GELU or SiLU replacing softmax
+ *     ("GEM Training: How Meta Doubled the Efficiency...", section
+ *     "What to watch"; "Meta redesigns AI training infrastructure...", section
+ *     "Custom Kernels and 5D Parallelism for Trillion-Parameter Scale").
+ *
+ *   JFA (jagged flash attention):
+ *       O_i = sum_{valid j} softmax_j(scale * <q_i, k_j> + bias_ij) v_j
+ *     FlashAttention run directly on jagged tensors with custom attention
+ *     biases, asymmetric query / key-value lengths and a backward pass
+ *     ("GEM Training...", section "What happened"; "Meta redesigns...",
+ *     section "Eliminating Compute Waste in Asymmetric Workloads").
+ *
+ * Data layout.  Values are token-major [T, H, D], contiguous (row stride H*D
+ * elements), bf16 or fp32.  Sample b owns query rows q_offsets[b] ..
+ * q_offsets[b+1]-1 and key / value rows kv_offsets[b] .. kv_offsets[b+1]-1;
+ * offsets are int32 [B+1], start at 0, never decrease and end at the row
+ * count.  Samples may be empty.  Within a sample, i and j are 0-based local
+ * positions and a pair (i, j) is valid iff j < Lk and, with causal masking,
+ * j <= i + Lk - Lq (bottom-right alignment; j <= i when Lq == Lk).
+ *
+ * Shared query block.  With q_offsets == NULL, q holds lq_fixed rows
+ * ([lq_fixed, H, D]) that every sample attends with (pooling by learned seed
+ * queries); the output still has one row block per sample:
+ * [B * lq_fixed, H, D], sample b at rows b * lq_fixed.  Forward only.
+ *
+ * Bias.  An fp32 table [H][bias_hi - bias_lo + 1] on the device, added after
+ * the scale, before the activation / softmax:
+ *   JA_BIAS_REL     table[h][clamp(i - j, bias_lo, bias_hi) - bias_lo]
+ *   JA_BIAS_KEYPOS  table[h][clamp(j, bias_lo, bias_hi) - bias_lo]
+ * No gradient is produced for the table.
+ *
+ * Ownership.  Every buffer belongs to the caller, including the workspace
+ * (ja_workspace_size bytes, 256-byte aligned, device memory).  The library
+ * allocates no device memory and keeps no state between calls besides loaded
+ * code objects; it may be called from several host threads on different
+ * streams with different workspaces.  Calls sharing one workspace must be
+ * ordered (same stream).
+ *
+ * Errors.  The return code is the only error channel.  Host-visible arguments
+ * are checked before anything is launched; on any error nothing is launched
+ * and no output is touched.  Offsets live in device memory and are not read by
+ * the host: offsets that break the rules above give undefined results.
+ *
+ * Asynchrony.  Every entry point enqueues its kernels on `stream` (a
+ * hipStream_t, NULL for the default stream) and returns without waiting.
+ * Outputs are fully overwritten (never accumulated); rows with no valid key
+ * get O = 0 (JFA: LSE = -inf) and all their gradients are 0.
+ */
+#ifndef JAGGED_ATTN_H
+#define JAGGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    JA_OK = 0,
+    JA_ERR_NULL = 1,        /* a required pointer is NULL */
+    JA_ERR_SHAPE = 2,       /* B, H, D, total rows or bias range out of range */
+    JA_ERR_UNSUPPORTED = 3, /* dtype / head_dim / act / bias kind / shared-query backward */
+    JA_ERR_WORKSPACE = 4,   /* workspace NULL, misaligned or smaller than ja_workspace_size */
+    JA_ERR_HIP = 6          /* a HIP launch failed (the HIP error is in ja_last_hip_error) */
+} ja_status;
+
+typedef enum { JA_BF16 = 0, JA_F32 = 1 } ja_dtype;
+typedef enum { JA_ACT_SILU = 0, JA_ACT_GELU_TANH = 1, JA_ACT_GELU_ERF = 2 } ja_act;
+typedef enum { JA_BIAS_NONE = 0, JA_BIAS_REL = 1, JA_BIAS_KEYPOS = 2 } ja_bias_kind;
+typedef enum { JA_PASS_FWD = 0, JA_PASS_BWD = 1 } ja_pass;
+
+/* Problem description: sizes by value, device pointers to the offsets and the
+ * bias table.  The struct itself is read on the host during the call only. */
+typedef struct ja_problem {
+    int32_t batch;               /* B >= 1 samples */
+    int32_t heads;               /* H >= 1 */
+    int32_t head_dim;            /* D in {32, 64, 128} */
+    int32_t dtype;               /* ja_dtype of q, k, v, o, dout, dq, dk, dv */
+    int64_t total_q;             /* rows of q: q_offsets[B], or lq_fixed when shared */
+    int64_t total_k;             /* rows of k and v: kv_offsets[B] */
+    const int32_t *q_offsets;    /* device [B+1], or NULL for a shared query block */
+    int32_t lq_fixed;            /* rows of the shared query block (q_offsets == NULL) */
+    int32_t causal;              /* 0 or 1 */
+    const int32_t *kv_offsets;   /* device [B+1] */
+    float scale;                 /* multiplies <q, k> (commonly 1/sqrt(D)) */
+    int32_t act;                 /* ja_act (GDPA only; ignored by JFA) */
+    int32_t bias_kind;           /* ja_bias_kind */
+    int32_t bias_lo, bias_hi;    /* bias index range, bias_lo <= bias_hi */
+    const float *bias_table;     /* device fp32 [H][bias_hi - bias_lo + 1], or NULL when no bias */
+} ja_problem;
+
+/* Workspace bytes that the given pass of either attention form needs (0 only
+ * for invalid problems).  Depends on B, H, D, total_q, total_k, lq_fixed and
+ * dtype; the same value serves GDPA and JFA. */
+size_t ja_workspace_size(const ja_problem *p, int pass);
+
+/* GDPA forward.  q [Tq, H, D] (or [lq_fixed, H, D]), k, v [Tk, H, D],
+ * o [Tq_out, H, D] written. */
+ja_status jagged_gdpa_fwd(const ja_problem *p, const void *q, const void *k, const void *v, void *o,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* GDPA backward of L = <O, dout>: dq [Tq, H, D], dk, dv [Tk, H, D] written.
+ * Needs q_offsets (no shared query block). */
+ja_status jagged_gdpa_bwd(const ja_problem *p, const void *q, const void *k, const void *v,
+                          const void *dout, void *dq, void *dk, void *dv, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* JFA forward.  o as for GDPA; lse fp32 [H, Tq_out] (head-major) receives the
+ * natural-log row log-sum-exp of the scores, -inf for rows with no valid key.
+ * o_residual (optional, NULL to skip; bf16 only, same shape as o) receives
+ * fp32(O) - bf16(O), the rounding residual of the bf16 output. */
+ja_status jagged_attn_fwd(const ja_problem *p, const void *q, const void *k, const void *v, void *o,
+                          float *lse, void *o_residual, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* JFA backward: takes the forward's o and lse; dq, dk, dv written.  The softmax
+ * backward needs delta_i = <dO_i, O_i>.  With o_residual NULL it is formed from
+ * the bf16 o alone (as FlashAttention does): o's rounding then perturbs every
+ * dS_ij of a row by P_ij times that error, which dominates rows whose gradient
+ * is small by cancellation.  Passing the forward's o_residual forms delta from
+ * o + o_residual, exact to fp32 rounding.  Ignored for fp32 tensors. */
+ja_status jagged_attn_bwd(const ja_problem *p, const void *q, const void *k, const void *v,
+                          const void *o, const void *o_residual, const void *dout,
+                          const float *lse, void *dq, void *dk, void *dv, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *ja_status_string(int status);
+
+/* The HIP error code of the most recent JA_ERR_HIP in the calling thread. */
+int ja_last_hip_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int ja_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JAGGED_ATTN_H */

@@ -1,0 +1,161 @@
+"""ctypes binding of libjagged_attn.so (include/jagged_attn.h).
+
+The functions named like the C entry points only marshal arguments: tensors
+become device pointers, the problem becomes a ``JaProblem`` struct and the
+stream is torch's current stream.  Every step of the computation runs in the
+library's HIP kernels; if the library is missing this module raises instead of
+falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libjagged_attn.so")
+
+JA_OK = 0
+STATUS = {0: "JA_OK", 1: "JA_ERR_NULL", 2: "JA_ERR_SHAPE", 3: "JA_ERR_UNSUPPORTED",
+          4: "JA_ERR_WORKSPACE", 6: "JA_ERR_HIP"}
+DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+ACTS = {"silu": 0, "gelu_tanh": 1, "gelu_erf": 2}
+BIAS = {"none": 0, "rel": 1, "keypos": 2}
+PASS_FWD, PASS_BWD = 0, 1
+
+EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_attn_fwd",
+           "jagged_attn_bwd", "ja_status_string", "ja_last_hip_error", "ja_version")
+
+
+class JaProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
+        ("q_offsets", ctypes.c_void_p), ("lq_fixed", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("kv_offsets", ctypes.c_void_p), ("scale", ctypes.c_float), ("act", ctypes.c_int32),
+        ("bias_kind", ctypes.c_int32), ("bias_lo", ctypes.c_int32), ("bias_hi", ctypes.c_int32),
+        ("bias_table", ctypes.c_void_p),
+    ]
+
+
+class JaError(RuntimeError):
+    def __init__(self, fn, status, lib):
+        self.status = status
+        msg = lib.ja_status_string(status).decode()
+        extra = f" (hip error {lib.ja_last_hip_error()})" if status == 6 else ""
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {msg}{extra}")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load(path: str = LIB_PATH):
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m recsys_jagged_attention_gdpa_amd.build`")
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        PP = ctypes.POINTER(JaProblem)
+        lib.ja_workspace_size.argtypes = [PP, ctypes.c_int]
+        lib.ja_workspace_size.restype = ctypes.c_size_t
+        lib.jagged_gdpa_fwd.argtypes = [PP, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.jagged_attn_fwd.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.jagged_gdpa_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.jagged_attn_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        for f in (lib.jagged_gdpa_fwd, lib.jagged_attn_fwd, lib.jagged_gdpa_bwd, lib.jagged_attn_bwd):
+            f.restype = ctypes.c_int
+        lib.ja_status_string.argtypes = [ctypes.c_int]
+        lib.ja_status_string.restype = ctypes.c_char_p
+        lib.ja_last_hip_error.argtypes = []
+        lib.ja_last_hip_error.restype = ctypes.c_int
+        lib.ja_version.argtypes = []
+        lib.ja_version.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(stream)
+
+
+def make_problem(*, batch, heads, head_dim, dtype, total_q, total_k, q_offsets, kv_offsets,
+                 lq_fixed=0, causal=False, scale=None, act="silu", bias_kind="none",
+                 bias_table=None, bias_lo=0, bias_hi=0) -> JaProblem:
+    """Fill a JaProblem.  Offsets and the bias table are device tensors (or raw pointers)."""
+    p = JaProblem()
+    p.batch, p.heads, p.head_dim = int(batch), int(heads), int(head_dim)
+    p.dtype = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    p.total_q, p.total_k = int(total_q), int(total_k)
+    p.q_offsets = _ptr(q_offsets)
+    p.lq_fixed = int(lq_fixed)
+    p.causal = int(bool(causal))
+    p.kv_offsets = _ptr(kv_offsets)
+    p.scale = float(head_dim ** -0.5 if scale is None else scale)
+    p.act = ACTS[act] if isinstance(act, str) else int(act)
+    p.bias_kind = BIAS[bias_kind] if isinstance(bias_kind, str) else int(bias_kind)
+    p.bias_lo, p.bias_hi = int(bias_lo), int(bias_hi)
+    p.bias_table = _ptr(bias_table)
+    return p
+
+
+def _check(fn, status):
+    if status != JA_OK:
+        raise JaError(fn, status, load())
+
+
+# ---- same-name wrappers of the C entry points (argument marshalling only) ----
+def ja_workspace_size(problem: JaProblem, pass_: int) -> int:
+    return int(load().ja_workspace_size(ctypes.byref(problem), int(pass_)))
+
+
+def jagged_gdpa_fwd(problem, q, k, v, o, workspace, stream=None):
+    _check("jagged_gdpa_fwd", load().jagged_gdpa_fwd(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
+
+
+def jagged_attn_fwd(problem, q, k, v, o, lse, o_residual, workspace, stream=None):
+    _check("jagged_attn_fwd", load().jagged_attn_fwd(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o_residual),
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def jagged_gdpa_bwd(problem, q, k, v, dout, dq, dk, dv, workspace, stream=None):
+    _check("jagged_gdpa_bwd", load().jagged_gdpa_bwd(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def jagged_attn_bwd(problem, q, k, v, o, o_residual, dout, lse, dq, dk, dv, workspace, stream=None):
+    _check("jagged_attn_bwd", load().jagged_attn_bwd(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_residual), _ptr(dout),
+        _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
+
+
+def _nbytes(t):
+    if t is None:
+        return 0
+    if isinstance(t, torch.Tensor):
+        return t.numel() * t.element_size()
+    raise TypeError("workspace must be a torch tensor")

@@ -1,0 +1,263 @@
+// C-ABI host layer: argument checks, workspace layout, kernel launches.
+// The declarations and their contracts are in include/jagged_attn.h.
+#include "jagged_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdint>
+
+#include "ja_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_DEVICES = 64;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Compute units of the current device, cached per device.
+int cu_count() {
+    static std::atomic<int> cache[MAX_DEVICES];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int64_t total_q_out(const ja_problem &p) {
+    return p.q_offsets ? p.total_q : (int64_t)p.batch * p.lq_fixed;
+}
+
+// Capacity of a unit list cutting `rows` jagged rows of B samples into tiles of `tile` rows.
+int64_t tile_cap(int64_t rows, int B, int tile) { return rows / tile + B + 1; }
+
+struct Layout {
+    size_t counters;  // 3 PlanCounters blocks
+    size_t tiles_q, tiles_k, tiles_s, delta, total;
+    int64_t cap_q, cap_k, cap_s;
+};
+
+Layout layout_of(const ja_problem &p, int pass) {
+    Layout L{};
+    const int64_t tq = p.q_offsets ? p.total_q : (int64_t)p.lq_fixed * p.batch;
+    L.cap_q = tile_cap(tq, p.batch, ja::Q_TILE);
+    L.cap_k = tile_cap(p.total_k, p.batch, ja::BWD_KV_UNIT);
+    L.cap_s = (int64_t)p.batch + 1;
+    size_t off = 0;
+    L.counters = off;
+    off += align_up(3 * sizeof(ja::PlanCounters));
+    L.tiles_q = off;
+    off += align_up((size_t)L.cap_q * sizeof(int2));
+    if (pass == JA_PASS_BWD) {
+        L.tiles_k = off;
+        off += align_up((size_t)L.cap_k * sizeof(int2));
+        L.tiles_s = off;
+        off += align_up((size_t)L.cap_s * sizeof(int2));
+        L.delta = off;
+        off += align_up((size_t)p.heads * (size_t)(p.total_q > 0 ? p.total_q : 1) * sizeof(float));
+    }
+    L.total = off;
+    return L;
+}
+
+ja_status check_problem(const ja_problem *p, int pass) {
+    if (!p) return JA_ERR_NULL;
+    if (p->batch < 1 || p->heads < 1) return JA_ERR_SHAPE;
+    if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) return JA_ERR_UNSUPPORTED;
+    if (p->dtype != JA_BF16 && p->dtype != JA_F32) return JA_ERR_UNSUPPORTED;
+    if (p->act < JA_ACT_SILU || p->act > JA_ACT_GELU_ERF) return JA_ERR_UNSUPPORTED;
+    if (p->bias_kind < JA_BIAS_NONE || p->bias_kind > JA_BIAS_KEYPOS) return JA_ERR_UNSUPPORTED;
+    if (p->causal != 0 && p->causal != 1) return JA_ERR_UNSUPPORTED;
+    if (!p->kv_offsets) return JA_ERR_NULL;
+    if (p->total_q < 0 || p->total_k < 0 || p->total_q > INT_MAX || p->total_k > INT_MAX) return JA_ERR_SHAPE;
+    if (!p->q_offsets) {
+        if (pass == JA_PASS_BWD) return JA_ERR_UNSUPPORTED;
+        if (p->lq_fixed < 0 || p->total_q != p->lq_fixed) return JA_ERR_SHAPE;
+        if ((int64_t)p->lq_fixed * p->batch > INT_MAX) return JA_ERR_SHAPE;
+    }
+    if (p->bias_kind != JA_BIAS_NONE) {
+        if (!p->bias_table) return JA_ERR_NULL;
+        if (p->bias_lo > p->bias_hi) return JA_ERR_SHAPE;
+        if ((int64_t)p->bias_hi - p->bias_lo + 1 > (1 << 24)) return JA_ERR_SHAPE;
+    }
+    if (!(p->scale == p->scale)) return JA_ERR_SHAPE;  // NaN scale
+    // Work-unit counts (tiles x heads) must fit in int32.
+    const Layout L = layout_of(*p, pass);
+    const int64_t cap = L.cap_q > L.cap_k ? L.cap_q : L.cap_k;
+    if (cap * p->heads > INT_MAX) return JA_ERR_SHAPE;
+    if (total_q_out(*p) * p->heads > (int64_t)INT_MAX * 64) return JA_ERR_SHAPE;
+    return JA_OK;
+}
+
+ja_status check_workspace(const ja_problem *p, int pass, void *ws, size_t bytes) {
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return JA_ERR_WORKSPACE;
+    if (bytes < layout_of(*p, pass).total) return JA_ERR_WORKSPACE;
+    return JA_OK;
+}
+
+ja::AttnParams base_params(const ja_problem &p, const Layout &L, void *ws) {
+    ja::AttnParams a{};
+    char *w = static_cast<char *>(ws);
+    a.q_off = p.q_offsets;
+    a.kv_off = p.kv_offsets;
+    a.lq_fixed = p.lq_fixed;
+    a.B = p.batch;
+    a.H = p.heads;
+    a.total_q_out = total_q_out(p);
+    a.total_q = p.total_q;
+    a.total_k = p.total_k;
+    a.scale = p.scale;
+    a.causal = p.causal;
+    a.bias_kind = p.bias_kind;
+    a.bias_lo = p.bias_lo;
+    a.bias_hi = p.bias_hi;
+    a.bias = p.bias_kind != JA_BIAS_NONE ? p.bias_table : nullptr;
+    if (a.bias == nullptr) a.bias_kind = JA_BIAS_NONE;
+    auto *ctr = reinterpret_cast<ja::PlanCounters *>(w + L.counters);
+    a.counters = ctr;
+    a.counters2 = ctr + 1;
+    a.counters3 = ctr + 2;
+    a.tiles = reinterpret_cast<const int2 *>(w + L.tiles_q);
+    a.tiles2 = reinterpret_cast<const int2 *>(w + L.tiles_k);
+    a.tiles3 = reinterpret_cast<const int2 *>(w + L.tiles_s);
+    a.delta = reinterpret_cast<float *>(w + L.delta);
+    return a;
+}
+
+ja::PlanParams plan_of(const ja_problem &p, int kind, int tile_rows, int inner_rows, int only_short,
+                       const int2 *tiles, int64_t cap, ja::PlanCounters *ctr) {
+    ja::PlanParams q{};
+    q.q_off = p.q_offsets;
+    q.kv_off = p.kv_offsets;
+    q.lq_fixed = p.lq_fixed;
+    q.B = p.batch;
+    q.H = p.heads;
+    q.causal = p.causal;
+    q.kind = kind;
+    q.tile_rows = tile_rows;
+    q.inner_rows = inner_rows;
+    q.only_short = only_short;
+    q.tiles = const_cast<int2 *>(tiles);
+    q.max_tiles = (int)cap;
+    q.counters = ctr;
+    return q;
+}
+
+ja_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return JA_OK;
+    g_last_hip_error = (int)e;
+    return JA_ERR_HIP;
+}
+
+ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, const void *v, void *o, float *lse,
+                  void *o_res, void *ws, size_t ws_bytes, void *stream) {
+    ja_status st = check_problem(p, JA_PASS_FWD);
+    if (st != JA_OK) return st;
+    if (!q || !k || !v || !o) return JA_ERR_NULL;
+    if (mode == 1 && !lse) return JA_ERR_NULL;
+    st = check_workspace(p, JA_PASS_FWD, ws, ws_bytes);
+    if (st != JA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Layout L = layout_of(*p, JA_PASS_FWD);
+    ja::AttnParams a = base_params(*p, L, ws);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = o;
+    a.lse = lse;
+    a.o_res_out = p->dtype == JA_BF16 ? o_res : nullptr;
+    if (p->dtype == JA_F32) return hip_status(ja::launch_fwd_f32(a, p->head_dim, mode, p->act, s));
+    ja::PlanParams pp[1] = {plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 0, a.tiles, L.cap_q, a.counters)};
+    hipError_t e = ja::launch_plan(pp, 1, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(ja::launch_fwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), s));
+}
+
+ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, const void *v, const void *o,
+                  const void *o_res, const void *dout, const float *lse, void *dq, void *dk, void *dv, void *ws,
+                  size_t ws_bytes, void *stream) {
+    ja_status st = check_problem(p, JA_PASS_BWD);
+    if (st != JA_OK) return st;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return JA_ERR_NULL;
+    if (mode == 1 && (!o || !lse)) return JA_ERR_NULL;
+    st = check_workspace(p, JA_PASS_BWD, ws, ws_bytes);
+    if (st != JA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Layout L = layout_of(*p, JA_PASS_BWD);
+    ja::AttnParams a = base_params(*p, L, ws);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.o_res = p->dtype == JA_BF16 ? o_res : nullptr;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.lse = const_cast<float *>(lse);
+    if (p->dtype == JA_F32) return hip_status(ja::launch_bwd_f32(a, p->head_dim, mode, p->act, s));
+    ja::PlanParams pp[3] = {
+        plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 1, a.tiles, L.cap_q, a.counters),
+        plan_of(*p, ja::PLAN_KV_TILES, ja::BWD_KV_UNIT, ja::BWD_Q_STEP, 1, a.tiles2, L.cap_k, a.counters2),
+        plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3)};
+    hipError_t e = ja::launch_plan(pp, 3, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(ja::launch_bwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ja_workspace_size(const ja_problem *p, int pass) {
+    if (pass != JA_PASS_FWD && pass != JA_PASS_BWD) return 0;
+    if (check_problem(p, pass) != JA_OK) return 0;
+    return layout_of(*p, pass).total;
+}
+
+ja_status jagged_gdpa_fwd(const ja_problem *p, const void *q, const void *k, const void *v, void *o, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return run_fwd(p, 0, q, k, v, o, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+ja_status jagged_attn_fwd(const ja_problem *p, const void *q, const void *k, const void *v, void *o, float *lse,
+                          void *o_residual, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_fwd(p, 1, q, k, v, o, lse, o_residual, workspace, workspace_bytes, stream);
+}
+
+ja_status jagged_gdpa_bwd(const ja_problem *p, const void *q, const void *k, const void *v, const void *dout, void *dq,
+                          void *dk, void *dv, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_bwd(p, 0, q, k, v, nullptr, nullptr, dout, nullptr, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+ja_status jagged_attn_bwd(const ja_problem *p, const void *q, const void *k, const void *v, const void *o,
+                          const void *o_residual, const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    return run_bwd(p, 1, q, k, v, o, o_residual, dout, lse, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+const char *ja_status_string(int status) {
+    switch (status) {
+    case JA_OK: return "ok";
+    case JA_ERR_NULL: return "a required pointer is NULL";
+    case JA_ERR_SHAPE: return "a size or range argument is out of range";
+    case JA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, activation, bias kind or pass";
+    case JA_ERR_WORKSPACE: return "workspace NULL, not 256-byte aligned, or too small";
+    case JA_ERR_HIP: return "a HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int ja_last_hip_error(void) { return g_last_hip_error; }
+
+int ja_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,502 @@
+// Backward kernels (bf16 in, fp32 accumulate) for GDPA and JFA on gfx950.
+//
+// With dP = dO V^T and X the scores:
+//   GDPA  dX = dP * act'(X),        P = act(X)
+//   JFA   dX = P * (dP - delta),    P = exp(X - LSE), delta_i = <dO_i, O_i>
+//   dV = P^T dO,  dK = scale dX^T Q,  dQ = scale dX K.
+//
+// The pages' backward avoids both redundant recomputation and atomic writes
+// by splitting the dQ computation off in a non-sequence-parallel scheme
+// ("Meta redesigns AI training infrastructure...", section "Eliminating
+// Compute Waste in Asymmetric Workloads").  Here every output row is written
+// exactly once, by one unit, with no atomics:
+//   * dK/dV units (sample, 128-key tile, head): each wave owns 32 keys and
+//     loops over the query rows that see them; dK, dV accumulate in registers.
+//   * dQ units (sample, 128-query tile, head): each wave owns 32 query rows and
+//     loops over the key tiles they see; dQ accumulates in registers.
+//     These two unit kinds recompute X and dP once each.
+//   * Fused units for samples with at most 32 keys, (sample, head): the keys
+//     stay resident and the unit loops over all query rows; dQ of each block
+//     is complete when the block is done, dK and dV when the sample is done,
+//     so nothing is recomputed.  This is the short key/value regime, where
+//     the pages pipeline across the outer loop because the inner loop has
+//     only one or two iterations ("Meta redesigns...", section "Custom Kernels
+//     and 5D Parallelism...").
+#include "ja_device.h"
+#include "ja_kernels.h"
+#include "ja_tiles.h"
+
+namespace ja {
+
+constexpr int BWD_THREADS = 256;
+
+// --------------------------------------------------------------- JFA delta
+// delta[h][r] = <dO[r, h, :], O[r, h, :]> (fp32 [H, Tq]), O taken as o + o_res when
+// the forward's rounding residual is given.  D/8 lanes per row,
+// one 16-byte chunk each, reduced by lane shuffles.
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(const AttnParams p) {
+    constexpr int TPR = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rowh = gid / TPR;  // r * H + h
+    const int c = (int)(gid % TPR);
+    const int64_t n = p.total_q * p.H;
+    float acc = 0.0f;
+    if (rowh < n) {
+        const bf16x8 o = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(p.o) + rowh * D + c * 8);
+        const bf16x8 d = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(p.dout) + rowh * D + c * 8);
+        if (p.o_res) {
+            // O = bf16 output + its rounding residual: delta exact to fp32 rounding
+            const bf16x8 r = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(p.o_res) + rowh * D + c * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(bf2f(o[e]) + bf2f(r[e]), bf2f(d[e]), acc);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(bf2f(o[e]), bf2f(d[e]), acc);
+        }
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (rowh < n && c == 0) {
+        const int64_t r = rowh / p.H;
+        const int h = (int)(rowh % p.H);
+        p.delta[(int64_t)h * p.total_q + r] = acc;
+    }
+}
+
+// Element-wise backward of one score: returns P (the weight used for dV)
+// and writes dX (without the scale factor).
+template <int MODE, int ACT>
+__device__ __forceinline__ float score_bwd(float s_raw, float scale, float bias, float dp, float lse2, float dlt,
+                                           bool valid, float &dx) {
+    const float x = __builtin_fmaf(s_raw, scale, bias);
+    if constexpr (MODE == GDPA) {
+        float y, dy;
+        act_fwd_grad<ACT>(x, y, dy);
+        dx = valid ? dp * dy : 0.0f;
+        return valid ? y : 0.0f;
+    } else {
+        const float pr = valid ? fast_exp2(__builtin_fmaf(x, LOG2E, -lse2)) : 0.0f;
+        dx = pr * (dp - dlt);
+        return pr;
+    }
+}
+
+// ------------------------------------------------------------- dQ units
+template <int D, int MODE, int ACT>
+__global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) {
+    constexpr int BN = KV_TILE;
+    constexpr int TILE_BYTES = BN * D * 2;
+    constexpr int NKK = D / 16, NDB = D / 32, NNB = BN / 32, NKS = BN / 16;
+    __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
+    __shared__ int s_unit;
+    lchar *const lbase = (lchar *)smem;
+
+    const bf16 *__restrict__ Q = static_cast<const bf16 *>(p.q);
+    const bf16 *__restrict__ K = static_cast<const bf16 *>(p.k);
+    const bf16 *__restrict__ V = static_cast<const bf16 *>(p.v);
+    const bf16 *__restrict__ G = static_cast<const bf16 *>(p.dout);
+    bf16 *__restrict__ dQ = static_cast<bf16 *>(p.dq);
+    const int H = p.H;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const int n_units = p.counters->units;
+    const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
+
+    for (;;) {
+        if (threadIdx.x == 0) s_unit = atomicAdd(&p.counters->cursor, 1);
+        __syncthreads();
+        const int w = s_unit;
+        __syncthreads();
+        if (w >= n_units) break;
+        const int2 tile = p.tiles[w / H];
+        const int h = w % H;
+        const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
+        const int i0 = tile.y * Q_TILE;
+        const int iw = i0 + wv * 32;
+        const int irow = iw + l32;
+        const bool row_ok = irow < s.lq;
+        const int i_last = (i0 + Q_TILE < s.lq ? i0 + Q_TILE : s.lq) - 1;
+        const int nkv = (key_end(i_last, s.lq, s.lk, p.causal) + BN - 1) / BN;
+        const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
+
+        bf16x8 qreg[NKK], greg[NKK];
+        load_row_operand<D>(qreg, Q, s.qs + irow, H, h, row_ok, g);
+        load_row_operand<D>(greg, G, s.qs + irow, H, h, row_ok, g);
+        float lse2 = 0.0f, dlt = 0.0f;
+        if constexpr (MODE == JFA) {
+            if (row_ok) {
+                lse2 = p.lse[(int64_t)h * p.total_q + s.qs + irow] * LOG2E;
+                dlt = p.delta[(int64_t)h * p.total_q + s.qs + irow];
+            }
+        }
+        const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
+
+        f32x16 dqacc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
+
+        PairLoader<BN, D, BWD_THREADS> ld;
+        if (nkv > 0) {
+            ld.load(K, V, s.ks, H, h, 0, s.lk, threadIdx.x);
+            ld.store(lbase, lbase + TILE_BYTES, threadIdx.x);
+        }
+        __syncthreads();
+
+        for (int jt = 0; jt < nkv; ++jt) {
+            const int j0 = jt * BN;
+            const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
+            const lchar *Vt = Kt + TILE_BYTES;
+            if (jt + 1 < nkv) ld.load(K, V, s.ks, H, h, j0 + BN, s.lk, threadIdx.x);
+
+            const bool masked = (j0 + BN > s.lk) || (p.causal && (j0 + BN - 1 > iw + s.lk - s.lq)) || !row_ok;
+            bf16x8 dsb[NKS];
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb) {
+                f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const int off = lds_off<D>(nb * 32 + l32, 2 * kk + g);
+                    sacc = mfma32(lds_read16(Kt, off), qreg[kk], sacc);
+                    dpacc = mfma32(lds_read16(Vt, off), greg[kk], dpacc);
+                }
+                float dx[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int j = j0 + nb * 32 + crow(e, g);
+                    const float bias = brow ? bias_at(bz, brow, irow, j) : 0.0f;
+                    const bool valid = !masked || (row_ok && j < my_kend);
+                    score_bwd<MODE, ACT>(sacc[e], p.scale, bias, dpacc[e], lse2, dlt, valid, dx[e]);
+                }
+                pack_operands(dx, dsb[2 * nb], dsb[2 * nb + 1]);
+            }
+            // dQ^T += K^T dX^T
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    dqacc[db] = mfma32(lds_read_tr_operand<D>(Kt, ks * 16, db * 32, lane), dsb[ks], dqacc[db]);
+            }
+            if (jt + 1 < nkv) {
+                lchar *Kn = lbase + ((jt + 1) & 1) * 2 * TILE_BYTES;
+                ld.store(Kn, Kn + TILE_BYTES, threadIdx.x);
+            }
+            __syncthreads();
+        }
+        if (row_ok) store_row_acc<D>(dQ + ((s.qs + irow) * H + h) * (int64_t)D, dqacc, p.scale, g);
+    }
+}
+
+// ----------------------------------------------------------- dK/dV units
+template <int D, int MODE, int ACT>
+__global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p) {
+    constexpr int BQ = BWD_Q_STEP;  // 64 query rows per step
+    constexpr int TILE_BYTES = BQ * D * 2;
+    constexpr int NKK = D / 16, NDB = D / 32;
+    __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
+    __shared__ float s_lse[BQ], s_dlt[BQ];
+    __shared__ int s_unit;
+    lchar *const Qt = (lchar *)smem;
+    lchar *const Gt = Qt + TILE_BYTES;
+
+    const bf16 *__restrict__ Q = static_cast<const bf16 *>(p.q);
+    const bf16 *__restrict__ K = static_cast<const bf16 *>(p.k);
+    const bf16 *__restrict__ V = static_cast<const bf16 *>(p.v);
+    const bf16 *__restrict__ G = static_cast<const bf16 *>(p.dout);
+    const int H = p.H;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const int n_units = p.counters2->units;
+    const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
+
+    for (;;) {
+        if (threadIdx.x == 0) s_unit = atomicAdd(&p.counters2->cursor, 1);
+        __syncthreads();
+        const int w = s_unit;
+        __syncthreads();
+        if (w >= n_units) break;
+        const int2 tile = p.tiles2[w / H];
+        const int h = w % H;
+        const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
+        const int jt0 = tile.y * BWD_KV_UNIT;
+        const int jw = jt0 + wv * 32;       // first key of this wave
+        const int jkey = jw + l32;          // this lane's key (C-layout column)
+        const bool key_ok = jkey < s.lk;
+        const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
+
+        bf16x8 kreg[NKK], vreg[NKK];
+        load_row_operand<D>(kreg, K, s.ks + jkey, H, h, key_ok, g);
+        load_row_operand<D>(vreg, V, s.ks + jkey, H, h, key_ok, g);
+        f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dkacc[db] = dvacc[db] = f32x16{};
+
+        // Query rows that see any key of the unit: i >= jt0 - (lk - lq) when causal.
+        int ia0 = p.causal ? jt0 - (s.lk - s.lq) : 0;
+        ia0 = ia0 < 0 ? 0 : ia0;
+        const int shift = s.lk - s.lq;  // causal: key j visible to row i iff j <= i + shift
+
+        PairLoader<BQ, D, BWD_THREADS> ld;
+        for (int ia = ia0; ia < s.lq; ia += BQ) {
+            ld.load(Q, G, s.qs, H, h, ia, s.lq, threadIdx.x);
+            if constexpr (MODE == JFA) {
+                if (threadIdx.x < BQ) {
+                    const int i = ia + threadIdx.x;
+                    const bool ok = i < s.lq;
+                    s_lse[threadIdx.x] = ok ? p.lse[(int64_t)h * p.total_q + s.qs + i] * LOG2E : 0.0f;
+                    s_dlt[threadIdx.x] = ok ? p.delta[(int64_t)h * p.total_q + s.qs + i] : 0.0f;
+                }
+            }
+            ld.store(Qt, Gt, threadIdx.x);
+            __syncthreads();
+
+            const bool masked = (ia + BQ > s.lq) || (p.causal && (jw + 31 > ia + shift));
+#pragma unroll
+            for (int qb = 0; qb < BQ / 32; ++qb) {
+                f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const int off = lds_off<D>(qb * 32 + l32, 2 * kk + g);
+                    sacc = mfma32(lds_read16(Qt, off), kreg[kk], sacc);
+                    dpacc = mfma32(lds_read16(Gt, off), vreg[kk], dpacc);
+                }
+                float pv[16], dx[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int il = qb * 32 + crow(e, g);
+                    const int i = ia + il;
+                    const float bias = brow ? bias_at(bz, brow, i, jkey) : 0.0f;
+                    const bool valid = !masked || (i < s.lq && (!p.causal || jkey <= i + shift));
+                    float lse2 = 0.0f, dlt = 0.0f;
+                    if constexpr (MODE == JFA) {
+                        lse2 = s_lse[il];
+                        dlt = s_dlt[il];
+                    }
+                    pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bias, dpacc[e], lse2, dlt, valid, dx[e]);
+                }
+                bf16x8 pb[2], dsb[2];
+                pack_operands(pv, pb[0], pb[1]);
+                pack_operands(dx, dsb[0], dsb[1]);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        dvacc[db] = mfma32(lds_read_tr_operand<D>(Gt, qb * 32 + ks * 16, db * 32, lane), pb[ks], dvacc[db]);
+                        dkacc[db] = mfma32(lds_read_tr_operand<D>(Qt, qb * 32 + ks * 16, db * 32, lane), dsb[ks], dkacc[db]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        if (key_ok) {
+            const int64_t off = ((s.ks + jkey) * H + h) * (int64_t)D;
+            store_row_acc<D>(static_cast<bf16 *>(p.dk) + off, dkacc, p.scale, g);
+            store_row_acc<D>(static_cast<bf16 *>(p.dv) + off, dvacc, 1.0f, g);
+        }
+    }
+}
+
+// ------------------------------------------------- fused short-K/V units
+// One unit per (sample, head) with at most 32 keys.  Waves take 32-row query
+// blocks in turn; each block computes X, dP once, then dV, dK (registers),
+// dX^T through a small LDS transpose, and dQ of the block.  At the end the
+// four waves' dK / dV partials are summed through LDS and stored.
+template <int D, int MODE, int ACT>
+__global__ __launch_bounds__(BWD_THREADS, 1) void fused_kernel(const AttnParams p) {
+    constexpr int NKK = D / 16, NDB = D / 32;
+    constexpr int KV_BYTES = 32 * D * 2;       // one 32-row tile
+    constexpr int DS_STRIDE = 80;              // bytes per row of the dX scratch (32 bf16 + pad)
+    constexpr int DS_BYTES = 32 * DS_STRIDE;
+    constexpr int WAVE_BYTES = 2 * KV_BYTES + DS_BYTES;
+    constexpr int RED_BYTES = 3 * NDB * 16 * 64 * 4;  // three waves' partials of one accumulator
+    constexpr int LOOP_BYTES = 2 * KV_BYTES + 4 * WAVE_BYTES;
+    constexpr int SMEM = LOOP_BYTES > 2 * KV_BYTES + RED_BYTES ? LOOP_BYTES : 2 * KV_BYTES + RED_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __shared__ int s_unit;
+    lchar *const Kt = (lchar *)smem;
+    lchar *const Vt = Kt + KV_BYTES;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    lchar *const Qw = Kt + 2 * KV_BYTES + wv * WAVE_BYTES;
+    lchar *const Gw = Qw + KV_BYTES;
+    lchar *const Sw = Gw + KV_BYTES;
+    float *const red = (float *)(smem + 2 * KV_BYTES);
+
+    const bf16 *__restrict__ Q = static_cast<const bf16 *>(p.q);
+    const bf16 *__restrict__ K = static_cast<const bf16 *>(p.k);
+    const bf16 *__restrict__ V = static_cast<const bf16 *>(p.v);
+    const bf16 *__restrict__ G = static_cast<const bf16 *>(p.dout);
+    const int H = p.H;
+    const int g = lane >> 5, l32 = lane & 31;
+    const int n_units = p.counters3->units;
+    const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
+
+    for (;;) {
+        if (threadIdx.x == 0) s_unit = atomicAdd(&p.counters3->cursor, 1);
+        __syncthreads();
+        const int w = s_unit;
+        __syncthreads();
+        if (w >= n_units) break;
+        const int2 tile = p.tiles3[w / H];
+        const int h = w % H;
+        const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
+        const int jkey = l32;
+        const bool key_ok = jkey < s.lk;
+        const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
+        const int shift = s.lk - s.lq;
+
+        {   // keys and values of the sample -> LDS (for the transposing reads of dQ)
+            PairLoader<32, D, BWD_THREADS> kv;
+            kv.load(K, V, s.ks, H, h, 0, s.lk, threadIdx.x);
+            kv.store(Kt, Vt, threadIdx.x);
+        }
+        bf16x8 kreg[NKK], vreg[NKK];
+        load_row_operand<D>(kreg, K, s.ks + jkey, H, h, key_ok, g);
+        load_row_operand<D>(vreg, V, s.ks + jkey, H, h, key_ok, g);
+        f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dkacc[db] = dvacc[db] = f32x16{};
+        __syncthreads();
+
+        const int nblk = (s.lq + 31) / 32;
+        for (int blk = wv; blk < nblk; blk += 4) {
+            const int ia = blk * 32;
+            {   // this wave's 32 query rows of Q and dO -> its LDS tiles
+                PairLoader<32, D, 64> qg;
+                qg.load(Q, G, s.qs, H, h, ia, s.lq, lane);
+                qg.store(Qw, Gw, lane);
+            }
+            float lse2[16], dlt[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                lse2[e] = 0.0f;
+                dlt[e] = 0.0f;
+                if constexpr (MODE == JFA) {
+                    const int i = ia + crow(e, g);
+                    if (i < s.lq) {
+                        lse2[e] = p.lse[(int64_t)h * p.total_q + s.qs + i] * LOG2E;
+                        dlt[e] = p.delta[(int64_t)h * p.total_q + s.qs + i];
+                    }
+                }
+            }
+            lds_wave_sync();
+
+            f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int off = lds_off<D>(l32, 2 * kk + g);
+                sacc = mfma32(lds_read16(Qw, off), kreg[kk], sacc);
+                dpacc = mfma32(lds_read16(Gw, off), vreg[kk], dpacc);
+            }
+            const bool masked = (ia + 32 > s.lq) || (s.lk < 32) || p.causal;
+            float pv[16], dx[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int i = ia + crow(e, g);
+                const float bias = brow ? bias_at(bz, brow, i, jkey) : 0.0f;
+                const bool valid = !masked || (i < s.lq && key_ok && (!p.causal || jkey <= i + shift));
+                pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bias, dpacc[e], lse2[e], dlt[e], valid, dx[e]);
+            }
+            bf16x8 pb[2], dsb[2];
+            pack_operands(pv, pb[0], pb[1]);
+            pack_operands(dx, dsb[0], dsb[1]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dvacc[db] = mfma32(lds_read_tr_operand<D>(Gw, ks * 16, db * 32, lane), pb[ks], dvacc[db]);
+                    dkacc[db] = mfma32(lds_read_tr_operand<D>(Qw, ks * 16, db * 32, lane), dsb[ks], dkacc[db]);
+                }
+            }
+            // dX (query i, key j) -> scratch row i, column j (bf16).
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int i = crow(e, g);
+                *reinterpret_cast<__attribute__((address_space(3))) bf16 *>(Sw + i * DS_STRIDE + jkey * 2) = f2bf(dx[e]);
+            }
+            lds_wave_sync();
+            // dQ^T = K^T dX^T: B operand = row l32 of the scratch, keys ks*16 + g*4 + 0..3 and +8.
+            bf16x8 dtb[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const lchar *row = Sw + l32 * DS_STRIDE + (ks * 16 + g * 4) * 2;
+                const u32x2 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x2 *>(row);
+                const u32x2 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x2 *>(row + 16);
+                dtb[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+            f32x16 dqacc[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                dqacc[db] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    dqacc[db] = mfma32(lds_read_tr_operand<D>(Kt, ks * 16, db * 32, lane), dtb[ks], dqacc[db]);
+            }
+            const int irow = ia + l32;
+            if (irow < s.lq)
+                store_row_acc<D>(static_cast<bf16 *>(p.dq) + ((s.qs + irow) * H + h) * (int64_t)D, dqacc, p.scale, g);
+            lds_wave_sync();
+        }
+
+        // Sum the four waves' dK / dV partials (lane-major so the LDS traffic
+        // is conflict-free) and store; wave 0 stores dK, wave 1 stores dV.
+        __syncthreads();
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            f32x16 (&acc)[NDB] = pass == 0 ? dkacc : dvacc;
+            if (wv > 0) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) red[((wv - 1) * NDB * 16 + db * 16 + e) * 64 + lane] = acc[db][e];
+            }
+            __syncthreads();
+            if (wv == 0) {
+#pragma unroll
+                for (int src = 0; src < 3; ++src)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[db][e] += red[(src * NDB * 16 + db * 16 + e) * 64 + lane];
+                if (key_ok) {
+                    const int64_t off = ((s.ks + jkey) * H + h) * (int64_t)D;
+                    if (pass == 0) store_row_acc<D>(static_cast<bf16 *>(p.dk) + off, acc, p.scale, g);
+                    else store_row_acc<D>(static_cast<bf16 *>(p.dv) + off, acc, 1.0f, g);
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// -------------------------------------------------------------- launches
+template <int D, int MODE, int ACT>
+static hipError_t launch_bwd_t(const AttnParams &p, int grid, hipStream_t st) {
+    if (MODE == JFA && p.total_q > 0) {
+        const int64_t threads = p.total_q * p.H * (D / 8);
+        hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, p);
+    }
+    hipLaunchKernelGGL((fused_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, p);
+    hipLaunchKernelGGL((dq_kernel<D, MODE, ACT>), dim3(grid), dim3(BWD_THREADS), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const AttnParams &p, int mode, int act, int grid, hipStream_t st) {
+    if (mode == JFA) return launch_bwd_t<D, JFA, SILU>(p, grid, st);
+    switch (act) {
+    case SILU: return launch_bwd_t<D, GDPA, SILU>(p, grid, st);
+    case GELU_TANH: return launch_bwd_t<D, GDPA, GELU_TANH>(p, grid, st);
+    default: return launch_bwd_t<D, GDPA, GELU_ERF>(p, grid, st);
+    }
+}
+
+hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t st) {
+    switch (D) {
+    case 32: return launch_bwd_d<32>(p, mode, act, grid, st);
+    case 64: return launch_bwd_d<64>(p, mode, act, grid, st);
+    default: return launch_bwd_d<128>(p, mode, act, grid, st);
+    }
+}
+
+}  // namespace ja

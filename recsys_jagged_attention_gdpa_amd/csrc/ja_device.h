@@ -1,0 +1,221 @@
+// Device-side building blocks shared by the gfx950 jagged attention kernels:
+// vector types, MFMA wrappers, the swizzled LDS tile layout, activations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ja {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+enum Mode { GDPA = 0, JFA = 1 };
+enum Act { SILU = 0, GELU_TANH = 1, GELU_ERF = 2 };
+enum BiasKind { BIAS_NONE = 0, BIAS_REL = 1, BIAS_KEYPOS = 2 };
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_32x32x16_bf16.  Lane layouts (checked on gfx950):
+//   A (32 x 16): lane l holds row l%32, k = (l/32)*8 + 0..7
+//   B (16 x 32): lane l holds col l%32, k = (l/32)*8 + 0..7
+//   C (32 x 32): lane l holds col l%32, rows (e/4)*8 + (l/32)*4 + e%4, e = 0..15
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row (within a 32-block) of accumulator element e for lane half g = l/32.
+__device__ __forceinline__ int crow(int e, int g) { return (e >> 2) * 8 + g * 4 + (e & 3); }
+
+// ------------------------------------------------------ LDS tile layout
+// A tile of R rows x D bf16 is stored row-major with its 16-byte chunks
+// permuted per row: chunk c of row r lives at chunk c ^ swz(r).  The
+// permutation keeps both access patterns the kernels use free of bank
+// conflicts: 16-byte row reads by 8+ consecutive rows at one chunk, and the
+// transposing 8-byte reads (4 consecutive rows x 64 bytes per 32 lanes).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+}
+
+// Byte offset of chunk c (8 bf16) of row r.
+template <int D>
+__device__ __forceinline__ int lds_off(int r, int c) {
+    return r * (D * 2) + ((c ^ swz<D>(r)) << 4);
+}
+
+// LDS pointers carry their address space so every tile access compiles to a
+// ds_* instruction.
+typedef __attribute__((address_space(3))) char lchar;
+typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
+typedef __attribute__((address_space(3))) u32x4 lu32x4;
+typedef __attribute__((address_space(3))) s16x4 ls16x4;
+typedef __attribute__((address_space(3))) float lfloat;
+
+__device__ __forceinline__ bf16x8 lds_read16(const lchar *base, int off) {
+    return *reinterpret_cast<const lbf16x8 *>(base + off);
+}
+
+__device__ __forceinline__ void lds_write16(lchar *base, int off, u32x4 v) {
+    *reinterpret_cast<lu32x4 *>(base + off) = v;
+}
+
+// Transposing read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
+// m supplies the address of 4 bf16; lane i receives element i%4 of the values
+// addressed by lanes 4j + i/4, j = 0..3.  With lane m addressing row
+// key0 + m/4, columns d0 + 4(m%4) .. +3 of a row-major tile, lane i receives
+// column d0 + i of rows key0 .. key0+3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const lchar *base, int off) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4 *)(base + off));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Transposed MFMA operand (row d = d0 + l%32 of the transposed tile, k = 8
+// rows of the original tile): rows r0 + g*4 + 0..3 and r0 + 8 + g*4 + 0..3 of
+// the row-major tile, with g = l/32.  This row order matches the accumulator
+// layout's row order (crow), so a C-layout block can be reused as the other
+// operand without any shuffle.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read_tr_operand(const lchar *tile, int r0, int d0, int lane) {
+    const int l16 = lane & 15;
+    const int G = lane >> 4;
+    const int g = G >> 1;
+    const int dcol = d0 + ((G & 1) << 4) + ((l16 & 3) << 2);
+    const int c = dcol >> 3;
+    const int within = (dcol & 7) << 1;
+    const int ra = r0 + g * 4 + (l16 >> 2);
+    const int rb = ra + 8;
+    bf16x4 lo = lds_read_tr(tile, lds_off<D>(ra, c) + within);
+    bf16x4 hi = lds_read_tr(tile, lds_off<D>(rb, c) + within);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ----------------------------------------------------------- conversions
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+__device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }  // round to nearest even
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(bf16)a, (bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ------------------------------------------------------------ activations
+// SiLU(x) = x * sigmoid(x); GELU (tanh form) = x * sigmoid(2u),
+// u = sqrt(2/pi) (x + 0.044715 x^3); GELU (erf form) = x * Phi(x).
+constexpr float GELU_C = 0.7978845608028654f;  // sqrt(2/pi)
+constexpr float GELU_A = 0.044715f;
+constexpr float INV_SQRT2 = 0.7071067811865476f;
+constexpr float INV_SQRT_2PI = 0.3989422804014327f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// sigmoid(z) with z given as -z * log2(e) (so one v_exp and one v_rcp).
+__device__ __forceinline__ float sigmoid_from_neg_log2(float nz) { return fast_rcp(1.0f + fast_exp2(nz)); }
+
+template <int ACT>
+__device__ __forceinline__ float act_fwd(float x) {
+    if constexpr (ACT == SILU) {
+        return x * sigmoid_from_neg_log2(-x * LOG2E);
+    } else if constexpr (ACT == GELU_TANH) {
+        const float x2 = x * x;
+        const float t = __builtin_fmaf(x2, -2.0f * LOG2E * GELU_C * GELU_A, -2.0f * LOG2E * GELU_C);
+        return x * sigmoid_from_neg_log2(x * t);
+    } else {
+        return 0.5f * x * (1.0f + erff(x * INV_SQRT2));
+    }
+}
+
+// Activation value and derivative together (backward).
+template <int ACT>
+__device__ __forceinline__ void act_fwd_grad(float x, float &y, float &dy) {
+    if constexpr (ACT == SILU) {
+        const float s = sigmoid_from_neg_log2(-x * LOG2E);
+        y = x * s;
+        dy = __builtin_fmaf(y, 1.0f - s, s);  // s (1 + x (1 - s))
+    } else if constexpr (ACT == GELU_TANH) {
+        const float x2 = x * x;
+        const float t = __builtin_fmaf(x2, -2.0f * LOG2E * GELU_C * GELU_A, -2.0f * LOG2E * GELU_C);
+        const float s = sigmoid_from_neg_log2(x * t);  // sigmoid(2u) = (1 + tanh u) / 2
+        y = x * s;
+        // d/dx [x s(2u)] = s + x * 2 s (1 - s) * u'(x),  u' = c (1 + 3 a x^2)
+        const float du = GELU_C * __builtin_fmaf(3.0f * GELU_A, x2, 1.0f);
+        dy = __builtin_fmaf(2.0f * x * s * (1.0f - s), du, s);
+    } else {
+        const float cdf = 0.5f * (1.0f + erff(x * INV_SQRT2));
+        const float pdf = INV_SQRT_2PI * fast_exp2(-0.5f * LOG2E * x * x);
+        y = x * cdf;
+        dy = __builtin_fmaf(x, pdf, cdf);
+    }
+}
+
+// Order this wave's LDS writes before its later LDS reads of other lanes'
+// data (waits for the LDS queue; also a compiler memory barrier).
+__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------- misc helpers
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+__device__ __forceinline__ float shfl_xor32(float v) {
+    // exchange with lane ^ 32 (the other half of the wave)
+    const int lane = threadIdx.x & 63;
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((lane ^ 32) << 2), __builtin_bit_cast(int, v)));
+}
+
+// Sample geometry shared by every kernel.
+struct Sample {
+    int64_t qs;  // first query row (global) of the sample
+    int64_t o0;  // first output row (global)
+    int64_t ks;  // first key row (global)
+    int lq, lk;
+};
+
+__device__ __forceinline__ Sample load_sample(const int32_t *q_off, int lq_fixed, const int32_t *kv_off, int b) {
+    Sample s;
+    if (q_off) {
+        const int a = q_off[b], e = q_off[b + 1];
+        s.qs = a;
+        s.o0 = a;
+        s.lq = e - a;
+    } else {
+        s.qs = 0;
+        s.o0 = (int64_t)b * lq_fixed;
+        s.lq = lq_fixed;
+    }
+    const int ka = kv_off[b], ke = kv_off[b + 1];
+    s.ks = ka;
+    s.lk = ke - ka;
+    return s;
+}
+
+// Keys visible to query row i (exclusive end) under the bottom-right causal rule.
+__device__ __forceinline__ int key_end(int i, int lq, int lk, int causal) {
+    if (!causal) return lk;
+    const int e = i + lk - lq + 1;
+    return e < 0 ? 0 : (e > lk ? lk : e);
+}
+
+struct BiasArgs {
+    const float *table;
+    int kind, lo, hi, width;
+};
+
+__device__ __forceinline__ float bias_at(const BiasArgs &bz, const float *row, int i, int j) {
+    if (bz.kind == BIAS_REL) return row[clampi(i - j, bz.lo, bz.hi) - bz.lo];
+    if (bz.kind == BIAS_KEYPOS) return row[clampi(j, bz.lo, bz.hi) - bz.lo];
+    return 0.0f;
+}
+
+}  // namespace ja

@@ -1,0 +1,240 @@
+// Forward kernels (bf16 in, fp32 accumulate) for GDPA and JFA on gfx950.
+//
+// GDPA: O_i = sum_j act(scale <q_i,k_j> + bias_ij) v_j, no normalisation —
+// "two matrix multiplications with an element-wise activation in between"
+// ("GEM Training: How Meta Doubled the Efficiency...", section "What to
+// watch").  Without a softmax there is no running maximum, no rescaling of the
+// accumulator and no final normaliser (the pages credit dropping that
+// correction stage for freeing resources: "Meta redesigns AI training
+// infrastructure...", section "Custom Kernels and 5D Parallelism...").
+// JFA: the same contraction with an online softmax (running max m and sum l,
+// accumulator rescaled when m grows), epilogue O / l and LSE = m + ln l.
+//
+// Structure: a persistent grid pulls (sample, 128-row query tile, head) units
+// from the planner's longest-first list.  Each of the 4 waves owns 32 query
+// rows and keeps them in registers; key / value tiles of 64 rows are staged in
+// LDS (double-buffered through registers) and shared by the 4 waves.
+//   S^T = K Q^T      (v_mfma_f32_32x32x16_bf16; A = K rows from LDS, B = Q)
+//   P^T = act(S^T)   (element-wise in registers)
+//   O^T += V^T P^T   (A = V^T by transposing LDS reads, B = P^T straight
+//                     from the S^T accumulator: its lane layout already is
+//                     the B-operand layout, keys permuted consistently)
+// Jagged masking is by offset subtraction: every index is sample-local and a
+// tile is masked element-wise only when it crosses the sample's key end or
+// the causal diagonal ("Meta redesigns...", section "Eliminating Compute
+// Waste in Asymmetric Workloads").  Key rows past the sample's end are loaded
+// as zeros.
+#include "ja_device.h"
+#include "ja_kernels.h"
+#include "ja_tiles.h"
+
+namespace ja {
+
+constexpr int FWD_THREADS = 256;
+constexpr int BM = Q_TILE;   // 128 query rows per unit
+constexpr int BN = KV_TILE;  // 64 keys per tile
+
+template <int D, int MODE, int ACT>
+__global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p) {
+    constexpr int TILE_BYTES = BN * D * 2;
+    constexpr int NKK = D / 16;  // k-steps over the head dimension
+    constexpr int NDB = D / 32;  // 32-wide blocks of the head dimension
+    constexpr int NNB = BN / 32; // 32-key blocks per tile
+    constexpr int NKS = BN / 16; // 16-key k-steps per tile
+    __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
+    __shared__ int s_unit;
+    lchar *const lbase = (lchar *)smem;
+
+    const bf16 *__restrict__ Q = static_cast<const bf16 *>(p.q);
+    const bf16 *__restrict__ K = static_cast<const bf16 *>(p.k);
+    const bf16 *__restrict__ V = static_cast<const bf16 *>(p.v);
+    bf16 *__restrict__ O = static_cast<bf16 *>(p.out);
+    const int H = p.B > 0 ? p.H : 1;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const int n_units = p.counters->units;
+    BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
+    const float sl2 = p.scale * LOG2E;
+
+    for (;;) {
+        if (threadIdx.x == 0) s_unit = atomicAdd(&p.counters->cursor, 1);
+        __syncthreads();
+        const int w = s_unit;
+        __syncthreads();
+        if (w >= n_units) break;
+        const int2 tile = p.tiles[w / H];
+        const int h = w % H;
+        const int b = tile.x;
+        const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, b);
+        const int i0 = tile.y * BM;            // first query row of the unit (sample-local)
+        const int iw = i0 + wv * 32;           // first row of this wave
+        const int irow = iw + l32;             // this lane's query row
+        const int i_last = (i0 + BM < s.lq ? i0 + BM : s.lq) - 1;
+        const int kend = key_end(i_last, s.lq, s.lk, p.causal);
+        const int nkv = (kend + BN - 1) / BN;
+        const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
+
+        // Q rows of this lane, in B-operand layout: chunk 2kk+g of row irow.
+        bf16x8 qreg[NKK];
+        load_row_operand<D>(qreg, Q, s.qs + irow, H, h, irow < s.lq, g);
+
+        f32x16 oacc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+        float m_run = -INFINITY, l_run = 0.0f;  // JFA running max (log2 units) and partial sum
+
+        PairLoader<BN, D, FWD_THREADS> ld;
+        if (nkv > 0) {
+            ld.load(K, V, s.ks, H, h, 0, s.lk, threadIdx.x);
+            ld.store(lbase, lbase + TILE_BYTES, threadIdx.x);
+        }
+        __syncthreads();
+
+        for (int jt = 0; jt < nkv; ++jt) {
+            const int j0 = jt * BN;
+            const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
+            const lchar *Vt = Kt + TILE_BYTES;
+            if (jt + 1 < nkv) ld.load(K, V, s.ks, H, h, j0 + BN, s.lk, threadIdx.x);
+
+            // S^T block per 32 keys: lane holds query irow, keys crow(e, g).
+            f32x16 sacc[NNB];
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb) {
+                sacc[nb] = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const bf16x8 a = lds_read16(Kt, lds_off<D>(nb * 32 + l32, 2 * kk + g));
+                    sacc[nb] = mfma32(a, qreg[kk], sacc[nb]);
+                }
+            }
+
+            // Element-wise stage.  A tile needs per-element masking only when it
+            // crosses the key end or (causal) the diagonal of this wave's rows.
+            const bool tail = j0 + BN > s.lk;
+            const bool diag = p.causal && (j0 + BN - 1 > iw + s.lk - s.lq);
+            const bool masked = tail || diag;
+            const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
+            bf16x8 pb[NKS];
+            if constexpr (MODE == GDPA) {
+#pragma unroll
+                for (int nb = 0; nb < NNB; ++nb) {
+                    float pv[16];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = j0 + nb * 32 + crow(e, g);
+                        float x = sacc[nb][e] * p.scale;
+                        if (brow) x += bias_at(bz, brow, irow, j);
+                        float y = act_fwd<ACT>(x);
+                        if (masked && j >= my_kend) y = 0.0f;
+                        pv[e] = y;
+                    }
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        bf16x8 t;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t[e] = f2bf(pv[hf * 8 + e]);
+                        pb[nb * 2 + hf] = t;
+                    }
+                }
+            } else {
+                float xs[NNB][16];
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int nb = 0; nb < NNB; ++nb) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = j0 + nb * 32 + crow(e, g);
+                        float x = sacc[nb][e] * sl2;
+                        if (brow) x += bias_at(bz, brow, irow, j) * LOG2E;
+                        if (masked && j >= my_kend) x = -INFINITY;
+                        xs[nb][e] = x;
+                        tmax = fmaxf(tmax, x);
+                    }
+                }
+                tmax = fmaxf(tmax, shfl_xor32(tmax));
+                const float m_new = fmaxf(m_run, tmax);
+                const float shift = m_new == -INFINITY ? 0.0f : m_new;
+                const float alpha = fast_exp2(m_run - shift);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+#pragma unroll
+                for (int nb = 0; nb < NNB; ++nb) {
+                    float pv[16];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        pv[e] = fast_exp2(xs[nb][e] - shift);
+                        l_run += pv[e];
+                    }
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        bf16x8 t;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t[e] = f2bf(pv[hf * 8 + e]);
+                        pb[nb * 2 + hf] = t;
+                    }
+                }
+            }
+
+            // O^T += V^T P^T over the tile's keys.
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const bf16x8 a = lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane);
+                    oacc[db] = mfma32(a, pb[ks], oacc[db]);
+                }
+            }
+
+            if (jt + 1 < nkv) {
+                lchar *Kn = lbase + ((jt + 1) & 1) * 2 * TILE_BYTES;
+                ld.store(Kn, Kn + TILE_BYTES, threadIdx.x);
+            }
+            __syncthreads();
+        }
+
+        // Epilogue: lane owns query row irow; d = db*32 + crow(e, g).
+        float norm = 1.0f;
+        if constexpr (MODE == JFA) {
+            const float l_tot = l_run + shfl_xor32(l_run);
+            const bool any = l_tot > 0.0f;
+            norm = any ? 1.0f / l_tot : 0.0f;
+            if (irow < s.lq && g == 0)
+                p.lse[(int64_t)h * p.total_q_out + s.o0 + irow] = any ? (m_run + log2f(l_tot)) * LN2 : -INFINITY;
+        }
+        if (irow < s.lq) {
+            const int64_t off = ((s.o0 + irow) * H + h) * (int64_t)D;
+            if (MODE == JFA && p.o_res_out)
+                store_row_acc_split<D>(O + off, static_cast<bf16 *>(p.o_res_out) + off, oacc, norm, g);
+            else
+                store_row_acc<D>(O + off, oacc, norm, g);
+        }
+    }
+}
+
+template <int D, int MODE, int ACT>
+static hipError_t launch_fwd_t(const AttnParams &p, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT>), dim3(grid), dim3(FWD_THREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_fwd_d(const AttnParams &p, int mode, int act, int grid, hipStream_t stream) {
+    if (mode == JFA) return launch_fwd_t<D, JFA, SILU>(p, grid, stream);
+    switch (act) {
+    case SILU: return launch_fwd_t<D, GDPA, SILU>(p, grid, stream);
+    case GELU_TANH: return launch_fwd_t<D, GDPA, GELU_TANH>(p, grid, stream);
+    default: return launch_fwd_t<D, GDPA, GELU_ERF>(p, grid, stream);
+    }
+}
+
+hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream) {
+    switch (D) {
+    case 32: return launch_fwd_d<32>(p, mode, act, grid, stream);
+    case 64: return launch_fwd_d<64>(p, mode, act, grid, stream);
+    default: return launch_fwd_d<128>(p, mode, act, grid, stream);
+    }
+}
+
+}  // namespace ja

@@ -1,0 +1,86 @@
+// Internal interface between the C-ABI host layer (ja_api.cpp) and the kernel
+// translation units: parameter blocks and launch functions.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ja {
+
+// Work-unit tiles: queries are cut into blocks of Q_TILE rows (forward and the
+// dQ units of backward), keys into blocks of KV_TILE rows.
+constexpr int Q_TILE = 128;
+constexpr int KV_TILE = 64;
+constexpr int BWD_KV_UNIT = 128;   // keys owned by one dK/dV unit
+constexpr int BWD_Q_STEP = 64;     // queries per inner step of a dK/dV unit
+constexpr int FUSED_MAX_LK = 32;   // samples with at most this many keys use the fused backward unit
+
+// Plan (scheduler) output lives at the start of the workspace.
+struct PlanCounters {
+    int units;   // number of work units (tiles x heads)
+    int cursor;  // next unit to hand out (persistent kernels pull from it)
+    int pad[62];
+};
+
+enum PlanKind {
+    PLAN_Q_TILES = 0,   // units = (sample, query tile of tile_rows rows); cost from the keys each row sees
+    PLAN_KV_TILES = 1,  // units = (sample, key tile of tile_rows rows); cost from the queries that see it
+    PLAN_SAMPLES = 2,   // units = whole samples (one tile each); cost from the query rows
+};
+
+struct PlanParams {
+    const int32_t *q_off;
+    const int32_t *kv_off;
+    int lq_fixed;
+    int B, H;
+    int causal;
+    int kind;
+    int tile_rows;   // rows per unit tile
+    int inner_rows;  // rows per inner-loop step (cost unit)
+    int only_short;  // PLAN_SAMPLES: keep samples with lk <= FUSED_MAX_LK; PLAN_KV/Q: skip them (1) or not (0)
+    int2 *tiles;     // out: (sample, tile) pairs, most expensive first
+    int max_tiles;
+    PlanCounters *counters;
+};
+
+struct AttnParams {
+    const void *q, *k, *v;
+    const void *o;      // JFA backward: forward output
+    const void *o_res;  // JFA backward: optional bf16 rounding residual of o
+    void *o_res_out;    // JFA forward: optional residual output
+    const void *dout;   // backward: upstream gradient
+    void *out;          // forward: O
+    void *dq, *dk, *dv; // backward outputs
+    float *lse;         // JFA forward: written; backward: read
+    float *delta;       // JFA backward: rowwise <dO, O>, [H, Tq]
+    const int32_t *q_off, *kv_off;
+    int lq_fixed;
+    int B, H;
+    int64_t total_q_out;  // rows of O (= Tq, or B * lq_fixed)
+    int64_t total_q, total_k;
+    float scale;
+    int causal;
+    int bias_kind, bias_lo, bias_hi;
+    const float *bias;
+    const int2 *tiles;
+    PlanCounters *counters;
+    const int2 *tiles2;       // backward: second unit list (dK/dV units)
+    PlanCounters *counters2;
+    const int2 *tiles3;       // backward: fused short-K/V units
+    PlanCounters *counters3;
+};
+
+// Plans up to PLAN_MAX lists in one launch (one workgroup per list).
+constexpr int PLAN_MAX = 3;
+struct PlanBatch {
+    PlanParams list[PLAN_MAX];
+};
+hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream);
+
+// mode: 0 GDPA, 1 JFA.  act: 0 SiLU, 1 GELU tanh, 2 GELU erf.
+hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream);
+hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream);
+hipError_t launch_fwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
+hipError_t launch_bwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
+
+}  // namespace ja

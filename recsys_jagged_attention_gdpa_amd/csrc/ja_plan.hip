@@ -1,0 +1,164 @@
+// Work-list planner: jagged offsets -> per-unit cost -> counting sort (most
+// expensive first) -> list of (sample, tile) pairs + unit counter + cursor.
+//
+// The pages report that naive jagged kernels leave compute units idle when
+// short sequences finish early and that software tile scheduling turned a 6x
+// imbalance into a near-balanced one ("GEM Training: How Meta Doubled the
+// Efficiency...", section "What happened"; "Meta redesigns AI training
+// infrastructure...", section "Custom Kernels and 5D Parallelism for
+// Trillion-Parameter Scale").  Here the balancing is longest-first greedy
+// dispatch: the persistent attention kernels pull units in this order from an
+// atomic cursor, so every workgroup takes the most expensive unit left.
+//
+// One workgroup of 1024 threads; all state in LDS.  The list only orders the
+// work: every output tile is owned by exactly one unit, so results do not
+// depend on the order or on which workgroup runs a unit.
+#include "ja_device.h"
+#include "ja_kernels.h"
+
+namespace ja {
+
+constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_BUCKETS = 2048;
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+struct PlanSample {
+    int lq, lk, ntiles;
+};
+
+__device__ __forceinline__ bool skipped_as_short(const PlanParams &p, int lk) {
+    return p.only_short && lk <= FUSED_MAX_LK;
+}
+
+__device__ PlanSample plan_sample(const PlanParams &p, int b) {
+    PlanSample s;
+    s.lq = p.q_off ? p.q_off[b + 1] - p.q_off[b] : p.lq_fixed;
+    s.lk = p.kv_off[b + 1] - p.kv_off[b];
+    s.lq = s.lq < 0 ? 0 : s.lq;
+    s.lk = s.lk < 0 ? 0 : s.lk;
+    if (p.kind == PLAN_Q_TILES) {
+        s.ntiles = skipped_as_short(p, s.lk) ? 0 : ceil_div(s.lq, p.tile_rows);
+    } else if (p.kind == PLAN_KV_TILES) {
+        s.ntiles = skipped_as_short(p, s.lk) ? 0 : ceil_div(s.lk, p.tile_rows);
+    } else {
+        s.ntiles = (s.lk <= FUSED_MAX_LK && (s.lq > 0 || s.lk > 0)) ? 1 : 0;
+    }
+    return s;
+}
+
+// Cost of tile t of a sample, in inner-loop steps (+1 for the unit's own
+// loads and stores).
+__device__ int tile_cost(const PlanParams &p, const PlanSample &s, int t) {
+    if (p.kind == PLAN_Q_TILES) {
+        int last = (t + 1) * p.tile_rows;
+        last = (last < s.lq ? last : s.lq) - 1;
+        const int kend = key_end(last, s.lq, s.lk, p.causal);
+        return ceil_div(kend, p.inner_rows) + 1;
+    }
+    if (p.kind == PLAN_KV_TILES) {
+        int first_q = 0;
+        if (p.causal) {
+            first_q = t * p.tile_rows - (s.lk - s.lq);
+            first_q = first_q < 0 ? 0 : first_q;
+        }
+        const int nq = s.lq - first_q;
+        return ceil_div(nq > 0 ? nq : 0, p.inner_rows) + 1;
+    }
+    return ceil_div(s.lq, p.inner_rows) + 1;
+}
+
+__device__ __forceinline__ int bucket_of(int cost) {
+    cost = cost < PLAN_BUCKETS - 1 ? cost : PLAN_BUCKETS - 1;
+    return PLAN_BUCKETS - 1 - cost;  // ascending bucket = descending cost
+}
+
+// Visit the tiles of a sample as runs of equal cost, in non-increasing cost
+// order: fn(first_tile, count, step, cost).
+template <class F>
+__device__ void for_each_run(const PlanParams &p, const PlanSample &s, F fn) {
+    if (s.ntiles == 0) return;
+    // causal query tiles get dearer with t; causal key tiles get cheaper.
+    const bool descending = p.causal && p.kind == PLAN_Q_TILES;
+    const int step = descending ? -1 : 1;
+    int t = descending ? s.ntiles - 1 : 0;
+    int left = s.ntiles;
+    while (left > 0) {
+        const int cost = tile_cost(p, s, t);
+        int n = 1;
+        if (p.causal) {
+            while (n < left && tile_cost(p, s, t + n * step) == cost) ++n;
+        } else {
+            n = left;  // every tile of a sample costs the same without causal masking
+        }
+        fn(t, n, step, cost);
+        t += n * step;
+        left -= n;
+    }
+}
+
+__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanBatch batch) {
+    const PlanParams &p = batch.list[blockIdx.x];
+    __shared__ int hist[PLAN_BUCKETS];
+    __shared__ int wave_tot[PLAN_THREADS / WAVE];
+    __shared__ int s_total;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < PLAN_BUCKETS; i += PLAN_THREADS) hist[i] = 0;
+    __syncthreads();
+
+    for (int b = tid; b < p.B; b += PLAN_THREADS) {
+        const PlanSample s = plan_sample(p, b);
+        for_each_run(p, s, [&](int, int n, int, int cost) { atomicAdd(&hist[bucket_of(cost)], n); });
+    }
+    __syncthreads();
+
+    // Exclusive scan of the histogram: thread tid owns buckets 2 tid, 2 tid + 1.
+    const int a = hist[2 * tid], c = hist[2 * tid + 1];
+    int incl = a + c;
+    const int lane = tid & (WAVE - 1), wv = tid / WAVE;
+    for (int d = 1; d < WAVE; d <<= 1) {
+        const int o = __shfl_up(incl, d, WAVE);
+        if (lane >= d) incl += o;
+    }
+    if (lane == WAVE - 1) wave_tot[wv] = incl;
+    __syncthreads();
+    if (wv == 0) {
+        int x = lane < PLAN_THREADS / WAVE ? wave_tot[lane] : 0;
+        for (int d = 1; d < PLAN_THREADS / WAVE; d <<= 1) {
+            const int o = __shfl_up(x, d, WAVE);
+            if (lane >= d) x += o;
+        }
+        if (lane < PLAN_THREADS / WAVE) wave_tot[lane] = x;  // inclusive over waves
+    }
+    __syncthreads();
+    const int excl = incl - (a + c) + (wv > 0 ? wave_tot[wv - 1] : 0);
+    if (tid == PLAN_THREADS - 1) s_total = excl + a + c;
+    __syncthreads();
+    hist[2 * tid] = excl;
+    hist[2 * tid + 1] = excl + a;
+    __syncthreads();
+
+    for (int b = tid; b < p.B; b += PLAN_THREADS) {
+        const PlanSample s = plan_sample(p, b);
+        for_each_run(p, s, [&](int t0, int n, int step, int cost) {
+            const int pos = atomicAdd(&hist[bucket_of(cost)], n);
+            for (int k = 0; k < n; ++k)
+                if (pos + k < p.max_tiles) p.tiles[pos + k] = make_int2(b, t0 + k * step);
+        });
+    }
+    if (tid == 0) {
+        const int n = s_total < p.max_tiles ? s_total : p.max_tiles;
+        p.counters->units = n * p.H;
+        p.counters->cursor = 0;
+    }
+}
+
+hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream) {
+    if (n < 1 || n > PLAN_MAX) return hipErrorInvalidValue;
+    PlanBatch batch{};
+    for (int i = 0; i < n; ++i) batch.list[i] = lists[i];
+    hipLaunchKernelGGL(plan_kernel, dim3(n), dim3(PLAN_THREADS), 0, stream, batch);
+    return hipGetLastError();
+}
+
+}  // namespace ja

@@ -1,0 +1,145 @@
+"""Tensor-level API over the C ABI: allocate outputs and workspace with torch,
+call the library, and expose autograd functions.
+
+    o = gdpa(q, k, v, q_offsets, kv_offsets, act="gelu_tanh")
+    o = jagged_attention(q, k, v, q_offsets, kv_offsets, causal=True)
+
+q is [Tq, H, D] (or [Lq, H, D] shared by every sample when q_offsets is None),
+k and v are [Tk, H, D]; offsets are int32 [B+1] on the same device.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def _problem(q, k, q_offsets, kv_offsets, *, causal, scale, act, bias, bias_kind, bias_lo,
+             bias_hi):
+    B = int(kv_offsets.numel()) - 1
+    H, D = int(q.shape[1]), int(q.shape[2])
+    return _lib.make_problem(
+        batch=B, heads=H, head_dim=D, dtype=q.dtype, total_q=int(q.shape[0]),
+        total_k=int(k.shape[0]), q_offsets=q_offsets, kv_offsets=kv_offsets,
+        lq_fixed=0 if q_offsets is not None else int(q.shape[0]), causal=causal, scale=scale,
+        act=act, bias_kind=bias_kind if bias is not None else "none", bias_table=bias,
+        bias_lo=bias_lo, bias_hi=bias_hi)
+
+
+def _check_inputs(q, k, v, q_offsets, kv_offsets, bias):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D device tensor")
+    if k.shape != v.shape or k.shape[1:] != q.shape[1:] or q.dtype != k.dtype or k.dtype != v.dtype:
+        raise ValueError("q, k, v shapes / dtypes disagree")
+    for name, t in (("q_offsets", q_offsets), ("kv_offsets", kv_offsets)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if bias is not None and (bias.dtype != torch.float32 or not bias.is_cuda or not bias.is_contiguous()):
+        raise ValueError("bias table must be a contiguous float32 device tensor")
+
+
+def _workspace(problem, pass_, device):
+    n = _lib.ja_workspace_size(problem, pass_)
+    if n == 0:
+        raise ValueError("invalid problem (ja_workspace_size returned 0)")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def gdpa_forward(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False,
+                 bias=None, bias_kind="none", bias_lo=0, bias_hi=0):
+    _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
+    p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act=act, bias=bias,
+                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi)
+    rows = q.shape[0] if q_offsets is not None else p.batch * q.shape[0]
+    o = torch.empty((rows, q.shape[1], q.shape[2]), dtype=q.dtype, device=q.device)
+    ws = _workspace(p, _lib.PASS_FWD, q.device)
+    _lib.jagged_gdpa_fwd(p, q, k, v, o, ws)
+    return o
+
+
+def attn_forward(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bias=None,
+                 bias_kind="none", bias_lo=0, bias_hi=0, residual=True):
+    """Returns (O, LSE[H, T], O_residual); O_residual is None for fp32 or residual=False."""
+    _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
+    p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act="silu", bias=bias,
+                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi)
+    rows = q.shape[0] if q_offsets is not None else p.batch * q.shape[0]
+    o = torch.empty((rows, q.shape[1], q.shape[2]), dtype=q.dtype, device=q.device)
+    lse = torch.empty((q.shape[1], rows), dtype=torch.float32, device=q.device)
+    o_res = torch.empty_like(o) if (residual and q.dtype == torch.bfloat16) else None
+    ws = _workspace(p, _lib.PASS_FWD, q.device)
+    _lib.jagged_attn_fwd(p, q, k, v, o, lse, o_res, ws)
+    return o, lse, o_res
+
+
+def gdpa_backward(q, k, v, dout, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False,
+                  bias=None, bias_kind="none", bias_lo=0, bias_hi=0):
+    _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
+    p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act=act, bias=bias,
+                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = _workspace(p, _lib.PASS_BWD, q.device)
+    _lib.jagged_gdpa_bwd(p, q, k, v, dout.contiguous(), dq, dk, dv, ws)
+    return dq, dk, dv
+
+
+def attn_backward(q, k, v, o, dout, lse, q_offsets, kv_offsets, *, o_residual=None, scale=None,
+                  causal=False, bias=None, bias_kind="none", bias_lo=0, bias_hi=0):
+    _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
+    p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act="silu", bias=bias,
+                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = _workspace(p, _lib.PASS_BWD, q.device)
+    _lib.jagged_attn_bwd(p, q, k, v, o, o_residual, dout.contiguous(), lse, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
+class _GDPAFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, q_offsets, kv_offsets, act, scale, causal, bias, bias_kind, bias_lo,
+                bias_hi):
+        kw = dict(act=act, scale=scale, causal=causal, bias=bias, bias_kind=bias_kind,
+                  bias_lo=bias_lo, bias_hi=bias_hi)
+        ctx.kw = kw
+        ctx.save_for_backward(q, k, v, q_offsets, kv_offsets)
+        return gdpa_forward(q, k, v, q_offsets, kv_offsets, **kw)
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, q_offsets, kv_offsets = ctx.saved_tensors
+        dq, dk, dv = gdpa_backward(q, k, v, do, q_offsets, kv_offsets, **ctx.kw)
+        return dq, dk, dv, None, None, None, None, None, None, None, None, None
+
+
+class _JFAFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, q_offsets, kv_offsets, scale, causal, bias, bias_kind, bias_lo,
+                bias_hi):
+        kw = dict(scale=scale, causal=causal, bias=bias, bias_kind=bias_kind, bias_lo=bias_lo,
+                  bias_hi=bias_hi)
+        o, lse, o_res = attn_forward(q, k, v, q_offsets, kv_offsets, **kw)
+        ctx.kw = kw
+        ctx.save_for_backward(q, k, v, o, lse, o_res, q_offsets, kv_offsets)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, o_res, q_offsets, kv_offsets = ctx.saved_tensors
+        dq, dk, dv = attn_backward(q, k, v, o, do, lse, q_offsets, kv_offsets, o_residual=o_res,
+                                   **ctx.kw)
+        return dq, dk, dv, None, None, None, None, None, None, None, None
+
+
+def gdpa(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False, bias=None,
+         bias_kind="none", bias_lo=0, bias_hi=0):
+    """Jagged GDPA with autograd (backward needs per-sample query offsets)."""
+    return _GDPAFunction.apply(q, k, v, q_offsets, kv_offsets, act, scale, causal, bias,
+                               bias_kind, bias_lo, bias_hi)
+
+
+def jagged_attention(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bias=None,
+                     bias_kind="none", bias_lo=0, bias_hi=0):
+    """Jagged flash attention (softmax) with autograd."""
+    return _JFAFunction.apply(q, k, v, q_offsets, kv_offsets, scale, causal, bias, bias_kind,
+                              bias_lo, bias_hi)

@@ -1,0 +1,92 @@
+"""Run the HIP path on a synthetic workload and compare it with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import recsys_jagged_attention_gdpa_amd as ja
+from tests.helpers import (oracle_bwd, oracle_fwd, row_check, softmax_grad_floor,
+                           structural_zero_rows)
+
+TAU = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(w, device="cuda"):
+    d = {}
+    d["q"] = w.q.to(device).contiguous()
+    d["k"] = w.k.to(device).contiguous()
+    d["v"] = w.v.to(device).contiguous()
+    d["q_off"] = None if w.q_off is None else torch.from_numpy(w.q_off).to(device)
+    d["kv_off"] = torch.from_numpy(w.kv_off).to(device)
+    d["bias"] = None if w.bias_table is None else w.bias_table.to(device).contiguous()
+    d["dout"] = None if w.dout is None else w.dout.to(device).contiguous()
+    return d
+
+
+def bias_kw(w, d):
+    return dict(bias=d["bias"], bias_kind=w.bias_kind, bias_lo=w.bias_lo, bias_hi=w.bias_hi)
+
+
+def gpu_fwd(w, d, residual=True):
+    if w.mode == "gdpa":
+        o = ja.gdpa_forward(d["q"], d["k"], d["v"], d["q_off"], d["kv_off"], act=w.act,
+                            scale=w.scale, causal=w.causal, **bias_kw(w, d))
+        return {"o": o}
+    o, lse, o_res = ja.attn_forward(d["q"], d["k"], d["v"], d["q_off"], d["kv_off"],
+                                    scale=w.scale, causal=w.causal, residual=residual,
+                                    **bias_kw(w, d))
+    return {"o": o, "lse": lse, "o_res": o_res}
+
+
+def gpu_bwd(w, d, fwd=None):
+    if w.mode == "gdpa":
+        dq, dk, dv = ja.gdpa_backward(d["q"], d["k"], d["v"], d["dout"], d["q_off"], d["kv_off"],
+                                      act=w.act, scale=w.scale, causal=w.causal, **bias_kw(w, d))
+    else:
+        fwd = fwd or gpu_fwd(w, d)
+        dq, dk, dv = ja.attn_backward(d["q"], d["k"], d["v"], fwd["o"], d["dout"], fwd["lse"],
+                                      d["q_off"], d["kv_off"], o_residual=fwd.get("o_res"),
+                                      scale=w.scale, causal=w.causal, **bias_kw(w, d))
+    return {"dq": dq, "dk": dk, "dv": dv}
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_lse(got_hq, want_th, what="lse", tol=1e-3):
+    """got [H, T] (GPU layout), want [T, H] (oracle layout)."""
+    g = got_hq.T
+    assert np.array_equal(np.isneginf(g), np.isneginf(want_th)), f"{what}: -inf pattern differs"
+    fin = np.isfinite(want_th)
+    if fin.any():
+        err = np.abs(g[fin] - want_th[fin]).max()
+        assert err <= tol, f"{what}: max |dLSE| {err:.3e} > {tol}"
+
+
+def parity(w, *, backward=True, tau=None, label=""):
+    """Full-tensor parity of the HIP path against the oracle for workload w."""
+    tau = tau or TAU[w.dtype]
+    announce(f"{label} mode={w.mode} B={w.B} H={w.H} D={w.D} dtype={w.dtype} causal={w.causal} "
+             f"bias={w.bias_kind} act={w.act} Tq={w.total_q} Tk={w.total_k}")
+    d = to_dev(w)
+    got = gpu_fwd(w, d)
+    torch.cuda.synchronize()
+    want = oracle_fwd(w)
+    zq_out, zq_in, zk = structural_zero_rows(w)
+    rep = {"o": row_check(np64(got["o"]), want["o"], tau, f"{label} O", zero_rows=zq_out)}
+    if w.mode == "jfa":
+        check_lse(np64(got["lse"]), want["lse"], f"{label} LSE")
+    if backward and w.dout is not None and w.q_off is not None:
+        g = gpu_bwd(w, d, got)
+        torch.cuda.synchronize()
+        wb = oracle_bwd(w)
+        for n, z in (("dq", zq_in), ("dk", zk), ("dv", zk)):
+            rep[n] = row_check(np64(g[n]), wb[n], tau, f"{label} {n}", zero_rows=z,
+                               abs_floor=softmax_grad_floor(w, n))
+    return rep

@@ -1,0 +1,86 @@
+"""The C-ABI library loads, exports every entry point its header declares, and
+rejects bad host-side arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from recsys_jagged_attention_gdpa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jagged_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(j[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    names = _declared_functions()
+    assert names == sorted(_lib.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.ja_version() >= 100
+    for code in (0, 1, 2, 3, 4, 6):
+        assert lib.ja_status_string(code)
+
+
+def _problem(**kw):
+    base = dict(batch=2, heads=2, head_dim=64, dtype=torch.bfloat16, total_q=10, total_k=12,
+                q_offsets=0x1000, kv_offsets=0x2000)
+    base.update(kw)
+    return _lib.make_problem(**base)
+
+
+def test_workspace_size_is_positive_and_aligned():
+    for pass_ in (_lib.PASS_FWD, _lib.PASS_BWD):
+        n = _lib.ja_workspace_size(_problem(), pass_)
+        assert n > 0 and n % 256 == 0
+    assert _lib.ja_workspace_size(_problem(), 7) == 0
+    big = _lib.ja_workspace_size(_problem(total_q=1 << 20), _lib.PASS_BWD)
+    assert big > _lib.ja_workspace_size(_problem(), _lib.PASS_BWD)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=48), 3), (dict(head_dim=256), 3), (dict(dtype=5), 3), (dict(act=9), 3),
+    (dict(bias_kind=4), 3), (dict(batch=0), 2), (dict(heads=0), 2), (dict(total_q=-1), 2),
+    (dict(kv_offsets=None), 1), (dict(bias_kind="rel", bias_table=None), 1),
+    (dict(bias_kind="rel", bias_table=0x3000, bias_lo=5, bias_hi=1), 2),
+    (dict(q_offsets=None, lq_fixed=3, total_q=4), 2),
+])
+def test_bad_problems_are_rejected_before_launch(kw, code):
+    lib = _lib.load()
+    p = _problem(**kw)
+    assert lib.ja_workspace_size(ctypes.byref(p), 0) == 0
+    P = ctypes.c_void_p
+    st = lib.jagged_gdpa_fwd(ctypes.byref(p), P(0x10), P(0x20), P(0x30), P(0x40), P(0x100),
+                             ctypes.c_size_t(1 << 30), None)
+    assert st == code, (kw, st)
+
+
+def test_null_tensors_and_workspace_errors():
+    lib = _lib.load()
+    p = _problem()
+    P = ctypes.c_void_p
+    ws = ctypes.c_size_t(1 << 30)
+    assert lib.jagged_gdpa_fwd(ctypes.byref(p), None, P(0x20), P(0x30), P(0x40), P(0x100), ws, None) == 1
+    assert lib.jagged_attn_fwd(ctypes.byref(p), P(0x10), P(0x20), P(0x30), P(0x40), None, None, P(0x100), ws, None) == 1
+    # misaligned, missing and too small workspaces
+    assert lib.jagged_gdpa_fwd(ctypes.byref(p), P(0x10), P(0x20), P(0x30), P(0x40), P(0x104), ws, None) == 4
+    assert lib.jagged_gdpa_fwd(ctypes.byref(p), P(0x10), P(0x20), P(0x30), P(0x40), None, ws, None) == 4
+    assert lib.jagged_gdpa_fwd(ctypes.byref(p), P(0x10), P(0x20), P(0x30), P(0x40), P(0x100),
+                               ctypes.c_size_t(64), None) == 4
+    # backward needs per-sample query offsets and every gradient buffer
+    ps = _problem(q_offsets=None, lq_fixed=10, total_q=10)
+    assert lib.jagged_gdpa_bwd(ctypes.byref(ps), P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(0x100), ws, None) == 3
+    assert lib.jagged_gdpa_bwd(ctypes.byref(p), P(1), P(2), P(3), P(4), None, P(6), P(7), P(0x100), ws, None) == 1
+    assert lib.jagged_attn_bwd(ctypes.byref(p), P(1), P(2), P(3), None, None, P(4), P(5), P(6), P(7),
+                               P(8), P(0x100), ws, None) == 1

@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Throughput of the jagged attention hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+planning, forward and backward (GDPA cross-attention with 32 keys per sample
+and jagged queries, B=1024, H=4, D=128, by default).  Inputs are resident in
+HBM before the timed region.  Prints ONE JSON line on stdout; details go to
+stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Metric: useful (unpadded) TFLOP/s of forward + backward.  Useful work counts
+only valid (query, key) pairs P: forward 4 D P, backward 10 D P (five
+GEMM-sized products per pair).  The dominant kernel is also placed on its
+roofline (HBM bytes or MFMA FLOPs per launch / its average duration, timed with
+HIP events recorded by the library around that kernel's launches).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from recsys_jagged_attention_gdpa_amd import _lib, synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+KERNEL_SOURCES = ["ja_fwd.hip", "ja_bwd.hip", "ja_plan.hip", "ja_tiles.h", "ja_device.h",
+                  "ja_kernels.h"]
+
+# Workloads: which roofline bounds them (short K/V streams Q / dO / O through HBM;
+# long sequences are MFMA work).
+BOUND = {"gdpa_xattn_short_kv": "hbm", "pma_gdpa_fwd": "hbm", "jfa_causal_self": "mfma",
+         "longtail_gdpa": "mfma", "tiny_gdpa_fp32": "hbm"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ accounting
+def valid_pairs(w) -> int:
+    """P summed over samples (per head); heads multiply it."""
+    lq = w.lq.astype(np.int64)
+    lk = w.lk.astype(np.int64)
+    if not w.causal:
+        return int((lq * lk).sum())
+    tot = 0
+    for a, b in zip(lq, lk):
+        i = np.arange(a, dtype=np.int64)
+        tot += int(np.clip(i + b - a + 1, 0, b).sum())
+    return tot
+
+
+def kernel_cost(w, kernel: str) -> tuple[float, float]:
+    """Algorithmic (bytes, flops) one launch of `kernel` processes for workload w."""
+    e = w.q.element_size()
+    HD = w.H * w.D
+    P = valid_pairs(w) * w.H
+    tq_out, tq, tk = w.total_q_out, w.total_q, w.total_k
+    q_rows = w.q.shape[0]
+    if kernel == "fwd":
+        b = e * HD * (q_rows + tq_out + 2 * tk) + (4 * w.H * tq_out if w.mode == "jfa" else 0)
+        return b, 4.0 * w.D * P
+    if kernel == "bwd_fused":  # read Q, dO, K, V; write dQ, dK, dV; five GEMMs per pair
+        return e * HD * (3 * tq + 4 * tk), 10.0 * w.D * P
+    if kernel == "bwd_kv":     # read Q, dO, K, V; write dK, dV; four GEMMs per pair
+        return e * HD * (2 * tq + 4 * tk), 8.0 * w.D * P
+    if kernel == "bwd_q":      # read Q, dO, K, V; write dQ; three GEMMs per pair
+        return e * HD * (3 * tq + 2 * tk), 6.0 * w.D * P
+    if kernel == "bwd_delta":
+        return e * HD * 2 * tq + 4 * w.H * tq, 2.0 * HD * tq
+    return 0.0, 0.0
+
+
+# ------------------------------------------------------------------ HIP events
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        self.made.append(ev)
+        return ev
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, rc
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.made:
+            self.hip.hipEventDestroy(ev)
+        self.made = []
+
+
+# ------------------------------------------------------------------ the step
+class Runner:
+    def __init__(self, w, device="cuda"):
+        self.w = w
+        dev = torch.device(device)
+        self.q = w.q.to(dev)
+        self.k = w.k.to(dev)
+        self.v = w.v.to(dev)
+        self.dout = None if w.dout is None else w.dout.to(dev)
+        self.q_off = None if w.q_off is None else torch.from_numpy(w.q_off).to(dev)
+        self.kv_off = torch.from_numpy(w.kv_off).to(dev)
+        self.bias = None if w.bias_table is None else w.bias_table.to(dev)
+        self.prob = _lib.make_problem(
+            batch=w.B, heads=w.H, head_dim=w.D, dtype=w.dtype, total_q=w.q.shape[0],
+            total_k=w.total_k, q_offsets=self.q_off, kv_offsets=self.kv_off,
+            lq_fixed=w.lq_fixed, causal=w.causal, scale=w.scale, act=w.act,
+            bias_kind=w.bias_kind, bias_table=self.bias, bias_lo=w.bias_lo, bias_hi=w.bias_hi)
+        rows = w.total_q_out
+        self.o = torch.empty((rows, w.H, w.D), dtype=w.dtype, device=dev)
+        self.lse = torch.empty((w.H, rows), dtype=torch.float32, device=dev)
+        self.o_res = torch.empty_like(self.o) if (w.mode == "jfa" and w.dtype == torch.bfloat16) else None
+        self.ws_f = torch.empty(_lib.ja_workspace_size(self.prob, _lib.PASS_FWD), dtype=torch.uint8, device=dev)
+        self.backward = bool(w.backward and w.q_off is not None and self.dout is not None)
+        if self.backward:
+            self.dq = torch.empty_like(self.q)
+            self.dk = torch.empty_like(self.k)
+            self.dv = torch.empty_like(self.v)
+            self.ws_b = torch.empty(_lib.ja_workspace_size(self.prob, _lib.PASS_BWD), dtype=torch.uint8, device=dev)
+
+    def kernels(self):
+        ks = ["plan", "fwd"]
+        if self.backward:
+            ks += ["bwd_fused", "bwd_kv", "bwd_q"] + (["bwd_delta"] if self.w.mode == "jfa" else [])
+        return ks
+
+    def step(self):
+        p, w = self.prob, self.w
+        if w.mode == "gdpa":
+            _lib.jagged_gdpa_fwd(p, self.q, self.k, self.v, self.o, self.ws_f)
+            if self.backward:
+                _lib.jagged_gdpa_bwd(p, self.q, self.k, self.v, self.dout, self.dq, self.dk, self.dv, self.ws_b)
+        else:
+            _lib.jagged_attn_fwd(p, self.q, self.k, self.v, self.o, self.lse, self.o_res, self.ws_f)
+            if self.backward:
+                _lib.jagged_attn_bwd(p, self.q, self.k, self.v, self.o, self.o_res, self.dout, self.lse,
+                                     self.dq, self.dk, self.dv, self.ws_b)
+
+
+def kernel_durations(runner, ev, kernels, reps=3):
+    """Average duration (ms) of each kernel over `reps` steps (events from the library)."""
+    out = {}
+    for kname in kernels:
+        pairs = [(ev.create(), ev.create()) for _ in range(reps)]
+        for a, b in pairs:
+            _lib.ja_profile_kernel(kname, a, b)
+            runner.step()
+        _lib.ja_profile_kernel(kname, None, None)
+        torch.cuda.synchronize()
+        out[kname] = sum(ev.elapsed_ms(a, b) for a, b in pairs) / reps
+    return out
+
+
+# ------------------------------------------------------------------ traffic
+def sources_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "recsys_jagged_attention_gdpa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("sources_digest") != sources_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU oracle
+def cpu_baseline(w, target_s=15.0):
+    """Time the fp64 oracle (forward + backward) on a bounded sample of samples."""
+    from oracle import ref  # test infrastructure: only this leg of the benchmark uses it
+    from tests.helpers import oracle_bwd, oracle_fwd
+
+    rng = np.random.default_rng(7)
+    order = rng.permutation(w.B)
+    cores = ref.max_threads()
+
+    def run(idx):
+        s = w.subset(sorted(int(i) for i in idx))
+        t0 = time.perf_counter()
+        oracle_fwd(s)
+        if w.backward and w.q_off is not None:
+            oracle_bwd(s)
+        dt = time.perf_counter() - t0
+        useful = (4.0 + (10.0 if (w.backward and w.q_off is not None) else 0.0)) * w.D * valid_pairs(s) * s.H
+        return dt, useful
+
+    n = max(1, min(w.B, 16))
+    dt, useful = run(order[:n])
+    while dt < target_s / 4 and n < w.B:
+        n = min(w.B, int(n * max(2.0, min(8.0, target_s / max(dt, 1e-3)))))
+        dt, useful = run(order[:n])
+    return {"value": useful / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.B} samples (random, seed 7), all heads, forward"
+                      f"{' + backward' if w.backward and w.q_off is not None else ''}, "
+                      f"fp64, {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gdpa_xattn_short_kv", choices=sorted(synth.CATALOGUE))
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(samples shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    _lib.load()
+
+    t0 = time.perf_counter()
+    w = synth.make(args.workload, args.seed)
+    log(f"[bench] workload {args.workload}: B={w.B} H={w.H} D={w.D} Tq={w.total_q} Tk={w.total_k} "
+        f"generated in {time.perf_counter() - t0:.1f}s")
+    runner = Runner(w)
+    ev = HipEvents()
+
+    for _ in range(args.warmup):
+        runner.step()
+    torch.cuda.synchronize()
+
+    # per-kernel durations (outside the timed region) to find the dominant kernel
+    durs = kernel_durations(runner, ev, runner.kernels())
+    dominant = max(durs, key=durs.get)
+    log("[bench] kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in durs.items()))
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
+
+    # timed region: exactly K steps, dominant kernel timed by events on its own stream
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for a, b in pairs:
+        _lib.ja_profile_kernel(dominant, a, b)
+        runner.step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    _lib.ja_profile_kernel(dominant, None, None)
+    dom_ms = sum(ev.elapsed_ms(a, b) for a, b in pairs) / args.steps
+    ev.close()
+
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    P = valid_pairs(w) * w.H
+    useful = (4.0 + (10.0 if runner.backward else 0.0)) * w.D * P
+    value = useful / (ms_per_step * 1e-3) / 1e12
+    dom_bytes, dom_flops = kernel_cost(w, dominant)
+    bound = BOUND.get(args.workload, "hbm")
+    if bound == "hbm":
+        achieved, peak, unit = dom_bytes / (dom_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = dom_flops / (dom_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    traffic = measured_traffic(args.workload, dominant)
+    lq = w.lq.astype(np.int64)
+    sparsity = 1.0 - float(lq.sum()) / (w.B * max(int(lq.max()), 1))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": "useful (unpadded) TFLOP/s fwd+bwd and % bf16 MFMA peak, sparsity-0.5 jagged",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": w.B, "H": w.H, "D": w.D,
+                   "total_q": w.total_q, "total_k": w.total_k, "act": w.act if w.mode == "gdpa" else "softmax",
+                   "causal": w.causal, "bias": w.bias_kind, "jagged_sparsity": round(sparsity, 4),
+                   "useful_pairs": P, "backward": runner.backward},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "algorithmic_bytes": dom_bytes,
+                     "algorithmic_flops": dom_flops, "avg_ms": round(dom_ms, 5)},
+        "kernel_ms": {k: round(v, 5) for k, v in durs.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

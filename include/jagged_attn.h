@@ -135,6 +135,22 @@ ja_status jagged_attn_bwd(const ja_problem *p, const void *q, const void *k, con
                           const float *lse, void *dq, void *dk, void *dv, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* Measurement aid.  Kernels a call may launch: */
+typedef enum {
+    JA_KERNEL_PLAN = 0,       /* work-list planner */
+    JA_KERNEL_FWD = 1,        /* forward attention */
+    JA_KERNEL_BWD_FUSED = 2,  /* backward, samples with <= 32 keys */
+    JA_KERNEL_BWD_KV = 3,     /* backward dK/dV units */
+    JA_KERNEL_BWD_Q = 4,      /* backward dQ units */
+    JA_KERNEL_BWD_DELTA = 5   /* JFA backward delta preprocess */
+} ja_kernel_id;
+
+/* From now on, in every call made by the calling thread, record start_event
+ * immediately before and stop_event immediately after launching kernel
+ * `kernel_id`, on the call's stream (both are hipEvent_t created by the
+ * caller).  NULL events switch this off.  Thread-local; never synchronises. */
+ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event);
+
 /* Human-readable name of a status code (static storage). */
 const char *ja_status_string(int status);
 

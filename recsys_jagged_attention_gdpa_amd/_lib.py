@@ -26,7 +26,9 @@ BIAS = {"none": 0, "rel": 1, "keypos": 2}
 PASS_FWD, PASS_BWD = 0, 1
 
 EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_attn_fwd",
-           "jagged_attn_bwd", "ja_status_string", "ja_last_hip_error", "ja_version")
+           "jagged_attn_bwd", "ja_profile_kernel", "ja_status_string", "ja_last_hip_error",
+           "ja_version")
+KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5}
 
 
 class JaProblem(ctypes.Structure):
@@ -72,6 +74,8 @@ def load(path: str = LIB_PATH):
         lib.jagged_attn_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in (lib.jagged_gdpa_fwd, lib.jagged_attn_fwd, lib.jagged_gdpa_bwd, lib.jagged_attn_bwd):
             f.restype = ctypes.c_int
+        lib.ja_profile_kernel.argtypes = [ctypes.c_int, P, P]
+        lib.ja_profile_kernel.restype = ctypes.c_int
         lib.ja_status_string.argtypes = [ctypes.c_int]
         lib.ja_status_string.restype = ctypes.c_char_p
         lib.ja_last_hip_error.argtypes = []
@@ -151,6 +155,13 @@ def jagged_attn_bwd(problem, q, k, v, o, o_residual, dout, lse, dq, dk, dv, work
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_residual), _ptr(dout),
         _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
+
+
+def ja_profile_kernel(kernel, start_event, stop_event):
+    """Record raw hipEvent_t handles around `kernel` ("fwd", "bwd_fused", ...) in later calls
+    on this thread; pass None, None to stop."""
+    kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    _check("ja_profile_kernel", load().ja_profile_kernel(kid, start_event, stop_event))
 
 
 def _nbytes(t):

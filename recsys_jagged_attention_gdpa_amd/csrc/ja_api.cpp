@@ -13,6 +13,7 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+thread_local ja::KernelTimer g_timer;
 
 constexpr size_t ALIGN = 256;
 constexpr int MAX_DEVICES = 64;
@@ -215,7 +216,18 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
 
 }  // namespace
 
+const ja::KernelTimer &ja::kernel_timer() { return g_timer; }
+
 extern "C" {
+
+ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event) {
+    if (kernel_id < JA_KERNEL_PLAN || kernel_id > JA_KERNEL_BWD_DELTA) return JA_ERR_UNSUPPORTED;
+    if ((start_event == nullptr) != (stop_event == nullptr)) return JA_ERR_NULL;
+    g_timer.which = start_event ? kernel_id : -1;
+    g_timer.start = static_cast<hipEvent_t>(start_event);
+    g_timer.stop = static_cast<hipEvent_t>(stop_event);
+    return JA_OK;
+}
 
 size_t ja_workspace_size(const ja_problem *p, int pass) {
     if (pass != JA_PASS_FWD && pass != JA_PASS_BWD) return 0;

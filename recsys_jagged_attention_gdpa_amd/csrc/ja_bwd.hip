@@ -471,13 +471,22 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void fused_kernel(const AttnParams 
 // -------------------------------------------------------------- launches
 template <int D, int MODE, int ACT>
 static hipError_t launch_bwd_t(const AttnParams &p, int grid, hipStream_t st) {
+    const KernelTimer &t = kernel_timer();
     if (MODE == JFA && p.total_q > 0) {
         const int64_t threads = p.total_q * p.H * (D / 8);
+        t.begin(K_BWD_DELTA, st);
         hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, p);
+        t.end(K_BWD_DELTA, st);
     }
+    t.begin(K_BWD_FUSED, st);
     hipLaunchKernelGGL((fused_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, p);
+    t.end(K_BWD_FUSED, st);
+    t.begin(K_BWD_KV, st);
     hipLaunchKernelGGL((dkdv_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, p);
+    t.end(K_BWD_KV, st);
+    t.begin(K_BWD_Q, st);
     hipLaunchKernelGGL((dq_kernel<D, MODE, ACT>), dim3(grid), dim3(BWD_THREADS), 0, st, p);
+    t.end(K_BWD_Q, st);
     return hipGetLastError();
 }
 

@@ -215,7 +215,10 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
 
 template <int D, int MODE, int ACT>
 static hipError_t launch_fwd_t(const AttnParams &p, int grid, hipStream_t stream) {
+    const KernelTimer &t = kernel_timer();
+    t.begin(K_FWD, stream);
     hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT>), dim3(grid), dim3(FWD_THREADS), 0, stream, p);
+    t.end(K_FWD, stream);
     return hipGetLastError();
 }
 

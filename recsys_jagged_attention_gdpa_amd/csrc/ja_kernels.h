@@ -77,6 +77,20 @@ struct PlanBatch {
 };
 hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream);
 
+// Optional per-kernel event recording around launches (measurement aid).
+enum KernelId { K_PLAN = 0, K_FWD = 1, K_BWD_FUSED = 2, K_BWD_KV = 3, K_BWD_Q = 4, K_BWD_DELTA = 5 };
+struct KernelTimer {
+    int which = -1;
+    hipEvent_t start = nullptr, stop = nullptr;
+    void begin(int id, hipStream_t s) const {
+        if (id == which && start) (void)hipEventRecord(start, s);
+    }
+    void end(int id, hipStream_t s) const {
+        if (id == which && stop) (void)hipEventRecord(stop, s);
+    }
+};
+const KernelTimer &kernel_timer();
+
 // mode: 0 GDPA, 1 JFA.  act: 0 SiLU, 1 GELU tanh, 2 GELU erf.
 hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream);
 hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream);

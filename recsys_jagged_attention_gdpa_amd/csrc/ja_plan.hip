@@ -157,7 +157,10 @@ hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream) {
     if (n < 1 || n > PLAN_MAX) return hipErrorInvalidValue;
     PlanBatch batch{};
     for (int i = 0; i < n; ++i) batch.list[i] = lists[i];
+    const KernelTimer &t = kernel_timer();
+    t.begin(K_PLAN, stream);
     hipLaunchKernelGGL(plan_kernel, dim3(n), dim3(PLAN_THREADS), 0, stream, batch);
+    t.end(K_PLAN, stream);
     return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ def kernel_cost(w, kernel: str) -> tuple[float, float]:
     P = valid_pairs(w) * w.H
     tq_out, tq, tk = w.total_q_out, w.total_q, w.total_k
     q_rows = w.q.shape[0]
-    if kernel == "fwd":
+    if kernel in ("fwd", "fwd_short"):
         b = e * HD * (q_rows + tq_out + 2 * tk) + (4 * w.H * tq_out if w.mode == "jfa" else 0)
         return b, 4.0 * w.D * P
     if kernel == "bwd_fused":  # read Q, dO, K, V; write dQ, dK, dV; five GEMMs per pair
@@ -142,7 +142,7 @@ class Runner:
             self.ws_b = torch.empty(_lib.ja_workspace_size(self.prob, _lib.PASS_BWD), dtype=torch.uint8, device=dev)
 
     def kernels(self):
-        ks = ["plan", "fwd"]
+        ks = ["plan", "fwd_short", "fwd"]
         if self.backward:
             ks += ["bwd_fused", "bwd_kv", "bwd_q"] + (["bwd_delta"] if self.w.mode == "jfa" else [])
         return ks
@@ -266,13 +266,14 @@ def main():
     log("[bench] kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in durs.items()))
 
     if args.calibrate_copy_mib:
+        # one element-wise kernel that reads n bytes and writes n bytes
         n = args.calibrate_copy_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {n} bytes done")
+        log(f"[bench] calibration copy kernel: read {n} bytes, wrote {n} bytes")
 
     # timed region: exactly K steps, dominant kernel timed by events on its own stream
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]

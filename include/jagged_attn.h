@@ -138,11 +138,12 @@ ja_status jagged_attn_bwd(const ja_problem *p, const void *q, const void *k, con
 /* Measurement aid.  Kernels a call may launch: */
 typedef enum {
     JA_KERNEL_PLAN = 0,       /* work-list planner */
-    JA_KERNEL_FWD = 1,        /* forward attention */
+    JA_KERNEL_FWD = 1,        /* forward attention, samples with > 32 keys */
     JA_KERNEL_BWD_FUSED = 2,  /* backward, samples with <= 32 keys */
     JA_KERNEL_BWD_KV = 3,     /* backward dK/dV units */
     JA_KERNEL_BWD_Q = 4,      /* backward dQ units */
-    JA_KERNEL_BWD_DELTA = 5   /* JFA backward delta preprocess */
+    JA_KERNEL_BWD_DELTA = 5,  /* JFA backward delta preprocess */
+    JA_KERNEL_FWD_SHORT = 6   /* forward attention, samples with <= 32 keys */
 } ja_kernel_id;
 
 /* From now on, in every call made by the calling thread, record start_event

@@ -28,7 +28,8 @@ PASS_FWD, PASS_BWD = 0, 1
 EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_attn_fwd",
            "jagged_attn_bwd", "ja_profile_kernel", "ja_status_string", "ja_last_hip_error",
            "ja_version")
-KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5}
+KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5,
+           "fwd_short": 6}
 
 
 class JaProblem(ctypes.Structure):

@@ -57,11 +57,11 @@ Layout layout_of(const ja_problem &p, int pass) {
     off += align_up(3 * sizeof(ja::PlanCounters));
     L.tiles_q = off;
     off += align_up((size_t)L.cap_q * sizeof(int2));
+    L.tiles_s = off;
+    off += align_up((size_t)L.cap_s * sizeof(int2));
     if (pass == JA_PASS_BWD) {
         L.tiles_k = off;
         off += align_up((size_t)L.cap_k * sizeof(int2));
-        L.tiles_s = off;
-        off += align_up((size_t)L.cap_s * sizeof(int2));
         L.delta = off;
         off += align_up((size_t)p.heads * (size_t)(p.total_q > 0 ? p.total_q : 1) * sizeof(float));
     }
@@ -176,8 +176,13 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
     a.lse = lse;
     a.o_res_out = p->dtype == JA_BF16 ? o_res : nullptr;
     if (p->dtype == JA_F32) return hip_status(ja::launch_fwd_f32(a, p->head_dim, mode, p->act, s));
-    ja::PlanParams pp[1] = {plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 0, a.tiles, L.cap_q, a.counters)};
-    hipError_t e = ja::launch_plan(pp, 1, s);
+    // two unit lists: query tiles of samples with more than 32 keys, and whole
+    // (sample, head) units of samples with at most 32 keys
+    a.tiles2 = a.tiles3;
+    a.counters2 = a.counters3;
+    ja::PlanParams pp[2] = {plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 1, a.tiles, L.cap_q, a.counters),
+                            plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3)};
+    hipError_t e = ja::launch_plan(pp, 2, s);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(ja::launch_fwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), s));
 }
@@ -221,7 +226,7 @@ const ja::KernelTimer &ja::kernel_timer() { return g_timer; }
 extern "C" {
 
 ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event) {
-    if (kernel_id < JA_KERNEL_PLAN || kernel_id > JA_KERNEL_BWD_DELTA) return JA_ERR_UNSUPPORTED;
+    if (kernel_id < JA_KERNEL_PLAN || kernel_id > JA_KERNEL_FWD_SHORT) return JA_ERR_UNSUPPORTED;
     if ((start_event == nullptr) != (stop_event == nullptr)) return JA_ERR_NULL;
     g_timer.which = start_event ? kernel_id : -1;
     g_timer.start = static_cast<hipEvent_t>(start_event);

@@ -101,6 +101,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int n_units = p.counters->units;
+    if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
     for (;;) {
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
                 for (int e = 0; e < 16; ++e) {
                     const int j = j0 + nb * 32 + crow(e, g);
                     const float bias = brow ? bias_at(bz, brow, irow, j) : 0.0f;
-                    const bool valid = !masked || (row_ok && j < my_kend);
+                    const bool valid = !masked | (row_ok & (j < my_kend));  // bitwise: no per-lane branches
                     score_bwd<MODE, ACT>(sacc[e], p.scale, bias, dpacc[e], lse2, dlt, valid, dx[e]);
                 }
                 pack_operands(dx, dsb[2 * nb], dsb[2 * nb + 1]);
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int n_units = p.counters2->units;
+    if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
     for (;;) {
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
                     const int il = qb * 32 + crow(e, g);
                     const int i = ia + il;
                     const float bias = brow ? bias_at(bz, brow, i, jkey) : 0.0f;
-                    const bool valid = !masked || (i < s.lq && (!p.causal || jkey <= i + shift));
+                    const bool valid = !masked | ((i < s.lq) & (!p.causal | (jkey <= i + shift)));
                     float lse2 = 0.0f, dlt = 0.0f;
                     if constexpr (MODE == JFA) {
                         lse2 = s_lse[il];
@@ -297,44 +299,40 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
 }
 
 // ------------------------------------------------- fused short-K/V units
-// One unit per (sample, head) with at most 32 keys.  Waves take 32-row query
-// blocks in turn; each block computes X, dP once, then dV, dK (registers),
-// dX^T through a small LDS transpose, and dQ of the block.  At the end the
-// four waves' dK / dV partials are summed through LDS and stored.
+// One unit per (sample, head) with at most 32 keys, run by ONE wave (the
+// workgroup is a single wave): the wave keeps K and V as MFMA operands in
+// registers, streams the sample's query rows in 32-row blocks, loading the
+// next block's Q and dO rows into registers while the current block is
+// computed (outer-loop pipelining: the inner loop over keys has one step),
+// and owns dK and dV for the whole sample, so no barrier and no cross-wave
+// reduction is needed.  A block computes X and dP once, dV and dK into
+// registers, dX^T through a small LDS transpose, and the block's complete dQ.
+// Memory accesses go through per-sample buffer descriptors (no branches
+// around them), so the next block's loads stay in flight.
 template <int D, int MODE, int ACT>
-__global__ __launch_bounds__(BWD_THREADS, 1) void fused_kernel(const AttnParams p) {
+__global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
     constexpr int NKK = D / 16, NDB = D / 32;
-    constexpr int KV_BYTES = 32 * D * 2;       // one 32-row tile
+    constexpr int TILE = 32 * D * 2;           // one 32-row tile
     constexpr int DS_STRIDE = 80;              // bytes per row of the dX scratch (32 bf16 + pad)
     constexpr int DS_BYTES = 32 * DS_STRIDE;
-    constexpr int WAVE_BYTES = 2 * KV_BYTES + DS_BYTES;
-    constexpr int RED_BYTES = 3 * NDB * 16 * 64 * 4;  // three waves' partials of one accumulator
-    constexpr int LOOP_BYTES = 2 * KV_BYTES + 4 * WAVE_BYTES;
-    constexpr int SMEM = LOOP_BYTES > 2 * KV_BYTES + RED_BYTES ? LOOP_BYTES : 2 * KV_BYTES + RED_BYTES;
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
-    __shared__ int s_unit;
-    lchar *const Kt = (lchar *)smem;
-    lchar *const Vt = Kt + KV_BYTES;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    lchar *const Qw = Kt + 2 * KV_BYTES + wv * WAVE_BYTES;
-    lchar *const Gw = Qw + KV_BYTES;
-    lchar *const Sw = Gw + KV_BYTES;
-    float *const red = (float *)(smem + 2 * KV_BYTES);
+    __shared__ __attribute__((aligned(16))) char smem[4 * TILE + DS_BYTES];
+    lchar *const Qt = (lchar *)smem;   // this block's Q rows
+    lchar *const Gt = Qt + TILE;       // this block's dO rows
+    lchar *const Kt = Gt + TILE;       // the sample's keys (resident for the unit)
+    lchar *const Vt = Kt + TILE;       // the sample's values
+    lchar *const Sx = Vt + TILE;       // dX transpose scratch
 
-    const bf16 *__restrict__ Q = static_cast<const bf16 *>(p.q);
-    const bf16 *__restrict__ K = static_cast<const bf16 *>(p.k);
-    const bf16 *__restrict__ V = static_cast<const bf16 *>(p.v);
-    const bf16 *__restrict__ G = static_cast<const bf16 *>(p.dout);
     const int H = p.H;
+    const int lane = threadIdx.x;
     const int g = lane >> 5, l32 = lane & 31;
     const int n_units = p.counters3->units;
+    if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
     for (;;) {
-        if (threadIdx.x == 0) s_unit = atomicAdd(&p.counters3->cursor, 1);
-        __syncthreads();
-        const int w = s_unit;
-        __syncthreads();
+        int w = 0;
+        if (lane == 0) w = atomicAdd(&p.counters3->cursor, 1);
+        w = __builtin_amdgcn_readfirstlane(w);
         if (w >= n_units) break;
         const int2 tile = p.tiles3[w / H];
         const int h = w % H;
@@ -343,58 +341,65 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void fused_kernel(const AttnParams 
         const bool key_ok = jkey < s.lk;
         const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
         const int shift = s.lk - s.lq;
+        const int nblk = (s.lq + 31) / 32;
+        const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h), Gs(p.dout, s.qs, s.lq, H, h), dQs(p.dq, s.qs, s.lq, H, h);
+        const HeadSlice<D> Ks(p.k, s.ks, s.lk, H, h), Vs(p.v, s.ks, s.lk, H, h);
+        const rsrc_t lse_r = make_rsrc(p.lse ? p.lse + (int64_t)h * p.total_q + s.qs : nullptr,
+                                       MODE == JFA ? (uint32_t)s.lq * 4u : 0u);
+        const rsrc_t dlt_r = make_rsrc(p.delta ? p.delta + (int64_t)h * p.total_q + s.qs : nullptr,
+                                       MODE == JFA ? (uint32_t)s.lq * 4u : 0u);
 
-        {   // keys and values of the sample -> LDS (for the transposing reads of dQ)
-            PairLoader<32, D, BWD_THREADS> kv;
-            kv.load(K, V, s.ks, H, h, 0, s.lk, threadIdx.x);
-            kv.store(Kt, Vt, threadIdx.x);
+        // Keys and values of the sample (rows past lk read as zeros) and the
+        // first query block; all waited for before the block loop, so that the
+        // waits the compiler derives inside the loop reflect only the loop's
+        // own order (next block's loads, then this block's stores).
+        PairSliceLoader<32, D, WAVE> nx;
+        {
+            PairSliceLoader<32, D, WAVE> kv;
+            kv.load(Ks, Vs, 0, lane);
+            nx.load(Qs, Gs, 0, lane);
+            kv.store(Kt, Vt, lane);
         }
-        bf16x8 kreg[NKK], vreg[NKK];
-        load_row_operand<D>(kreg, K, s.ks + jkey, H, h, key_ok, g);
-        load_row_operand<D>(vreg, V, s.ks + jkey, H, h, key_ok, g);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
         f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dkacc[db] = dvacc[db] = f32x16{};
-        __syncthreads();
 
-        const int nblk = (s.lq + 31) / 32;
-        for (int blk = wv; blk < nblk; blk += 4) {
+        for (int blk = 0; blk < nblk; ++blk) {
             const int ia = blk * 32;
-            {   // this wave's 32 query rows of Q and dO -> its LDS tiles
-                PairLoader<32, D, 64> qg;
-                qg.load(Q, G, s.qs, H, h, ia, s.lq, lane);
-                qg.store(Qw, Gw, lane);
-            }
-            float lse2[16], dlt[16];
+            nx.store(Qt, Gt, lane);
+            lds_wave_sync();
+            float lse2[16], dlt[16], bv[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                lse2[e] = 0.0f;
-                dlt[e] = 0.0f;
-                if constexpr (MODE == JFA) {
-                    const int i = ia + crow(e, g);
-                    if (i < s.lq) {
-                        lse2[e] = p.lse[(int64_t)h * p.total_q + s.qs + i] * LOG2E;
-                        dlt[e] = p.delta[(int64_t)h * p.total_q + s.qs + i];
-                    }
-                }
+                const uint32_t off = (uint32_t)(ia + crow(e, g)) * 4u;
+                lse2[e] = MODE == JFA ? buf_load_f32(lse_r, off) * LOG2E : 0.0f;
+                dlt[e] = MODE == JFA ? buf_load_f32(dlt_r, off) : 0.0f;
+                bv[e] = 0.0f;
             }
-            lds_wave_sync();
+            if (brow) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) bv[e] = bias_at(bz, brow, ia + crow(e, g), jkey);
+            }
+            nx.load(Qs, Gs, ia + 32, lane);  // next block; past the sample: zeros, no traffic
+            __builtin_amdgcn_sched_barrier(0);  // keep the next block's loads ahead of this block's work
 
+            // X = Q K^T and dP = dO V^T: lane holds key jkey, query rows crow(e, g).
             f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const int off = lds_off<D>(l32, 2 * kk + g);
-                sacc = mfma32(lds_read16(Qw, off), kreg[kk], sacc);
-                dpacc = mfma32(lds_read16(Gw, off), vreg[kk], dpacc);
+                sacc = mfma32(lds_read16(Qt, off), lds_read16(Kt, off), sacc);
+                dpacc = mfma32(lds_read16(Gt, off), lds_read16(Vt, off), dpacc);
             }
-            const bool masked = (ia + 32 > s.lq) || (s.lk < 32) || p.causal;
+            const bool masked = (ia + 32 > s.lq) | (s.lk < 32) | (p.causal != 0);
             float pv[16], dx[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int i = ia + crow(e, g);
-                const float bias = brow ? bias_at(bz, brow, i, jkey) : 0.0f;
-                const bool valid = !masked || (i < s.lq && key_ok && (!p.causal || jkey <= i + shift));
-                pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bias, dpacc[e], lse2[e], dlt[e], valid, dx[e]);
+                const bool valid = !masked | ((i < s.lq) & key_ok & (!p.causal | (jkey <= i + shift)));
+                pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bv[e], dpacc[e], lse2[e], dlt[e], valid, dx[e]);
             }
             bf16x8 pb[2], dsb[2];
             pack_operands(pv, pb[0], pb[1]);
@@ -403,68 +408,43 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void fused_kernel(const AttnParams 
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    dvacc[db] = mfma32(lds_read_tr_operand<D>(Gw, ks * 16, db * 32, lane), pb[ks], dvacc[db]);
-                    dkacc[db] = mfma32(lds_read_tr_operand<D>(Qw, ks * 16, db * 32, lane), dsb[ks], dkacc[db]);
+                    dvacc[db] = mfma32(lds_read_tr_operand<D>(Gt, ks * 16, db * 32, lane), pb[ks], dvacc[db]);
+                    dkacc[db] = mfma32(lds_read_tr_operand<D>(Qt, ks * 16, db * 32, lane), dsb[ks], dkacc[db]);
                 }
             }
-            // dX (query i, key j) -> scratch row i, column j (bf16).
+            // dX (query i, key j) -> scratch row i, column j; read back as dX^T operands.
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int i = crow(e, g);
-                *reinterpret_cast<__attribute__((address_space(3))) bf16 *>(Sw + i * DS_STRIDE + jkey * 2) = f2bf(dx[e]);
+                *reinterpret_cast<__attribute__((address_space(3))) bf16 *>(Sx + i * DS_STRIDE + jkey * 2) = f2bf(dx[e]);
             }
             lds_wave_sync();
-            // dQ^T = K^T dX^T: B operand = row l32 of the scratch, keys ks*16 + g*4 + 0..3 and +8.
             bf16x8 dtb[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const lchar *row = Sw + l32 * DS_STRIDE + (ks * 16 + g * 4) * 2;
+                const lchar *row = Sx + l32 * DS_STRIDE + (ks * 16 + g * 4) * 2;
                 const u32x2 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x2 *>(row);
                 const u32x2 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x2 *>(row + 16);
                 dtb[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
-            f32x16 dqacc[NDB];
+            // dQ^T = K^T dX^T, one 32-wide block of the head dimension at a time.
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                dqacc[db] = f32x16{};
+                f32x16 acc = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    dqacc[db] = mfma32(lds_read_tr_operand<D>(Kt, ks * 16, db * 32, lane), dtb[ks], dqacc[db]);
+                    acc = mfma32(lds_read_tr_operand<D>(Kt, ks * 16, db * 32, lane), dtb[ks], acc);
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    dQs.store8(ia + l32, db * 32 + r4 * 8 + g * 4,
+                               u32x2{pack2(acc[r4 * 4 + 0] * p.scale, acc[r4 * 4 + 1] * p.scale),
+                                     pack2(acc[r4 * 4 + 2] * p.scale, acc[r4 * 4 + 3] * p.scale)});
             }
-            const int irow = ia + l32;
-            if (irow < s.lq)
-                store_row_acc<D>(static_cast<bf16 *>(p.dq) + ((s.qs + irow) * H + h) * (int64_t)D, dqacc, p.scale, g);
-            lds_wave_sync();
+            lds_wave_sync();  // every LDS read of this block is done before the next stores
         }
-
-        // Sum the four waves' dK / dV partials (lane-major so the LDS traffic
-        // is conflict-free) and store; wave 0 stores dK, wave 1 stores dV.
-        __syncthreads();
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            f32x16 (&acc)[NDB] = pass == 0 ? dkacc : dvacc;
-            if (wv > 0) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) red[((wv - 1) * NDB * 16 + db * 16 + e) * 64 + lane] = acc[db][e];
-            }
-            __syncthreads();
-            if (wv == 0) {
-#pragma unroll
-                for (int src = 0; src < 3; ++src)
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[db][e] += red[(src * NDB * 16 + db * 16 + e) * 64 + lane];
-                if (key_ok) {
-                    const int64_t off = ((s.ks + jkey) * H + h) * (int64_t)D;
-                    if (pass == 0) store_row_acc<D>(static_cast<bf16 *>(p.dk) + off, acc, p.scale, g);
-                    else store_row_acc<D>(static_cast<bf16 *>(p.dv) + off, acc, 1.0f, g);
-                }
-            }
-            __syncthreads();
-        }
+        const HeadSlice<D> dKs(p.dk, s.ks, s.lk, H, h), dVs(p.dv, s.ks, s.lk, H, h);
+        store_row_acc<D>(dKs, jkey, dkacc, p.scale, g);
+        store_row_acc<D>(dVs, jkey, dvacc, 1.0f, g);
     }
 }
 
@@ -479,7 +459,7 @@ static hipError_t launch_bwd_t(const AttnParams &p, int grid, hipStream_t st) {
         t.end(K_BWD_DELTA, st);
     }
     t.begin(K_BWD_FUSED, st);
-    hipLaunchKernelGGL((fused_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, p);
+    hipLaunchKernelGGL((fused_kernel<D, MODE, ACT>), dim3(2 * grid), dim3(WAVE), 0, st, p);
     t.end(K_BWD_FUSED, st);
     t.begin(K_BWD_KV, st);
     hipLaunchKernelGGL((dkdv_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, p);

@@ -165,6 +165,42 @@ __device__ __forceinline__ void act_fwd_grad(float x, float &y, float &dy) {
 // data (waits for the LDS queue; also a compiler memory barrier).
 __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// --------------------------------------------------------- buffer access
+// Bounds-checked loads and stores through a buffer descriptor: offsets at or
+// past num_records read as zero and are not stored.  A descriptor per
+// (sample, head) slice turns the ragged row tail into a hardware bound, so the
+// streaming loops carry no branches around their memory operations (branches
+// there force the compiler to wait for every outstanding access).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_FLAGS = 0x00020000;  // raw 32-bit data format (gfx9 family)
+constexpr uint32_t OOB = 0xFFFFFFFFu;   // an offset that is always out of range
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, RSRC_FLAGS);
+}
+// Bytes spanned by `rows` rows of one head in a [T, H, D] slice starting at that head's first row.
+__device__ __forceinline__ uint32_t rows_span(int rows, int H, int D, int esize) {
+    return rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * H * D + D) * esize) : 0u;
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory
+// operations are outstanding, leaving the LDS / export counters unconstrained.
+__device__ __host__ constexpr int waitcnt_vm(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 // ---------------------------------------------------------- misc helpers
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 

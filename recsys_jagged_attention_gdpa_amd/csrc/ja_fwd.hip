@@ -53,6 +53,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int n_units = p.counters->units;
+    if (n_units == 0) return;
     BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
     const float sl2 = p.scale * LOG2E;
 
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
                         float x = sacc[nb][e] * p.scale;
                         if (brow) x += bias_at(bz, brow, irow, j);
                         float y = act_fwd<ACT>(x);
-                        if (masked && j >= my_kend) y = 0.0f;
+                        y = (masked & (j >= my_kend)) ? 0.0f : y;  // bitwise: no per-lane branches
                         pv[e] = y;
                     }
 #pragma unroll
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
                         const int j = j0 + nb * 32 + crow(e, g);
                         float x = sacc[nb][e] * sl2;
                         if (brow) x += bias_at(bz, brow, irow, j) * LOG2E;
-                        if (masked && j >= my_kend) x = -INFINITY;
+                        x = (masked & (j >= my_kend)) ? -INFINITY : x;
                         xs[nb][e] = x;
                         tmax = fmaxf(tmax, x);
                     }
@@ -213,9 +214,156 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
     }
 }
 
+// ------------------------------------------------------------------------
+// Short key/value samples (at most 32 keys), one unit per (sample, head).
+// The inner loop over key tiles would have a single iteration, so the
+// pipelining moves to the outer loop ("Meta redesigns...", section "Custom
+// Kernels and 5D Parallelism...": outer-loop software pipelining when the
+// inner loop runs one or two iterations): K and V stay in LDS for the whole
+// sample, each wave claims 32-row query blocks from a per-unit counter, and
+// it loads its next block's Q rows into registers while the current block is
+// computed.  Loads and stores go through per-sample buffer descriptors, so the
+// loop body has no branches around memory operations and the next block's
+// loads stay in flight across the current block's stores.
+template <int D, int MODE, int ACT>
+__global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnParams p) {
+    constexpr int KV_BYTES = 32 * D * 2;
+    constexpr int NKK = D / 16, NDB = D / 32;
+    __shared__ __attribute__((aligned(16))) char smem[2 * KV_BYTES];
+    __shared__ int s_unit, s_blk;
+    lchar *const Kt = (lchar *)smem;
+    lchar *const Vt = Kt + KV_BYTES;
+
+    const int H = p.H;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const int n_units = p.counters2->units;
+    if (n_units == 0) return;
+    const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
+    const float sl2 = p.scale * LOG2E;
+
+    for (;;) {
+        if (threadIdx.x == 0) {
+            s_unit = atomicAdd(&p.counters2->cursor, 1);
+            s_blk = FWD_THREADS / WAVE;  // blocks 0..3 go to waves 0..3
+        }
+        __syncthreads();
+        const int w = s_unit;
+        if (w >= n_units) break;
+        const int2 tile = p.tiles2[w / H];
+        const int h = w % H;
+        const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
+        const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
+        {
+            PairLoader<32, D, FWD_THREADS> kv;
+            kv.load(static_cast<const bf16 *>(p.k), static_cast<const bf16 *>(p.v), s.ks, H, h, 0, s.lk, threadIdx.x);
+            kv.store(Kt, Vt, threadIdx.x);
+        }
+        const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h);
+        const HeadSlice<D> Os(p.out, s.o0, s.lq, H, h);
+        // the residual (JFA, optional) and LSE slices; zero-sized when not written
+        const bool res = MODE == JFA && p.o_res_out != nullptr;
+        const HeadSlice<D> Rs(res ? p.o_res_out : p.out, s.o0, res ? s.lq : 0, H, h);
+        const rsrc_t lse_r = make_rsrc(MODE == JFA ? p.lse + (int64_t)h * p.total_q_out + s.o0 : p.lse,
+                                       MODE == JFA ? (uint32_t)s.lq * 4u : 0u);
+        const int nblk = (s.lq + 31) / 32;
+        const bool masked = s.lk < 32 || p.causal;
+        // One 32-row query block, with Q rows in `qreg`; the next block's rows
+        // are loaded into `qnext` first, so they are in flight meanwhile.
+        auto block = [&](int blk, const bf16x8 (&qreg)[NKK], bf16x8 (&qnext)[NKK]) -> int {
+            const int irow = blk * 32 + l32;
+            float bv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) bv[e] = 0.0f;
+            if (brow) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) bv[e] = bias_at(bz, brow, irow, crow(e, g));
+            }
+            int nxt = 0;
+            if (lane == 0) nxt = atomicAdd(&s_blk, 1);
+            nxt = __builtin_amdgcn_readfirstlane(nxt);
+            load_row_operand<D>(qnext, Qs, nxt * 32 + l32, g);  // past the sample: zeros, no traffic
+            __builtin_amdgcn_sched_barrier(0);  // keep the next block's loads ahead of this block's work
+
+            f32x16 sacc = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                sacc = mfma32(lds_read16(Kt, lds_off<D>(l32, 2 * kk + g)), qreg[kk], sacc);
+            const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
+            float pv[16];
+            float norm = 1.0f, lse_row = 0.0f;
+            if constexpr (MODE == GDPA) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int j = crow(e, g);
+                    const float y = act_fwd<ACT>(__builtin_fmaf(sacc[e], p.scale, bv[e]));
+                    pv[e] = (masked & (j >= my_kend)) ? 0.0f : y;  // bitwise: no per-lane branches
+                }
+            } else {
+                float m = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int j = crow(e, g);
+                    float x = __builtin_fmaf(sacc[e], sl2, bv[e] * LOG2E);
+                    x = (masked & (j >= my_kend)) ? -INFINITY : x;
+                    pv[e] = x;
+                    m = fmaxf(m, x);
+                }
+                m = fmaxf(m, shfl_xor32(m));
+                const float shift = m == -INFINITY ? 0.0f : m;
+                float l = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    pv[e] = fast_exp2(pv[e] - shift);
+                    l += pv[e];
+                }
+                l += shfl_xor32(l);
+                norm = l > 0.0f ? 1.0f / l : 0.0f;
+                lse_row = l > 0.0f ? (m + log2f(l)) * LN2 : -INFINITY;
+            }
+            bf16x8 pb[2];
+            pack_operands(pv, pb[0], pb[1]);
+            f32x16 oacc[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                oacc[db] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    oacc[db] = mfma32(lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane), pb[ks], oacc[db]);
+            }
+            if constexpr (MODE == JFA) {
+                buf_store_f32(lse_r, g == 0 ? (uint32_t)irow * 4u : OOB, lse_row);
+                store_row_acc_split<D>(Os, Rs, irow, oacc, norm, g);
+            } else {
+                store_row_acc<D>(Os, irow, oacc, norm, g);
+            }
+            return nxt;
+        };
+
+        int blk = wv;
+        bf16x8 qa[NKK], qb[NKK];
+        load_row_operand<D>(qa, Qs, blk * 32 + l32, g);
+        // Enter the loop with nothing outstanding, so the loop's waits cover
+        // only the previous block's prefetch, not its stores.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+        // two register sets alternate, so no copy waits on the loads in flight
+        for (;;) {
+            if (blk >= nblk) break;
+            blk = block(blk, qa, qb);
+            if (blk >= nblk) break;
+            blk = block(blk, qb, qa);
+        }
+        __syncthreads();  // K / V of this unit are no longer read
+    }
+}
+
 template <int D, int MODE, int ACT>
 static hipError_t launch_fwd_t(const AttnParams &p, int grid, hipStream_t stream) {
     const KernelTimer &t = kernel_timer();
+    t.begin(K_FWD_SHORT, stream);
+    hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT>), dim3(grid), dim3(FWD_THREADS), 0, stream, p);
+    t.end(K_FWD_SHORT, stream);
     t.begin(K_FWD, stream);
     hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT>), dim3(grid), dim3(FWD_THREADS), 0, stream, p);
     t.end(K_FWD, stream);

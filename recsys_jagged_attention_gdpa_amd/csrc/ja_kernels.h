@@ -64,7 +64,7 @@ struct AttnParams {
     const float *bias;
     const int2 *tiles;
     PlanCounters *counters;
-    const int2 *tiles2;       // backward: second unit list (dK/dV units)
+    const int2 *tiles2;       // backward: dK/dV units; forward: short-K/V units
     PlanCounters *counters2;
     const int2 *tiles3;       // backward: fused short-K/V units
     PlanCounters *counters3;
@@ -78,7 +78,7 @@ struct PlanBatch {
 hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream);
 
 // Optional per-kernel event recording around launches (measurement aid).
-enum KernelId { K_PLAN = 0, K_FWD = 1, K_BWD_FUSED = 2, K_BWD_KV = 3, K_BWD_Q = 4, K_BWD_DELTA = 5 };
+enum KernelId { K_PLAN = 0, K_FWD = 1, K_BWD_FUSED = 2, K_BWD_KV = 3, K_BWD_Q = 4, K_BWD_DELTA = 5, K_FWD_SHORT = 6 };
 struct KernelTimer {
     int which = -1;
     hipEvent_t start = nullptr, stop = nullptr;

@@ -45,6 +45,96 @@ struct PairLoader {
     }
 };
 
+// A slice of one head of a [T, H, D] bf16 tensor: rows 0 .. rows-1 starting at
+// global row `row0`, read and written through a bounds-checked descriptor.
+template <int D>
+struct HeadSlice {
+    rsrc_t r;
+    uint32_t row_bytes;  // H * D * 2
+    __device__ __forceinline__ HeadSlice(const void *base, int64_t row0, int rows, int H, int h) {
+        const bf16 *p = static_cast<const bf16 *>(base) + (row0 * H + h) * (int64_t)D;
+        r = make_rsrc(p, rows_span(rows, H, D, 2));
+        row_bytes = (uint32_t)(H * D * 2);
+    }
+    // 16 bytes (chunk c = 8 bf16) of row `row`; zeros past the slice.
+    __device__ __forceinline__ u32x4 load16(int row, int c) const {
+        return buf_load16(r, (uint32_t)row * row_bytes + (uint32_t)c * 16u);
+    }
+    __device__ __forceinline__ void store8(int row, int d, u32x2 v) const {
+        buf_store8(r, (uint32_t)row * row_bytes + (uint32_t)d * 2u, v);
+    }
+};
+
+// ROWS rows of two head slices (Q and dO) staged through registers into the
+// swizzled LDS layout by NT threads; rows past the slice become zeros.
+template <int ROWS, int D, int NT>
+struct PairSliceLoader {
+    static constexpr int CHUNKS = ROWS * D / 8;
+    static constexpr int PER_THREAD = CHUNKS / NT;
+    static_assert(PER_THREAD >= 1 && CHUNKS % NT == 0, "tile / thread count mismatch");
+    u32x4 a[PER_THREAD], b[PER_THREAD];
+    __device__ __forceinline__ void load(const HeadSlice<D> &A, const HeadSlice<D> &B, int r0, int tid) {
+#pragma unroll
+        for (int it = 0; it < PER_THREAD; ++it) {
+            const int cid = tid + it * NT;
+            const int r = cid / (D / 8), c = cid % (D / 8);
+            a[it] = A.load16(r0 + r, c);
+            b[it] = B.load16(r0 + r, c);
+        }
+    }
+    __device__ __forceinline__ void store(lchar *ta, lchar *tb, int tid) const {
+#pragma unroll
+        for (int it = 0; it < PER_THREAD; ++it) {
+            const int cid = tid + it * NT;
+            const int r = cid / (D / 8), c = cid % (D / 8);
+            lds_write16(ta, lds_off<D>(r, c), a[it]);
+            lds_write16(tb, lds_off<D>(r, c), b[it]);
+        }
+    }
+};
+
+// One lane's row of a head slice in MFMA operand layout (chunk 2kk+g for k-step kk).
+template <int D>
+__device__ __forceinline__ void load_row_operand(bf16x8 (&reg)[D / 16], const HeadSlice<D> &S, int row, int g) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) reg[kk] = __builtin_bit_cast(bf16x8, S.load16(row, 2 * kk + g));
+}
+
+// Store a D^T-layout accumulator block set (lane owns row `row` of the slice;
+// element e of block db is column db*32 + crow(e, g)) as bf16 times `mul`.
+// Rows past the slice are dropped by the descriptor.
+template <int D>
+__device__ __forceinline__ void store_row_acc(const HeadSlice<D> &S, int row, const f32x16 (&acc)[D / 32], float mul,
+                                              int g) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            S.store8(row, db * 32 + r4 * 8 + g * 4,
+                     u32x2{pack2(acc[db][r4 * 4 + 0] * mul, acc[db][r4 * 4 + 1] * mul),
+                           pack2(acc[db][r4 * 4 + 2] * mul, acc[db][r4 * 4 + 3] * mul)});
+}
+
+// As above, and also store the rounding residual x - bf16(x) into R.
+template <int D>
+__device__ __forceinline__ void store_row_acc_split(const HeadSlice<D> &S, const HeadSlice<D> &R, int row,
+                                                    const f32x16 (&acc)[D / 32], float mul, int g) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            float x[4], rs[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x[t] = acc[db][r4 * 4 + t] * mul;
+                rs[t] = x[t] - bf2f(f2bf(x[t]));
+            }
+            const int d = db * 32 + r4 * 8 + g * 4;
+            S.store8(row, d, u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])});
+            R.store8(row, d, u32x2{pack2(rs[0], rs[1]), pack2(rs[2], rs[3])});
+        }
+}
+
 // One lane's row of a tile in MFMA operand layout (chunk 2kk+g for k-step kk),
 // read straight from global memory; zeros when the row is out of range.
 template <int D>

@@ -86,26 +86,26 @@ __device__ __forceinline__ float score_bwd(float s_raw, float scale, float bias,
 template <int D, int MODE, int ACT>
 __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) {
     constexpr int BN = KV_TILE;
+    constexpr int BM = Q_TILE;
     constexpr int TILE_BYTES = BN * D * 2;
-    constexpr int NKK = D / 16, NDB = D / 32, NNB = BN / 32, NKS = BN / 16;
+    constexpr int NKK = D / 16, NDB = D / 32, NNB = BN / 32;
+    constexpr int WIN = BM + BN - 1;
+    static_assert(WIN <= BWD_THREADS, "one bias window entry per thread");
     __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
+    __shared__ float s_bias[2][WIN];
     __shared__ int s_unit;
     lchar *const lbase = (lchar *)smem;
 
-    const bf16 *__restrict__ Q = static_cast<const bf16 *>(p.q);
-    const bf16 *__restrict__ K = static_cast<const bf16 *>(p.k);
-    const bf16 *__restrict__ V = static_cast<const bf16 *>(p.v);
-    const bf16 *__restrict__ G = static_cast<const bf16 *>(p.dout);
-    bf16 *__restrict__ dQ = static_cast<bf16 *>(p.dq);
     const int H = p.H;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int n_units = p.counters->units;
     if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
     for (;;) {
-        if (threadIdx.x == 0) s_unit = atomicAdd(&p.counters->cursor, 1);
+        if (tid == 0) s_unit = atomicAdd(&p.counters->cursor, 1);
         __syncthreads();
         const int w = s_unit;
         __syncthreads();
@@ -113,23 +113,27 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
         const int2 tile = p.tiles[w / H];
         const int h = w % H;
         const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
-        const int i0 = tile.y * Q_TILE;
+        const int i0 = tile.y * BM;
         const int iw = i0 + wv * 32;
         const int irow = iw + l32;
         const bool row_ok = irow < s.lq;
-        const int i_last = (i0 + Q_TILE < s.lq ? i0 + Q_TILE : s.lq) - 1;
+        const int i_last = (i0 + BM < s.lq ? i0 + BM : s.lq) - 1;
         const int nkv = (key_end(i_last, s.lq, s.lk, p.causal) + BN - 1) / BN;
-        const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
+        const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h), Gs(p.dout, s.qs, s.lq, H, h), dQs(p.dq, s.qs, s.lq, H, h);
+        const HeadSlice<D> Ks(p.k, s.ks, s.lk, H, h), Vs(p.v, s.ks, s.lk, H, h);
+        const rsrc_t brs = make_rsrc(bz.kind ? bz.table + (int64_t)h * bz.width : nullptr,
+                                     bz.kind ? (uint32_t)bz.width * 4u : 0u);
 
         bf16x8 qreg[NKK], greg[NKK];
-        load_row_operand<D>(qreg, Q, s.qs + irow, H, h, row_ok, g);
-        load_row_operand<D>(greg, G, s.qs + irow, H, h, row_ok, g);
+        load_row_operand<D>(qreg, Qs, irow, g);
+        load_row_operand<D>(greg, Gs, irow, g);
         float lse2 = 0.0f, dlt = 0.0f;
         if constexpr (MODE == JFA) {
-            if (row_ok) {
-                lse2 = p.lse[(int64_t)h * p.total_q + s.qs + irow] * LOG2E;
-                dlt = p.delta[(int64_t)h * p.total_q + s.qs + irow];
-            }
+            const uint32_t off = irow < s.lq ? (uint32_t)(h * p.total_q + s.qs + irow) * 4u : OOB;
+            const rsrc_t lr = make_rsrc(p.lse, (uint32_t)(p.total_q * p.H) * 4u);
+            const rsrc_t dr = make_rsrc(p.delta, (uint32_t)(p.total_q * p.H) * 4u);
+            lse2 = buf_load_f32(lr, off) * LOG2E;
+            dlt = buf_load_f32(dr, off);
         }
         const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
 
@@ -137,21 +141,32 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
-        PairLoader<BN, D, BWD_THREADS> ld;
-        if (nkv > 0) {
-            ld.load(K, V, s.ks, H, h, 0, s.lk, threadIdx.x);
-            ld.store(lbase, lbase + TILE_BYTES, threadIdx.x);
-        }
+        PairSliceLoader<BN, D, BWD_THREADS> ld;
+        float bnext = 0.0f;
+        auto load_tile = [&](int jt) {
+            ld.load(Ks, Vs, jt * BN, tid);
+            const BiasWindow bw = bias_window(bz, i0, BM, jt * BN, BN);
+            bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
+        };
+        auto store_tile = [&](int buf) {
+            lchar *kt = lbase + buf * 2 * TILE_BYTES;
+            ld.store(kt, kt + TILE_BYTES, tid);
+            if (tid < WIN) s_bias[buf][tid] = bnext;
+        };
+        load_tile(0);
+        store_tile(0);
         __syncthreads();
 
         for (int jt = 0; jt < nkv; ++jt) {
             const int j0 = jt * BN;
             const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             const lchar *Vt = Kt + TILE_BYTES;
-            if (jt + 1 < nkv) ld.load(K, V, s.ks, H, h, j0 + BN, s.lk, threadIdx.x);
+            const float *bwin = s_bias[jt & 1];
+            const BiasWindow bw = bias_window(bz, i0, BM, j0, BN);
+            load_tile(jt + 1);  // past the last tile: zeros, no traffic
+            __builtin_amdgcn_sched_barrier(0);
 
-            const bool masked = (j0 + BN > s.lk) || (p.causal && (j0 + BN - 1 > iw + s.lk - s.lq)) || !row_ok;
-            bf16x8 dsb[NKS];
+            const bool masked = (j0 + BN > s.lk) | (p.causal && (j0 + BN - 1 > iw + s.lk - s.lq)) | !row_ok;
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb) {
                 f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -165,26 +180,23 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int j = j0 + nb * 32 + crow(e, g);
-                    const float bias = brow ? bias_at(bz, brow, irow, j) : 0.0f;
+                    const float bias = bz.kind ? bwin[bias_window_index(bz, bw, irow, j)] : 0.0f;
                     const bool valid = !masked | (row_ok & (j < my_kend));  // bitwise: no per-lane branches
                     score_bwd<MODE, ACT>(sacc[e], p.scale, bias, dpacc[e], lse2, dlt, valid, dx[e]);
                 }
-                pack_operands(dx, dsb[2 * nb], dsb[2 * nb + 1]);
-            }
-            // dQ^T += K^T dX^T
+                bf16x8 dsb[2];
+                pack_operands(dx, dsb[0], dsb[1]);
+                // dQ^T += K^T dX^T over this block's 32 keys
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
+                for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dqacc[db] = mfma32(lds_read_tr_operand<D>(Kt, ks * 16, db * 32, lane), dsb[ks], dqacc[db]);
+                    for (int db = 0; db < NDB; ++db)
+                        dqacc[db] = mfma32(lds_read_tr_operand<D>(Kt, nb * 32 + hf * 16, db * 32, lane), dsb[hf], dqacc[db]);
             }
-            if (jt + 1 < nkv) {
-                lchar *Kn = lbase + ((jt + 1) & 1) * 2 * TILE_BYTES;
-                ld.store(Kn, Kn + TILE_BYTES, threadIdx.x);
-            }
+            store_tile((jt + 1) & 1);
             __syncthreads();
         }
-        if (row_ok) store_row_acc<D>(dQ + ((s.qs + irow) * H + h) * (int64_t)D, dqacc, p.scale, g);
+        store_row_acc<D>(dQs, irow, dqacc, p.scale, g);
     }
 }
 
@@ -192,27 +204,27 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
 template <int D, int MODE, int ACT>
 __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p) {
     constexpr int BQ = BWD_Q_STEP;  // 64 query rows per step
+    constexpr int BK = BWD_KV_UNIT; // 128 keys per unit
     constexpr int TILE_BYTES = BQ * D * 2;
     constexpr int NKK = D / 16, NDB = D / 32;
-    __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
-    __shared__ float s_lse[BQ], s_dlt[BQ];
+    constexpr int WIN = BQ + BK - 1;
+    static_assert(WIN <= BWD_THREADS, "one bias window entry per thread");
+    __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
+    __shared__ float s_lse[2][BQ], s_dlt[2][BQ];
+    __shared__ float s_bias[2][WIN];
     __shared__ int s_unit;
-    lchar *const Qt = (lchar *)smem;
-    lchar *const Gt = Qt + TILE_BYTES;
+    lchar *const lbase = (lchar *)smem;
 
-    const bf16 *__restrict__ Q = static_cast<const bf16 *>(p.q);
-    const bf16 *__restrict__ K = static_cast<const bf16 *>(p.k);
-    const bf16 *__restrict__ V = static_cast<const bf16 *>(p.v);
-    const bf16 *__restrict__ G = static_cast<const bf16 *>(p.dout);
     const int H = p.H;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int n_units = p.counters2->units;
     if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
     for (;;) {
-        if (threadIdx.x == 0) s_unit = atomicAdd(&p.counters2->cursor, 1);
+        if (tid == 0) s_unit = atomicAdd(&p.counters2->cursor, 1);
         __syncthreads();
         const int w = s_unit;
         __syncthreads();
@@ -220,15 +232,21 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
         const int2 tile = p.tiles2[w / H];
         const int h = w % H;
         const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
-        const int jt0 = tile.y * BWD_KV_UNIT;
+        const int jt0 = tile.y * BK;
         const int jw = jt0 + wv * 32;       // first key of this wave
         const int jkey = jw + l32;          // this lane's key (C-layout column)
-        const bool key_ok = jkey < s.lk;
-        const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
+        const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h), Gs(p.dout, s.qs, s.lq, H, h);
+        const HeadSlice<D> Ks(p.k, s.ks, s.lk, H, h), Vs(p.v, s.ks, s.lk, H, h);
+        const rsrc_t brs = make_rsrc(bz.kind ? bz.table + (int64_t)h * bz.width : nullptr,
+                                     bz.kind ? (uint32_t)bz.width * 4u : 0u);
+        const rsrc_t lr = make_rsrc(MODE == JFA ? p.lse + (int64_t)h * p.total_q + s.qs : nullptr,
+                                    MODE == JFA ? (uint32_t)s.lq * 4u : 0u);
+        const rsrc_t dr = make_rsrc(MODE == JFA ? p.delta + (int64_t)h * p.total_q + s.qs : nullptr,
+                                    MODE == JFA ? (uint32_t)s.lq * 4u : 0u);
 
         bf16x8 kreg[NKK], vreg[NKK];
-        load_row_operand<D>(kreg, K, s.ks + jkey, H, h, key_ok, g);
-        load_row_operand<D>(vreg, V, s.ks + jkey, H, h, key_ok, g);
+        load_row_operand<D>(kreg, Ks, jkey, g);
+        load_row_operand<D>(vreg, Vs, jkey, g);
         f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dkacc[db] = dvacc[db] = f32x16{};
@@ -237,22 +255,44 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
         int ia0 = p.causal ? jt0 - (s.lk - s.lq) : 0;
         ia0 = ia0 < 0 ? 0 : ia0;
         const int shift = s.lk - s.lq;  // causal: key j visible to row i iff j <= i + shift
+        const int nsteps = ia0 < s.lq ? (s.lq - ia0 + BQ - 1) / BQ : 0;
 
-        PairLoader<BQ, D, BWD_THREADS> ld;
-        for (int ia = ia0; ia < s.lq; ia += BQ) {
-            ld.load(Q, G, s.qs, H, h, ia, s.lq, threadIdx.x);
+        PairSliceLoader<BQ, D, BWD_THREADS> ld;
+        float bnext = 0.0f, lnext = 0.0f, dnext = 0.0f;
+        auto load_step = [&](int st) {
+            const int ia = ia0 + st * BQ;
+            ld.load(Qs, Gs, ia, tid);
+            const BiasWindow bw = bias_window(bz, ia, BQ, jt0, BK);
+            bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
             if constexpr (MODE == JFA) {
-                if (threadIdx.x < BQ) {
-                    const int i = ia + threadIdx.x;
-                    const bool ok = i < s.lq;
-                    s_lse[threadIdx.x] = ok ? p.lse[(int64_t)h * p.total_q + s.qs + i] * LOG2E : 0.0f;
-                    s_dlt[threadIdx.x] = ok ? p.delta[(int64_t)h * p.total_q + s.qs + i] : 0.0f;
-                }
+                const uint32_t off = tid < BQ ? (uint32_t)(ia + tid) * 4u : OOB;
+                lnext = buf_load_f32(lr, off) * LOG2E;
+                dnext = buf_load_f32(dr, off);
             }
-            ld.store(Qt, Gt, threadIdx.x);
-            __syncthreads();
+        };
+        auto store_step = [&](int buf) {
+            lchar *qt = lbase + buf * 2 * TILE_BYTES;
+            ld.store(qt, qt + TILE_BYTES, tid);
+            if (tid < WIN) s_bias[buf][tid] = bnext;
+            if (MODE == JFA && tid < BQ) {
+                s_lse[buf][tid] = lnext;
+                s_dlt[buf][tid] = dnext;
+            }
+        };
+        load_step(0);
+        store_step(0);
+        __syncthreads();
 
-            const bool masked = (ia + BQ > s.lq) || (p.causal && (jw + 31 > ia + shift));
+        for (int st = 0; st < nsteps; ++st) {
+            const int ia = ia0 + st * BQ;
+            const lchar *Qt = lbase + (st & 1) * 2 * TILE_BYTES;
+            const lchar *Gt = Qt + TILE_BYTES;
+            const float *bwin = s_bias[st & 1];
+            const BiasWindow bw = bias_window(bz, ia, BQ, jt0, BK);
+            load_step(st + 1);  // past the last step: zeros, no traffic
+            __builtin_amdgcn_sched_barrier(0);
+
+            const bool masked = (ia + BQ > s.lq) | (p.causal && (jw + 31 > ia + shift));
 #pragma unroll
             for (int qb = 0; qb < BQ / 32; ++qb) {
                 f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -267,13 +307,10 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
                 for (int e = 0; e < 16; ++e) {
                     const int il = qb * 32 + crow(e, g);
                     const int i = ia + il;
-                    const float bias = brow ? bias_at(bz, brow, i, jkey) : 0.0f;
+                    const float bias = bz.kind ? bwin[bias_window_index(bz, bw, i, jkey)] : 0.0f;
                     const bool valid = !masked | ((i < s.lq) & (!p.causal | (jkey <= i + shift)));
-                    float lse2 = 0.0f, dlt = 0.0f;
-                    if constexpr (MODE == JFA) {
-                        lse2 = s_lse[il];
-                        dlt = s_dlt[il];
-                    }
+                    const float lse2 = MODE == JFA ? s_lse[st & 1][il] : 0.0f;
+                    const float dlt = MODE == JFA ? s_dlt[st & 1][il] : 0.0f;
                     pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bias, dpacc[e], lse2, dlt, valid, dx[e]);
                 }
                 bf16x8 pb[2], dsb[2];
@@ -288,13 +325,12 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
                     }
                 }
             }
+            store_step((st + 1) & 1);
             __syncthreads();
         }
-        if (key_ok) {
-            const int64_t off = ((s.ks + jkey) * H + h) * (int64_t)D;
-            store_row_acc<D>(static_cast<bf16 *>(p.dk) + off, dkacc, p.scale, g);
-            store_row_acc<D>(static_cast<bf16 *>(p.dv) + off, dvacc, 1.0f, g);
-        }
+        const HeadSlice<D> dKs(p.dk, s.ks, s.lk, H, h), dVs(p.dv, s.ks, s.lk, H, h);
+        store_row_acc<D>(dKs, jkey, dkacc, p.scale, g);
+        store_row_acc<D>(dVs, jkey, dvacc, 1.0f, g);
     }
 }
 

@@ -125,6 +125,25 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 // sigmoid(z) with z given as -z * log2(e) (so one v_exp and one v_rcp).
 __device__ __forceinline__ float sigmoid_from_neg_log2(float nz) { return fast_rcp(1.0f + fast_exp2(nz)); }
 
+// Standard normal CDF Phi(x) and density phi(x), via the Abramowitz & Stegun
+// approximation 7.1.26 of erf (|error| <= 1.5e-7): for u = |x|/sqrt(2),
+// erf(u) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-u^2),
+// t = 1 / (1 + p u).  exp(-u^2) = sqrt(2 pi) phi(x) is shared by both results.
+__device__ __forceinline__ void normal_cdf_pdf(float x, float &cdf, float &pdf) {
+    constexpr float P = 0.3275911f, A1 = 0.254829592f, A2 = -0.284496736f, A3 = 1.421413741f,
+                    A4 = -1.453152027f, A5 = 1.061405429f;
+    const float u = fabsf(x) * INV_SQRT2;
+    const float t = fast_rcp(__builtin_fmaf(P, u, 1.0f));
+    const float e = fast_exp2(-u * u * LOG2E);  // exp(-u^2)
+    float poly = __builtin_fmaf(A5, t, A4);
+    poly = __builtin_fmaf(poly, t, A3);
+    poly = __builtin_fmaf(poly, t, A2);
+    poly = __builtin_fmaf(poly, t, A1);
+    const float erf_u = 1.0f - poly * t * e;   // erf(|x| / sqrt 2)
+    cdf = 0.5f + copysignf(0.5f * erf_u, x);
+    pdf = INV_SQRT_2PI * e;
+}
+
 template <int ACT>
 __device__ __forceinline__ float act_fwd(float x) {
     if constexpr (ACT == SILU) {
@@ -134,7 +153,9 @@ __device__ __forceinline__ float act_fwd(float x) {
         const float t = __builtin_fmaf(x2, -2.0f * LOG2E * GELU_C * GELU_A, -2.0f * LOG2E * GELU_C);
         return x * sigmoid_from_neg_log2(x * t);
     } else {
-        return 0.5f * x * (1.0f + erff(x * INV_SQRT2));
+        float cdf, pdf;
+        normal_cdf_pdf(x, cdf, pdf);
+        return x * cdf;
     }
 }
 
@@ -154,8 +175,8 @@ __device__ __forceinline__ void act_fwd_grad(float x, float &y, float &dy) {
         const float du = GELU_C * __builtin_fmaf(3.0f * GELU_A, x2, 1.0f);
         dy = __builtin_fmaf(2.0f * x * s * (1.0f - s), du, s);
     } else {
-        const float cdf = 0.5f * (1.0f + erff(x * INV_SQRT2));
-        const float pdf = INV_SQRT_2PI * fast_exp2(-0.5f * LOG2E * x * x);
+        float cdf, pdf;
+        normal_cdf_pdf(x, cdf, pdf);
         y = x * cdf;
         dy = __builtin_fmaf(x, pdf, cdf);
     }
@@ -247,6 +268,36 @@ struct BiasArgs {
     const float *table;
     int kind, lo, hi, width;
 };
+
+// Window of a head's bias row that a tile of rows [i0, i0 + ni) and keys
+// [j0, j0 + nj) can touch: table indices (after clamping) lo_idx .. hi_idx.
+// The window has at most ni + nj - 1 entries for relative positions and nj
+// for key positions, whatever the table's width, so it is staged in LDS next
+// to the tile's keys and values.
+struct BiasWindow {
+    int first;  // first table index (offset from bias_lo) of the window
+    int len;    // entries in the window (0 without bias)
+};
+
+__device__ __forceinline__ BiasWindow bias_window(const BiasArgs &bz, int i0, int ni, int j0, int nj) {
+    BiasWindow w{0, 0};
+    if (bz.kind == BIAS_REL) {
+        const int a = clampi(i0 - (j0 + nj - 1), bz.lo, bz.hi), b = clampi(i0 + ni - 1 - j0, bz.lo, bz.hi);
+        w.first = a - bz.lo;
+        w.len = b - a + 1;
+    } else if (bz.kind == BIAS_KEYPOS) {
+        const int a = clampi(j0, bz.lo, bz.hi), b = clampi(j0 + nj - 1, bz.lo, bz.hi);
+        w.first = a - bz.lo;
+        w.len = b - a + 1;
+    }
+    return w;
+}
+
+// Index into a staged window for pair (i, j).
+__device__ __forceinline__ int bias_window_index(const BiasArgs &bz, const BiasWindow &w, int i, int j) {
+    const int idx = bz.kind == BIAS_REL ? clampi(i - j, bz.lo, bz.hi) : clampi(j, bz.lo, bz.hi);
+    return idx - bz.lo - w.first;
+}
 
 __device__ __forceinline__ float bias_at(const BiasArgs &bz, const float *row, int i, int j) {
     if (bz.kind == BIAS_REL) return row[clampi(i - j, bz.lo, bz.hi) - bz.lo];

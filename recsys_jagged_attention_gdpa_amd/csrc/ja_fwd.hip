@@ -41,61 +41,79 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
     constexpr int NDB = D / 32;  // 32-wide blocks of the head dimension
     constexpr int NNB = BN / 32; // 32-key blocks per tile
     constexpr int NKS = BN / 16; // 16-key k-steps per tile
+    constexpr int WIN = BM + BN - 1;  // largest bias window of a (unit, key tile)
+    static_assert(WIN <= FWD_THREADS, "one bias window entry per thread");
     __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
+    __shared__ float s_bias[2][WIN];
     __shared__ int s_unit;
     lchar *const lbase = (lchar *)smem;
 
-    const bf16 *__restrict__ Q = static_cast<const bf16 *>(p.q);
-    const bf16 *__restrict__ K = static_cast<const bf16 *>(p.k);
-    const bf16 *__restrict__ V = static_cast<const bf16 *>(p.v);
-    bf16 *__restrict__ O = static_cast<bf16 *>(p.out);
-    const int H = p.B > 0 ? p.H : 1;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int H = p.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int n_units = p.counters->units;
     if (n_units == 0) return;
-    BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
+    const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
     const float sl2 = p.scale * LOG2E;
 
     for (;;) {
-        if (threadIdx.x == 0) s_unit = atomicAdd(&p.counters->cursor, 1);
+        if (tid == 0) s_unit = atomicAdd(&p.counters->cursor, 1);
         __syncthreads();
         const int w = s_unit;
         __syncthreads();
         if (w >= n_units) break;
         const int2 tile = p.tiles[w / H];
         const int h = w % H;
-        const int b = tile.x;
-        const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, b);
+        const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
         const int i0 = tile.y * BM;            // first query row of the unit (sample-local)
         const int iw = i0 + wv * 32;           // first row of this wave
         const int irow = iw + l32;             // this lane's query row
         const int i_last = (i0 + BM < s.lq ? i0 + BM : s.lq) - 1;
         const int kend = key_end(i_last, s.lq, s.lk, p.causal);
         const int nkv = (kend + BN - 1) / BN;
-        const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
+        const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h), Os(p.out, s.o0, s.lq, H, h);
+        const HeadSlice<D> Ks(p.k, s.ks, s.lk, H, h), Vs(p.v, s.ks, s.lk, H, h);
+        const bool res = MODE == JFA && p.o_res_out != nullptr;
+        const HeadSlice<D> Rs(res ? p.o_res_out : p.out, s.o0, res ? s.lq : 0, H, h);
+        const rsrc_t brs = make_rsrc(bz.kind ? bz.table + (int64_t)h * bz.width : nullptr,
+                                     bz.kind ? (uint32_t)bz.width * 4u : 0u);
 
         // Q rows of this lane, in B-operand layout: chunk 2kk+g of row irow.
         bf16x8 qreg[NKK];
-        load_row_operand<D>(qreg, Q, s.qs + irow, H, h, irow < s.lq, g);
+        load_row_operand<D>(qreg, Qs, irow, g);
 
         f32x16 oacc[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
         float m_run = -INFINITY, l_run = 0.0f;  // JFA running max (log2 units) and partial sum
 
-        PairLoader<BN, D, FWD_THREADS> ld;
-        if (nkv > 0) {
-            ld.load(K, V, s.ks, H, h, 0, s.lk, threadIdx.x);
-            ld.store(lbase, lbase + TILE_BYTES, threadIdx.x);
-        }
+        // Key / value tile jt and the bias window it needs go through registers
+        // into LDS buffer (jt & 1); loads past the sample read zeros.
+        PairSliceLoader<BN, D, FWD_THREADS> ld;
+        float bnext = 0.0f;
+        auto load_tile = [&](int jt) {
+            ld.load(Ks, Vs, jt * BN, tid);
+            const BiasWindow bw = bias_window(bz, i0, BM, jt * BN, BN);
+            bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
+        };
+        auto store_tile = [&](int buf) {
+            lchar *kt = lbase + buf * 2 * TILE_BYTES;
+            ld.store(kt, kt + TILE_BYTES, tid);
+            if (tid < WIN) s_bias[buf][tid] = bnext;
+        };
+        load_tile(0);
+        store_tile(0);
         __syncthreads();
 
         for (int jt = 0; jt < nkv; ++jt) {
             const int j0 = jt * BN;
             const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             const lchar *Vt = Kt + TILE_BYTES;
-            if (jt + 1 < nkv) ld.load(K, V, s.ks, H, h, j0 + BN, s.lk, threadIdx.x);
+            const float *bwin = s_bias[jt & 1];
+            const BiasWindow bw = bias_window(bz, i0, BM, j0, BN);
+            load_tile(jt + 1);  // past the last tile: zeros, no traffic
+            __builtin_amdgcn_sched_barrier(0);
 
             // S^T block per 32 keys: lane holds query irow, keys crow(e, g).
             f32x16 sacc[NNB];
@@ -116,6 +134,16 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
             const bool masked = tail || diag;
             const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
             bf16x8 pb[NKS];
+            float xs[NNB][16];
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int j = j0 + nb * 32 + crow(e, g);
+                    const float b = bz.kind ? bwin[bias_window_index(bz, bw, irow, j)] : 0.0f;
+                    xs[nb][e] = MODE == GDPA ? __builtin_fmaf(sacc[nb][e], p.scale, b)
+                                             : __builtin_fmaf(sacc[nb][e], sl2, b * LOG2E);
+                }
             if constexpr (MODE == GDPA) {
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb) {
@@ -123,35 +151,21 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int j = j0 + nb * 32 + crow(e, g);
-                        float x = sacc[nb][e] * p.scale;
-                        if (brow) x += bias_at(bz, brow, irow, j);
-                        float y = act_fwd<ACT>(x);
-                        y = (masked & (j >= my_kend)) ? 0.0f : y;  // bitwise: no per-lane branches
-                        pv[e] = y;
+                        const float y = act_fwd<ACT>(xs[nb][e]);
+                        pv[e] = (masked & (j >= my_kend)) ? 0.0f : y;  // bitwise: no per-lane branches
                     }
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        bf16x8 t;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) t[e] = f2bf(pv[hf * 8 + e]);
-                        pb[nb * 2 + hf] = t;
-                    }
+                    pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
                 }
             } else {
-                float xs[NNB][16];
                 float tmax = -INFINITY;
 #pragma unroll
-                for (int nb = 0; nb < NNB; ++nb) {
+                for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int j = j0 + nb * 32 + crow(e, g);
-                        float x = sacc[nb][e] * sl2;
-                        if (brow) x += bias_at(bz, brow, irow, j) * LOG2E;
-                        x = (masked & (j >= my_kend)) ? -INFINITY : x;
-                        xs[nb][e] = x;
-                        tmax = fmaxf(tmax, x);
+                        xs[nb][e] = (masked & (j >= my_kend)) ? -INFINITY : xs[nb][e];
+                        tmax = fmaxf(tmax, xs[nb][e]);
                     }
-                }
                 tmax = fmaxf(tmax, shfl_xor32(tmax));
                 const float m_new = fmaxf(m_run, tmax);
                 const float shift = m_new == -INFINITY ? 0.0f : m_new;
@@ -168,13 +182,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
                         pv[e] = fast_exp2(xs[nb][e] - shift);
                         l_run += pv[e];
                     }
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        bf16x8 t;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) t[e] = f2bf(pv[hf * 8 + e]);
-                        pb[nb * 2 + hf] = t;
-                    }
+                    pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
                 }
             }
 
@@ -188,10 +196,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
                 }
             }
 
-            if (jt + 1 < nkv) {
-                lchar *Kn = lbase + ((jt + 1) & 1) * 2 * TILE_BYTES;
-                ld.store(Kn, Kn + TILE_BYTES, threadIdx.x);
-            }
+            store_tile((jt + 1) & 1);
             __syncthreads();
         }
 
@@ -201,15 +206,11 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
             const float l_tot = l_run + shfl_xor32(l_run);
             const bool any = l_tot > 0.0f;
             norm = any ? 1.0f / l_tot : 0.0f;
-            if (irow < s.lq && g == 0)
-                p.lse[(int64_t)h * p.total_q_out + s.o0 + irow] = any ? (m_run + log2f(l_tot)) * LN2 : -INFINITY;
-        }
-        if (irow < s.lq) {
-            const int64_t off = ((s.o0 + irow) * H + h) * (int64_t)D;
-            if (MODE == JFA && p.o_res_out)
-                store_row_acc_split<D>(O + off, static_cast<bf16 *>(p.o_res_out) + off, oacc, norm, g);
-            else
-                store_row_acc<D>(O + off, oacc, norm, g);
+            const rsrc_t lr = make_rsrc(p.lse + (int64_t)h * p.total_q_out + s.o0, (uint32_t)s.lq * 4u);
+            buf_store_f32(lr, g == 0 ? (uint32_t)irow * 4u : OOB, any ? (m_run + log2f(l_tot)) * LN2 : -INFINITY);
+            store_row_acc_split<D>(Os, Rs, irow, oacc, norm, g);
+        } else {
+            store_row_acc<D>(Os, irow, oacc, norm, g);
         }
     }
 }

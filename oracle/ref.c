@@ -173,77 +173,79 @@ static int row_stats(const problem *p, int h, const sample *s, int64_t i, double
     return any;
 }
 
-/* Forward over one (sample, head) slice.  softmax = 0: GDPA, 1: JFA. */
-static void fwd_slice(const problem *p, int softmax, int b, int h, double *o, double *lse) {
+/* Global query row r (0 <= r < rows of the output) -> its sample. */
+static int sample_of_out_row(const problem *p, int64_t r) {
+    if (!p->q_off) return (int)(r / p->lq_fixed);
+    int lo = 0, hi = p->B - 1; /* last b with q_off[b] <= r */
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (p->q_off[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+static int sample_of_key_row(const problem *p, int64_t r) {
+    int lo = 0, hi = p->B - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (p->kv_off[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+/* Forward of one query row i of sample b, head h.  softmax = 0: GDPA, 1: JFA. */
+static void fwd_row(const problem *p, int softmax, int b, int h, int64_t i, double *o, double *lse) {
     sample s = sample_rows(p, b);
     const int D = p->D;
-    for (int64_t i = 0; i < s.lq; ++i) {
-        double *oi = orow(p, o, s.o0 + i, h);
-        for (int d = 0; d < D; ++d) oi[d] = 0.0;
-        double m = 0.0, l = 1.0;
-        if (softmax) {
-            int any = row_stats(p, h, &s, i, &m, &l);
-            if (lse) lse[(s.o0 + i) * p->H + h] = any ? m + log(l) : -INFINITY;
-            if (!any) continue;
-        }
-        for (int64_t j = 0; j < s.lk; ++j) {
-            if (!is_valid(p, i, j, s.lq, s.lk)) continue;
-            double x = score(p, h, &s, i, j);
-            double w = softmax ? exp(x - m) / l : act_f(p->act, x);
-            const float *vj = row_of(p, p->v, s.ks + j, h);
-            for (int d = 0; d < D; ++d) oi[d] += w * (double)vj[d];
-        }
+    double *oi = orow(p, o, s.o0 + i, h);
+    for (int d = 0; d < D; ++d) oi[d] = 0.0;
+    double m = 0.0, l = 1.0;
+    if (softmax) {
+        int any = row_stats(p, h, &s, i, &m, &l);
+        if (lse) lse[(s.o0 + i) * p->H + h] = any ? m + log(l) : -INFINITY;
+        if (!any) return;
+    }
+    for (int64_t j = 0; j < s.lk; ++j) {
+        if (!is_valid(p, i, j, s.lq, s.lk)) continue;
+        double x = score(p, h, &s, i, j);
+        double w = softmax ? exp(x - m) / l : act_f(p->act, x);
+        const float *vj = row_of(p, p->v, s.ks + j, h);
+        for (int d = 0; d < D; ++d) oi[d] += w * (double)vj[d];
     }
 }
 
-/* Backward over one (sample, head) slice.  dQ rows of the sample and dK / dV
- * rows of the sample belong to this slice alone, so no reduction across
- * slices is needed (shared query blocks are not supported in backward). */
-static void bwd_slice(const problem *p, int softmax, int b, int h, const float *dout,
-                      double *dq, double *dk, double *dv, double *xrow, double *dprow) {
-    sample s = sample_rows(p, b);
-    const int D = p->D;
-    for (int64_t j = 0; j < s.lk; ++j) {
-        double *dkj = orow(p, dk, s.ks + j, h), *dvj = orow(p, dv, s.ks + j, h);
-        for (int d = 0; d < D; ++d) { dkj[d] = 0.0; dvj[d] = 0.0; }
+/* Weight W_ij (act(X) or softmax P) and dX_ij of one valid pair, given the
+ * row's softmax statistics m, l and delta = sum_k P_ik dP_ik (JFA only). */
+static void pair_bwd(const problem *p, int softmax, int h, const sample *s, int64_t i, int64_t j,
+                     const float *doi, double m, double l, double delta, double *w, double *dx) {
+    double x = score(p, h, s, i, j);
+    const float *vj = row_of(p, p->v, s->ks + j, h);
+    double dp = 0.0;
+    for (int d = 0; d < p->D; ++d) dp += (double)doi[d] * (double)vj[d];
+    if (softmax) {
+        *w = exp(x - m) / l;
+        *dx = *w * (dp - delta);
+    } else {
+        *w = act_f(p->act, x);
+        *dx = dp * act_grad(p->act, x);
     }
-    for (int64_t i = 0; i < s.lq; ++i) {
-        double *dqi = orow(p, dq, s.qs + i, h);
-        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
-        const float *doi = row_of(p, dout, s.o0 + i, h);
-        const float *qi = row_of(p, p->q, s.qs + i, h);
-        double m = 0.0, l = 1.0;
-        if (softmax && !row_stats(p, h, &s, i, &m, &l)) continue;
-        /* weights W_ij (act(X) or softmax P) and dP_ij for this row */
-        double delta = 0.0;
-        for (int64_t j = 0; j < s.lk; ++j) {
-            if (!is_valid(p, i, j, s.lq, s.lk)) continue;
-            xrow[j] = score(p, h, &s, i, j);
-            const float *vj = row_of(p, p->v, s.ks + j, h);
-            double dp = 0.0;
-            for (int d = 0; d < D; ++d) dp += (double)doi[d] * (double)vj[d];
-            dprow[j] = dp;
-            if (softmax) delta += exp(xrow[j] - m) / l * dp;
-        }
-        for (int64_t j = 0; j < s.lk; ++j) {
-            if (!is_valid(p, i, j, s.lq, s.lk)) continue;
-            double w, dx;
-            if (softmax) {
-                w = exp(xrow[j] - m) / l;
-                dx = w * (dprow[j] - delta);
-            } else {
-                w = act_f(p->act, xrow[j]);
-                dx = dprow[j] * act_grad(p->act, xrow[j]);
-            }
-            const float *kj = row_of(p, p->k, s.ks + j, h);
-            double *dkj = orow(p, dk, s.ks + j, h), *dvj = orow(p, dv, s.ks + j, h);
-            for (int d = 0; d < D; ++d) {
-                dqi[d] += p->scale * dx * (double)kj[d];
-                dkj[d] += p->scale * dx * (double)qi[d];
-                dvj[d] += w * (double)doi[d];
-            }
-        }
+}
+
+/* Softmax statistics of query row i (JFA): m, l, and delta_i = sum_j P_ij dP_ij. */
+static int row_bwd_stats(const problem *p, int h, const sample *s, int64_t i, const float *doi,
+                         double *m, double *l, double *delta) {
+    if (!row_stats(p, h, s, i, m, l)) return 0;
+    double dl = 0.0;
+    for (int64_t j = 0; j < s->lk; ++j) {
+        if (!is_valid(p, i, j, s->lq, s->lk)) continue;
+        double w, dx;
+        pair_bwd(p, 1, h, s, i, j, doi, *m, *l, 0.0, &w, &dx);  /* dx = P_ij dP_ij here */
+        dl += dx;
     }
+    *delta = dl;
+    return 1;
 }
 
 static int nthreads_or_default(int nthreads) {
@@ -253,15 +255,6 @@ static int nthreads_or_default(int nthreads) {
     (void)nthreads;
     return 1;
 #endif
-}
-
-static int max_lk(const problem *p) {
-    int64_t mx = 0;
-    for (int b = 0; b < p->B; ++b) {
-        int64_t lk = (int64_t)p->kv_off[b + 1] - p->kv_off[b];
-        if (lk > mx) mx = lk;
-    }
-    return (int)mx;
 }
 
 static problem make_problem(const float *q, const float *k, const float *v, const int32_t *q_off,
@@ -276,34 +269,95 @@ static problem make_problem(const float *q, const float *k, const float *v, cons
     return p;
 }
 
-static void run_fwd(const problem *p, int softmax, double *o, double *lse, int nthreads) {
-    const int64_t n = (int64_t)p->B * p->H;
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads_or_default(nthreads))
-    for (int64_t u = 0; u < n; ++u) fwd_slice(p, softmax, (int)(u / p->H), (int)(u % p->H), o, lse);
+static int64_t out_rows(const problem *p) {
+    return p->q_off ? (int64_t)p->q_off[p->B] : (int64_t)p->B * p->lq_fixed;
 }
 
+/* Every output row (all heads) is independent: parallel over rows. */
+static void run_fwd(const problem *p, int softmax, double *o, double *lse, int nthreads) {
+    const int64_t n = out_rows(p) * p->H;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads_or_default(nthreads))
+    for (int64_t u = 0; u < n; ++u) {
+        const int64_t r = u / p->H;
+        const int h = (int)(u % p->H);
+        const int b = sample_of_out_row(p, r);
+        const int64_t o0 = p->q_off ? p->q_off[b] : (int64_t)b * p->lq_fixed;
+        fwd_row(p, softmax, b, h, r - o0, o, lse);
+    }
+}
+
+/* Backward: (1) per query row, the softmax statistics (JFA); (2) dQ per query
+ * row, summing over its keys; (3) dK and dV per key row, summing over the
+ * query rows that see it.  Each output row is written by one iteration, so
+ * every phase is parallel over rows and needs no reduction across threads. */
 static int run_bwd(const problem *p, int softmax, const float *dout, double *dq, double *dk,
                    double *dv, int nthreads) {
     if (!p->q_off) return 1;
-    const int64_t n = (int64_t)p->B * p->H;
-    const int lkmax = max_lk(p) + 1;
-    int rc = 0;
-#pragma omp parallel num_threads(nthreads_or_default(nthreads))
-    {
-        double *xrow = (double *)malloc(sizeof(double) * lkmax);
-        double *dprow = (double *)malloc(sizeof(double) * lkmax);
-        if (!xrow || !dprow) {
-#pragma omp atomic write
-            rc = 2;
-        } else {
-#pragma omp for schedule(dynamic, 1)
-            for (int64_t u = 0; u < n; ++u)
-                bwd_slice(p, softmax, (int)(u / p->H), (int)(u % p->H), dout, dq, dk, dv, xrow, dprow);
-        }
-        free(xrow);
-        free(dprow);
+    const int64_t tq = p->q_off[p->B], tk = p->kv_off[p->B];
+    const int H = p->H, D = p->D;
+    double *st = NULL; /* per (row, head): m, l, delta, valid */
+    if (softmax) {
+        st = (double *)malloc(sizeof(double) * 4 * (size_t)(tq > 0 ? tq : 1) * H);
+        if (!st) return 2;
     }
-    return rc;
+    const int nt = nthreads_or_default(nthreads);
+    if (softmax) {
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nt)
+        for (int64_t u = 0; u < tq * H; ++u) {
+            const int64_t r = u / H;
+            const int h = (int)(u % H);
+            const int b = sample_of_out_row(p, r);
+            sample s = sample_rows(p, b);
+            double *sr = st + 4 * u;
+            sr[3] = row_bwd_stats(p, h, &s, r - s.qs, row_of(p, dout, r, h), &sr[0], &sr[1], &sr[2]);
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nt)
+    for (int64_t u = 0; u < tq * H; ++u) {
+        const int64_t r = u / H;
+        const int h = (int)(u % H);
+        const int b = sample_of_out_row(p, r);
+        sample s = sample_rows(p, b);
+        const int64_t i = r - s.qs;
+        double *dqi = orow(p, dq, r, h);
+        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+        const double *sr = softmax ? st + 4 * u : NULL;
+        if (softmax && sr[3] == 0.0) continue;
+        const float *doi = row_of(p, dout, r, h);
+        for (int64_t j = 0; j < s.lk; ++j) {
+            if (!is_valid(p, i, j, s.lq, s.lk)) continue;
+            double w, dx;
+            pair_bwd(p, softmax, h, &s, i, j, doi, sr ? sr[0] : 0.0, sr ? sr[1] : 1.0,
+                     sr ? sr[2] : 0.0, &w, &dx);
+            const float *kj = row_of(p, p->k, s.ks + j, h);
+            for (int d = 0; d < D; ++d) dqi[d] += p->scale * dx * (double)kj[d];
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nt)
+    for (int64_t u = 0; u < tk * H; ++u) {
+        const int64_t r = u / H;
+        const int h = (int)(u % H);
+        const int b = sample_of_key_row(p, r);
+        sample s = sample_rows(p, b);
+        const int64_t j = r - s.ks;
+        double *dkj = orow(p, dk, r, h), *dvj = orow(p, dv, r, h);
+        for (int d = 0; d < D; ++d) { dkj[d] = 0.0; dvj[d] = 0.0; }
+        for (int64_t i = 0; i < s.lq; ++i) {
+            if (!is_valid(p, i, j, s.lq, s.lk)) continue;
+            const double *sr = softmax ? st + 4 * ((s.qs + i) * H + h) : NULL;
+            const float *doi = row_of(p, dout, s.qs + i, h);
+            const float *qi = row_of(p, p->q, s.qs + i, h);
+            double w, dx;
+            pair_bwd(p, softmax, h, &s, i, j, doi, sr ? sr[0] : 0.0, sr ? sr[1] : 1.0,
+                     sr ? sr[2] : 0.0, &w, &dx);
+            for (int d = 0; d < D; ++d) {
+                dkj[d] += p->scale * dx * (double)qi[d];
+                dvj[d] += w * (double)doi[d];
+            }
+        }
+    }
+    free(st);
+    return 0;
 }
 
 /* ------------------------------------------------------------ exported API */

@@ -1,0 +1,79 @@
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark
+times (the library's own persistent grids over the whole batch).
+
+The GPU runs the whole batch; the oracle recomputes sampled (sample, head)
+slices one by one: always the longest sample, plus seeded random ones.  Each
+slice is compared row by row with the same bar as the small parity tests.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from recsys_jagged_attention_gdpa_amd import synth
+from tests.gpu_helpers import TAU, announce, check_lse, gpu_bwd, gpu_fwd, np64, to_dev
+from tests.helpers import (oracle_bwd, oracle_fwd, row_check, softmax_grad_floor,
+                           structural_zero_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _single_head(w, b, h):
+    """Workload holding only sample b and head h (contiguous copies)."""
+    s = w.subset([b])
+    pick = lambda t: None if t is None else t[:, h:h + 1, :].contiguous()
+    tab = None if s.bias_table is None else s.bias_table[h:h + 1].contiguous()
+    return synth.Workload(**{**s.__dict__, "H": 1, "q": pick(s.q), "k": pick(s.k), "v": pick(s.v),
+                             "dout": pick(s.dout), "bias_table": tab})
+
+
+# (workload, random slices besides the longest sample)
+CASES = [("tiny_gdpa_fp32", 2), ("gdpa_xattn_short_kv", 3), ("jfa_causal_self", 1),
+         ("pma_gdpa_fwd", 3), ("longtail_gdpa", 1)]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,n_random", CASES)
+def test_full_size_sampled_slices(name, n_random):
+    t0 = time.time()
+    w = synth.make(name)
+    announce(f"full-size {name}: B={w.B} H={w.H} D={w.D} Tq={w.total_q} Tk={w.total_k} "
+             f"(generated in {time.time() - t0:.1f}s)")
+    d = to_dev(w)
+    f = gpu_fwd(w, d)
+    g = gpu_bwd(w, d, f) if (w.backward and w.q_off is not None) else None
+    torch.cuda.synchronize()
+    out = {k: v.detach().cpu() for k, v in f.items() if v is not None}
+    if g is not None:
+        out.update({k: v.detach().cpu() for k, v in g.items()})
+    del d, f, g
+    torch.cuda.empty_cache()
+    announce(f"full-size {name}: GPU done at {time.time() - t0:.1f}s")
+
+    rng = np.random.default_rng(77)
+    lens = w.lq if w.q_off is not None else w.lk
+    longest = int(np.argmax(lens * w.lk))
+    picks = [(longest, int(rng.integers(w.H)))]
+    for b in rng.choice(w.B, size=min(n_random, w.B), replace=False):
+        picks.append((int(b), int(rng.integers(w.H))))
+    tau = TAU[w.dtype]
+    for b, h in picks:
+        ws = _single_head(w, b, h)
+        want = oracle_fwd(ws)
+        o0 = b * w.lq_fixed if w.q_off is None else int(w.q_off[b])
+        n = int(ws.total_q_out)
+        zq_out, zq_in, zk = structural_zero_rows(ws)
+        row_check(np64(out["o"][o0:o0 + n, h:h + 1]), want["o"], tau, f"{name} b={b} h={h} O",
+                  zero_rows=zq_out)
+        if w.mode == "jfa":
+            check_lse(np64(out["lse"][h:h + 1, o0:o0 + n]), want["lse"], f"{name} b={b} h={h} LSE")
+        if "dq" in out:
+            wb = oracle_bwd(ws)
+            k0, k1 = int(w.kv_off[b]), int(w.kv_off[b + 1])
+            for nm, z, rows in (("dq", zq_in, slice(o0, o0 + n)), ("dk", zk, slice(k0, k1)),
+                                ("dv", zk, slice(k0, k1))):
+                row_check(np64(out[nm][rows, h:h + 1]), wb[nm], tau, f"{name} b={b} h={h} {nm}",
+                          zero_rows=z, abs_floor=softmax_grad_floor(ws, nm))
+        announce(f"full-size {name}: slice b={b} (Lq={int(ws.lq[0])}, Lk={int(ws.lk[0])}) h={h} "
+                 f"ok at {time.time() - t0:.1f}s")

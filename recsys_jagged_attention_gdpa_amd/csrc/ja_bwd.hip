@@ -463,24 +463,22 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
                 const u32x2 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x2 *>(row + 16);
                 dtb[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
-            // dQ^T = K^T dX^T, one 32-wide block of the head dimension at a time.
+            // dQ^T = K^T dX^T, one 32-wide block of the head dimension at a time;
+            // the block's Q tile is no longer read, so it stages dQ for the store.
+            f32x16 dqacc[NDB];
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                f32x16 acc = f32x16{};
+                dqacc[db] = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    acc = mfma32(lds_read_tr_operand<D>(Kt, ks * 16, db * 32, lane), dtb[ks], acc);
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4)
-                    dQs.store8(ia + l32, db * 32 + r4 * 8 + g * 4,
-                               u32x2{pack2(acc[r4 * 4 + 0] * p.scale, acc[r4 * 4 + 1] * p.scale),
-                                     pack2(acc[r4 * 4 + 2] * p.scale, acc[r4 * 4 + 3] * p.scale)});
+                    dqacc[db] = mfma32(lds_read_tr_operand<D>(Kt, ks * 16, db * 32, lane), dtb[ks], dqacc[db]);
             }
+            store_tile<D>(dQs, Qt, ia, dqacc, p.scale, lane);
             lds_wave_sync();  // every LDS read of this block is done before the next stores
         }
         const HeadSlice<D> dKs(p.dk, s.ks, s.lk, H, h), dVs(p.dv, s.ks, s.lk, H, h);
-        store_row_acc<D>(dKs, jkey, dkacc, p.scale, g);
-        store_row_acc<D>(dVs, jkey, dvacc, 1.0f, g);
+        store_tile<D>(dKs, Qt, 0, dkacc, p.scale, lane);
+        store_tile<D>(dVs, Gt, 0, dvacc, 1.0f, lane);
     }
 }
 

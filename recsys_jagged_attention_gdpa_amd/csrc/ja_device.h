@@ -212,6 +212,9 @@ __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, u32x2 v) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
 __device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
 }

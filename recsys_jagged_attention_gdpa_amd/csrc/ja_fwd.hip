@@ -230,13 +230,15 @@ template <int D, int MODE, int ACT>
 __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnParams p) {
     constexpr int KV_BYTES = 32 * D * 2;
     constexpr int NKK = D / 16, NDB = D / 32;
-    __shared__ __attribute__((aligned(16))) char smem[2 * KV_BYTES];
+    constexpr int NWAVES = FWD_THREADS / WAVE;
+    __shared__ __attribute__((aligned(16))) char smem[(2 + NWAVES) * KV_BYTES];
     __shared__ int s_unit, s_blk;
     lchar *const Kt = (lchar *)smem;
     lchar *const Vt = Kt + KV_BYTES;
 
     const int H = p.H;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    lchar *const Ot = Vt + KV_BYTES * (1 + wv);  // this wave's output staging tile
     const int g = lane >> 5, l32 = lane & 31;
     const int n_units = p.counters2->units;
     if (n_units == 0) return;
@@ -332,12 +334,9 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
                 for (int ks = 0; ks < 2; ++ks)
                     oacc[db] = mfma32(lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane), pb[ks], oacc[db]);
             }
-            if constexpr (MODE == JFA) {
-                buf_store_f32(lse_r, g == 0 ? (uint32_t)irow * 4u : OOB, lse_row);
-                store_row_acc_split<D>(Os, Rs, irow, oacc, norm, g);
-            } else {
-                store_row_acc<D>(Os, irow, oacc, norm, g);
-            }
+            if constexpr (MODE == JFA) buf_store_f32(lse_r, g == 0 ? (uint32_t)irow * 4u : OOB, lse_row);
+            store_tile<D>(Os, Ot, blk * 32, oacc, norm, lane);
+            if (MODE == JFA && res) store_tile<D, true>(Rs, Ot, blk * 32, oacc, norm, lane);
             return nxt;
         };
 

@@ -63,6 +63,9 @@ struct HeadSlice {
     __device__ __forceinline__ void store8(int row, int d, u32x2 v) const {
         buf_store8(r, (uint32_t)row * row_bytes + (uint32_t)d * 2u, v);
     }
+    __device__ __forceinline__ void store16(int row, int c, u32x4 v) const {
+        buf_store16(r, (uint32_t)row * row_bytes + (uint32_t)c * 16u, v);
+    }
 };
 
 // ROWS rows of two head slices (Q and dO) staged through registers into the
@@ -113,6 +116,53 @@ __device__ __forceinline__ void store_row_acc(const HeadSlice<D> &S, int row, co
             S.store8(row, db * 32 + r4 * 8 + g * 4,
                      u32x2{pack2(acc[db][r4 * 4 + 0] * mul, acc[db][r4 * 4 + 1] * mul),
                            pack2(acc[db][r4 * 4 + 2] * mul, acc[db][r4 * 4 + 3] * mul)});
+}
+
+// Output tiles leave a wave as whole rows: the D^T-layout accumulators (lane
+// owns row l32; element e of block db is column db*32 + crow(e, g)) are first
+// written, as bf16 times `mul`, into a 32 x D swizzled LDS tile owned by the
+// wave, then read back row-major and stored with 16 bytes per lane (4 rows of
+// 256 bytes per instruction for D = 128).  Writing 8-byte pieces of 32
+// different rows straight to memory costs about a fifth of the achievable
+// HBM bandwidth.  RESID stages the rounding residual x - bf16(x) instead.
+template <int D, bool RESID = false>
+__device__ __forceinline__ void stage_row_acc(lchar *st, const f32x16 (&acc)[D / 32], float mul, int l32, int g) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            float x[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x[t] = acc[db][r4 * 4 + t] * mul;
+                if (RESID) x[t] = x[t] - bf2f(f2bf(x[t]));
+            }
+            const u32x2 v{pack2(x[0], x[1]), pack2(x[2], x[3])};
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(st + lds_off<D>(l32, db * 4 + r4) + g * 8) = v;
+        }
+}
+
+// Store a staged 32 x D tile as rows row0 .. row0+31 of S (one wave; rows past
+// the slice are dropped by the descriptor).
+template <int D>
+__device__ __forceinline__ void store_staged(const HeadSlice<D> &S, const lchar *st, int row0, int lane) {
+    constexpr int CH = D / 8;
+#pragma unroll
+    for (int it = 0; it < 32 * CH / WAVE; ++it) {
+        const int cid = lane + it * WAVE;
+        const int r = cid / CH, c = cid % CH;
+        S.store16(row0 + r, c, __builtin_bit_cast(u32x4, lds_read16(st, lds_off<D>(r, c))));
+    }
+}
+
+// Stage and store one accumulator tile (the two steps above, with the LDS
+// write -> read ordering in between).
+template <int D, bool RESID = false>
+__device__ __forceinline__ void store_tile(const HeadSlice<D> &S, lchar *st, int row0, const f32x16 (&acc)[D / 32],
+                                           float mul, int lane) {
+    stage_row_acc<D, RESID>(st, acc, mul, lane & 31, lane >> 5);
+    lds_wave_sync();
+    store_staged<D>(S, st, row0, lane);
 }
 
 // As above, and also store the rounding residual x - bf16(x) into R.

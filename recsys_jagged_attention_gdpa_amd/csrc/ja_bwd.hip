@@ -389,9 +389,9 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
         // first query block; all waited for before the block loop, so that the
         // waits the compiler derives inside the loop reflect only the loop's
         // own order (next block's loads, then this block's stores).
-        PairSliceLoader<32, D, WAVE> nx;
+        PairSliceLoader<32, D, WAVE, CP_NT> nx;
         {
-            PairSliceLoader<32, D, WAVE> kv;
+            PairSliceLoader<32, D, WAVE, CP_NT> kv;
             kv.load(Ks, Vs, 0, lane);
             nx.load(Qs, Gs, 0, lane);
             kv.store(Kt, Vt, lane);
@@ -410,8 +410,8 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const uint32_t off = (uint32_t)(ia + crow(e, g)) * 4u;
-                lse2[e] = MODE == JFA ? buf_load_f32(lse_r, off) * LOG2E : 0.0f;
-                dlt[e] = MODE == JFA ? buf_load_f32(dlt_r, off) : 0.0f;
+                lse2[e] = MODE == JFA ? buf_load_f32<CP_NT>(lse_r, off) * LOG2E : 0.0f;
+                dlt[e] = MODE == JFA ? buf_load_f32<CP_NT>(dlt_r, off) : 0.0f;
                 bv[e] = 0.0f;
             }
             if (brow) {

@@ -203,20 +203,29 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ uint32_t rows_span(int rows, int H, int D, int esize) {
     return rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * H * D + D) * esize) : 0u;
 }
+// Cache policy of an access: CP_NT marks data touched once (streamed inputs,
+// outputs), so it does not displace data that other units re-read from L2.
+constexpr int CP_DEFAULT = 0;
+constexpr int CP_NT = 2;
+template <int CP = CP_DEFAULT>
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP);
 }
+template <int CP = CP_DEFAULT>
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CP));
 }
+template <int CP = CP_DEFAULT>
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, u32x2 v) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, CP);
 }
+template <int CP = CP_DEFAULT>
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, CP);
 }
+template <int CP = CP_DEFAULT>
 __device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, CP);
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory

@@ -57,20 +57,22 @@ struct HeadSlice {
         row_bytes = (uint32_t)(H * D * 2);
     }
     // 16 bytes (chunk c = 8 bf16) of row `row`; zeros past the slice.
+    template <int CP = CP_DEFAULT>
     __device__ __forceinline__ u32x4 load16(int row, int c) const {
-        return buf_load16(r, (uint32_t)row * row_bytes + (uint32_t)c * 16u);
+        return buf_load16<CP>(r, (uint32_t)row * row_bytes + (uint32_t)c * 16u);
     }
     __device__ __forceinline__ void store8(int row, int d, u32x2 v) const {
         buf_store8(r, (uint32_t)row * row_bytes + (uint32_t)d * 2u, v);
     }
+    template <int CP = CP_DEFAULT>
     __device__ __forceinline__ void store16(int row, int c, u32x4 v) const {
-        buf_store16(r, (uint32_t)row * row_bytes + (uint32_t)c * 16u, v);
+        buf_store16<CP>(r, (uint32_t)row * row_bytes + (uint32_t)c * 16u, v);
     }
 };
 
 // ROWS rows of two head slices (Q and dO) staged through registers into the
 // swizzled LDS layout by NT threads; rows past the slice become zeros.
-template <int ROWS, int D, int NT>
+template <int ROWS, int D, int NT, int CP = CP_DEFAULT>
 struct PairSliceLoader {
     static constexpr int CHUNKS = ROWS * D / 8;
     static constexpr int PER_THREAD = CHUNKS / NT;
@@ -81,8 +83,8 @@ struct PairSliceLoader {
         for (int it = 0; it < PER_THREAD; ++it) {
             const int cid = tid + it * NT;
             const int r = cid / (D / 8), c = cid % (D / 8);
-            a[it] = A.load16(r0 + r, c);
-            b[it] = B.load16(r0 + r, c);
+            a[it] = A.template load16<CP>(r0 + r, c);
+            b[it] = B.template load16<CP>(r0 + r, c);
         }
     }
     __device__ __forceinline__ void store(lchar *ta, lchar *tb, int tid) const {
@@ -97,10 +99,10 @@ struct PairSliceLoader {
 };
 
 // One lane's row of a head slice in MFMA operand layout (chunk 2kk+g for k-step kk).
-template <int D>
+template <int D, int CP = CP_DEFAULT>
 __device__ __forceinline__ void load_row_operand(bf16x8 (&reg)[D / 16], const HeadSlice<D> &S, int row, int g) {
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) reg[kk] = __builtin_bit_cast(bf16x8, S.load16(row, 2 * kk + g));
+    for (int kk = 0; kk < D / 16; ++kk) reg[kk] = __builtin_bit_cast(bf16x8, S.template load16<CP>(row, 2 * kk + g));
 }
 
 // Store a D^T-layout accumulator block set (lane owns row `row` of the slice;
@@ -151,7 +153,7 @@ __device__ __forceinline__ void store_staged(const HeadSlice<D> &S, const lchar 
     for (int it = 0; it < 32 * CH / WAVE; ++it) {
         const int cid = lane + it * WAVE;
         const int r = cid / CH, c = cid % CH;
-        S.store16(row0 + r, c, __builtin_bit_cast(u32x4, lds_read16(st, lds_off<D>(r, c))));
+        S.template store16<CP_NT>(row0 + r, c, __builtin_bit_cast(u32x4, lds_read16(st, lds_off<D>(r, c))));
     }
 }
 

@@ -272,9 +272,12 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
         const int nblk = (s.lq + 31) / 32;
         const bool masked = s.lk < 32 || p.causal;
         // One 32-row query block, with Q rows in `qreg`; the next block's rows
-        // are loaded into `qnext` first, so they are in flight meanwhile.
-        auto block = [&](int blk, const bf16x8 (&qreg)[NKK], bf16x8 (&qnext)[NKK]) -> int {
+        // are loaded into `qnext` first, so they are in flight meanwhile.  The
+        // wave's LDS tile holds the block's Q rows, then its output rows.
+        auto block = [&](int blk, const WaveTile<D> &qreg, WaveTile<D> &qnext) -> int {
             const int irow = blk * 32 + l32;
+            qreg.store(Ot, lane);
+            lds_wave_sync();
             float bv[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) bv[e] = 0.0f;
@@ -285,13 +288,15 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
             int nxt = 0;
             if (lane == 0) nxt = atomicAdd(&s_blk, 1);
             nxt = __builtin_amdgcn_readfirstlane(nxt);
-            load_row_operand<D>(qnext, Qs, nxt * 32 + l32, g);  // past the sample: zeros, no traffic
+            qnext.load(Qs, nxt * 32, lane);  // past the sample: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);  // keep the next block's loads ahead of this block's work
 
             f32x16 sacc = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                sacc = mfma32(lds_read16(Kt, lds_off<D>(l32, 2 * kk + g)), qreg[kk], sacc);
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int off = lds_off<D>(l32, 2 * kk + g);
+                sacc = mfma32(lds_read16(Kt, off), lds_read16(Ot, off), sacc);
+            }
             const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
             float pv[16];
             float norm = 1.0f, lse_row = 0.0f;
@@ -326,23 +331,27 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
             }
             bf16x8 pb[2];
             pack_operands(pv, pb[0], pb[1]);
-            f32x16 oacc[NDB];
+            if constexpr (MODE == JFA) buf_store_f32(lse_r, g == 0 ? (uint32_t)irow * 4u : OOB, lse_row);
+            // One 32-wide block of the head dimension at a time, staged as it
+            // completes, so only one accumulator block is live.  The optional
+            // rounding residual (JFA) is written straight from the registers.
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                oacc[db] = f32x16{};
+                f32x16 acc = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    oacc[db] = mfma32(lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane), pb[ks], oacc[db]);
+                    acc = mfma32(lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane), pb[ks], acc);
+                stage_acc_block<D>(Ot, acc, db, norm, l32, g);
+                if (MODE == JFA && res) store_resid_block<D>(Rs, irow, acc, db, norm, g);
             }
-            if constexpr (MODE == JFA) buf_store_f32(lse_r, g == 0 ? (uint32_t)irow * 4u : OOB, lse_row);
-            store_tile<D>(Os, Ot, blk * 32, oacc, norm, lane);
-            if (MODE == JFA && res) store_tile<D, true>(Rs, Ot, blk * 32, oacc, norm, lane);
+            lds_wave_sync();
+            store_staged<D>(Os, Ot, blk * 32, lane);
             return nxt;
         };
 
         int blk = wv;
-        bf16x8 qa[NKK], qb[NKK];
-        load_row_operand<D>(qa, Qs, blk * 32 + l32, g);
+        WaveTile<D> qa, qb;
+        qa.load(Qs, blk * 32, lane);
         // Enter the loop with nothing outstanding, so the loop's waits cover
         // only the previous block's prefetch, not its stores.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));

@@ -98,6 +98,29 @@ struct PairSliceLoader {
     }
 };
 
+// A 32-row tile of one head slice, loaded by one wave with 16 bytes per lane
+// (whole rows per instruction) into registers, then written to a swizzled LDS
+// tile; rows past the slice become zeros.
+template <int D, int CP = CP_DEFAULT>
+struct WaveTile {
+    static constexpr int PER_LANE = 32 * D / 8 / WAVE;
+    u32x4 a[PER_LANE];
+    __device__ __forceinline__ void load(const HeadSlice<D> &S, int r0, int lane) {
+#pragma unroll
+        for (int it = 0; it < PER_LANE; ++it) {
+            const int cid = lane + it * WAVE;
+            a[it] = S.template load16<CP>(r0 + cid / (D / 8), cid % (D / 8));
+        }
+    }
+    __device__ __forceinline__ void store(lchar *t, int lane) const {
+#pragma unroll
+        for (int it = 0; it < PER_LANE; ++it) {
+            const int cid = lane + it * WAVE;
+            lds_write16(t, lds_off<D>(cid / (D / 8), cid % (D / 8)), a[it]);
+        }
+    }
+};
+
 // One lane's row of a head slice in MFMA operand layout (chunk 2kk+g for k-step kk).
 template <int D, int CP = CP_DEFAULT>
 __device__ __forceinline__ void load_row_operand(bf16x8 (&reg)[D / 16], const HeadSlice<D> &S, int row, int g) {
@@ -128,20 +151,41 @@ __device__ __forceinline__ void store_row_acc(const HeadSlice<D> &S, int row, co
 // different rows straight to memory costs about a fifth of the achievable
 // HBM bandwidth.  RESID stages the rounding residual x - bf16(x) instead.
 template <int D, bool RESID = false>
+__device__ __forceinline__ void stage_acc_block(lchar *st, const f32x16 &acc, int db, float mul, int l32, int g) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+        float x[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x[t] = acc[r4 * 4 + t] * mul;
+            if (RESID) x[t] = x[t] - bf2f(f2bf(x[t]));
+        }
+        const u32x2 v{pack2(x[0], x[1]), pack2(x[2], x[3])};
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(st + lds_off<D>(l32, db * 4 + r4) + g * 8) = v;
+    }
+}
+
+// The rounding residual x - bf16(x) of one accumulator block (x = acc * mul),
+// stored straight from the D^T layout (lane owns row `row`).
+template <int D>
+__device__ __forceinline__ void store_resid_block(const HeadSlice<D> &R, int row, const f32x16 &acc, int db, float mul,
+                                                  int g) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+        float rs[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float x = acc[r4 * 4 + t] * mul;
+            rs[t] = x - bf2f(f2bf(x));
+        }
+        R.store8(row, db * 32 + r4 * 8 + g * 4, u32x2{pack2(rs[0], rs[1]), pack2(rs[2], rs[3])});
+    }
+}
+
+template <int D, bool RESID = false>
 __device__ __forceinline__ void stage_row_acc(lchar *st, const f32x16 (&acc)[D / 32], float mul, int l32, int g) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            float x[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                x[t] = acc[db][r4 * 4 + t] * mul;
-                if (RESID) x[t] = x[t] - bf2f(f2bf(x[t]));
-            }
-            const u32x2 v{pack2(x[0], x[1]), pack2(x[2], x[3])};
-            *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(st + lds_off<D>(l32, db * 4 + r4) + g * 8) = v;
-        }
+    for (int db = 0; db < D / 32; ++db) stage_acc_block<D, RESID>(st, acc[db], db, mul, l32, g);
 }
 
 // Store a staged 32 x D tile as rows row0 .. row0+31 of S (one wave; rows past

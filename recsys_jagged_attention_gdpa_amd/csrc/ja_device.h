@@ -211,6 +211,11 @@ template <int CP = CP_DEFAULT>
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP);
 }
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes dst + 16 i (dst wave-uniform); out-of-range lanes write zeros.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, __attribute__((address_space(3))) void *dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, (int)off, 0, 0, 0);
+}
 template <int CP = CP_DEFAULT>
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CP));
@@ -236,6 +241,30 @@ __device__ __host__ constexpr int waitcnt_vm(int n) {
 
 // ---------------------------------------------------------- misc helpers
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Max / sum of a value over lanes l and l ^ 32 (the two halves of the wave
+// hold different keys of the same query rows).  v_permlane32_swap exchanges
+// lanes 32..63 of its first register with lanes 0..31 of its second, so with
+// both holding v every lane ends up with its own and its partner's value, and
+// no LDS round trip is needed.  It is issued as inline assembly because the
+// compiler folds the builtin's two results into one when both inputs are the
+// same value; the s_nop covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void pair_swap(float &a, float &b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float pair_max(float v) {
+    float a = v, b = v;
+    pair_swap(a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float v) {
+    float a = v, b = v;
+    pair_swap(a, b);
+    return a + b;
+}
+
+// True on every lane when the predicate holds on any lane (a wave-uniform test).
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
 __device__ __forceinline__ float shfl_xor32(float v) {
     // exchange with lane ^ 32 (the other half of the wave)

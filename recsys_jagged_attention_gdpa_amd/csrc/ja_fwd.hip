@@ -33,6 +33,7 @@ namespace ja {
 constexpr int FWD_THREADS = 256;
 constexpr int BM = Q_TILE;   // 128 query rows per unit
 constexpr int BN = KV_TILE;  // 64 keys per tile
+constexpr float RESCALE_SLACK = 8.0f;  // log2 units a running softmax max may lag the true max
 
 template <int D, int MODE, int ACT>
 __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p) {
@@ -88,19 +89,20 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
         float m_run = -INFINITY, l_run = 0.0f;  // JFA running max (log2 units) and partial sum
 
-        // Key / value tile jt and the bias window it needs go through registers
-        // into LDS buffer (jt & 1); loads past the sample read zeros.
-        PairSliceLoader<BN, D, FWD_THREADS> ld;
+        // Key / value tile jt is copied straight into LDS buffer (jt & 1); the
+        // bias window it needs goes through a register.  Loads past the sample
+        // read zeros.
         float bnext = 0.0f;
         auto load_tile = [&](int jt) {
-            ld.load(Ks, Vs, jt * BN, tid);
+            lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
+            dma_tile<BN, D, FWD_THREADS>(kt, Ks, jt * BN, tid);
+            dma_tile<BN, D, FWD_THREADS>(kt + TILE_BYTES, Vs, jt * BN, tid);
             const BiasWindow bw = bias_window(bz, i0, BM, jt * BN, BN);
             bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
         };
         auto store_tile = [&](int buf) {
-            lchar *kt = lbase + buf * 2 * TILE_BYTES;
-            ld.store(kt, kt + TILE_BYTES, tid);
-            if (tid < WIN) s_bias[buf][tid] = bnext;
+            if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;  // JFA works in log2 units
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tile has landed
         };
         load_tile(0);
         store_tile(0);
@@ -128,58 +130,72 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
             }
 
             // Element-wise stage.  A tile needs per-element masking only when it
-            // crosses the key end or (causal) the diagonal of this wave's rows.
+            // crosses the key end or (causal) the diagonal of this wave's rows;
+            // that test and the bias kind are wave-uniform, so each variant is
+            // a straight-line loop behind one scalar branch.
             const bool tail = j0 + BN > s.lk;
             const bool diag = p.causal && (j0 + BN - 1 > iw + s.lk - s.lq);
             const bool masked = tail || diag;
             const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
             bf16x8 pb[NKS];
-            float xs[NNB][16];
-#pragma unroll
-            for (int nb = 0; nb < NNB; ++nb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = j0 + nb * 32 + crow(e, g);
-                    const float b = bz.kind ? bwin[bias_window_index(bz, bw, irow, j)] : 0.0f;
-                    xs[nb][e] = MODE == GDPA ? __builtin_fmaf(sacc[nb][e], p.scale, b)
-                                             : __builtin_fmaf(sacc[nb][e], sl2, b * LOG2E);
-                }
-            if constexpr (MODE == GDPA) {
-#pragma unroll
-                for (int nb = 0; nb < NNB; ++nb) {
-                    float pv[16];
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int j = j0 + nb * 32 + crow(e, g);
-                        const float y = act_fwd<ACT>(xs[nb][e]);
-                        pv[e] = (masked & (j >= my_kend)) ? 0.0f : y;  // bitwise: no per-lane branches
-                    }
-                    pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
-                }
-            } else {
-                float tmax = -INFINITY;
+            // x = scale * s + bias (JFA: in log2 units); without bias only the
+            // scale is applied, folded into later arithmetic where possible.
+            if (bz.kind) {
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int j = j0 + nb * 32 + crow(e, g);
-                        xs[nb][e] = (masked & (j >= my_kend)) ? -INFINITY : xs[nb][e];
-                        tmax = fmaxf(tmax, xs[nb][e]);
+                        const float b = bwin[bias_window_index(bz, bw, irow, j)];
+                        sacc[nb][e] = __builtin_fmaf(sacc[nb][e], MODE == GDPA ? p.scale : sl2, b);
                     }
-                tmax = fmaxf(tmax, shfl_xor32(tmax));
-                const float m_new = fmaxf(m_run, tmax);
-                const float shift = m_new == -INFINITY ? 0.0f : m_new;
-                const float alpha = fast_exp2(m_run - shift);
-                m_run = m_new;
-                l_run *= alpha;
+            }
+            const float xmul = bz.kind ? 1.0f : (MODE == GDPA ? p.scale : sl2);  // remaining scale
+            if constexpr (MODE == GDPA) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+                for (int nb = 0; nb < NNB; ++nb) {
+                    float pv[16];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) pv[e] = act_fwd<ACT>(sacc[nb][e] * xmul);
+                    if (masked) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            pv[e] = (j0 + nb * 32 + crow(e, g) >= my_kend) ? 0.0f : pv[e];
+                    }
+                    pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
+                }
+            } else {
+                if (masked) {
+#pragma unroll
+                    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            sacc[nb][e] = (j0 + nb * 32 + crow(e, g) >= my_kend) ? -INFINITY : sacc[nb][e];
+                }
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[nb][e]);
+                tmax = pair_max(tmax) * xmul;  // xmul > 0, so the max commutes with it
+                // The running max is only moved (and O, l rescaled) when the tile's
+                // max exceeds it by more than RESCALE_SLACK (log2 units); otherwise
+                // P is formed against the stale max and stays below 2^RESCALE_SLACK.
+                if (wave_any(tmax > m_run + RESCALE_SLACK)) {
+                    const float m_new = fmaxf(m_run, tmax);
+                    const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run - m_new);
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+                }
+                const float nm = m_run == -INFINITY ? 0.0f : -m_run;
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb) {
                     float pv[16];
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        pv[e] = fast_exp2(xs[nb][e] - shift);
+                        pv[e] = fast_exp2(__builtin_fmaf(sacc[nb][e], xmul, nm));
                         l_run += pv[e];
                     }
                     pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
@@ -203,7 +219,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
         // Epilogue: lane owns query row irow; d = db*32 + crow(e, g).
         float norm = 1.0f;
         if constexpr (MODE == JFA) {
-            const float l_tot = l_run + shfl_xor32(l_run);
+            const float l_tot = pair_sum(l_run);
             const bool any = l_tot > 0.0f;
             norm = any ? 1.0f / l_tot : 0.0f;
             const rsrc_t lr = make_rsrc(p.lse + (int64_t)h * p.total_q_out + s.o0, (uint32_t)s.lq * 4u);

@@ -98,6 +98,26 @@ struct PairSliceLoader {
     }
 };
 
+// ROWS x D tile of one head slice copied by NT threads straight from global
+// memory into the swizzled LDS layout (buffer_load ... lds: lane i of an
+// instruction writes LDS bytes base + 16 i .. +15, so each lane fetches the
+// logical chunk that the swizzle puts in its slot).  Rows past the slice land
+// as zeros.  The copy is complete once this wave's vector-memory counter has
+// drained; other waves' parts need a barrier after that.
+template <int ROWS, int D, int NT>
+__device__ __forceinline__ void dma_tile(lchar *tile, const HeadSlice<D> &S, int r0, int tid) {
+    constexpr int CH = D / 8, SLOTS = ROWS * CH, PER_INSTR = NT / WAVE * WAVE;
+    static_assert(SLOTS % NT == 0, "tile / thread count mismatch");
+    const int wv = tid / WAVE, lane = tid % WAVE;
+#pragma unroll
+    for (int it = 0; it < SLOTS / NT; ++it) {
+        const int first = it * PER_INSTR + wv * WAVE;  // first slot of this wave's instruction
+        const int q = first + lane;
+        const int r = q / CH, c = (q % CH) ^ swz<D>(r);
+        buf_load16_lds(S.r, tile + first * 16, (uint32_t)(r0 + r) * S.row_bytes + (uint32_t)c * 16u);
+    }
+}
+
 // A 32-row tile of one head slice, loaded by one wave with 16 bytes per lane
 // (whole rows per instruction) into registers, then written to a swizzled LDS
 // tile; rows past the slice become zeros.

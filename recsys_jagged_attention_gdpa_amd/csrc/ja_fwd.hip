@@ -64,8 +64,9 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
         const int w = s_unit;
         __syncthreads();
         if (w >= n_units) break;
-        const int2 tile = p.tiles[w / H];
-        const int h = w % H;
+        const UnitRef u = tile_unit(p.tiles, w, n_units, H);
+        const int2 tile = u.tile;
+        const int h = u.h;
         const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
         const int i0 = tile.y * BM;            // first query row of the unit (sample-local)
         const int iw = i0 + wv * 32;           // first row of this wave

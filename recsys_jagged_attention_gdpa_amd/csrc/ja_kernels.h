@@ -70,6 +70,19 @@ struct AttnParams {
     PlanCounters *counters3;
 };
 
+// Units of the tile lists (PLAN_Q_TILES, PLAN_KV_TILES) are numbered
+// head-major: unit w is entry w % n of the list (n = units / H) for head
+// w / n, so consecutive units are consecutive tiles of one (sample, head).
+// Whole-sample lists use unit w = entry w / H, head w % H.
+struct UnitRef {
+    int2 tile;
+    int h;
+};
+__device__ __forceinline__ UnitRef tile_unit(const int2 *tiles, int w, int n_units, int H) {
+    const int n = n_units / H;
+    return UnitRef{tiles[w % n], w / n};
+}
+
 // Plans up to PLAN_MAX lists in one launch (one workgroup per list).
 constexpr int PLAN_MAX = 3;
 struct PlanBatch {

@@ -1,6 +1,14 @@
 // Work-list planner: jagged offsets -> per-unit cost -> counting sort (most
 // expensive first) -> list of (sample, tile) pairs + unit counter + cursor.
 //
+// Tile lists (query tiles, key tiles) are ordered sample by sample: samples
+// by total cost, most expensive first, and each sample's tiles together, most
+// expensive first.  The kernels number their units head-major over the list,
+// so consecutive units are consecutive tiles of one (sample, head): the
+// workgroups that pick them up at about the same time stream the same keys
+// and values (or queries) and share them through the caches instead of each
+// fetching them from HBM.  Whole-sample lists are ordered unit by unit.
+//
 // The pages report that naive jagged kernels leave compute units idle when
 // short sequences finish early and that software tile scheduling turned a 6x
 // imbalance into a near-balanced one ("GEM Training: How Meta Doubled the
@@ -73,6 +81,29 @@ __device__ __forceinline__ int bucket_of(int cost) {
     return PLAN_BUCKETS - 1 - cost;  // ascending bucket = descending cost
 }
 
+// Bucket of a whole sample's cost on a logarithmic scale (32 steps per
+// octave), so any total up to 2^31 fits the histogram; descending cost.
+__device__ __forceinline__ int sample_bucket_of(int64_t cost) {
+    if (cost < 1) cost = 1;
+    if (cost > 0x7fffffff) cost = 0x7fffffff;
+    const uint32_t c = (uint32_t)cost;
+    const int l = 31 - __builtin_clz(c);
+    const int frac = l >= 5 ? (int)((c >> (l - 5)) & 31u) : (int)((c << (5 - l)) & 31u);
+    return PLAN_BUCKETS - 1 - (l * 32 + frac);
+}
+
+__device__ __forceinline__ bool grouped(const PlanParams &p) { return p.kind != PLAN_SAMPLES; }
+
+template <class F>
+__device__ void for_each_run(const PlanParams &p, const PlanSample &s, F fn);
+
+// Total cost and tile count of a sample.
+__device__ int64_t sample_cost(const PlanParams &p, const PlanSample &s) {
+    int64_t c = 0;
+    for_each_run(p, s, [&](int, int n, int, int cost) { c += (int64_t)n * cost; });
+    return c;
+}
+
 // Visit the tiles of a sample as runs of equal cost, in non-increasing cost
 // order: fn(first_tile, count, step, cost).
 template <class F>
@@ -108,7 +139,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanBatch batc
 
     for (int b = tid; b < p.B; b += PLAN_THREADS) {
         const PlanSample s = plan_sample(p, b);
-        for_each_run(p, s, [&](int, int n, int, int cost) { atomicAdd(&hist[bucket_of(cost)], n); });
+        if (grouped(p)) {
+            if (s.ntiles > 0) atomicAdd(&hist[sample_bucket_of(sample_cost(p, s))], s.ntiles);
+        } else {
+            for_each_run(p, s, [&](int, int n, int, int cost) { atomicAdd(&hist[bucket_of(cost)], n); });
+        }
     }
     __syncthreads();
 
@@ -140,11 +175,20 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanBatch batc
 
     for (int b = tid; b < p.B; b += PLAN_THREADS) {
         const PlanSample s = plan_sample(p, b);
-        for_each_run(p, s, [&](int t0, int n, int step, int cost) {
-            const int pos = atomicAdd(&hist[bucket_of(cost)], n);
-            for (int k = 0; k < n; ++k)
-                if (pos + k < p.max_tiles) p.tiles[pos + k] = make_int2(b, t0 + k * step);
-        });
+        if (grouped(p)) {
+            if (s.ntiles == 0) continue;
+            int pos = atomicAdd(&hist[sample_bucket_of(sample_cost(p, s))], s.ntiles);
+            for_each_run(p, s, [&](int t0, int n, int step, int) {
+                for (int k = 0; k < n; ++k, ++pos)
+                    if (pos < p.max_tiles) p.tiles[pos] = make_int2(b, t0 + k * step);
+            });
+        } else {
+            for_each_run(p, s, [&](int t0, int n, int step, int cost) {
+                const int pos = atomicAdd(&hist[bucket_of(cost)], n);
+                for (int k = 0; k < n; ++k)
+                    if (pos + k < p.max_tiles) p.tiles[pos + k] = make_int2(b, t0 + k * step);
+            });
+        }
     }
     if (tid == 0) {
         const int n = s_total < p.max_tiles ? s_total : p.max_tiles;

@@ -142,21 +142,25 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
-        PairSliceLoader<BN, D, BWD_THREADS> ld;
+        // Key / value tile jt is copied straight into LDS buffer (jt & 1); the
+        // bias window (JFA: in log2 units) goes through a register.
         float bnext = 0.0f;
         auto load_tile = [&](int jt) {
-            ld.load(Ks, Vs, jt * BN, tid);
+            lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
+            dma_tile<BN, D, BWD_THREADS>(kt, Ks, jt * BN, tid);
+            dma_tile<BN, D, BWD_THREADS>(kt + TILE_BYTES, Vs, jt * BN, tid);
             const BiasWindow bw = bias_window(bz, i0, BM, jt * BN, BN);
             bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
         };
         auto store_tile = [&](int buf) {
-            lchar *kt = lbase + buf * 2 * TILE_BYTES;
-            ld.store(kt, kt + TILE_BYTES, tid);
-            if (tid < WIN) s_bias[buf][tid] = bnext;
+            if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tile has landed
         };
         load_tile(0);
         store_tile(0);
         __syncthreads();
+        const float sl = MODE == JFA ? p.scale * LOG2E : p.scale;
+        const float nl = -lse2;
 
         for (int jt = 0; jt < nkv; ++jt) {
             const int j0 = jt * BN;
@@ -167,7 +171,8 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
             load_tile(jt + 1);  // past the last tile: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);
 
-            const bool masked = (j0 + BN > s.lk) | (p.causal && (j0 + BN - 1 > iw + s.lk - s.lq)) | !row_ok;
+            // Wave-uniform: does this tile cross the key end, the diagonal or the query end?
+            const bool masked = (j0 + BN > s.lk) | (p.causal && (j0 + BN - 1 > iw + s.lk - s.lq)) | (iw + 32 > s.lq);
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb) {
                 f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -177,13 +182,30 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
                     sacc = mfma32(lds_read16(Kt, off), qreg[kk], sacc);
                     dpacc = mfma32(lds_read16(Vt, off), greg[kk], dpacc);
                 }
+                if (bz.kind) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        sacc[e] = __builtin_fmaf(sacc[e], sl, bwin[bias_window_index(bz, bw, irow, j0 + nb * 32 + crow(e, g))]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) sacc[e] *= sl;
+                }
                 float dx[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int j = j0 + nb * 32 + crow(e, g);
-                    const float bias = bz.kind ? bwin[bias_window_index(bz, bw, irow, j)] : 0.0f;
-                    const bool valid = !masked | (row_ok & (j < my_kend));  // bitwise: no per-lane branches
-                    score_bwd<MODE, ACT>(sacc[e], p.scale, bias, dpacc[e], lse2, dlt, valid, dx[e]);
+                    if constexpr (MODE == JFA) {
+                        dx[e] = fast_exp2(sacc[e] + nl) * (dpacc[e] - dlt);
+                    } else {
+                        float y, dy;
+                        act_fwd_grad<ACT>(sacc[e], y, dy);
+                        dx[e] = dpacc[e] * dy;
+                    }
+                }
+                if (masked) {
+                    // invalid pairs (and rows without a visible key, LSE = -inf) give nothing
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        dx[e] = (row_ok & (j0 + nb * 32 + crow(e, g) < my_kend)) ? dx[e] : 0.0f;
                 }
                 bf16x8 dsb[2];
                 pack_operands(dx, dsb[0], dsb[1]);
@@ -211,7 +233,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
     constexpr int WIN = BQ + BK - 1;
     static_assert(WIN <= BWD_THREADS, "one bias window entry per thread");
     __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
-    __shared__ float s_lse[2][BQ], s_dlt[2][BQ];
+    __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
+    __shared__ __attribute__((aligned(16))) float s_dlt[2][BQ];
     __shared__ float s_bias[2][WIN];
     __shared__ int s_unit;
     lchar *const lbase = (lchar *)smem;
@@ -259,31 +282,35 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
         const int shift = s.lk - s.lq;  // causal: key j visible to row i iff j <= i + shift
         const int nsteps = ia0 < s.lq ? (s.lq - ia0 + BQ - 1) / BQ : 0;
 
-        PairSliceLoader<BQ, D, BWD_THREADS> ld;
+        // Query / dO rows of step st are copied straight into LDS buffer
+        // (st & 1); the step's LSE, delta and bias window go through registers.
+        // JFA stores -LSE and the bias in log2 units, so P = exp2(fma(s, sl2, b - lse2)).
         float bnext = 0.0f, lnext = 0.0f, dnext = 0.0f;
         auto load_step = [&](int st) {
             const int ia = ia0 + st * BQ;
-            ld.load(Qs, Gs, ia, tid);
+            lchar *qt = lbase + (st & 1) * 2 * TILE_BYTES;
+            dma_tile<BQ, D, BWD_THREADS>(qt, Qs, ia, tid);
+            dma_tile<BQ, D, BWD_THREADS>(qt + TILE_BYTES, Gs, ia, tid);
             const BiasWindow bw = bias_window(bz, ia, BQ, jt0, BK);
             bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
             if constexpr (MODE == JFA) {
                 const uint32_t off = tid < BQ ? (uint32_t)(ia + tid) * 4u : OOB;
-                lnext = buf_load_f32(lr, off) * LOG2E;
+                lnext = buf_load_f32(lr, off);
                 dnext = buf_load_f32(dr, off);
             }
         };
         auto store_step = [&](int buf) {
-            lchar *qt = lbase + buf * 2 * TILE_BYTES;
-            ld.store(qt, qt + TILE_BYTES, tid);
-            if (tid < WIN) s_bias[buf][tid] = bnext;
+            if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;
             if (MODE == JFA && tid < BQ) {
-                s_lse[buf][tid] = lnext;
+                s_lse[buf][tid] = -lnext * LOG2E;
                 s_dlt[buf][tid] = dnext;
             }
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tiles has landed
         };
         load_step(0);
         store_step(0);
         __syncthreads();
+        const float sl = MODE == JFA ? p.scale * LOG2E : p.scale;
 
         for (int st = 0; st < nsteps; ++st) {
             const int ia = ia0 + st * BQ;
@@ -294,6 +321,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
             load_step(st + 1);  // past the last step: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);
 
+            // Wave-uniform: does this step cross the query end or the diagonal?
             const bool masked = (ia + BQ > s.lq) | (p.causal && (jw + 31 > ia + shift));
 #pragma unroll
             for (int qb = 0; qb < BQ / 32; ++qb) {
@@ -304,16 +332,49 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
                     sacc = mfma32(lds_read16(Qt, off), kreg[kk], sacc);
                     dpacc = mfma32(lds_read16(Gt, off), vreg[kk], dpacc);
                 }
-                float pv[16], dx[16];
+                // x = s * sl + bias; invalid pairs are zeroed after the element-wise
+                // stage (rows without any visible key have LSE = -inf, so their
+                // exponent is not finite and must not be used).
+                if (bz.kind) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int il = qb * 32 + crow(e, g);
-                    const int i = ia + il;
-                    const float bias = bz.kind ? bwin[bias_window_index(bz, bw, i, jkey)] : 0.0f;
-                    const bool valid = !masked | ((i < s.lq) & (!p.causal | (jkey <= i + shift)));
-                    const float lse2 = MODE == JFA ? s_lse[st & 1][il] : 0.0f;
-                    const float dlt = MODE == JFA ? s_dlt[st & 1][il] : 0.0f;
-                    pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bias, dpacc[e], lse2, dlt, valid, dx[e]);
+                    for (int e = 0; e < 16; ++e)
+                        sacc[e] = __builtin_fmaf(sacc[e], sl, bwin[bias_window_index(bz, bw, ia + qb * 32 + crow(e, g), jkey)]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) sacc[e] *= sl;
+                }
+                float pv[16], dx[16];
+                if constexpr (MODE == JFA) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int il = qb * 32 + r4 * 8 + g * 4;  // rows crow(4 r4 .. 4 r4 + 3, g)
+                        const f32x4 nl = *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>(
+                            (const lchar *)&s_lse[st & 1][il]);
+                        const f32x4 dl = *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>(
+                            (const lchar *)&s_dlt[st & 1][il]);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int e = r4 * 4 + t;
+                            pv[e] = fast_exp2(sacc[e] + nl[t]);
+                            dx[e] = pv[e] * (dpacc[e] - dl[t]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        float dy;
+                        act_fwd_grad<ACT>(sacc[e], pv[e], dy);
+                        dx[e] = dpacc[e] * dy;
+                    }
+                }
+                if (masked) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int i = ia + qb * 32 + crow(e, g);
+                        const bool valid = (i < s.lq) & (!p.causal | (jkey <= i + shift));
+                        pv[e] = valid ? pv[e] : 0.0f;
+                        dx[e] = valid ? dx[e] : 0.0f;
+                    }
                 }
                 bf16x8 pb[2], dsb[2];
                 pack_operands(pv, pb[0], pb[1]);

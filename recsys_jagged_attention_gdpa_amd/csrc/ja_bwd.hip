@@ -104,12 +104,14 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
     if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
+    const int xcd = xcd_id();
+    int slices_done = 0;
     for (;;) {
-        if (tid == 0) s_unit = atomicAdd(&p.counters->cursor, 1);
+        if (tid == 0) s_unit = next_tile_unit(p.counters, n_units, xcd, slices_done);
         __syncthreads();
         const int w = s_unit;
         __syncthreads();
-        if (w >= n_units) break;
+        if (w < 0) break;
         const UnitRef u = tile_unit(p.tiles, w, n_units, H);
         const int2 tile = u.tile;
         const int h = u.h;
@@ -247,12 +249,14 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
     if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
+    const int xcd = xcd_id();
+    int slices_done = 0;
     for (;;) {
-        if (tid == 0) s_unit = atomicAdd(&p.counters2->cursor, 1);
+        if (tid == 0) s_unit = next_tile_unit(p.counters2, n_units, xcd, slices_done);
         __syncthreads();
         const int w = s_unit;
         __syncthreads();
-        if (w >= n_units) break;
+        if (w < 0) break;
         const UnitRef u = tile_unit(p.tiles2, w, n_units, H);
         const int2 tile = u.tile;
         const int h = u.h;

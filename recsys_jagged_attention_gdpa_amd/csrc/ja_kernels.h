@@ -15,11 +15,17 @@ constexpr int BWD_KV_UNIT = 128;   // keys owned by one dK/dV unit
 constexpr int BWD_Q_STEP = 64;     // queries per inner step of a dK/dV unit
 constexpr int FUSED_MAX_LK = 32;   // samples with at most this many keys use the fused backward unit
 
+// The chip's accelerator dies (XCDs), each with its own L2.
+constexpr int XCDS = 8;
+
 // Plan (scheduler) output lives at the start of the workspace.
 struct PlanCounters {
     int units;   // number of work units (tiles x heads)
-    int cursor;  // next unit to hand out (persistent kernels pull from it)
-    int pad[62];
+    int cursor;  // next unit to hand out (whole-sample lists)
+    int pad[30];
+    // Tile lists: the units are cut into XCDS contiguous slices, slice c
+    // handed out by xcursor[c][0] (one 128-byte line per slice).
+    int xcursor[XCDS][32];
 };
 
 enum PlanKind {
@@ -81,6 +87,25 @@ struct UnitRef {
 __device__ __forceinline__ UnitRef tile_unit(const int2 *tiles, int w, int n_units, int H) {
     const int n = n_units / H;
     return UnitRef{tiles[w % n], w / n};
+}
+
+// The XCD this workgroup runs on (hardware register XCC_ID).
+__device__ __forceinline__ int xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (XCDS - 1); }
+
+// Next unit of a tile list for a workgroup on XCD `xcd`: its own slice first,
+// so the tiles of one (sample, head) — adjacent in the list — run on one XCD
+// and share their keys and values (or queries) in that XCD's L2; then the
+// other slices in turn once its own is exhausted.  `k` counts the slices this
+// workgroup has exhausted (start at 0).  Returns -1 when no unit is left.
+__device__ __forceinline__ int next_tile_unit(PlanCounters *c, int n_units, int xcd, int &k) {
+    while (k < XCDS) {
+        const int sl = (xcd + k) & (XCDS - 1);
+        const int b = (int)((int64_t)n_units * sl / XCDS), e = (int)((int64_t)n_units * (sl + 1) / XCDS);
+        const int w = b + atomicAdd(&c->xcursor[sl][0], 1);
+        if (w < e) return w;
+        ++k;
+    }
+    return -1;
 }
 
 // Plans up to PLAN_MAX lists in one launch (one workgroup per list).

@@ -195,6 +195,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanBatch batc
         p.counters->units = n * p.H;
         p.counters->cursor = 0;
     }
+    if (tid < XCDS) p.counters->xcursor[tid][0] = 0;
 }
 
 hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream) {

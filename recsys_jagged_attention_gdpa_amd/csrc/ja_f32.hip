@@ -210,17 +210,28 @@ static inline unsigned grid_for(int64_t n) { return (unsigned)((n + F32_THREADS 
 template <int D, int MODE, int ACT>
 static hipError_t fwd_f32_t(const AttnParams &p, hipStream_t st) {
     const int64_t n = p.total_q_out * p.H;
+    const KernelTimer &t = kernel_timer();
+    t.begin(K_FWD, st);
     if (n > 0) hipLaunchKernelGGL((fwd_f32_kernel<D, MODE, ACT>), dim3(grid_for(n)), dim3(F32_THREADS), 0, st, p);
+    t.end(K_FWD, st);
     return hipGetLastError();
 }
 
 template <int D, int MODE, int ACT>
 static hipError_t bwd_f32_t(const AttnParams &p, hipStream_t st) {
     const int64_t nq = p.total_q * p.H, nk = p.total_k * p.H;
-    if (MODE == JFA && nq > 0)
-        hipLaunchKernelGGL((delta_f32_kernel<D>), dim3(grid_for(nq)), dim3(F32_THREADS), 0, st, p);
+    const KernelTimer &t = kernel_timer();
+    if (MODE == JFA) {
+        t.begin(K_BWD_DELTA, st);
+        if (nq > 0) hipLaunchKernelGGL((delta_f32_kernel<D>), dim3(grid_for(nq)), dim3(F32_THREADS), 0, st, p);
+        t.end(K_BWD_DELTA, st);
+    }
+    t.begin(K_BWD_Q, st);
     if (nq > 0) hipLaunchKernelGGL((dq_f32_kernel<D, MODE, ACT>), dim3(grid_for(nq)), dim3(F32_THREADS), 0, st, p);
+    t.end(K_BWD_Q, st);
+    t.begin(K_BWD_KV, st);
     if (nk > 0) hipLaunchKernelGGL((dkdv_f32_kernel<D, MODE, ACT>), dim3(grid_for(nk)), dim3(F32_THREADS), 0, st, p);
+    t.end(K_BWD_KV, st);
     return hipGetLastError();
 }
 

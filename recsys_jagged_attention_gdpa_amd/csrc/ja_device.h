@@ -212,9 +212,19 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP);
 }
 // 16 bytes per lane from global memory straight into LDS: lane i of the wave
-// writes dst + 16 i (dst wave-uniform); out-of-range lanes write zeros.
+// writes dst + 16 i (dst wave-uniform, in M0); out-of-range lanes write zeros.
+// Issued as inline assembly on purpose: the compiler does not know which LDS
+// bytes a copy of this kind writes, so after the builtin form it waits for the
+// copy to land before the next LDS read of any buffer, which serialises the
+// prefetch of the next tile with the reads of the current one.  Callers wait
+// for completion themselves (vmcnt, then a barrier for other waves' parts)
+// before reading the destination; nothing else in these kernels uses M0.
 __device__ __forceinline__ void buf_load16_lds(rsrc_t r, __attribute__((address_space(3))) void *dst, uint32_t off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, (int)off, 0, 0, 0);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(r)
+                 : "memory");
 }
 template <int CP = CP_DEFAULT>
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {

@@ -180,11 +180,15 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
     // (sample, head) units of samples with at most 32 keys
     a.tiles2 = a.tiles3;
     a.counters2 = a.counters3;
-    ja::PlanParams pp[2] = {plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 1, a.tiles, L.cap_q, a.counters),
+    // One shared block of at most 32 query rows (known here, since it is not
+    // jagged): one-wave units over 32-row tiles instead of 4-wave 128-row ones.
+    const bool few_q = p->q_offsets == nullptr && p->lq_fixed <= ja::FEW_Q_ROWS;
+    const int q_tile = few_q ? ja::FEW_Q_ROWS : ja::Q_TILE, kv_tile = few_q ? 32 : ja::KV_TILE;
+    ja::PlanParams pp[2] = {plan_of(*p, ja::PLAN_Q_TILES, q_tile, kv_tile, 1, a.tiles, L.cap_q, a.counters),
                             plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3)};
     hipError_t e = ja::launch_plan(pp, 2, s);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(ja::launch_fwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), s));
+    return hip_status(ja::launch_fwd_bf16(a, p->head_dim, mode, p->act, cu_count(), few_q, s));
 }
 
 ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, const void *v, const void *o,

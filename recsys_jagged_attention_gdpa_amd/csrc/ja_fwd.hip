@@ -31,19 +31,23 @@
 namespace ja {
 
 constexpr int FWD_THREADS = 256;
-constexpr int BM = Q_TILE;   // 128 query rows per unit
-constexpr int BN = KV_TILE;  // 64 keys per tile
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units a running softmax max may lag the true max
 
-template <int D, int MODE, int ACT>
-__global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p) {
+// WAVES waves per workgroup, each owning 32 query rows of the unit's tile
+// (BM = 32 WAVES rows), key tiles of BN rows.  The usual shape is 4 waves x
+// 64-key tiles; with one block of at most 32 shared query rows (pooling by
+// learned seed queries) a 1-wave, 32-key shape does no work on padding rows.
+template <int D, int MODE, int ACT, int WAVES, int BN>
+__global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(const AttnParams p) {
+    constexpr int NT = WAVES * WAVE;
+    constexpr int BM = 32 * WAVES;
     constexpr int TILE_BYTES = BN * D * 2;
     constexpr int NKK = D / 16;  // k-steps over the head dimension
     constexpr int NDB = D / 32;  // 32-wide blocks of the head dimension
     constexpr int NNB = BN / 32; // 32-key blocks per tile
     constexpr int NKS = BN / 16; // 16-key k-steps per tile
     constexpr int WIN = BM + BN - 1;  // largest bias window of a (unit, key tile)
-    static_assert(WIN <= FWD_THREADS, "one bias window entry per thread");
+    static_assert(WIN <= NT, "one bias window entry per thread");
     __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
     __shared__ float s_bias[2][WIN];
     __shared__ int s_unit;
@@ -98,8 +102,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(const AttnParams p)
         float bnext = 0.0f;
         auto load_tile = [&](int jt) {
             lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
-            dma_tile<BN, D, FWD_THREADS>(kt, Ks, jt * BN, tid);
-            dma_tile<BN, D, FWD_THREADS>(kt + TILE_BYTES, Vs, jt * BN, tid);
+            dma_tile<BN, D, NT>(kt, Ks, jt * BN, tid);
+            dma_tile<BN, D, NT>(kt + TILE_BYTES, Vs, jt * BN, tid);
             const BiasWindow bw = bias_window(bz, i0, BM, jt * BN, BN);
             bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
         };
@@ -387,32 +391,35 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
 }
 
 template <int D, int MODE, int ACT>
-static hipError_t launch_fwd_t(const AttnParams &p, int grid, hipStream_t stream) {
+static hipError_t launch_fwd_t(const AttnParams &p, int cus, bool few_q, hipStream_t stream) {
     const KernelTimer &t = kernel_timer();
     t.begin(K_FWD_SHORT, stream);
-    hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT>), dim3(grid), dim3(FWD_THREADS), 0, stream, p);
+    hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT>), dim3(2 * cus), dim3(FWD_THREADS), 0, stream, p);
     t.end(K_FWD_SHORT, stream);
     t.begin(K_FWD, stream);
-    hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT>), dim3(grid), dim3(FWD_THREADS), 0, stream, p);
+    if (few_q)  // every unit is one block of <= 32 shared query rows
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, 32>), dim3(8 * cus), dim3(WAVE), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE>), dim3(2 * cus), dim3(4 * WAVE), 0, stream, p);
     t.end(K_FWD, stream);
     return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_fwd_d(const AttnParams &p, int mode, int act, int grid, hipStream_t stream) {
-    if (mode == JFA) return launch_fwd_t<D, JFA, SILU>(p, grid, stream);
+static hipError_t launch_fwd_d(const AttnParams &p, int mode, int act, int cus, bool few_q, hipStream_t stream) {
+    if (mode == JFA) return launch_fwd_t<D, JFA, SILU>(p, cus, few_q, stream);
     switch (act) {
-    case SILU: return launch_fwd_t<D, GDPA, SILU>(p, grid, stream);
-    case GELU_TANH: return launch_fwd_t<D, GDPA, GELU_TANH>(p, grid, stream);
-    default: return launch_fwd_t<D, GDPA, GELU_ERF>(p, grid, stream);
+    case SILU: return launch_fwd_t<D, GDPA, SILU>(p, cus, few_q, stream);
+    case GELU_TANH: return launch_fwd_t<D, GDPA, GELU_TANH>(p, cus, few_q, stream);
+    default: return launch_fwd_t<D, GDPA, GELU_ERF>(p, cus, few_q, stream);
     }
 }
 
-hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream) {
+hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, hipStream_t stream) {
     switch (D) {
-    case 32: return launch_fwd_d<32>(p, mode, act, grid, stream);
-    case 64: return launch_fwd_d<64>(p, mode, act, grid, stream);
-    default: return launch_fwd_d<128>(p, mode, act, grid, stream);
+    case 32: return launch_fwd_d<32>(p, mode, act, cus, few_q, stream);
+    case 64: return launch_fwd_d<64>(p, mode, act, cus, few_q, stream);
+    default: return launch_fwd_d<128>(p, mode, act, cus, few_q, stream);
     }
 }
 

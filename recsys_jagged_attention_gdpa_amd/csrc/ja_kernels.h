@@ -130,7 +130,10 @@ struct KernelTimer {
 const KernelTimer &kernel_timer();
 
 // mode: 0 GDPA, 1 JFA.  act: 0 SiLU, 1 GELU tanh, 2 GELU erf.
-hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream);
+// cus: compute units; few_q: every sample has one shared block of <= 32 query
+// rows (q_offsets NULL, lq_fixed <= FEW_Q_ROWS), planned as 32-row query tiles.
+constexpr int FEW_Q_ROWS = 32;
+hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, hipStream_t stream);
 hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream);
 hipError_t launch_fwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
 hipError_t launch_bwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);

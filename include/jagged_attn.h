@@ -70,7 +70,8 @@ typedef enum {
     JA_OK = 0,
     JA_ERR_NULL = 1,        /* a required pointer is NULL */
     JA_ERR_SHAPE = 2,       /* B, H, D, total rows or bias range out of range */
-    JA_ERR_UNSUPPORTED = 3, /* dtype / head_dim / act / bias kind / shared-query backward */
+    JA_ERR_UNSUPPORTED = 3, /* dtype / head_dim / act / bias kind / shared-query backward, or a
+                               [rows, H, D] tensor of 4 GiB or more (split such a batch) */
     JA_ERR_WORKSPACE = 4,   /* workspace NULL, misaligned or smaller than ja_workspace_size */
     JA_ERR_HIP = 6          /* a HIP launch failed (the HIP error is in ja_last_hip_error) */
 } ja_status;

@@ -90,6 +90,13 @@ ja_status check_problem(const ja_problem *p, int pass) {
         if ((int64_t)p->bias_hi - p->bias_lo + 1 > (1 << 24)) return JA_ERR_SHAPE;
     }
     if (!(p->scale == p->scale)) return JA_ERR_SHAPE;  // NaN scale
+    // Kernels address a (sample, head) slice with 32-bit byte offsets; bounding
+    // every [rows, H, D] tensor below 4 GiB bounds every slice (the sample
+    // lengths themselves live on the device).
+    const int64_t row_bytes = (int64_t)p->heads * p->head_dim * (p->dtype == JA_BF16 ? 2 : 4);
+    const int64_t q_rows = total_q_out(*p) > p->total_q ? total_q_out(*p) : p->total_q;
+    if (q_rows * row_bytes > (int64_t)UINT32_MAX || p->total_k * row_bytes > (int64_t)UINT32_MAX)
+        return JA_ERR_UNSUPPORTED;
     // Work-unit counts (tiles x heads) must fit in int32.
     const Layout L = layout_of(*p, pass);
     const int64_t cap = L.cap_q > L.cap_k ? L.cap_q : L.cap_k;
@@ -270,7 +277,7 @@ const char *ja_status_string(int status) {
     case JA_OK: return "ok";
     case JA_ERR_NULL: return "a required pointer is NULL";
     case JA_ERR_SHAPE: return "a size or range argument is out of range";
-    case JA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, activation, bias kind or pass";
+    case JA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, activation, bias kind or pass, or a tensor of 4 GiB or more";
     case JA_ERR_WORKSPACE: return "workspace NULL, not 256-byte aligned, or too small";
     case JA_ERR_HIP: return "a HIP launch failed";
     default: return "unknown status";

@@ -132,9 +132,9 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
         load_row_operand<D>(greg, Gs, irow, g);
         float lse2 = 0.0f, dlt = 0.0f;
         if constexpr (MODE == JFA) {
-            const uint32_t off = irow < s.lq ? (uint32_t)(h * p.total_q + s.qs + irow) * 4u : OOB;
-            const rsrc_t lr = make_rsrc(p.lse, (uint32_t)(p.total_q * p.H) * 4u);
-            const rsrc_t dr = make_rsrc(p.delta, (uint32_t)(p.total_q * p.H) * 4u);
+            const uint32_t off = (uint32_t)irow * 4u;  // rows past the sample read zeros
+            const rsrc_t lr = make_rsrc(p.lse + (int64_t)h * p.total_q + s.qs, (uint32_t)s.lq * 4u);
+            const rsrc_t dr = make_rsrc(p.delta + (int64_t)h * p.total_q + s.qs, (uint32_t)s.lq * 4u);
             lse2 = buf_load_f32(lr, off) * LOG2E;
             dlt = buf_load_f32(dr, off);
         }
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
 // ----------------------------------------------------------- dK/dV units
 template <int D, int MODE, int ACT>
 __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p) {
-    constexpr int BQ = BWD_Q_STEP;  // 64 query rows per step
+    constexpr int BQ = BWD_Q_STEP;  // query rows per step
     constexpr int BK = BWD_KV_UNIT; // 128 keys per unit
     constexpr int TILE_BYTES = BQ * D * 2;
     constexpr int NKK = D / 16, NDB = D / 32;

@@ -12,7 +12,7 @@ namespace ja {
 constexpr int Q_TILE = 128;
 constexpr int KV_TILE = 64;
 constexpr int BWD_KV_UNIT = 128;   // keys owned by one dK/dV unit
-constexpr int BWD_Q_STEP = 64;     // queries per inner step of a dK/dV unit
+constexpr int BWD_Q_STEP = 128;    // queries per inner step of a dK/dV unit
 constexpr int FUSED_MAX_LK = 32;   // samples with at most this many keys use the fused backward unit
 
 // The chip's accelerator dies (XCDs), each with its own L2.

@@ -46,6 +46,9 @@
  * streams with different workspaces.  Calls sharing one workspace must be
  * ordered (same stream).
  *
+ * Empty tensors.  A tensor with no rows (total_q, total_k or the output rows
+ * equal to 0) is never read or written, and its pointer may be NULL.
+ *
  * Errors.  The return code is the only error channel.  Host-visible arguments
  * are checked before anything is launched; on any error nothing is launched
  * and no output is touched.  Offsets live in device memory and are not read by

@@ -169,8 +169,10 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
                   void *o_res, void *ws, size_t ws_bytes, void *stream) {
     ja_status st = check_problem(p, JA_PASS_FWD);
     if (st != JA_OK) return st;
-    if (!q || !k || !v || !o) return JA_ERR_NULL;
-    if (mode == 1 && !lse) return JA_ERR_NULL;
+    // A tensor with no rows is never touched, so its pointer may be NULL.
+    const bool has_q = p->total_q > 0, has_o = total_q_out(*p) > 0, has_k = p->total_k > 0;
+    if ((has_q && !q) || (has_k && (!k || !v)) || (has_o && !o)) return JA_ERR_NULL;
+    if (mode == 1 && has_o && !lse) return JA_ERR_NULL;
     st = check_workspace(p, JA_PASS_FWD, ws, ws_bytes);
     if (st != JA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -203,8 +205,10 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
                   size_t ws_bytes, void *stream) {
     ja_status st = check_problem(p, JA_PASS_BWD);
     if (st != JA_OK) return st;
-    if (!q || !k || !v || !dout || !dq || !dk || !dv) return JA_ERR_NULL;
-    if (mode == 1 && (!o || !lse)) return JA_ERR_NULL;
+    // A tensor with no rows is never touched, so its pointer may be NULL.
+    const bool has_q = p->total_q > 0, has_k = p->total_k > 0;
+    if ((has_q && (!q || !dout || !dq)) || (has_k && (!k || !v || !dk || !dv))) return JA_ERR_NULL;
+    if (mode == 1 && has_q && (!o || !lse)) return JA_ERR_NULL;
     st = check_workspace(p, JA_PASS_BWD, ws, ws_bytes);
     if (st != JA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);

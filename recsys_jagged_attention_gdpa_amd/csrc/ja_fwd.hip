@@ -37,7 +37,11 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 units a running softmax max may l
 // (BM = 32 WAVES rows), key tiles of BN rows.  The usual shape is 4 waves x
 // 64-key tiles; with one block of at most 32 shared query rows (pooling by
 // learned seed queries) a 1-wave, 32-key shape does no work on padding rows.
-template <int D, int MODE, int ACT, int WAVES, int BN>
+// SPLIT (JFA with the rounding residual requested): P enters the PV product as
+// bf16(P) plus its bf16 residual, two MFMAs into the same accumulator, so O
+// (and delta = <dO, O> formed from it in backward) is accurate to ~2^-17
+// rather than carrying the 2^-9 rounding of P.
+template <int D, int MODE, int ACT, int WAVES, int BN, bool SPLIT>
 __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(const AttnParams p) {
     constexpr int NT = WAVES * WAVE;
     constexpr int BM = 32 * WAVES;
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             const bool diag = p.causal && (j0 + BN - 1 > iw + s.lk - s.lq);
             const bool masked = tail || diag;
             const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
-            bf16x8 pb[NKS];
+            bf16x8 pb[NKS], pbl[SPLIT ? NKS : 1];
             // x = scale * s + bias (JFA: in log2 units); without bias only the
             // scale is applied, folded into later arithmetic where possible.
             if (bz.kind) {
@@ -206,6 +210,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                         l_run += pv[e];
                     }
                     pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
+                    if constexpr (SPLIT) pack_residual_operands(pv, pbl[2 * nb], pbl[2 * nb + 1]);
                 }
             }
 
@@ -216,6 +221,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                 for (int db = 0; db < NDB; ++db) {
                     const bf16x8 a = lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane);
                     oacc[db] = mfma32(a, pb[ks], oacc[db]);
+                    if constexpr (SPLIT) oacc[db] = mfma32(a, pbl[ks % (SPLIT ? NKS : 1)], oacc[db]);
                 }
             }
 
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
 // computed.  Loads and stores go through per-sample buffer descriptors, so the
 // loop body has no branches around memory operations and the next block's
 // loads stay in flight across the current block's stores.
-template <int D, int MODE, int ACT>
+template <int D, int MODE, int ACT, bool SPLIT>
 __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnParams p) {
     constexpr int KV_BYTES = 32 * D * 2;
     constexpr int NKK = D / 16, NDB = D / 32;
@@ -352,8 +358,9 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
                 norm = l > 0.0f ? 1.0f / l : 0.0f;
                 lse_row = l > 0.0f ? (m + log2f(l)) * LN2 : -INFINITY;
             }
-            bf16x8 pb[2];
+            bf16x8 pb[2], pbl[2];
             pack_operands(pv, pb[0], pb[1]);
+            if constexpr (SPLIT) pack_residual_operands(pv, pbl[0], pbl[1]);
             if constexpr (MODE == JFA) buf_store_f32(lse_r, g == 0 ? (uint32_t)irow * 4u : OOB, lse_row);
             // One 32-wide block of the head dimension at a time, staged as it
             // completes, so only one accumulator block is live.  The optional
@@ -362,8 +369,11 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
             for (int db = 0; db < NDB; ++db) {
                 f32x16 acc = f32x16{};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    acc = mfma32(lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane), pb[ks], acc);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 a = lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane);
+                    acc = mfma32(a, pb[ks], acc);
+                    if constexpr (SPLIT) acc = mfma32(a, pbl[ks], acc);
+                }
                 stage_acc_block<D>(Ot, acc, db, norm, l32, g);
                 if (MODE == JFA && res) store_resid_block<D>(Rs, irow, acc, db, norm, g);
             }
@@ -390,19 +400,25 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
     }
 }
 
-template <int D, int MODE, int ACT>
-static hipError_t launch_fwd_t(const AttnParams &p, int cus, bool few_q, hipStream_t stream) {
+template <int D, int MODE, int ACT, bool SPLIT>
+static hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, hipStream_t stream) {
     const KernelTimer &t = kernel_timer();
     t.begin(K_FWD_SHORT, stream);
-    hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT>), dim3(2 * cus), dim3(FWD_THREADS), 0, stream, p);
+    hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT, SPLIT>), dim3(2 * cus), dim3(FWD_THREADS), 0, stream, p);
     t.end(K_FWD_SHORT, stream);
     t.begin(K_FWD, stream);
     if (few_q)  // every unit is one block of <= 32 shared query rows
-        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, 32>), dim3(8 * cus), dim3(WAVE), 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, 32, SPLIT>), dim3(8 * cus), dim3(WAVE), 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE>), dim3(2 * cus), dim3(4 * WAVE), 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE, SPLIT>), dim3(2 * cus), dim3(4 * WAVE), 0, stream, p);
     t.end(K_FWD, stream);
     return hipGetLastError();
+}
+
+template <int D, int MODE, int ACT>
+static hipError_t launch_fwd_t(const AttnParams &p, int cus, bool few_q, hipStream_t stream) {
+    if (MODE == JFA && p.o_res_out) return launch_fwd_s<D, MODE, ACT, true>(p, cus, few_q, stream);
+    return launch_fwd_s<D, MODE, ACT, false>(p, cus, few_q, stream);
 }
 
 template <int D>

@@ -306,6 +306,17 @@ __device__ __forceinline__ void store_row_acc_split(bf16 *row_ptr, bf16 *res_ptr
 
 // Pack 16 fp32 accumulator values (C layout of one 32x32 block) into the two
 // bf16x8 B operands of the 16-wide k-steps they cover.
+// The bf16 rounding residuals v - bf16(v), packed like pack_operands: with
+// both packings as operands, two MFMAs into one accumulator multiply by v to
+// about 2^-17 relative instead of 2^-9.
+__device__ __forceinline__ void pack_residual_operands(const float (&v)[16], bf16x8 &lo, bf16x8 &hi) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        lo[e] = f2bf(v[e] - bf2f(f2bf(v[e])));
+        hi[e] = f2bf(v[8 + e] - bf2f(f2bf(v[8 + e])));
+    }
+}
+
 __device__ __forceinline__ void pack_operands(const float (&v)[16], bf16x8 &lo, bf16x8 &hi) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

@@ -149,3 +149,21 @@ def test_shared_query_block_sizes(mode, rows, D, causal):
                      shared_q=rows, act="gelu_erf", causal=causal, bias_kind="rel", bias_lo=-50,
                      bias_hi=40, bias_sigma=0.3, with_dout=False)
     parity(w, backward=False, label=f"shared-q {mode} rows={rows} D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+@pytest.mark.parametrize("lq,lk", [([0, 0, 0], [0, 0, 0]), ([0, 0], [0, 40]), ([3, 70, 0], [0, 0, 0]),
+                                   ([5, 200], [0, 0])])
+def test_empty_batches_and_keyless_rows(mode, lq, lk):
+    # Nothing to compute (no pairs at all): every output row is exactly zero
+    # (JFA: LSE = -inf), including rows that exist but see no key.
+    w = synth.custom(mode=mode, lq=lq, lk=lk, H=2, D=64, seed=2)
+    parity(w, label=f"empty {mode} lq={lq} lk={lk}")
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+@pytest.mark.parametrize("H,D,scale", [(1, 32, 0.3), (16, 64, None), (5, 128, 0.05)])
+def test_head_counts_and_explicit_scale(mode, H, D, scale):
+    w = synth.custom(mode=mode, lq=[150, 1, 40, 33], lk=[90, 300, 32, 65], H=H, D=D, seed=H * D, scale=scale,
+                     act="silu", causal=True)
+    parity(w, label=f"{mode} H={H} D={D} scale={scale}")

@@ -327,25 +327,38 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
 
             // Wave-uniform: does this step cross the query end or the diagonal?
             const bool masked = (ia + BQ > s.lq) | (p.causal && (jw + 31 > ia + shift));
+            // Software pipeline over the step's 32-row blocks: the next block's S
+            // and dP products are issued inside the current block's element-wise
+            // stage (one basic block), so the scheduler can interleave the matrix
+            // and vector work of this single wave per SIMD.
+            f32x16 sa = f32x16{}, da = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int off = lds_off<D>(l32, 2 * kk + g);
+                sa = mfma32(lds_read16(Qt, off), kreg[kk], sa);
+                da = mfma32(lds_read16(Gt, off), vreg[kk], da);
+            }
 #pragma unroll
             for (int qb = 0; qb < BQ / 32; ++qb) {
-                f32x16 sacc = f32x16{}, dpacc = f32x16{};
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    const int off = lds_off<D>(qb * 32 + l32, 2 * kk + g);
-                    sacc = mfma32(lds_read16(Qt, off), kreg[kk], sacc);
-                    dpacc = mfma32(lds_read16(Gt, off), vreg[kk], dpacc);
-                }
                 // x = s * sl + bias; invalid pairs are zeroed after the element-wise
                 // stage (rows without any visible key have LSE = -inf, so their
                 // exponent is not finite and must not be used).
                 if (bz.kind) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
-                        sacc[e] = __builtin_fmaf(sacc[e], sl, bwin[bias_window_index(bz, bw, ia + qb * 32 + crow(e, g), jkey)]);
+                        sa[e] = __builtin_fmaf(sa[e], sl, bwin[bias_window_index(bz, bw, ia + qb * 32 + crow(e, g), jkey)]);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) sacc[e] *= sl;
+                    for (int e = 0; e < 16; ++e) sa[e] *= sl;
+                }
+                f32x16 sn = f32x16{}, dn = f32x16{};
+                if (qb + 1 < BQ / 32) {
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) {
+                        const int off = lds_off<D>((qb + 1) * 32 + l32, 2 * kk + g);
+                        sn = mfma32(lds_read16(Qt, off), kreg[kk], sn);
+                        dn = mfma32(lds_read16(Gt, off), vreg[kk], dn);
+                    }
                 }
                 float pv[16], dx[16];
                 if constexpr (MODE == JFA) {
@@ -359,16 +372,16 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
                             const int e = r4 * 4 + t;
-                            pv[e] = fast_exp2(sacc[e] + nl[t]);
-                            dx[e] = pv[e] * (dpacc[e] - dl[t]);
+                            pv[e] = fast_exp2(sa[e] + nl[t]);
+                            dx[e] = pv[e] * (da[e] - dl[t]);
                         }
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         float dy;
-                        act_fwd_grad<ACT>(sacc[e], pv[e], dy);
-                        dx[e] = dpacc[e] * dy;
+                        act_fwd_grad<ACT>(sa[e], pv[e], dy);
+                        dx[e] = da[e] * dy;
                     }
                 }
                 if (masked) {
@@ -391,6 +404,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
                         dkacc[db] = mfma32(lds_read_tr_operand<D>(Qt, qb * 32 + ks * 16, db * 32, lane), dsb[ks], dkacc[db]);
                     }
                 }
+                sa = sn;
+                da = dn;
             }
             store_step((st + 1) & 1);
             __syncthreads();

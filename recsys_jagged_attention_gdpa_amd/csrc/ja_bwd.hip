@@ -43,11 +43,12 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams p) {
     const int64_t n = p.total_q * p.H;
     float acc = 0.0f;
     if (rowh < n) {
-        const bf16x8 o = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(p.o) + rowh * D + c * 8);
+        // O and its residual are read only here: nontemporal
+        const bf16x8 o = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(p.o) + rowh * D + c * 8));
         const bf16x8 d = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(p.dout) + rowh * D + c * 8);
         if (p.o_res) {
             // O = bf16 output + its rounding residual: delta exact to fp32 rounding
-            const bf16x8 r = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(p.o_res) + rowh * D + c * 8);
+            const bf16x8 r = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(p.o_res) + rowh * D + c * 8));
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(bf2f(o[e]) + bf2f(r[e]), bf2f(d[e]), acc);
         } else {

@@ -94,14 +94,26 @@ __device__ __forceinline__ int sample_bucket_of(int64_t cost) {
 
 __device__ __forceinline__ bool grouped(const PlanParams &p) { return p.kind != PLAN_SAMPLES; }
 
-template <class F>
-__device__ void for_each_run(const PlanParams &p, const PlanSample &s, F fn);
-
-// Total cost and tile count of a sample.
+// Cost of a whole sample for ordering the tile lists: its valid (query, key)
+// pairs, in closed form (a sum over rows of the clamped causal key counts),
+// so a sample with many tiles is not walked tile by tile.
 __device__ int64_t sample_cost(const PlanParams &p, const PlanSample &s) {
-    int64_t c = 0;
-    for_each_run(p, s, [&](int, int n, int, int cost) { c += (int64_t)n * cost; });
-    return c;
+    const int64_t lq = s.lq, lk = s.lk;
+    if (!p.causal) return lq * lk;
+    // row i sees clamp(i + lk - lq + 1, 0, lk) keys
+    auto tri = [](int64_t n) { return n * (n + 1) / 2; };  // 1 + ... + n
+    const int64_t i0 = lq - lk > 0 ? lq - lk : 0;              // first row that sees a key
+    const int64_t n = lq - i0;                                  // rows that see keys: counts lk - n + 1 .. lk
+    return n > 0 ? tri(lk) - tri(lk - n) : 0;
+}
+
+// Emit a sample's tiles in non-increasing cost order without evaluating the
+// costs: causal query tiles get dearer with t, causal key tiles cheaper, and
+// without causal masking every tile of a sample costs the same.
+template <class F>
+__device__ void for_each_tile_desc(const PlanParams &p, const PlanSample &s, F fn) {
+    const bool descending = p.causal && p.kind == PLAN_Q_TILES;
+    for (int k = 0; k < s.ntiles; ++k) fn(descending ? s.ntiles - 1 - k : k);
 }
 
 // Visit the tiles of a sample as runs of equal cost, in non-increasing cost
@@ -178,9 +190,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanBatch batc
         if (grouped(p)) {
             if (s.ntiles == 0) continue;
             int pos = atomicAdd(&hist[sample_bucket_of(sample_cost(p, s))], s.ntiles);
-            for_each_run(p, s, [&](int t0, int n, int step, int) {
-                for (int k = 0; k < n; ++k, ++pos)
-                    if (pos < p.max_tiles) p.tiles[pos] = make_int2(b, t0 + k * step);
+            for_each_tile_desc(p, s, [&](int t) {
+                if (pos < p.max_tiles) p.tiles[pos] = make_int2(b, t);
+                ++pos;
             });
         } else {
             for_each_run(p, s, [&](int t0, int n, int step, int cost) {

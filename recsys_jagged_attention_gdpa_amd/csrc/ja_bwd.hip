@@ -152,8 +152,8 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
             lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             dma_tile<BN, D, BWD_THREADS>(kt, Ks, jt * BN, tid);
             dma_tile<BN, D, BWD_THREADS>(kt + TILE_BYTES, Vs, jt * BN, tid);
-            const BiasWindow bw = bias_window(bz, i0, BM, jt * BN, BN);
-            bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
+            const int bi = bias_stage_rowmajor(bz, i0, BM, jt * BN, BN, tid);
+            bnext = buf_load_f32(brs, bi >= 0 ? (uint32_t)bi * 4u : OOB);
         };
         auto store_tile = [&](int buf) {
             if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;
@@ -170,7 +170,6 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
             const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             const lchar *Vt = Kt + TILE_BYTES;
             const float *bwin = s_bias[jt & 1];
-            const BiasWindow bw = bias_window(bz, i0, BM, j0, BN);
             load_tile(jt + 1);  // past the last tile: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);
 
@@ -186,9 +185,11 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
                     dpacc = mfma32(lds_read16(Vt, off), greg[kk], dpacc);
                 }
                 if (bz.kind) {
+                    // raw window: entry (i0 + BM - 1 - irow) + (j - j0) (REL) or j - j0 (KEYPOS)
+                    const int bbase = (bz.kind == BIAS_REL ? BM - 1 - wv * 32 - l32 : 0) + g * 4 + nb * 32;
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
-                        sacc[e] = __builtin_fmaf(sacc[e], sl, bwin[bias_window_index(bz, bw, irow, j0 + nb * 32 + crow(e, g))]);
+                        sacc[e] = __builtin_fmaf(sacc[e], sl, bwin[bbase + (e >> 2) * 8 + (e & 3)]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) sacc[e] *= sl;
@@ -296,8 +297,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
             lchar *qt = lbase + (st & 1) * 2 * TILE_BYTES;
             dma_tile<BQ, D, BWD_THREADS>(qt, Qs, ia, tid);
             dma_tile<BQ, D, BWD_THREADS>(qt + TILE_BYTES, Gs, ia, tid);
-            const BiasWindow bw = bias_window(bz, ia, BQ, jt0, BK);
-            bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
+            const int bi = bias_stage_keymajor(bz, ia, BQ, jt0, BK, tid);
+            bnext = buf_load_f32(brs, bi >= 0 ? (uint32_t)bi * 4u : OOB);
             if constexpr (MODE == JFA) {
                 const uint32_t off = tid < BQ ? (uint32_t)(ia + tid) * 4u : OOB;
                 lnext = buf_load_f32(lr, off);
@@ -322,7 +323,6 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
             const lchar *Qt = lbase + (st & 1) * 2 * TILE_BYTES;
             const lchar *Gt = Qt + TILE_BYTES;
             const float *bwin = s_bias[st & 1];
-            const BiasWindow bw = bias_window(bz, ia, BQ, jt0, BK);
             load_step(st + 1);  // past the last step: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);
 
@@ -344,10 +344,15 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
                 // x = s * sl + bias; invalid pairs are zeroed after the element-wise
                 // stage (rows without any visible key have LSE = -inf, so their
                 // exponent is not finite and must not be used).
-                if (bz.kind) {
+                if (bz.kind == BIAS_REL) {
+                    // raw window: entry (jt0 + BK - 1 - jkey) + (i - ia)
+                    const int bbase = BK - 1 - wv * 32 - l32 + g * 4 + qb * 32;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        sa[e] = __builtin_fmaf(sa[e], sl, bwin[bias_window_index(bz, bw, ia + qb * 32 + crow(e, g), jkey)]);
+                    for (int e = 0; e < 16; ++e) sa[e] = __builtin_fmaf(sa[e], sl, bwin[bbase + (e >> 2) * 8 + (e & 3)]);
+                } else if (bz.kind == BIAS_KEYPOS) {
+                    const float b = bwin[wv * 32 + l32];  // entry jkey - jt0, the same for every row
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) sa[e] = __builtin_fmaf(sa[e], sl, b);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) sa[e] *= sl;

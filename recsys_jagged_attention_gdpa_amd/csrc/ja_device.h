@@ -317,34 +317,28 @@ struct BiasArgs {
     int kind, lo, hi, width;
 };
 
-// Window of a head's bias row that a tile of rows [i0, i0 + ni) and keys
-// [j0, j0 + nj) can touch: table indices (after clamping) lo_idx .. hi_idx.
-// The window has at most ni + nj - 1 entries for relative positions and nj
-// for key positions, whatever the table's width, so it is staged in LDS next
-// to the tile's keys and values.
-struct BiasWindow {
-    int first;  // first table index (offset from bias_lo) of the window
-    int len;    // entries in the window (0 without bias)
-};
-
-__device__ __forceinline__ BiasWindow bias_window(const BiasArgs &bz, int i0, int ni, int j0, int nj) {
-    BiasWindow w{0, 0};
-    if (bz.kind == BIAS_REL) {
-        const int a = clampi(i0 - (j0 + nj - 1), bz.lo, bz.hi), b = clampi(i0 + ni - 1 - j0, bz.lo, bz.hi);
-        w.first = a - bz.lo;
-        w.len = b - a + 1;
-    } else if (bz.kind == BIAS_KEYPOS) {
-        const int a = clampi(j0, bz.lo, bz.hi), b = clampi(j0 + nj - 1, bz.lo, bz.hi);
-        w.first = a - bz.lo;
-        w.len = b - a + 1;
-    }
-    return w;
+// Raw bias windows.  A tile's window in LDS holds, for every relative
+// position (or key) the tile can touch, the already-clamped table value, so a
+// lookup is a per-lane base plus a compile-time offset (no per-element index
+// arithmetic):
+//  * row-major tiles (a lane owns a query row, its elements run over keys:
+//    forward and dQ units), rows [i0, i0 + ni), keys [j0, j0 + nj):
+//    REL    entry p = table[clamp(i0 + ni - 1 - j0 - p)]; (i, j) reads (i0 + ni - 1 - i) + (j - j0)
+//    KEYPOS entry p = table[clamp(j0 + p)];            (i, j) reads j - j0
+//  * key-major tiles (a lane owns a key, its elements run over query rows:
+//    dK/dV units):
+//    REL    entry p = table[clamp(i0 - (j0 + nj - 1) + p)]; (i, j) reads (j0 + nj - 1 - j) + (i - i0)
+//    KEYPOS entry p = table[clamp(j0 + p)];                   (i, j) reads j - j0
+// The table offset (from bias_lo) thread t stages, or -1 for no entry.
+__device__ __forceinline__ int bias_stage_rowmajor(const BiasArgs &bz, int i0, int ni, int j0, int nj, int t) {
+    if (bz.kind == BIAS_REL) return t < ni + nj - 1 ? clampi(i0 + ni - 1 - j0 - t, bz.lo, bz.hi) - bz.lo : -1;
+    if (bz.kind == BIAS_KEYPOS) return t < nj ? clampi(j0 + t, bz.lo, bz.hi) - bz.lo : -1;
+    return -1;
 }
-
-// Index into a staged window for pair (i, j).
-__device__ __forceinline__ int bias_window_index(const BiasArgs &bz, const BiasWindow &w, int i, int j) {
-    const int idx = bz.kind == BIAS_REL ? clampi(i - j, bz.lo, bz.hi) : clampi(j, bz.lo, bz.hi);
-    return idx - bz.lo - w.first;
+__device__ __forceinline__ int bias_stage_keymajor(const BiasArgs &bz, int i0, int ni, int j0, int nj, int t) {
+    if (bz.kind == BIAS_REL) return t < ni + nj - 1 ? clampi(i0 - (j0 + nj - 1) + t, bz.lo, bz.hi) - bz.lo : -1;
+    if (bz.kind == BIAS_KEYPOS) return t < nj ? clampi(j0 + t, bz.lo, bz.hi) - bz.lo : -1;
+    return -1;
 }
 
 __device__ __forceinline__ float bias_at(const BiasArgs &bz, const float *row, int i, int j) {

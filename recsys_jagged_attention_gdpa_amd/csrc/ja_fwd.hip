@@ -108,8 +108,8 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             dma_tile<BN, D, NT>(kt, Ks, jt * BN, tid);
             dma_tile<BN, D, NT>(kt + TILE_BYTES, Vs, jt * BN, tid);
-            const BiasWindow bw = bias_window(bz, i0, BM, jt * BN, BN);
-            bnext = buf_load_f32(brs, tid < bw.len ? (uint32_t)(bw.first + tid) * 4u : OOB);
+            const int bi = bias_stage_rowmajor(bz, i0, BM, jt * BN, BN, tid);
+            bnext = buf_load_f32(brs, bi >= 0 ? (uint32_t)bi * 4u : OOB);
         };
         auto store_tile = [&](int buf) {
             if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;  // JFA works in log2 units
@@ -124,7 +124,6 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             const lchar *Vt = Kt + TILE_BYTES;
             const float *bwin = s_bias[jt & 1];
-            const BiasWindow bw = bias_window(bz, i0, BM, j0, BN);
             load_tile(jt + 1);  // past the last tile: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);
 
@@ -152,12 +151,13 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             // x = scale * s + bias (JFA: in log2 units); without bias only the
             // scale is applied, folded into later arithmetic where possible.
             if (bz.kind) {
+                // raw window: entry (i0 + BM - 1 - irow) + (j - j0) (REL) or j - j0 (KEYPOS)
+                const int bbase = (bz.kind == BIAS_REL ? BM - 1 - wv * 32 - l32 : 0) + g * 4;
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const int j = j0 + nb * 32 + crow(e, g);
-                        const float b = bwin[bias_window_index(bz, bw, irow, j)];
+                        const float b = bwin[bbase + nb * 32 + (e >> 2) * 8 + (e & 3)];
                         sacc[nb][e] = __builtin_fmaf(sacc[nb][e], MODE == GDPA ? p.scale : sl2, b);
                     }
             }

@@ -163,11 +163,17 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             }
             const float xmul = bz.kind ? 1.0f : (MODE == GDPA ? p.scale : sl2);  // remaining scale
             if constexpr (MODE == GDPA) {
+                if (!bz.kind) {
+#pragma unroll
+                    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) sacc[nb][e] *= p.scale;
+                }
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb) {
                     float pv[16];
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) pv[e] = act_fwd<ACT>(sacc[nb][e] * xmul);
+                    for (int e = 0; e < 16; ++e) pv[e] = act_fwd<ACT>(sacc[nb][e]);
                     if (masked) {
 #pragma unroll
                         for (int e = 0; e < 16; ++e)

@@ -145,11 +145,15 @@ class Runner:
         self.q_off = None if w.q_off is None else torch.from_numpy(w.q_off).to(dev)
         self.kv_off = torch.from_numpy(w.kv_off).to(dev)
         self.bias = None if w.bias_table is None else w.bias_table.to(dev)
+        # the longest key sequence is known when the batch is formed: passing it
+        # lets the library leave out its long-sequence kernels when none can have work
+        self.max_kv_len = int(w.lk.max()) if w.B > 0 else 0
         self.prob = _lib.make_problem(
             batch=w.B, heads=w.H, head_dim=w.D, dtype=w.dtype, total_q=w.q.shape[0],
             total_k=w.total_k, q_offsets=self.q_off, kv_offsets=self.kv_off,
             lq_fixed=w.lq_fixed, causal=w.causal, scale=w.scale, act=w.act,
-            bias_kind=w.bias_kind, bias_table=self.bias, bias_lo=w.bias_lo, bias_hi=w.bias_hi)
+            bias_kind=w.bias_kind, bias_table=self.bias, bias_lo=w.bias_lo, bias_hi=w.bias_hi,
+            max_kv_len=self.max_kv_len)
         rows = w.total_q_out
         self.o = torch.empty((rows, w.H, w.D), dtype=w.dtype, device=dev)
         self.lse = torch.empty((w.H, rows), dtype=torch.float32, device=dev)
@@ -168,9 +172,11 @@ class Runner:
             if self.backward:
                 ks += (["bwd_delta"] if self.w.mode == "jfa" else []) + ["bwd_q", "bwd_kv"]
             return ks
-        ks = ["plan", "fwd_short", "fwd"]
+        long_units = not (0 < self.max_kv_len <= SHORT_KV)  # else those kernels are not launched
+        ks = ["plan", "fwd_short"] + (["fwd"] if long_units else [])
         if self.backward:
-            ks += ["bwd_fused", "bwd_kv", "bwd_q"] + (["bwd_delta"] if self.w.mode == "jfa" else [])
+            ks += ["bwd_fused"] + (["bwd_kv", "bwd_q"] if long_units else [])
+            ks += ["bwd_delta"] if self.w.mode == "jfa" else []
         return ks
 
     def step(self):

@@ -102,6 +102,11 @@ typedef struct ja_problem {
     int32_t bias_kind;           /* ja_bias_kind */
     int32_t bias_lo, bias_hi;    /* bias index range, bias_lo <= bias_hi */
     const float *bias_table;     /* device fp32 [H][bias_hi - bias_lo + 1], or NULL when no bias */
+    int32_t max_kv_len;          /* 0 = unknown, else an upper bound on every sample's key count
+                                    (kv_offsets[b+1] - kv_offsets[b]).  At most 32 lets the
+                                    library skip launching its long-sequence kernels; a bound
+                                    that some sample exceeds gives undefined results, like
+                                    invalid offsets.  Negative: JA_ERR_SHAPE. */
 } ja_problem;
 
 /* Workspace bytes that the given pass of either attention form needs (0 only

@@ -90,6 +90,7 @@ ja_status check_problem(const ja_problem *p, int pass) {
         if ((int64_t)p->bias_hi - p->bias_lo + 1 > (1 << 24)) return JA_ERR_SHAPE;
     }
     if (!(p->scale == p->scale)) return JA_ERR_SHAPE;  // NaN scale
+    if (p->max_kv_len < 0) return JA_ERR_SHAPE;
     // Kernels address a (sample, head) slice with 32-bit byte offsets; bounding
     // every [rows, H, D] tensor below 4 GiB bounds every slice (the sample
     // lengths themselves live on the device).
@@ -193,11 +194,13 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
     // jagged): one-wave units over 32-row tiles instead of 4-wave 128-row ones.
     const bool few_q = p->q_offsets == nullptr && p->lq_fixed <= ja::FEW_Q_ROWS;
     const int q_tile = few_q ? ja::FEW_Q_ROWS : ja::Q_TILE, kv_tile = few_q ? 32 : ja::KV_TILE;
-    ja::PlanParams pp[2] = {plan_of(*p, ja::PLAN_Q_TILES, q_tile, kv_tile, 1, a.tiles, L.cap_q, a.counters),
-                            plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3)};
-    hipError_t e = ja::launch_plan(pp, 2, s);
+    // The caller's bound on key counts may rule out every long-sequence unit.
+    const bool long_units = !(p->max_kv_len > 0 && p->max_kv_len <= ja::FUSED_MAX_LK);
+    ja::PlanParams pp[2] = {plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3),
+                            plan_of(*p, ja::PLAN_Q_TILES, q_tile, kv_tile, 1, a.tiles, L.cap_q, a.counters)};
+    hipError_t e = ja::launch_plan(pp, long_units ? 2 : 1, s);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(ja::launch_fwd_bf16(a, p->head_dim, mode, p->act, cu_count(), few_q, s));
+    return hip_status(ja::launch_fwd_bf16(a, p->head_dim, mode, p->act, cu_count(), few_q, long_units, s));
 }
 
 ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, const void *v, const void *o,
@@ -225,13 +228,14 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
     a.dv = dv;
     a.lse = const_cast<float *>(lse);
     if (p->dtype == JA_F32) return hip_status(ja::launch_bwd_f32(a, p->head_dim, mode, p->act, s));
+    const bool long_units = !(p->max_kv_len > 0 && p->max_kv_len <= ja::FUSED_MAX_LK);
     ja::PlanParams pp[3] = {
+        plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3),
         plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 1, a.tiles, L.cap_q, a.counters),
-        plan_of(*p, ja::PLAN_KV_TILES, ja::BWD_KV_UNIT, ja::BWD_Q_STEP, 1, a.tiles2, L.cap_k, a.counters2),
-        plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3)};
-    hipError_t e = ja::launch_plan(pp, 3, s);
+        plan_of(*p, ja::PLAN_KV_TILES, ja::BWD_KV_UNIT, ja::BWD_Q_STEP, 1, a.tiles2, L.cap_k, a.counters2)};
+    hipError_t e = ja::launch_plan(pp, long_units ? 3 : 1, s);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(ja::launch_bwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), s));
+    return hip_status(ja::launch_bwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), long_units, s));
 }
 
 }  // namespace

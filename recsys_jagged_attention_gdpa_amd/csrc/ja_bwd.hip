@@ -572,7 +572,7 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
 
 // -------------------------------------------------------------- launches
 template <int D, int MODE, int ACT>
-static hipError_t launch_bwd_t(const AttnParams &p, int grid, hipStream_t st) {
+static hipError_t launch_bwd_t(const AttnParams &p, int grid, bool long_units, hipStream_t st) {
     const KernelTimer &t = kernel_timer();
     if (MODE == JFA && p.total_q > 0) {
         const int64_t threads = p.total_q * p.H * (D / 8);
@@ -583,6 +583,7 @@ static hipError_t launch_bwd_t(const AttnParams &p, int grid, hipStream_t st) {
     t.begin(K_BWD_FUSED, st);
     hipLaunchKernelGGL((fused_kernel<D, MODE, ACT>), dim3(2 * grid), dim3(WAVE), 0, st, p);
     t.end(K_BWD_FUSED, st);
+    if (!long_units) return hipGetLastError();
     t.begin(K_BWD_KV, st);
     hipLaunchKernelGGL((dkdv_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, p);
     t.end(K_BWD_KV, st);
@@ -593,20 +594,21 @@ static hipError_t launch_bwd_t(const AttnParams &p, int grid, hipStream_t st) {
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const AttnParams &p, int mode, int act, int grid, hipStream_t st) {
-    if (mode == JFA) return launch_bwd_t<D, JFA, SILU>(p, grid, st);
+static hipError_t launch_bwd_d(const AttnParams &p, int mode, int act, int grid, bool lu, hipStream_t st) {
+    if (mode == JFA) return launch_bwd_t<D, JFA, SILU>(p, grid, lu, st);
     switch (act) {
-    case SILU: return launch_bwd_t<D, GDPA, SILU>(p, grid, st);
-    case GELU_TANH: return launch_bwd_t<D, GDPA, GELU_TANH>(p, grid, st);
-    default: return launch_bwd_t<D, GDPA, GELU_ERF>(p, grid, st);
+    case SILU: return launch_bwd_t<D, GDPA, SILU>(p, grid, lu, st);
+    case GELU_TANH: return launch_bwd_t<D, GDPA, GELU_TANH>(p, grid, lu, st);
+    default: return launch_bwd_t<D, GDPA, GELU_ERF>(p, grid, lu, st);
     }
 }
 
-hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t st) {
+hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, bool long_units,
+                           hipStream_t st) {
     switch (D) {
-    case 32: return launch_bwd_d<32>(p, mode, act, grid, st);
-    case 64: return launch_bwd_d<64>(p, mode, act, grid, st);
-    default: return launch_bwd_d<128>(p, mode, act, grid, st);
+    case 32: return launch_bwd_d<32>(p, mode, act, grid, long_units, st);
+    case 64: return launch_bwd_d<64>(p, mode, act, grid, long_units, st);
+    default: return launch_bwd_d<128>(p, mode, act, grid, long_units, st);
     }
 }
 

@@ -407,11 +407,12 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
 }
 
 template <int D, int MODE, int ACT, bool SPLIT>
-static hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, hipStream_t stream) {
+static hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, bool long_units, hipStream_t stream) {
     const KernelTimer &t = kernel_timer();
     t.begin(K_FWD_SHORT, stream);
     hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT, SPLIT>), dim3(2 * cus), dim3(FWD_THREADS), 0, stream, p);
     t.end(K_FWD_SHORT, stream);
+    if (!long_units) return hipGetLastError();
     t.begin(K_FWD, stream);
     if (few_q)  // every unit is one block of <= 32 shared query rows
         hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, 32, SPLIT>), dim3(8 * cus), dim3(WAVE), 0, stream, p);
@@ -422,26 +423,28 @@ static hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, hipStre
 }
 
 template <int D, int MODE, int ACT>
-static hipError_t launch_fwd_t(const AttnParams &p, int cus, bool few_q, hipStream_t stream) {
-    if (MODE == JFA && p.o_res_out) return launch_fwd_s<D, MODE, ACT, true>(p, cus, few_q, stream);
-    return launch_fwd_s<D, MODE, ACT, false>(p, cus, few_q, stream);
+static hipError_t launch_fwd_t(const AttnParams &p, int cus, bool few_q, bool long_units, hipStream_t stream) {
+    if (MODE == JFA && p.o_res_out) return launch_fwd_s<D, MODE, ACT, true>(p, cus, few_q, long_units, stream);
+    return launch_fwd_s<D, MODE, ACT, false>(p, cus, few_q, long_units, stream);
 }
 
 template <int D>
-static hipError_t launch_fwd_d(const AttnParams &p, int mode, int act, int cus, bool few_q, hipStream_t stream) {
-    if (mode == JFA) return launch_fwd_t<D, JFA, SILU>(p, cus, few_q, stream);
+static hipError_t launch_fwd_d(const AttnParams &p, int mode, int act, int cus, bool few_q, bool lu,
+                               hipStream_t stream) {
+    if (mode == JFA) return launch_fwd_t<D, JFA, SILU>(p, cus, few_q, lu, stream);
     switch (act) {
-    case SILU: return launch_fwd_t<D, GDPA, SILU>(p, cus, few_q, stream);
-    case GELU_TANH: return launch_fwd_t<D, GDPA, GELU_TANH>(p, cus, few_q, stream);
-    default: return launch_fwd_t<D, GDPA, GELU_ERF>(p, cus, few_q, stream);
+    case SILU: return launch_fwd_t<D, GDPA, SILU>(p, cus, few_q, lu, stream);
+    case GELU_TANH: return launch_fwd_t<D, GDPA, GELU_TANH>(p, cus, few_q, lu, stream);
+    default: return launch_fwd_t<D, GDPA, GELU_ERF>(p, cus, few_q, lu, stream);
     }
 }
 
-hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, hipStream_t stream) {
+hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, bool long_units,
+                           hipStream_t stream) {
     switch (D) {
-    case 32: return launch_fwd_d<32>(p, mode, act, cus, few_q, stream);
-    case 64: return launch_fwd_d<64>(p, mode, act, cus, few_q, stream);
-    default: return launch_fwd_d<128>(p, mode, act, cus, few_q, stream);
+    case 32: return launch_fwd_d<32>(p, mode, act, cus, few_q, long_units, stream);
+    case 64: return launch_fwd_d<64>(p, mode, act, cus, few_q, long_units, stream);
+    default: return launch_fwd_d<128>(p, mode, act, cus, few_q, long_units, stream);
     }
 }
 

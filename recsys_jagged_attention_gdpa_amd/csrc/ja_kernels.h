@@ -133,8 +133,12 @@ const KernelTimer &kernel_timer();
 // cus: compute units; few_q: every sample has one shared block of <= 32 query
 // rows (q_offsets NULL, lq_fixed <= FEW_Q_ROWS), planned as 32-row query tiles.
 constexpr int FEW_Q_ROWS = 32;
-hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, hipStream_t stream);
-hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream);
+// long_units: launch the long-sequence kernels (false when no sample has more
+// than FUSED_MAX_LK keys, so only the short-K/V units have work).
+hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, bool long_units,
+                           hipStream_t stream);
+hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, bool long_units,
+                           hipStream_t stream);
 hipError_t launch_fwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
 hipError_t launch_bwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
 

@@ -6,6 +6,8 @@ call the library, and expose autograd functions.
 
 q is [Tq, H, D] (or [Lq, H, D] shared by every sample when q_offsets is None),
 k and v are [Tk, H, D]; offsets are int32 [B+1] on the same device.
+max_kv_len (0 = unknown) is an optional upper bound on every sample's key
+count; a bound of at most 32 lets the library skip its long-sequence kernels.
 """
 from __future__ import annotations
 
@@ -15,7 +17,7 @@ from . import _lib
 
 
 def _problem(q, k, q_offsets, kv_offsets, *, causal, scale, act, bias, bias_kind, bias_lo,
-             bias_hi):
+             bias_hi, max_kv_len=0):
     B = int(kv_offsets.numel()) - 1
     H, D = int(q.shape[1]), int(q.shape[2])
     return _lib.make_problem(
@@ -23,7 +25,7 @@ def _problem(q, k, q_offsets, kv_offsets, *, causal, scale, act, bias, bias_kind
         total_k=int(k.shape[0]), q_offsets=q_offsets, kv_offsets=kv_offsets,
         lq_fixed=0 if q_offsets is not None else int(q.shape[0]), causal=causal, scale=scale,
         act=act, bias_kind=bias_kind if bias is not None else "none", bias_table=bias,
-        bias_lo=bias_lo, bias_hi=bias_hi)
+        bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len)
 
 
 def _check_inputs(q, k, v, q_offsets, kv_offsets, bias):
@@ -47,10 +49,10 @@ def _workspace(problem, pass_, device):
 
 
 def gdpa_forward(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False,
-                 bias=None, bias_kind="none", bias_lo=0, bias_hi=0):
+                 bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0):
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act=act, bias=bias,
-                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi)
+                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len)
     rows = q.shape[0] if q_offsets is not None else p.batch * q.shape[0]
     o = torch.empty((rows, q.shape[1], q.shape[2]), dtype=q.dtype, device=q.device)
     ws = _workspace(p, _lib.PASS_FWD, q.device)
@@ -59,11 +61,11 @@ def gdpa_forward(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, caus
 
 
 def attn_forward(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bias=None,
-                 bias_kind="none", bias_lo=0, bias_hi=0, residual=True):
+                 bias_kind="none", bias_lo=0, bias_hi=0, residual=True, max_kv_len=0):
     """Returns (O, LSE[H, T], O_residual); O_residual is None for fp32 or residual=False."""
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act="silu", bias=bias,
-                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi)
+                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len)
     rows = q.shape[0] if q_offsets is not None else p.batch * q.shape[0]
     o = torch.empty((rows, q.shape[1], q.shape[2]), dtype=q.dtype, device=q.device)
     lse = torch.empty((q.shape[1], rows), dtype=torch.float32, device=q.device)
@@ -74,10 +76,10 @@ def attn_forward(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bi
 
 
 def gdpa_backward(q, k, v, dout, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False,
-                  bias=None, bias_kind="none", bias_lo=0, bias_hi=0):
+                  bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0):
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act=act, bias=bias,
-                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi)
+                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = _workspace(p, _lib.PASS_BWD, q.device)
     _lib.jagged_gdpa_bwd(p, q, k, v, dout.contiguous(), dq, dk, dv, ws)
@@ -85,10 +87,10 @@ def gdpa_backward(q, k, v, dout, q_offsets, kv_offsets, *, act="silu", scale=Non
 
 
 def attn_backward(q, k, v, o, dout, lse, q_offsets, kv_offsets, *, o_residual=None, scale=None,
-                  causal=False, bias=None, bias_kind="none", bias_lo=0, bias_hi=0):
+                  causal=False, bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0):
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act="silu", bias=bias,
-                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi)
+                 bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = _workspace(p, _lib.PASS_BWD, q.device)
     _lib.jagged_attn_bwd(p, q, k, v, o, o_residual, dout.contiguous(), lse, dq, dk, dv, ws)
@@ -98,9 +100,9 @@ def attn_backward(q, k, v, o, dout, lse, q_offsets, kv_offsets, *, o_residual=No
 class _GDPAFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, q_offsets, kv_offsets, act, scale, causal, bias, bias_kind, bias_lo,
-                bias_hi):
+                bias_hi, max_kv_len):
         kw = dict(act=act, scale=scale, causal=causal, bias=bias, bias_kind=bias_kind,
-                  bias_lo=bias_lo, bias_hi=bias_hi)
+                  bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len)
         ctx.kw = kw
         ctx.save_for_backward(q, k, v, q_offsets, kv_offsets)
         return gdpa_forward(q, k, v, q_offsets, kv_offsets, **kw)
@@ -109,15 +111,15 @@ class _GDPAFunction(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, q_offsets, kv_offsets = ctx.saved_tensors
         dq, dk, dv = gdpa_backward(q, k, v, do, q_offsets, kv_offsets, **ctx.kw)
-        return dq, dk, dv, None, None, None, None, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None, None, None, None, None
 
 
 class _JFAFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, q_offsets, kv_offsets, scale, causal, bias, bias_kind, bias_lo,
-                bias_hi):
+                bias_hi, max_kv_len):
         kw = dict(scale=scale, causal=causal, bias=bias, bias_kind=bias_kind, bias_lo=bias_lo,
-                  bias_hi=bias_hi)
+                  bias_hi=bias_hi, max_kv_len=max_kv_len)
         o, lse, o_res = attn_forward(q, k, v, q_offsets, kv_offsets, **kw)
         ctx.kw = kw
         ctx.save_for_backward(q, k, v, o, lse, o_res, q_offsets, kv_offsets)
@@ -128,18 +130,18 @@ class _JFAFunction(torch.autograd.Function):
         q, k, v, o, lse, o_res, q_offsets, kv_offsets = ctx.saved_tensors
         dq, dk, dv = attn_backward(q, k, v, o, do, lse, q_offsets, kv_offsets, o_residual=o_res,
                                    **ctx.kw)
-        return dq, dk, dv, None, None, None, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None, None, None, None
 
 
 def gdpa(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False, bias=None,
-         bias_kind="none", bias_lo=0, bias_hi=0):
+         bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0):
     """Jagged GDPA with autograd (backward needs per-sample query offsets)."""
     return _GDPAFunction.apply(q, k, v, q_offsets, kv_offsets, act, scale, causal, bias,
-                               bias_kind, bias_lo, bias_hi)
+                               bias_kind, bias_lo, bias_hi, max_kv_len)
 
 
 def jagged_attention(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bias=None,
-                     bias_kind="none", bias_lo=0, bias_hi=0):
+                     bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0):
     """Jagged flash attention (softmax) with autograd."""
     return _JFAFunction.apply(q, k, v, q_offsets, kv_offsets, scale, causal, bias, bias_kind,
-                              bias_lo, bias_hi)
+                              bias_lo, bias_hi, max_kv_len)

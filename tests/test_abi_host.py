@@ -3,6 +3,7 @@ rejects bad host-side arguments before launching anything (no GPU needed)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 import torch
@@ -33,6 +34,25 @@ def test_library_exports_every_declared_symbol():
         assert lib.ja_status_string(code)
 
 
+def test_problem_struct_layout_matches_header(tmp_path):
+    # Compile the header with the host C compiler and compare every field's
+    # offset and the struct size with the binding's ctypes mirror.
+    fields = [f[0] for f in _lib.JaProblem._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join(f'    printf("{f} %zu\\n", offsetof(ja_problem, {f}));\n' for f in fields)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "jagged_attn.h"\n'
+                   'int main(void) {\n' + body +
+                   '    printf("sizeof %zu\\n", sizeof(ja_problem));\n    return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                        text=True).stdout.splitlines())
+    for f in fields:
+        assert int(out[f]) == getattr(_lib.JaProblem, f).offset, f
+    assert int(out["sizeof"]) == ctypes.sizeof(_lib.JaProblem)
+
+
 def _problem(**kw):
     base = dict(batch=2, heads=2, head_dim=64, dtype=torch.bfloat16, total_q=10, total_k=12,
                 q_offsets=0x1000, kv_offsets=0x2000)
@@ -54,7 +74,7 @@ def test_workspace_size_is_positive_and_aligned():
     (dict(bias_kind=4), 3), (dict(batch=0), 2), (dict(heads=0), 2), (dict(total_q=-1), 2),
     (dict(kv_offsets=None), 1), (dict(bias_kind="rel", bias_table=None), 1),
     (dict(bias_kind="rel", bias_table=0x3000, bias_lo=5, bias_hi=1), 2),
-    (dict(q_offsets=None, lq_fixed=3, total_q=4), 2),
+    (dict(q_offsets=None, lq_fixed=3, total_q=4), 2), (dict(max_kv_len=-1), 2),
     # slices are addressed with 32-bit offsets: tensors of 4 GiB or more are refused
     (dict(total_q=1 << 24, heads=64, head_dim=128), 3), (dict(total_k=1 << 24, heads=16, head_dim=128), 3),
     (dict(total_q=1 << 23, heads=1, head_dim=128, dtype=torch.float32), 3),  # exactly 4 GiB

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from recsys_jagged_attention_gdpa_amd import synth
-from tests.gpu_helpers import parity
+from tests.gpu_helpers import gpu_bwd, gpu_fwd, parity, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -167,3 +167,31 @@ def test_head_counts_and_explicit_scale(mode, H, D, scale):
     w = synth.custom(mode=mode, lq=[150, 1, 40, 33], lk=[90, 300, 32, 65], H=H, D=D, seed=H * D, scale=scale,
                      act="silu", causal=True)
     parity(w, label=f"{mode} H={H} D={D} scale={scale}")
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+@pytest.mark.parametrize("hint", [32, 33])
+def test_key_count_bound_hint(mode, hint):
+    # Every sample has at most 32 keys.  A bound of at most 32 leaves the
+    # long-sequence kernels unlaunched; the results must not change (the same
+    # short-K/V units compute every output either way).
+    lq, lk = [1, 70, 300, 0, 129, 5, 2], [32, 1, 17, 0, 31, 32, 0]
+    w = synth.custom(mode=mode, lq=lq, lk=lk, H=2, D=128, seed=hint, act="gelu_erf", causal=True,
+                     bias_kind="rel", bias_lo=-40, bias_hi=10, bias_sigma=0.3)
+    parity(w, label=f"hint {mode} max_kv_len={hint}", max_kv_len=hint)
+    d = to_dev(w)
+    base = gpu_fwd(w, d)
+    d["max_kv_len"] = hint
+    hinted = gpu_fwd(w, d)
+    for n in base:
+        if base[n] is not None:
+            assert torch.equal(base[n], hinted[n]), n
+    gb, gh = gpu_bwd(w, {**d, "max_kv_len": 0}, base), gpu_bwd(w, d, hinted)
+    for n in ("dq", "dk", "dv"):
+        assert torch.equal(gb[n], gh[n]), n
+
+
+def test_key_count_bound_hint_shared_queries():
+    w = synth.custom(mode="gdpa", lq=None, lk=[32, 0, 1, 31, 17], H=2, D=64, seed=9, shared_q=16,
+                     act="silu", with_dout=False)
+    parity(w, backward=False, label="hint shared-q", max_kv_len=32)

@@ -31,6 +31,12 @@
  *   GDPA:  dX_ij = dP_ij act'(X_ij),   dV_j = sum_i act(X_ij) dO_i
  *   JFA:   dX_ij = P_ij (dP_ij - sum_k P_ik dP_ik),  dV_j = sum_i P_ij dO_i
  *   dQ_i = scale sum_j dX_ij k_j,   dK_j = scale sum_i dX_ij q_i
+ *   bias table (the pages list custom attention biases among what the jagged
+ *   kernels support, "GEM Training...", section "What happened"; the table
+ *   enters X additively, so dL/dtable sums dX over the pairs that read each
+ *   entry):  dTable[h][c] = sum over samples and valid pairs (i, j) whose
+ *   index (REL: clamp(i - j, lo, hi) - lo; KEYPOS: clamp(j, lo, hi) - lo) is c
+ *   of dX_ij
  *
  * Inputs are float32 arrays (bf16 values are exactly representable in
  * float32); all arithmetic is double.  Layout is token-major [T, H, D] with
@@ -360,6 +366,42 @@ static int run_bwd(const problem *p, int softmax, const float *dout, double *dq,
     return 0;
 }
 
+/* Gradient of L with respect to the bias table: each (sample, head) adds the
+ * dX of its valid pairs to the entry the pair reads, into its own row of
+ * partial sums; the rows are then added sample by sample in order. */
+static int run_dbias(const problem *p, int softmax, const float *dout, double *dtable, int nthreads) {
+    if (!p->q_off || p->bias_kind == BIAS_NONE) return 1;
+    const int B = p->B, H = p->H;
+    const int64_t W = (int64_t)p->bias_hi - p->bias_lo + 1;
+    double *part = (double *)calloc((size_t)(B > 0 ? B : 1) * H * W, sizeof(double));
+    if (!part) return 2;
+    const int nt = nthreads_or_default(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t u = 0; u < (int64_t)B * H; ++u) {
+        const int b = (int)(u / H), h = (int)(u % H);
+        sample s = sample_rows(p, b);
+        double *row = part + u * W;
+        for (int64_t i = 0; i < s.lq; ++i) {
+            const float *doi = row_of(p, dout, s.qs + i, h);
+            double m = 0.0, l = 1.0, delta = 0.0;
+            if (softmax && !row_bwd_stats(p, h, &s, i, doi, &m, &l, &delta)) continue;
+            for (int64_t j = 0; j < s.lk; ++j) {
+                if (!is_valid(p, i, j, s.lq, s.lk)) continue;
+                double w, dx;
+                pair_bwd(p, softmax, h, &s, i, j, doi, m, l, delta, &w, &dx);
+                const int64_t pos = p->bias_kind == BIAS_REL ? i - j : j;
+                row[clampi(pos, p->bias_lo, p->bias_hi) - p->bias_lo] += dx;
+            }
+        }
+    }
+    for (int64_t c = 0; c < (int64_t)H * W; ++c) dtable[c] = 0.0;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int64_t c = 0; c < W; ++c) dtable[(int64_t)h * W + c] += part[((int64_t)b * H + h) * W + c];
+    free(part);
+    return 0;
+}
+
 /* ------------------------------------------------------------ exported API */
 /* act: 0 SiLU, 1 GELU (tanh form), 2 GELU (erf form).
  * bias_kind: 0 none, 1 REL (query minus key), 2 KEYPOS (key position).
@@ -402,6 +444,25 @@ int ref_attn_bwd(const float *q, const float *k, const float *v, const float *do
     problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, bias_kind,
                              bias_table, bias_lo, bias_hi);
     return run_bwd(&p, 1, dout, dq, dk, dv, nthreads);
+}
+
+/* dL/dtable [H][bias_hi - bias_lo + 1] of L = <O, dout> (needs a bias kind). */
+int ref_gdpa_dbias(const float *q, const float *k, const float *v, const float *dout, double *dtable,
+                   const int32_t *q_off, const int32_t *kv_off, int B, int H, int D, double scale,
+                   int act, int causal, int bias_kind, const float *bias_table, int bias_lo,
+                   int bias_hi, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, bias_kind,
+                             bias_table, bias_lo, bias_hi);
+    return run_dbias(&p, 0, dout, dtable, nthreads);
+}
+
+int ref_attn_dbias(const float *q, const float *k, const float *v, const float *dout, double *dtable,
+                   const int32_t *q_off, const int32_t *kv_off, int B, int H, int D, double scale,
+                   int causal, int bias_kind, const float *bias_table, int bias_lo, int bias_hi,
+                   int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, bias_kind,
+                             bias_table, bias_lo, bias_hi);
+    return run_dbias(&p, 1, dout, dtable, nthreads);
 }
 
 /* Element-wise activation and derivative, exported so the tests can pin them

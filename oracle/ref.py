@@ -45,10 +45,12 @@ def _load():
         lib.ref_attn_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P, I, I, I, D, I, I, P, I, I, I]
         lib.ref_gdpa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, D, I, I, I, P, I, I, I]
         lib.ref_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, D, I, I, P, I, I, I]
+        lib.ref_gdpa_dbias.argtypes = [P, P, P, P, P, P, P, I, I, I, D, I, I, I, P, I, I, I]
+        lib.ref_attn_dbias.argtypes = [P, P, P, P, P, P, P, I, I, I, D, I, I, P, I, I, I]
         lib.ref_act.argtypes = [I, P, P, P, ctypes.c_int64]
         lib.ref_max_threads.argtypes = []
         for f in (lib.ref_gdpa_fwd, lib.ref_attn_fwd, lib.ref_gdpa_bwd, lib.ref_attn_bwd,
-                  lib.ref_max_threads):
+                  lib.ref_gdpa_dbias, lib.ref_attn_dbias, lib.ref_max_threads):
             f.restype = ctypes.c_int
         lib.ref_act.restype = None
         _lib = lib
@@ -159,6 +161,37 @@ def attn_bwd(q, k, v, dout, q_off, kv_off, *, scale, causal=False, bias_kind="no
     """JFA backward of L = <O, dout>: returns (dQ, dK, dV) in float64."""
     return _bwd(_load().ref_attn_bwd, False, q, k, v, dout, q_off, kv_off, scale, None, causal,
                 bias_kind, bias_table, bias_lo, bias_hi, nthreads)
+
+
+def _dbias(fn, with_act, q, k, v, dout, q_off, kv_off, scale, act, causal, bias_kind, bias_table,
+           bias_lo, bias_hi, nthreads):
+    assert q_off is not None and bias_kind != "none"
+    a = _Args(q, k, v, q_off, kv_off, 0, bias_kind, bias_table, bias_lo, bias_hi)
+    do = _f32(dout)
+    assert do.shape == a.q.shape
+    dt = np.empty((a.H, a.bias_hi - a.bias_lo + 1), dtype=np.float64)
+    args = [_ptr(a.q), _ptr(a.k), _ptr(a.v), _ptr(do), _ptr(dt), _ptr(a.q_off), _ptr(a.kv_off),
+            a.B, a.H, a.D, float(scale)]
+    if with_act:
+        args.append(ACTS[act])
+    args += [int(causal), a.bias_kind, _ptr(a.bias_table), a.bias_lo, a.bias_hi, int(nthreads)]
+    rc = fn(*args)
+    assert rc == 0, rc
+    return dt
+
+
+def gdpa_dbias(q, k, v, dout, q_off, kv_off, *, scale, act, causal=False, bias_kind,
+               bias_table, bias_lo, bias_hi, nthreads=0):
+    """GDPA: dL/dtable [H, hi - lo + 1] of L = <O, dout> (float64)."""
+    return _dbias(_load().ref_gdpa_dbias, True, q, k, v, dout, q_off, kv_off, scale, act, causal,
+                  bias_kind, bias_table, bias_lo, bias_hi, nthreads)
+
+
+def attn_dbias(q, k, v, dout, q_off, kv_off, *, scale, causal=False, bias_kind, bias_table,
+               bias_lo, bias_hi, nthreads=0):
+    """JFA: dL/dtable [H, hi - lo + 1] of L = <O, dout> (float64)."""
+    return _dbias(_load().ref_attn_dbias, False, q, k, v, dout, q_off, kv_off, scale, None, causal,
+                  bias_kind, bias_table, bias_lo, bias_hi, nthreads)
 
 
 def act(name, x):

@@ -69,8 +69,9 @@ def dense(w, *, grads=True):
     mask = mask.unsqueeze(1)  # [B, 1, Lq, Lk]
 
     x = w.scale * torch.matmul(qp, kp.transpose(-1, -2))
+    tab = None
     if w.bias_kind != "none":
-        tab = w.bias_table.double()
+        tab = w.bias_table.double().clone().requires_grad_(grads)
         ii, jj = torch.arange(Lq).view(Lq, 1), torch.arange(Lk).view(1, Lk)
         idx = (ii - jj) if w.bias_kind == "rel" else jj.expand(Lq, Lk)
         idx = idx.clamp(w.bias_lo, w.bias_hi) - w.bias_lo
@@ -102,4 +103,6 @@ def dense(w, *, grads=True):
         res["dq"] = q.grad.numpy()
         res["dk"] = k.grad.numpy()
         res["dv"] = v.grad.numpy()
+        if tab is not None:
+            res["dbias"] = tab.grad.numpy()
     return res

@@ -29,6 +29,15 @@ def oracle_bwd(w, nthreads=0):
     return {"dq": dq, "dk": dk, "dv": dv}
 
 
+def oracle_dbias(w, nthreads=0):
+    """dL/dtable [H, hi - lo + 1] for a workload with a bias table and per-sample queries."""
+    if w.mode == "gdpa":
+        return ref.gdpa_dbias(w.q, w.k, w.v, w.dout, w.q_off, w.kv_off, scale=w.scale, act=w.act,
+                              causal=w.causal, nthreads=nthreads, **bias_kw(w))
+    return ref.attn_dbias(w.q, w.k, w.v, w.dout, w.q_off, w.kv_off, scale=w.scale,
+                          causal=w.causal, nthreads=nthreads, **bias_kw(w))
+
+
 def max_rel(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)

@@ -4,10 +4,12 @@ Each check below is fixed by mathematics rather than by re-typing the oracle:
   * activations against torch's library SiLU / GELU and textbook normal-CDF values;
   * per-sample identity: a jagged batch equals each sample run alone, and equals
     torch's scaled_dot_product_attention (JFA) per sample;
-  * central finite differences of L = <O, dO> against the oracle's gradients;
+  * central finite differences of L = <O, dO> against the oracle's gradients
+    (inputs and the bias table);
   * closed forms: one key, zero queries, all-ones values, constant bias, empty samples,
     a hand-worked two-key example;
-  * JFA gradient identities: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i.
+  * JFA gradient identities: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i; the
+    bias-table gradient sums to zero over the table (softmax rows sum to one).
 """
 import math
 
@@ -18,7 +20,7 @@ import torch.nn.functional as F
 
 from oracle import ref
 from recsys_jagged_attention_gdpa_amd import synth
-from tests.helpers import max_rel, oracle_bwd, oracle_fwd
+from tests.helpers import max_rel, oracle_bwd, oracle_dbias, oracle_fwd
 
 
 # ------------------------------------------------------------------ activations
@@ -151,6 +153,43 @@ def test_gradients_match_central_differences(mode, act, causal, bias):
             fd = (_loss(w, **args_p) - _loss(w, **args_m)) / 2.0
             an = float((g[name] * d.double().numpy()).sum())
             assert abs(fd - an) <= 1e-7 * max(abs(an), 1e-3), (name, fd, an)
+
+
+@pytest.mark.parametrize("mode,act,causal,bias,lo,hi", [
+    ("gdpa", "silu", True, "rel", -3, 5), ("gdpa", "gelu_tanh", False, "keypos", 1, 6),
+    ("gdpa", "gelu_erf", True, "keypos", 0, 40), ("jfa", "silu", True, "rel", -2, 2),
+    ("jfa", "silu", False, "keypos", 0, 3)])
+def test_bias_table_gradient_matches_central_differences(mode, act, causal, bias, lo, hi):
+    w = _w(mode, 11, act=act, causal=causal, bias_kind=bias, bias_lo=lo, bias_hi=hi)
+    # The oracle reads the table as float32: use bf16-valued entries (tiny ones
+    # zeroed) so that entry +- 2^-14 is exact in float32.
+    tab = w.bias_table.to(torch.bfloat16).float()
+    tab[tab.abs() < 2.0 ** -10] = 0.0
+    w = synth.Workload(**{**w.__dict__, "bias_table": tab})
+    g = oracle_dbias(w)
+    base = tab.double()
+    rng = np.random.default_rng(5)
+    for _ in range(3):
+        d = torch.from_numpy(rng.integers(-1, 2, size=tuple(base.shape)).astype(np.float64) * 2.0 ** -14)
+        assert torch.equal((base + d).float().double(), base + d)
+        assert torch.equal((base - d).float().double(), base - d)
+        lp = float((oracle_fwd(synth.Workload(**{**w.__dict__, "bias_table": base + d}))["o"]
+                    * w.dout.double().numpy()).sum())
+        lm = float((oracle_fwd(synth.Workload(**{**w.__dict__, "bias_table": base - d}))["o"]
+                    * w.dout.double().numpy()).sum())
+        fd = (lp - lm) / 2.0
+        an = float((g * d.numpy()).sum())
+        assert abs(fd - an) <= 1e-7 * max(abs(an), 1e-6), (fd, an)
+
+
+def test_jfa_bias_table_gradient_sums_to_zero():
+    # Every valid pair reads exactly one table entry and sum_j dX_ij = 0 for a
+    # softmax row, so each head's table gradient sums to zero.
+    for bias, lo, hi in (("rel", -5, 5), ("keypos", 0, 3)):
+        w = _w("jfa", 3, causal=True, bias_kind=bias, bias_lo=lo, bias_hi=hi)
+        g = oracle_dbias(w)
+        assert np.abs(g).max() > 1e-3
+        assert np.abs(g.sum(axis=1)).max() <= 1e-12 * np.abs(g).sum()
 
 
 # ---------------------------------------------------------------- closed forms

@@ -102,6 +102,8 @@ def kernel_cost(w, kernel: str) -> tuple[float, float]:
         return e * HD * (3 * tq + 2 * tk), 6.0 * w.D * P
     if kernel == "bwd_delta":
         return e * HD * 2 * tq + 4 * w.H * tq, 2.0 * HD * tq
+    if kernel == "bwd_dbias":  # read Q, dO, K, V; recompute S and dP (two GEMMs per pair)
+        return e * HD * (2 * tq + 2 * tk), 4.0 * w.D * P
     return 0.0, 0.0
 
 
@@ -135,7 +137,7 @@ class HipEvents:
 
 # ------------------------------------------------------------------ the step
 class Runner:
-    def __init__(self, w, device="cuda"):
+    def __init__(self, w, device="cuda", bias_grad=False):
         self.w = w
         dev = torch.device(device)
         self.q = w.q.to(dev)
@@ -160,23 +162,30 @@ class Runner:
         self.o_res = torch.empty_like(self.o) if (w.mode == "jfa" and w.dtype == torch.bfloat16) else None
         self.ws_f = torch.empty(_lib.ja_workspace_size(self.prob, _lib.PASS_FWD), dtype=torch.uint8, device=dev)
         self.backward = bool(w.backward and w.q_off is not None and self.dout is not None)
+        self.bias_grad = bool(bias_grad and self.backward and self.bias is not None)
+        if bias_grad and not self.bias_grad:
+            raise SystemExit("--bias-grad needs a workload with a backward pass and a bias table")
+        self.db = torch.empty_like(self.bias) if self.bias_grad else None
         if self.backward:
             self.dq = torch.empty_like(self.q)
             self.dk = torch.empty_like(self.k)
             self.dv = torch.empty_like(self.v)
-            self.ws_b = torch.empty(_lib.ja_workspace_size(self.prob, _lib.PASS_BWD), dtype=torch.uint8, device=dev)
+            pass_b = _lib.PASS_BWD_DBIAS if self.bias_grad else _lib.PASS_BWD
+            self.ws_b = torch.empty(_lib.ja_workspace_size(self.prob, pass_b), dtype=torch.uint8, device=dev)
 
     def kernels(self):
         if self.w.dtype == torch.float32:  # plain fp32 kernels: no planner, no short / fused units
             ks = ["fwd"]
             if self.backward:
                 ks += (["bwd_delta"] if self.w.mode == "jfa" else []) + ["bwd_q", "bwd_kv"]
+                ks += ["bwd_dbias"] if self.bias_grad else []
             return ks
         long_units = not (0 < self.max_kv_len <= SHORT_KV)  # else those kernels are not launched
         ks = ["plan", "fwd_short"] + (["fwd"] if long_units else [])
         if self.backward:
             ks += ["bwd_fused"] + (["bwd_kv", "bwd_q"] if long_units else [])
             ks += ["bwd_delta"] if self.w.mode == "jfa" else []
+            ks += ["bwd_dbias"] if self.bias_grad else []
         return ks
 
     def step(self):
@@ -184,12 +193,13 @@ class Runner:
         if w.mode == "gdpa":
             _lib.jagged_gdpa_fwd(p, self.q, self.k, self.v, self.o, self.ws_f)
             if self.backward:
-                _lib.jagged_gdpa_bwd(p, self.q, self.k, self.v, self.dout, self.dq, self.dk, self.dv, self.ws_b)
+                _lib.jagged_gdpa_bwd(p, self.q, self.k, self.v, self.dout, self.dq, self.dk, self.dv, self.db,
+                                     self.ws_b)
         else:
             _lib.jagged_attn_fwd(p, self.q, self.k, self.v, self.o, self.lse, self.o_res, self.ws_f)
             if self.backward:
                 _lib.jagged_attn_bwd(p, self.q, self.k, self.v, self.o, self.o_res, self.dout, self.lse,
-                                     self.dq, self.dk, self.dv, self.ws_b)
+                                     self.dq, self.dk, self.dv, self.db, self.ws_b)
 
 
 def kernel_durations(runner, ev, kernels, reps=3):
@@ -230,7 +240,7 @@ def measured_traffic(workload, kernel):
 # Device-side kernel names of the library's kernels, as profilers list them.
 KERNEL_SYMBOLS = {"plan": "plan_kernel", "fwd": "ja::fwd_kernel<", "fwd_short": "fwd_short_kernel",
                   "bwd_fused": "ja::fused_kernel<", "bwd_kv": "dkdv_kernel<", "bwd_q": "dq_kernel<",
-                  "bwd_delta": "delta_kernel<"}
+                  "bwd_delta": "delta_kernel<", "bwd_dbias": "dbias_kernel<"}
 
 
 def write_traffic(workload, kernel, fetch_csv, write_csv, copy_mib, command):
@@ -339,6 +349,10 @@ def main():
                          "uses no GPU")
     ap.add_argument("--kernel", default=None, choices=sorted(KERNEL_SYMBOLS))
     ap.add_argument("--command", default="", help="the rocprofv3 command the csv files came from")
+    ap.add_argument("--bias-grad", action="store_true",
+                    help="also compute the bias table's gradient in every backward pass")
+    ap.add_argument("--roofline-kernel", default=None, choices=sorted(KERNEL_SYMBOLS),
+                    help="place this kernel on the roofline instead of the slowest one")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -361,7 +375,7 @@ def main():
     w = synth.make(args.workload, args.seed)
     log(f"[bench] workload {args.workload}: B={w.B} H={w.H} D={w.D} Tq={w.total_q} Tk={w.total_k} "
         f"generated in {time.perf_counter() - t0:.1f}s")
-    runner = Runner(w)
+    runner = Runner(w, bias_grad=args.bias_grad)
     ev = HipEvents()
 
     for _ in range(args.warmup):
@@ -371,6 +385,10 @@ def main():
     # per-kernel durations (outside the timed region) to find the dominant kernel
     durs = kernel_durations(runner, ev, runner.kernels())
     dominant = max(durs, key=durs.get)
+    if args.roofline_kernel:
+        if args.roofline_kernel not in durs:
+            raise SystemExit(f"kernel {args.roofline_kernel} does not run in this workload")
+        dominant = args.roofline_kernel
     log("[bench] kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in durs.items()))
 
     if args.calibrate_copy_mib:
@@ -426,7 +444,7 @@ def main():
         "config": {"workload": args.workload, "B": w.B, "H": w.H, "D": w.D,
                    "total_q": w.total_q, "total_k": w.total_k, "act": w.act if w.mode == "gdpa" else "softmax",
                    "causal": w.causal, "bias": w.bias_kind, "jagged_sparsity": round(sparsity, 4),
-                   "useful_pairs": P, "backward": runner.backward},
+                   "useful_pairs": P, "backward": runner.backward, "bias_grad": runner.bias_grad},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),

@@ -37,7 +37,8 @@
  * the scale, before the activation / softmax:
  *   JA_BIAS_REL     table[h][clamp(i - j, bias_lo, bias_hi) - bias_lo]
  *   JA_BIAS_KEYPOS  table[h][clamp(j, bias_lo, bias_hi) - bias_lo]
- * No gradient is produced for the table.
+ * The backward entry points can also return the table's gradient (dbias,
+ * below).
  *
  * Ownership.  Every buffer belongs to the caller, including the workspace
  * (ja_workspace_size bytes, 256-byte aligned, device memory).  The library
@@ -82,7 +83,11 @@ typedef enum {
 typedef enum { JA_BF16 = 0, JA_F32 = 1 } ja_dtype;
 typedef enum { JA_ACT_SILU = 0, JA_ACT_GELU_TANH = 1, JA_ACT_GELU_ERF = 2 } ja_act;
 typedef enum { JA_BIAS_NONE = 0, JA_BIAS_REL = 1, JA_BIAS_KEYPOS = 2 } ja_bias_kind;
-typedef enum { JA_PASS_FWD = 0, JA_PASS_BWD = 1 } ja_pass;
+typedef enum {
+    JA_PASS_FWD = 0,
+    JA_PASS_BWD = 1,
+    JA_PASS_BWD_DBIAS = 2 /* backward that also returns the bias-table gradient */
+} ja_pass;
 
 /* Problem description: sizes by value, device pointers to the offsets and the
  * bias table.  The struct itself is read on the host during the call only. */
@@ -111,7 +116,8 @@ typedef struct ja_problem {
 
 /* Workspace bytes that the given pass of either attention form needs (0 only
  * for invalid problems).  Depends on B, H, D, total_q, total_k, lq_fixed and
- * dtype; the same value serves GDPA and JFA. */
+ * dtype (JA_PASS_BWD_DBIAS: also the bias range); the same value serves GDPA
+ * and JFA. */
 size_t ja_workspace_size(const ja_problem *p, int pass);
 
 /* GDPA forward.  q [Tq, H, D] (or [lq_fixed, H, D]), k, v [Tk, H, D],
@@ -120,10 +126,19 @@ ja_status jagged_gdpa_fwd(const ja_problem *p, const void *q, const void *k, con
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* GDPA backward of L = <O, dout>: dq [Tq, H, D], dk, dv [Tk, H, D] written.
- * Needs q_offsets (no shared query block). */
+ * Needs q_offsets (no shared query block).
+ *
+ * dbias (optional, NULL to skip): device fp32 [H][bias_hi - bias_lo + 1],
+ * written with dL/dtable: entry c of head h sums dX_ij = dL/dX_ij over the
+ * valid pairs (i, j) of every sample that read it (REL: clamp(i - j), KEYPOS:
+ * clamp(j)), the bias being additive in X.  Needs a bias kind and a table
+ * row of at most 4096 entries (else JA_ERR_UNSUPPORTED), and a workspace of
+ * ja_workspace_size(p, JA_PASS_BWD_DBIAS) bytes (else JA_ERR_WORKSPACE).
+ * The custom biases are listed on "GEM Training: How Meta Doubled the
+ * Efficiency...", section "What happened". */
 ja_status jagged_gdpa_bwd(const ja_problem *p, const void *q, const void *k, const void *v,
-                          const void *dout, void *dq, void *dk, void *dv, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          const void *dout, void *dq, void *dk, void *dv, float *dbias,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* JFA forward.  o as for GDPA; lse fp32 [H, Tq_out] (head-major) receives the
  * natural-log row log-sum-exp of the scores, -inf for rows with no valid key.
@@ -138,11 +153,12 @@ ja_status jagged_attn_fwd(const ja_problem *p, const void *q, const void *k, con
  * the bf16 o alone (as FlashAttention does): o's rounding then perturbs every
  * dS_ij of a row by P_ij times that error, which dominates rows whose gradient
  * is small by cancellation.  Passing the forward's o_residual forms delta from
- * o + o_residual, exact to fp32 rounding.  Ignored for fp32 tensors. */
+ * o + o_residual, exact to fp32 rounding.  Ignored for fp32 tensors.
+ * dbias as for jagged_gdpa_bwd, with dX_ij = P_ij (dP_ij - delta_i). */
 ja_status jagged_attn_bwd(const ja_problem *p, const void *q, const void *k, const void *v,
                           const void *o, const void *o_residual, const void *dout,
-                          const float *lse, void *dq, void *dk, void *dv, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          const float *lse, void *dq, void *dk, void *dv, float *dbias,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* Measurement aid.  Kernels a call may launch: */
 typedef enum {
@@ -152,7 +168,8 @@ typedef enum {
     JA_KERNEL_BWD_KV = 3,     /* backward dK/dV units */
     JA_KERNEL_BWD_Q = 4,      /* backward dQ units */
     JA_KERNEL_BWD_DELTA = 5,  /* JFA backward delta preprocess */
-    JA_KERNEL_FWD_SHORT = 6   /* forward attention, samples with <= 32 keys */
+    JA_KERNEL_FWD_SHORT = 6,  /* forward attention, samples with <= 32 keys */
+    JA_KERNEL_BWD_DBIAS = 7   /* bias-table gradient (both of its kernels) */
 } ja_kernel_id;
 
 /* From now on, in every call made by the calling thread, record start_event

@@ -23,13 +23,13 @@ STATUS = {0: "JA_OK", 1: "JA_ERR_NULL", 2: "JA_ERR_SHAPE", 3: "JA_ERR_UNSUPPORTE
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 ACTS = {"silu": 0, "gelu_tanh": 1, "gelu_erf": 2}
 BIAS = {"none": 0, "rel": 1, "keypos": 2}
-PASS_FWD, PASS_BWD = 0, 1
+PASS_FWD, PASS_BWD, PASS_BWD_DBIAS = 0, 1, 2
 
 EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_attn_fwd",
            "jagged_attn_bwd", "ja_profile_kernel", "ja_status_string", "ja_last_hip_error",
            "ja_version")
 KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5,
-           "fwd_short": 6}
+           "fwd_short": 6, "bwd_dbias": 7}
 
 
 class JaProblem(ctypes.Structure):
@@ -71,8 +71,8 @@ def load(path: str = LIB_PATH):
         lib.ja_workspace_size.restype = ctypes.c_size_t
         lib.jagged_gdpa_fwd.argtypes = [PP, P, P, P, P, P, ctypes.c_size_t, P]
         lib.jagged_attn_fwd.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        lib.jagged_gdpa_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        lib.jagged_attn_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.jagged_gdpa_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.jagged_attn_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in (lib.jagged_gdpa_fwd, lib.jagged_attn_fwd, lib.jagged_gdpa_bwd, lib.jagged_attn_bwd):
             f.restype = ctypes.c_int
         lib.ja_profile_kernel.argtypes = [ctypes.c_int, P, P]
@@ -146,16 +146,17 @@ def jagged_attn_fwd(problem, q, k, v, o, lse, o_residual, workspace, stream=None
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def jagged_gdpa_bwd(problem, q, k, v, dout, dq, dk, dv, workspace, stream=None):
+def jagged_gdpa_bwd(problem, q, k, v, dout, dq, dk, dv, dbias, workspace, stream=None):
     _check("jagged_gdpa_bwd", load().jagged_gdpa_bwd(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+        _ptr(dv), _ptr(dbias), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def jagged_attn_bwd(problem, q, k, v, o, o_residual, dout, lse, dq, dk, dv, workspace, stream=None):
+def jagged_attn_bwd(problem, q, k, v, o, o_residual, dout, lse, dq, dk, dv, dbias, workspace,
+                    stream=None):
     _check("jagged_attn_bwd", load().jagged_attn_bwd(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_residual), _ptr(dout),
-        _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace),
+        _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
 
 

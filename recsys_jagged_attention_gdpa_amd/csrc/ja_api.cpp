@@ -41,10 +41,12 @@ int64_t total_q_out(const ja_problem &p) {
 int64_t tile_cap(int64_t rows, int B, int tile) { return rows / tile + B + 1; }
 
 struct Layout {
-    size_t counters;  // 3 PlanCounters blocks
-    size_t tiles_q, tiles_k, tiles_s, delta, total;
+    size_t counters;  // 4 PlanCounters blocks
+    size_t tiles_q, tiles_k, tiles_s, delta, tiles_a, dbias_part, total;
     int64_t cap_q, cap_k, cap_s;
 };
+
+int64_t bias_width(const ja_problem &p) { return (int64_t)p.bias_hi - p.bias_lo + 1; }
 
 Layout layout_of(const ja_problem &p, int pass) {
     Layout L{};
@@ -54,16 +56,22 @@ Layout layout_of(const ja_problem &p, int pass) {
     L.cap_s = (int64_t)p.batch + 1;
     size_t off = 0;
     L.counters = off;
-    off += align_up(3 * sizeof(ja::PlanCounters));
+    off += align_up(4 * sizeof(ja::PlanCounters));
     L.tiles_q = off;
     off += align_up((size_t)L.cap_q * sizeof(int2));
     L.tiles_s = off;
     off += align_up((size_t)L.cap_s * sizeof(int2));
-    if (pass == JA_PASS_BWD) {
+    if (pass == JA_PASS_BWD || pass == JA_PASS_BWD_DBIAS) {
         L.tiles_k = off;
         off += align_up((size_t)L.cap_k * sizeof(int2));
         L.delta = off;
         off += align_up((size_t)p.heads * (size_t)(p.total_q > 0 ? p.total_q : 1) * sizeof(float));
+    }
+    if (pass == JA_PASS_BWD_DBIAS) {
+        L.tiles_a = off;  // query tiles of every sample
+        off += align_up((size_t)L.cap_q * sizeof(int2));
+        L.dbias_part = off;
+        off += align_up((size_t)ja::DBIAS_GRID * p.heads * (size_t)bias_width(p) * sizeof(float));
     }
     L.total = off;
     return L;
@@ -80,7 +88,7 @@ ja_status check_problem(const ja_problem *p, int pass) {
     if (!p->kv_offsets) return JA_ERR_NULL;
     if (p->total_q < 0 || p->total_k < 0 || p->total_q > INT_MAX || p->total_k > INT_MAX) return JA_ERR_SHAPE;
     if (!p->q_offsets) {
-        if (pass == JA_PASS_BWD) return JA_ERR_UNSUPPORTED;
+        if (pass != JA_PASS_FWD) return JA_ERR_UNSUPPORTED;
         if (p->lq_fixed < 0 || p->total_q != p->lq_fixed) return JA_ERR_SHAPE;
         if ((int64_t)p->lq_fixed * p->batch > INT_MAX) return JA_ERR_SHAPE;
     }
@@ -89,6 +97,9 @@ ja_status check_problem(const ja_problem *p, int pass) {
         if (p->bias_lo > p->bias_hi) return JA_ERR_SHAPE;
         if ((int64_t)p->bias_hi - p->bias_lo + 1 > (1 << 24)) return JA_ERR_SHAPE;
     }
+    // The bias-gradient pass needs a table and keeps one row of it per wave in LDS.
+    if (pass == JA_PASS_BWD_DBIAS && (p->bias_kind == JA_BIAS_NONE || bias_width(*p) > ja::DBIAS_MAX_BINS))
+        return JA_ERR_UNSUPPORTED;
     if (!(p->scale == p->scale)) return JA_ERR_SHAPE;  // NaN scale
     if (p->max_kv_len < 0) return JA_ERR_SHAPE;
     // Kernels address a (sample, head) slice with 32-bit byte offsets; bounding
@@ -134,10 +145,13 @@ ja::AttnParams base_params(const ja_problem &p, const Layout &L, void *ws) {
     a.counters = ctr;
     a.counters2 = ctr + 1;
     a.counters3 = ctr + 2;
+    a.counters4 = ctr + 3;
     a.tiles = reinterpret_cast<const int2 *>(w + L.tiles_q);
     a.tiles2 = reinterpret_cast<const int2 *>(w + L.tiles_k);
     a.tiles3 = reinterpret_cast<const int2 *>(w + L.tiles_s);
+    a.tiles4 = reinterpret_cast<const int2 *>(w + L.tiles_a);
     a.delta = reinterpret_cast<float *>(w + L.delta);
+    a.dbias_part = reinterpret_cast<float *>(w + L.dbias_part);
     return a;
 }
 
@@ -204,23 +218,25 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
 }
 
 ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, const void *v, const void *o,
-                  const void *o_res, const void *dout, const float *lse, void *dq, void *dk, void *dv, void *ws,
-                  size_t ws_bytes, void *stream) {
-    ja_status st = check_problem(p, JA_PASS_BWD);
+                  const void *o_res, const void *dout, const float *lse, void *dq, void *dk, void *dv, float *dbias,
+                  void *ws, size_t ws_bytes, void *stream) {
+    const int pass = dbias ? JA_PASS_BWD_DBIAS : JA_PASS_BWD;
+    ja_status st = check_problem(p, pass);
     if (st != JA_OK) return st;
     // A tensor with no rows is never touched, so its pointer may be NULL.
     const bool has_q = p->total_q > 0, has_k = p->total_k > 0;
     if ((has_q && (!q || !dout || !dq)) || (has_k && (!k || !v || !dk || !dv))) return JA_ERR_NULL;
     if (mode == 1 && has_q && (!o || !lse)) return JA_ERR_NULL;
-    st = check_workspace(p, JA_PASS_BWD, ws, ws_bytes);
+    st = check_workspace(p, pass, ws, ws_bytes);
     if (st != JA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const Layout L = layout_of(*p, JA_PASS_BWD);
+    const Layout L = layout_of(*p, pass);
     ja::AttnParams a = base_params(*p, L, ws);
     a.q = q;
     a.k = k;
     a.v = v;
     a.o = o;
+    a.dbias = dbias;
     a.o_res = p->dtype == JA_BF16 ? o_res : nullptr;
     a.dout = dout;
     a.dq = dq;
@@ -229,13 +245,20 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
     a.lse = const_cast<float *>(lse);
     if (p->dtype == JA_F32) return hip_status(ja::launch_bwd_f32(a, p->head_dim, mode, p->act, s));
     const bool long_units = !(p->max_kv_len > 0 && p->max_kv_len <= ja::FUSED_MAX_LK);
-    ja::PlanParams pp[3] = {
-        plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3),
-        plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 1, a.tiles, L.cap_q, a.counters),
-        plan_of(*p, ja::PLAN_KV_TILES, ja::BWD_KV_UNIT, ja::BWD_Q_STEP, 1, a.tiles2, L.cap_k, a.counters2)};
-    hipError_t e = ja::launch_plan(pp, long_units ? 3 : 1, s);
+    ja::PlanParams pp[ja::PLAN_MAX];
+    int n = 0;
+    pp[n++] = plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3);
+    if (long_units) {
+        pp[n++] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 1, a.tiles, L.cap_q, a.counters);
+        pp[n++] = plan_of(*p, ja::PLAN_KV_TILES, ja::BWD_KV_UNIT, ja::BWD_Q_STEP, 1, a.tiles2, L.cap_k, a.counters2);
+    }
+    if (dbias)  // query tiles of every sample, short ones included
+        pp[n++] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 0, a.tiles4, L.cap_q, a.counters4);
+    hipError_t e = ja::launch_plan(pp, n, s);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(ja::launch_bwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), long_units, s));
+    e = ja::launch_bwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), long_units, s);
+    if (e == hipSuccess && dbias) e = ja::launch_dbias_bf16(a, p->head_dim, mode, p->act, s);
+    return hip_status(e);
 }
 
 }  // namespace
@@ -245,7 +268,7 @@ const ja::KernelTimer &ja::kernel_timer() { return g_timer; }
 extern "C" {
 
 ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event) {
-    if (kernel_id < JA_KERNEL_PLAN || kernel_id > JA_KERNEL_FWD_SHORT) return JA_ERR_UNSUPPORTED;
+    if (kernel_id < JA_KERNEL_PLAN || kernel_id > JA_KERNEL_BWD_DBIAS) return JA_ERR_UNSUPPORTED;
     if ((start_event == nullptr) != (stop_event == nullptr)) return JA_ERR_NULL;
     g_timer.which = start_event ? kernel_id : -1;
     g_timer.start = static_cast<hipEvent_t>(start_event);
@@ -254,7 +277,7 @@ ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event) 
 }
 
 size_t ja_workspace_size(const ja_problem *p, int pass) {
-    if (pass != JA_PASS_FWD && pass != JA_PASS_BWD) return 0;
+    if (pass != JA_PASS_FWD && pass != JA_PASS_BWD && pass != JA_PASS_BWD_DBIAS) return 0;
     if (check_problem(p, pass) != JA_OK) return 0;
     return layout_of(*p, pass).total;
 }
@@ -270,14 +293,15 @@ ja_status jagged_attn_fwd(const ja_problem *p, const void *q, const void *k, con
 }
 
 ja_status jagged_gdpa_bwd(const ja_problem *p, const void *q, const void *k, const void *v, const void *dout, void *dq,
-                          void *dk, void *dv, void *workspace, size_t workspace_bytes, void *stream) {
-    return run_bwd(p, 0, q, k, v, nullptr, nullptr, dout, nullptr, dq, dk, dv, workspace, workspace_bytes, stream);
+                          void *dk, void *dv, float *dbias, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_bwd(p, 0, q, k, v, nullptr, nullptr, dout, nullptr, dq, dk, dv, dbias, workspace, workspace_bytes,
+                   stream);
 }
 
 ja_status jagged_attn_bwd(const ja_problem *p, const void *q, const void *k, const void *v, const void *o,
                           const void *o_residual, const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                          void *workspace, size_t workspace_bytes, void *stream) {
-    return run_bwd(p, 1, q, k, v, o, o_residual, dout, lse, dq, dk, dv, workspace, workspace_bytes, stream);
+                          float *dbias, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_bwd(p, 1, q, k, v, o, o_residual, dout, lse, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
 }
 
 const char *ja_status_string(int status) {

@@ -1,0 +1,263 @@
+// Gradient of the attention bias table (bf16 in, fp32 accumulate) on gfx950.
+//
+// The bias enters the scores additively, X = scale QK^T + bias, so the
+// gradient of a table entry is the sum of dX over the (query, key) pairs that
+// read it: REL entries collect the diagonals i - j of dX, KEYPOS entries its
+// columns j, clamped into [lo, hi].  The pages list custom attention biases
+// among what the jagged kernels support ("GEM Training: How Meta Doubled the
+// Efficiency...", section "What happened"); their gradient is not described
+// there, so this is the plain derivative of that additive term.
+//
+// One pass over (sample, 128-query tile, head) units recomputes S = QK^T and
+// dP = dO V^T per 64-key tile on the matrix cores (as the dQ units do) and
+// forms dX; each wave then stages its 32 x 32 blocks of dX in LDS and sums
+// them along diagonals (REL) or columns (KEYPOS) into its own row of per-entry
+// sums in LDS.  The result is deterministic: the grid is fixed (DBIAS_GRID
+// workgroups), workgroup g takes units g, g + G, g + 2G, ... in order, and
+// units are numbered head-major, so each workgroup sees every head in one
+// contiguous run; when its head changes it adds its four wave rows in a fixed
+// order and writes one partial row per (workgroup, head).  A second kernel
+// adds the G partial rows of each head in workgroup order.  No atomics.
+#include "ja_device.h"
+#include "ja_kernels.h"
+#include "ja_tiles.h"
+
+namespace ja {
+
+constexpr int DBIAS_THREADS = 256;
+constexpr int SCR_STRIDE = 33;  // floats per row of a wave's 32 x 32 staging block (odd: no bank conflicts)
+
+// Sum of v over the 64 lanes, the same butterfly order on every call.
+__device__ __forceinline__ float wave_sum_fixed(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+template <int D, int MODE, int ACT>
+__global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParams p) {
+    constexpr int BN = KV_TILE;
+    constexpr int BM = Q_TILE;
+    constexpr int TILE_BYTES = BN * D * 2;
+    constexpr int NKK = D / 16, NNB = BN / 32;
+    constexpr int WIN = BM + BN - 1;
+    static_assert(WIN <= DBIAS_THREADS, "one bias window entry per thread");
+    __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
+    __shared__ float s_bias[2][WIN];
+    __shared__ float s_bins[4][DBIAS_MAX_BINS];
+    __shared__ float s_scr[4][32 * SCR_STRIDE];
+    lchar *const lbase = (lchar *)smem;
+
+    const int H = p.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
+    const int W = bz.width;
+    const int n_units = p.counters4->units;
+    float *bins = s_bins[wv];
+    float *scr = s_scr[wv];
+    for (int c = tid; c < 4 * DBIAS_MAX_BINS; c += DBIAS_THREADS) (&s_bins[0][0])[c] = 0.0f;
+
+    // Partial row (workgroup, head hh) of the output sums.
+    auto part_row = [&](int hh) { return p.dbias_part + ((int64_t)blockIdx.x * H + hh) * W; };
+    // Write this workgroup's sums for head hh (the four wave rows added in
+    // order) and clear them; heads strictly between hh and h_next get zero rows.
+    auto flush = [&](int hh, int h_next) {
+        __syncthreads();
+        if (hh >= 0) {
+            float *row = part_row(hh);
+            for (int c = tid; c < W; c += DBIAS_THREADS) {
+                row[c] = ((s_bins[0][c] + s_bins[1][c]) + s_bins[2][c]) + s_bins[3][c];
+                s_bins[0][c] = s_bins[1][c] = s_bins[2][c] = s_bins[3][c] = 0.0f;
+            }
+        }
+        for (int z = hh + 1; z < h_next; ++z) {
+            float *row = part_row(z);
+            for (int c = tid; c < W; c += DBIAS_THREADS) row[c] = 0.0f;
+        }
+        __syncthreads();
+    };
+
+    int h_cur = -1;
+    for (int w = blockIdx.x; w < n_units; w += gridDim.x) {
+        const UnitRef u = tile_unit(p.tiles4, w, n_units, H);
+        const int2 tile = u.tile;
+        const int h = u.h;
+        if (h != h_cur) {
+            flush(h_cur, h);
+            h_cur = h;
+        }
+        const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
+        const int i0 = tile.y * BM;
+        const int iw = i0 + wv * 32;
+        const int irow = iw + l32;
+        const bool row_ok = irow < s.lq;
+        const int i_last = (i0 + BM < s.lq ? i0 + BM : s.lq) - 1;
+        const int nkv = (key_end(i_last, s.lq, s.lk, p.causal) + BN - 1) / BN;
+        const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h), Gs(p.dout, s.qs, s.lq, H, h);
+        const HeadSlice<D> Ks(p.k, s.ks, s.lk, H, h), Vs(p.v, s.ks, s.lk, H, h);
+        const rsrc_t brs = make_rsrc(bz.table + (int64_t)h * W, (uint32_t)W * 4u);
+
+        bf16x8 qreg[NKK], greg[NKK];
+        load_row_operand<D>(qreg, Qs, irow, g);
+        load_row_operand<D>(greg, Gs, irow, g);
+        float lse2 = 0.0f, dlt = 0.0f;
+        if constexpr (MODE == JFA) {
+            const uint32_t off = (uint32_t)irow * 4u;  // rows past the sample read zeros
+            const rsrc_t lr = make_rsrc(p.lse + (int64_t)h * p.total_q + s.qs, (uint32_t)s.lq * 4u);
+            const rsrc_t dr = make_rsrc(p.delta + (int64_t)h * p.total_q + s.qs, (uint32_t)s.lq * 4u);
+            lse2 = buf_load_f32(lr, off) * LOG2E;
+            dlt = buf_load_f32(dr, off);
+        }
+        const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
+
+        // Key / value tile jt is copied straight into LDS buffer (jt & 1); the
+        // bias window (JFA: in log2 units) goes through a register.
+        float bnext = 0.0f;
+        auto load_tile = [&](int jt) {
+            lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
+            dma_tile<BN, D, DBIAS_THREADS>(kt, Ks, jt * BN, tid);
+            dma_tile<BN, D, DBIAS_THREADS>(kt + TILE_BYTES, Vs, jt * BN, tid);
+            const int bi = bias_stage_rowmajor(bz, i0, BM, jt * BN, BN, tid);
+            bnext = buf_load_f32(brs, bi >= 0 ? (uint32_t)bi * 4u : OOB);
+        };
+        auto store_tile = [&](int buf) {
+            if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tile has landed
+        };
+        load_tile(0);
+        store_tile(0);
+        __syncthreads();
+        const float sl = MODE == JFA ? p.scale * LOG2E : p.scale;
+        const float nl = -lse2;
+
+        for (int jt = 0; jt < nkv; ++jt) {
+            const int j0 = jt * BN;
+            const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
+            const lchar *Vt = Kt + TILE_BYTES;
+            const float *bwin = s_bias[jt & 1];
+            load_tile(jt + 1);  // past the last tile: zeros, no traffic
+            __builtin_amdgcn_sched_barrier(0);
+
+            // Wave-uniform: does this tile cross the key end, the diagonal or the query end?
+            const bool masked = (j0 + BN > s.lk) | (p.causal && (j0 + BN - 1 > iw + s.lk - s.lq)) | (iw + 32 > s.lq);
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb) {
+                f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const int off = lds_off<D>(nb * 32 + l32, 2 * kk + g);
+                    sacc = mfma32(lds_read16(Kt, off), qreg[kk], sacc);
+                    dpacc = mfma32(lds_read16(Vt, off), greg[kk], dpacc);
+                }
+                // raw window: entry (i0 + BM - 1 - irow) + (j - j0) (REL) or j - j0 (KEYPOS)
+                const int bbase = (bz.kind == BIAS_REL ? BM - 1 - wv * 32 - l32 : 0) + g * 4 + nb * 32;
+                float dx[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float x = __builtin_fmaf(sacc[e], sl, bwin[bbase + (e >> 2) * 8 + (e & 3)]);
+                    if constexpr (MODE == JFA) {
+                        dx[e] = fast_exp2(x + nl) * (dpacc[e] - dlt);
+                    } else {
+                        float y, dy;
+                        act_fwd_grad<ACT>(x, y, dy);
+                        dx[e] = dpacc[e] * dy;
+                    }
+                }
+                if (masked) {
+                    // invalid pairs (and rows without a visible key, LSE = -inf) give nothing
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        dx[e] = (row_ok & (j0 + nb * 32 + crow(e, g) < my_kend)) ? dx[e] : 0.0f;
+                }
+
+                // Stage the 32 x 32 block (row irow - iw = l32, key crow(e, g)) and
+                // sum it along one line per lane.
+#pragma unroll
+                for (int e = 0; e < 16; ++e) scr[l32 * SCR_STRIDE + crow(e, g)] = dx[e];
+                lds_wave_sync();
+                const int jb = j0 + nb * 32;  // first key of the block
+                float v = 0.0f;
+                int pos;  // table position of this lane's line
+                bool line = true;
+                if (bz.kind == BIAS_REL) {
+                    // lane d < 63 sums the diagonal r - c = d - 31 of the block
+                    const int dl = lane - 31;
+#pragma unroll
+                    for (int r = 0; r < 32; ++r) {
+                        const int c = r - dl;
+                        if (c >= 0 && c < 32) v += scr[r * SCR_STRIDE + c];
+                    }
+                    pos = iw - jb + dl;
+                    line = lane < 63;
+                } else {
+                    // lane c < 32 sums column c (key jb + c) over the block's rows
+                    const int c = lane & 31;
+#pragma unroll
+                    for (int r = 0; r < 32; ++r) v += scr[r * SCR_STRIDE + c];
+                    pos = jb + c;
+                    line = lane < 32;
+                }
+                lds_wave_sync();  // the block's reads are done before the next block's writes
+                v = line ? v : 0.0f;
+                const int bin = clampi(pos, bz.lo, bz.hi) - bz.lo;
+                // Lines of distinct positions hit distinct interior entries; the two
+                // end entries collect every clamped line, summed across the wave first.
+                const float lo_sum = wave_sum_fixed(line && bin == 0 ? v : 0.0f);
+                const float hi_sum = wave_sum_fixed(line && bin == W - 1 && bin != 0 ? v : 0.0f);
+                if (line && bin > 0 && bin < W - 1) bins[bin] += v;
+                if (lane == 0) {
+                    bins[0] += lo_sum;
+                    if (W > 1) bins[W - 1] += hi_sum;
+                }
+            }
+            store_tile((jt + 1) & 1);
+            __syncthreads();
+        }
+    }
+    flush(h_cur, H);
+}
+
+// dbias[h][c] = sum over workgroups g (in order) of partial row (g, h), entry c.
+__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *part, float *out, int H, int W, int G) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)H * W) return;
+    const int h = (int)(idx / W), c = (int)(idx % W);
+    float s = 0.0f;
+    for (int gi = 0; gi < G; ++gi) s += part[((int64_t)gi * H + h) * W + c];
+    out[idx] = s;
+}
+
+template <int D, int MODE, int ACT>
+static hipError_t launch_dbias_t(const AttnParams &p, hipStream_t st) {
+    const int W = p.bias_hi - p.bias_lo + 1;
+    const int64_t n = (int64_t)p.H * W;
+    const KernelTimer &t = kernel_timer();
+    t.begin(K_BWD_DBIAS, st);
+    hipLaunchKernelGGL((dbias_kernel<D, MODE, ACT>), dim3(DBIAS_GRID), dim3(DBIAS_THREADS), 0, st, p);
+    hipLaunchKernelGGL(dbias_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float *)p.dbias_part, p.dbias, p.H, W, DBIAS_GRID);
+    t.end(K_BWD_DBIAS, st);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dbias_d(const AttnParams &p, int mode, int act, hipStream_t st) {
+    if (mode == JFA) return launch_dbias_t<D, JFA, SILU>(p, st);
+    switch (act) {
+    case SILU: return launch_dbias_t<D, GDPA, SILU>(p, st);
+    case GELU_TANH: return launch_dbias_t<D, GDPA, GELU_TANH>(p, st);
+    default: return launch_dbias_t<D, GDPA, GELU_ERF>(p, st);
+    }
+}
+
+hipError_t launch_dbias_bf16(const AttnParams &p, int D, int mode, int act, hipStream_t st) {
+    switch (D) {
+    case 32: return launch_dbias_d<32>(p, mode, act, st);
+    case 64: return launch_dbias_d<64>(p, mode, act, st);
+    default: return launch_dbias_d<128>(p, mode, act, st);
+    }
+}
+
+}  // namespace ja

@@ -205,6 +205,58 @@ __global__ __launch_bounds__(F32_THREADS) void dkdv_f32_kernel(const AttnParams 
     }
 }
 
+// Gradient of the bias table: one thread per (head, table entry c) adds dX of
+// every valid pair that reads entry c, sample by sample in order.  An interior
+// entry is one relative position (REL: i - j = lo + c) or one key (KEYPOS:
+// j = lo + c), so only those pairs are visited; the two end entries also take
+// every clamped position and scan the pairs beyond them.
+template <int D, int MODE, int ACT>
+__global__ __launch_bounds__(F32_THREADS) void dbias_f32_kernel(const AttnParams p) {
+    const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
+    const int64_t gid = (int64_t)blockIdx.x * F32_THREADS + threadIdx.x;
+    if (gid >= (int64_t)p.H * bz.width) return;
+    const int h = (int)(gid / bz.width), c = (int)(gid % bz.width);
+    const float *brow = bz.table + (int64_t)h * bz.width;
+    const float *Q = static_cast<const float *>(p.q);
+    const float *K = static_cast<const float *>(p.k);
+    const float *V = static_cast<const float *>(p.v);
+    const float *G = static_cast<const float *>(p.dout);
+    const bool first = c == 0, last = c == bz.width - 1;
+    const int target = bz.lo + c;  // position read by entry c when not clamped
+    float acc = 0.0f;
+    for (int b = 0; b < p.B; ++b) {
+        const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, b);
+        for (int i = 0; i < s.lq; ++i) {
+            const int64_t r = s.qs + i;
+            const float *qi = Q + (r * p.H + h) * (int64_t)D;
+            const float *gi = G + (r * p.H + h) * (int64_t)D;
+            const int kend = key_end(i, s.lq, s.lk, p.causal);
+            // keys of row i whose position maps to entry c: [ja, jb)
+            int ja = 0, jb = kend;
+            if (bz.kind == BIAS_REL) {  // position i - j
+                if (!last) ja = i - target;              // i - j <= target
+                if (!first) jb = min(jb, i - target + 1);  // i - j >= target
+            } else {                    // position j
+                if (!first) ja = target;
+                if (!last) jb = min(jb, target + 1);
+            }
+            ja = ja < 0 ? 0 : ja;
+            for (int j = ja; j < jb; ++j) {
+                const float *kj = K + ((s.ks + j) * p.H + h) * (int64_t)D;
+                const float *vj = V + ((s.ks + j) * p.H + h) * (int64_t)D;
+                const float x = p.scale * dot_f32(qi, kj, D) + bias_at(bz, brow, i, j);
+                const float dp = dot_f32(gi, vj, D);
+                if constexpr (MODE == GDPA) {
+                    acc += dp * act_grad_f32<ACT>(x);
+                } else {
+                    acc += expf(x - p.lse[(int64_t)h * p.total_q + r]) * (dp - p.delta[(int64_t)h * p.total_q + r]);
+                }
+            }
+        }
+    }
+    p.dbias[gid] = acc;
+}
+
 static inline unsigned grid_for(int64_t n) { return (unsigned)((n + F32_THREADS - 1) / F32_THREADS); }
 
 template <int D, int MODE, int ACT>
@@ -232,6 +284,12 @@ static hipError_t bwd_f32_t(const AttnParams &p, hipStream_t st) {
     t.begin(K_BWD_KV, st);
     if (nk > 0) hipLaunchKernelGGL((dkdv_f32_kernel<D, MODE, ACT>), dim3(grid_for(nk)), dim3(F32_THREADS), 0, st, p);
     t.end(K_BWD_KV, st);
+    if (p.dbias) {
+        const int64_t nb = (int64_t)p.H * (p.bias_hi - p.bias_lo + 1);
+        t.begin(K_BWD_DBIAS, st);
+        hipLaunchKernelGGL((dbias_f32_kernel<D, MODE, ACT>), dim3(grid_for(nb)), dim3(F32_THREADS), 0, st, p);
+        t.end(K_BWD_DBIAS, st);
+    }
     return hipGetLastError();
 }
 

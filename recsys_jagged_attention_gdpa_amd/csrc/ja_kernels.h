@@ -14,6 +14,8 @@ constexpr int KV_TILE = 64;
 constexpr int BWD_KV_UNIT = 128;   // keys owned by one dK/dV unit
 constexpr int BWD_Q_STEP = 128;    // queries per inner step of a dK/dV unit
 constexpr int FUSED_MAX_LK = 32;   // samples with at most this many keys use the fused backward unit
+constexpr int DBIAS_GRID = 256;    // workgroups of the bias-gradient pass (fixed: fixes the summation order)
+constexpr int DBIAS_MAX_BINS = 4096;  // largest bias table row the gradient pass takes
 
 // The chip's accelerator dies (XCDs), each with its own L2.
 constexpr int XCDS = 8;
@@ -74,6 +76,10 @@ struct AttnParams {
     PlanCounters *counters2;
     const int2 *tiles3;       // backward: fused short-K/V units
     PlanCounters *counters3;
+    const int2 *tiles4;       // bias gradient: query tiles of every sample
+    PlanCounters *counters4;
+    float *dbias;             // bias gradient output [H][hi - lo + 1], or NULL
+    float *dbias_part;        // bias gradient partial rows [DBIAS_GRID][H][hi - lo + 1]
 };
 
 // Units of the tile lists (PLAN_Q_TILES, PLAN_KV_TILES) are numbered
@@ -109,14 +115,17 @@ __device__ __forceinline__ int next_tile_unit(PlanCounters *c, int n_units, int 
 }
 
 // Plans up to PLAN_MAX lists in one launch (one workgroup per list).
-constexpr int PLAN_MAX = 3;
+constexpr int PLAN_MAX = 4;
 struct PlanBatch {
     PlanParams list[PLAN_MAX];
 };
 hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream);
 
 // Optional per-kernel event recording around launches (measurement aid).
-enum KernelId { K_PLAN = 0, K_FWD = 1, K_BWD_FUSED = 2, K_BWD_KV = 3, K_BWD_Q = 4, K_BWD_DELTA = 5, K_FWD_SHORT = 6 };
+enum KernelId {
+    K_PLAN = 0, K_FWD = 1, K_BWD_FUSED = 2, K_BWD_KV = 3, K_BWD_Q = 4, K_BWD_DELTA = 5, K_FWD_SHORT = 6,
+    K_BWD_DBIAS = 7
+};
 struct KernelTimer {
     int which = -1;
     hipEvent_t start = nullptr, stop = nullptr;
@@ -139,6 +148,8 @@ hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cu
                            hipStream_t stream);
 hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, bool long_units,
                            hipStream_t stream);
+// Bias-table gradient (p.dbias, p.dbias_part, p.tiles4 / p.counters4 planned).
+hipError_t launch_dbias_bf16(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
 hipError_t launch_fwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
 hipError_t launch_bwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
 

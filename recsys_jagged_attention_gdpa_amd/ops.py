@@ -75,26 +75,40 @@ def attn_forward(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bi
     return o, lse, o_res
 
 
+def _dbias_out(p, bias, with_dbias):
+    """Bias-gradient output [H, hi - lo + 1] and the workspace pass that goes with it."""
+    if not with_dbias:
+        return None, _lib.PASS_BWD
+    if bias is None:
+        raise ValueError("with_dbias needs a bias table")
+    return torch.empty_like(bias), _lib.PASS_BWD_DBIAS
+
+
 def gdpa_backward(q, k, v, dout, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False,
-                  bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0):
+                  bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, with_dbias=False):
+    """(dQ, dK, dV), plus the bias table's gradient last when with_dbias."""
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act=act, bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = _workspace(p, _lib.PASS_BWD, q.device)
-    _lib.jagged_gdpa_bwd(p, q, k, v, dout.contiguous(), dq, dk, dv, ws)
-    return dq, dk, dv
+    db, pass_ = _dbias_out(p, bias, with_dbias)
+    ws = _workspace(p, pass_, q.device)
+    _lib.jagged_gdpa_bwd(p, q, k, v, dout.contiguous(), dq, dk, dv, db, ws)
+    return (dq, dk, dv, db) if with_dbias else (dq, dk, dv)
 
 
 def attn_backward(q, k, v, o, dout, lse, q_offsets, kv_offsets, *, o_residual=None, scale=None,
-                  causal=False, bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0):
+                  causal=False, bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0,
+                  with_dbias=False):
+    """(dQ, dK, dV), plus the bias table's gradient last when with_dbias."""
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act="silu", bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = _workspace(p, _lib.PASS_BWD, q.device)
-    _lib.jagged_attn_bwd(p, q, k, v, o, o_residual, dout.contiguous(), lse, dq, dk, dv, ws)
-    return dq, dk, dv
+    db, pass_ = _dbias_out(p, bias, with_dbias)
+    ws = _workspace(p, pass_, q.device)
+    _lib.jagged_attn_bwd(p, q, k, v, o, o_residual, dout.contiguous(), lse, dq, dk, dv, db, ws)
+    return (dq, dk, dv, db) if with_dbias else (dq, dk, dv)
 
 
 class _GDPAFunction(torch.autograd.Function):
@@ -110,8 +124,10 @@ class _GDPAFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do):
         q, k, v, q_offsets, kv_offsets = ctx.saved_tensors
-        dq, dk, dv = gdpa_backward(q, k, v, do, q_offsets, kv_offsets, **ctx.kw)
-        return dq, dk, dv, None, None, None, None, None, None, None, None, None, None
+        want_db = ctx.needs_input_grad[8]  # the bias table
+        g = gdpa_backward(q, k, v, do, q_offsets, kv_offsets, with_dbias=want_db, **ctx.kw)
+        db = g[3] if want_db else None
+        return g[0], g[1], g[2], None, None, None, None, None, db, None, None, None, None
 
 
 class _JFAFunction(torch.autograd.Function):
@@ -128,20 +144,24 @@ class _JFAFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse, o_res, q_offsets, kv_offsets = ctx.saved_tensors
-        dq, dk, dv = attn_backward(q, k, v, o, do, lse, q_offsets, kv_offsets, o_residual=o_res,
-                                   **ctx.kw)
-        return dq, dk, dv, None, None, None, None, None, None, None, None, None
+        want_db = ctx.needs_input_grad[7]  # the bias table
+        g = attn_backward(q, k, v, o, do, lse, q_offsets, kv_offsets, o_residual=o_res,
+                          with_dbias=want_db, **ctx.kw)
+        db = g[3] if want_db else None
+        return g[0], g[1], g[2], None, None, None, None, db, None, None, None, None
 
 
 def gdpa(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False, bias=None,
          bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0):
-    """Jagged GDPA with autograd (backward needs per-sample query offsets)."""
+    """Jagged GDPA with autograd (backward needs per-sample query offsets; a bias table
+    that requires grad gets its gradient)."""
     return _GDPAFunction.apply(q, k, v, q_offsets, kv_offsets, act, scale, causal, bias,
                                bias_kind, bias_lo, bias_hi, max_kv_len)
 
 
 def jagged_attention(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bias=None,
                      bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0):
-    """Jagged flash attention (softmax) with autograd."""
+    """Jagged flash attention (softmax) with autograd (a bias table that requires grad gets
+    its gradient)."""
     return _JFAFunction.apply(q, k, v, q_offsets, kv_offsets, scale, causal, bias, bias_kind,
                               bias_lo, bias_hi, max_kv_len)

@@ -103,7 +103,38 @@ def test_null_tensors_and_workspace_errors():
                                ctypes.c_size_t(64), None) == 4
     # backward needs per-sample query offsets and every gradient buffer
     ps = _problem(q_offsets=None, lq_fixed=10, total_q=10)
-    assert lib.jagged_gdpa_bwd(ctypes.byref(ps), P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(0x100), ws, None) == 3
-    assert lib.jagged_gdpa_bwd(ctypes.byref(p), P(1), P(2), P(3), P(4), None, P(6), P(7), P(0x100), ws, None) == 1
+    assert lib.jagged_gdpa_bwd(ctypes.byref(ps), P(1), P(2), P(3), P(4), P(5), P(6), P(7), None, P(0x100), ws,
+                               None) == 3
+    assert lib.jagged_gdpa_bwd(ctypes.byref(p), P(1), P(2), P(3), P(4), None, P(6), P(7), None, P(0x100), ws,
+                               None) == 1
     assert lib.jagged_attn_bwd(ctypes.byref(p), P(1), P(2), P(3), None, None, P(4), P(5), P(6), P(7),
-                               P(8), P(0x100), ws, None) == 1
+                               P(8), None, P(0x100), ws, None) == 1
+
+
+def test_bias_gradient_arguments():
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    rel = _problem(bias_kind="rel", bias_table=0x3000, bias_lo=-40, bias_hi=40)
+    nob = _problem()
+    n1 = lib.ja_workspace_size(ctypes.byref(rel), _lib.PASS_BWD)
+    n2 = lib.ja_workspace_size(ctypes.byref(rel), _lib.PASS_BWD_DBIAS)
+    assert n2 > n1 > 0 and n2 % 256 == 0
+    assert lib.ja_workspace_size(ctypes.byref(nob), _lib.PASS_BWD_DBIAS) == 0  # no table, no gradient
+    wide = _problem(bias_kind="keypos", bias_table=0x3000, bias_lo=0, bias_hi=4096)  # 4097 entries
+    assert lib.ja_workspace_size(ctypes.byref(wide), _lib.PASS_BWD_DBIAS) == 0
+    ok = _problem(bias_kind="keypos", bias_table=0x3000, bias_lo=0, bias_hi=4095)
+    assert lib.ja_workspace_size(ctypes.byref(ok), _lib.PASS_BWD_DBIAS) > 0
+
+    def gdpa(prob, db, nbytes):
+        return lib.jagged_gdpa_bwd(ctypes.byref(prob), P(1), P(2), P(3), P(4), P(5), P(6), P(7), db, P(0x100),
+                                   ctypes.c_size_t(nbytes), None)
+
+    def jfa(prob, db, nbytes):
+        return lib.jagged_attn_bwd(ctypes.byref(prob), P(1), P(2), P(3), P(9), None, P(4), P(5), P(6), P(7),
+                                   P(8), db, P(0x100), ctypes.c_size_t(nbytes), None)
+
+    for fn in (gdpa, jfa):
+        assert fn(nob, P(0x500), 1 << 30) == 3         # gradient of a table that does not exist
+        assert fn(wide, P(0x500), 1 << 30) == 3        # row too long for the gradient pass
+        assert fn(rel, P(0x500), n1) == 4              # workspace sized for the plain backward
+        assert fn(rel, P(0x500), n2 - 1) == 4

@@ -465,6 +465,51 @@ int ref_attn_dbias(const float *q, const float *k, const float *v, const float *
     return run_dbias(&p, 1, dout, dtable, nthreads);
 }
 
+/* One entry c of head h of the GDPA table gradient, summed sample by sample.
+ * An interior entry is read by one relative position (REL: j = i - (lo + c))
+ * or one key (KEYPOS: j = lo + c) per query row, so only those pairs are
+ * visited; the end entries (c = 0 or c = hi - lo) scan every pair of a row. */
+int ref_gdpa_dbias_entry(const float *q, const float *k, const float *v, const float *dout,
+                         double *out, const int32_t *q_off, const int32_t *kv_off, int B, int H,
+                         int D, double scale, int act, int causal, int bias_kind,
+                         const float *bias_table, int bias_lo, int bias_hi, int h, int c,
+                         int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, bias_kind,
+                             bias_table, bias_lo, bias_hi);
+    const int64_t W = (int64_t)bias_hi - bias_lo + 1;
+    if (!q_off || p.bias_kind == BIAS_NONE || h < 0 || h >= H || c < 0 || c >= W) return 1;
+    const int interior = c > 0 && c < W - 1;
+    double *per_b = (double *)calloc((size_t)(B > 0 ? B : 1), sizeof(double));
+    if (!per_b) return 2;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads_or_default(nthreads))
+    for (int b = 0; b < B; ++b) {
+        sample s = sample_rows(&p, b);
+        double acc = 0.0;
+        for (int64_t i = 0; i < s.lq; ++i) {
+            const float *doi = row_of(&p, dout, s.qs + i, h);
+            int64_t j0 = 0, j1 = s.lk;
+            if (interior) {
+                j0 = p.bias_kind == BIAS_REL ? i - (bias_lo + c) : (int64_t)bias_lo + c;
+                j1 = j0 + 1;
+            }
+            for (int64_t j = j0 < 0 ? 0 : j0; j < j1 && j < s.lk; ++j) {
+                if (!is_valid(&p, i, j, s.lq, s.lk)) continue;
+                const int64_t pos = p.bias_kind == BIAS_REL ? i - j : j;
+                if (clampi(pos, bias_lo, bias_hi) - bias_lo != c) continue;
+                double w, dx;
+                pair_bwd(&p, 0, h, &s, i, j, doi, 0.0, 1.0, 0.0, &w, &dx);
+                acc += dx;
+            }
+        }
+        per_b[b] = acc;
+    }
+    double tot = 0.0;
+    for (int b = 0; b < B; ++b) tot += per_b[b];
+    *out = tot;
+    free(per_b);
+    return 0;
+}
+
 /* Element-wise activation and derivative, exported so the tests can pin them
  * against library implementations. */
 void ref_act(int act, const double *x, double *y, double *dy, int64_t n) {

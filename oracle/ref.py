@@ -47,10 +47,13 @@ def _load():
         lib.ref_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, D, I, I, P, I, I, I]
         lib.ref_gdpa_dbias.argtypes = [P, P, P, P, P, P, P, I, I, I, D, I, I, I, P, I, I, I]
         lib.ref_attn_dbias.argtypes = [P, P, P, P, P, P, P, I, I, I, D, I, I, P, I, I, I]
+        lib.ref_gdpa_dbias_entry.argtypes = [P, P, P, P, P, P, P, I, I, I, D, I, I, I, P, I, I, I, I,
+                                             I]
         lib.ref_act.argtypes = [I, P, P, P, ctypes.c_int64]
         lib.ref_max_threads.argtypes = []
         for f in (lib.ref_gdpa_fwd, lib.ref_attn_fwd, lib.ref_gdpa_bwd, lib.ref_attn_bwd,
-                  lib.ref_gdpa_dbias, lib.ref_attn_dbias, lib.ref_max_threads):
+                  lib.ref_gdpa_dbias, lib.ref_attn_dbias, lib.ref_gdpa_dbias_entry,
+                  lib.ref_max_threads):
             f.restype = ctypes.c_int
         lib.ref_act.restype = None
         _lib = lib
@@ -192,6 +195,20 @@ def attn_dbias(q, k, v, dout, q_off, kv_off, *, scale, causal=False, bias_kind, 
     """JFA: dL/dtable [H, hi - lo + 1] of L = <O, dout> (float64)."""
     return _dbias(_load().ref_attn_dbias, False, q, k, v, dout, q_off, kv_off, scale, None, causal,
                   bias_kind, bias_table, bias_lo, bias_hi, nthreads)
+
+
+def gdpa_dbias_entry(q, k, v, dout, q_off, kv_off, *, scale, act, causal=False, bias_kind,
+                     bias_table, bias_lo, bias_hi, h, c, nthreads=0):
+    """One entry (head h, index c) of the GDPA table gradient, in float64."""
+    a = _Args(q, k, v, q_off, kv_off, 0, bias_kind, bias_table, bias_lo, bias_hi)
+    do = _f32(dout)
+    out = np.zeros(1, dtype=np.float64)
+    rc = _load().ref_gdpa_dbias_entry(_ptr(a.q), _ptr(a.k), _ptr(a.v), _ptr(do), _ptr(out),
+                                      _ptr(a.q_off), _ptr(a.kv_off), a.B, a.H, a.D, float(scale),
+                                      ACTS[act], int(causal), a.bias_kind, _ptr(a.bias_table),
+                                      a.bias_lo, a.bias_hi, int(h), int(c), int(nthreads))
+    assert rc == 0, rc
+    return float(out[0])
 
 
 def act(name, x):

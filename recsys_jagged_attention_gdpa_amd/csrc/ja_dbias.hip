@@ -12,12 +12,16 @@
 // dP = dO V^T per 64-key tile on the matrix cores (as the dQ units do) and
 // forms dX; each wave then stages its 32 x 32 blocks of dX in LDS and sums
 // them along diagonals (REL) or columns (KEYPOS) into its own row of per-entry
-// sums in LDS.  The result is deterministic: the grid is fixed (DBIAS_GRID
-// workgroups), workgroup g takes units g, g + G, g + 2G, ... in order, and
-// units are numbered head-major, so each workgroup sees every head in one
-// contiguous run; when its head changes it adds its four wave rows in a fixed
-// order and writes one partial row per (workgroup, head).  A second kernel
-// adds the G partial rows of each head in workgroup order.  No atomics.
+// sums in LDS.  Blocks whose positions all clamp to one end of the table (far
+// from the diagonal, the common case on long samples) skip the staging: their
+// dX only adds into a per-lane register, reduced once per unit.
+//
+// The result is deterministic: the grid is fixed (DBIAS_GRID workgroups),
+// workgroup g takes units g, g + G, g + 2G, ... in order, and units are
+// numbered head-major, so each workgroup sees every head in one contiguous
+// run; when its head changes it adds its four wave rows in a fixed order and
+// writes one partial row per (workgroup, head).  A second kernel adds the G
+// partial rows of each head in workgroup order.  No atomics.
 #include "ja_device.h"
 #include "ja_kernels.h"
 #include "ja_tiles.h"
@@ -111,6 +115,7 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
             dlt = buf_load_f32(dr, off);
         }
         const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
+        float acc_lo = 0.0f, acc_hi = 0.0f;  // this lane's dX of blocks clamped whole to an end entry
 
         // Key / value tile jt is copied straight into LDS buffer (jt & 1); the
         // bias window (JFA: in log2 units) goes through a register.
@@ -172,12 +177,26 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
                         dx[e] = (row_ok & (j0 + nb * 32 + crow(e, g) < my_kend)) ? dx[e] : 0.0f;
                 }
 
+                const int jb = j0 + nb * 32;  // first key of the block
+                // Positions the block covers (wave-uniform).  A block whose every
+                // position clamps to one end entry only adds into a register.
+                const int pmin = bz.kind == BIAS_REL ? iw - jb - 31 : jb;
+                const int pmax = bz.kind == BIAS_REL ? iw - jb + 31 : jb + 31;
+                if (pmax <= bz.lo) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc_lo += dx[e];
+                    continue;
+                }
+                if (pmin >= bz.hi) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc_hi += dx[e];
+                    continue;
+                }
                 // Stage the 32 x 32 block (row irow - iw = l32, key crow(e, g)) and
                 // sum it along one line per lane.
 #pragma unroll
                 for (int e = 0; e < 16; ++e) scr[l32 * SCR_STRIDE + crow(e, g)] = dx[e];
                 lds_wave_sync();
-                const int jb = j0 + nb * 32;  // first key of the block
                 float v = 0.0f;
                 int pos;  // table position of this lane's line
                 bool line = true;
@@ -214,6 +233,13 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
             }
             store_tile((jt + 1) & 1);
             __syncthreads();
+        }
+        {
+            const float lo_sum = wave_sum_fixed(acc_lo), hi_sum = wave_sum_fixed(acc_hi);
+            if (lane == 0) {
+                bins[0] += lo_sum;
+                bins[W - 1] += hi_sum;
+            }
         }
     }
     flush(h_cur, H);

@@ -77,3 +77,45 @@ def test_full_size_sampled_slices(name, n_random):
                           zero_rows=z, abs_floor=softmax_grad_floor(ws, nm))
         announce(f"full-size {name}: slice b={b} (Lq={int(ws.lq[0])}, Lk={int(ws.lk[0])}) h={h} "
                  f"ok at {time.time() - t0:.1f}s")
+
+
+@pytest.mark.timeout(900)
+def test_full_size_bias_gradient_sampled_entries():
+    # The long-tail workload's backward with the bias-table gradient, whole batch,
+    # in the library's launch configuration.  The oracle recomputes sampled
+    # interior entries one by one (an interior entry is read by one relative
+    # position, so it costs one pass over the query rows); each is compared
+    # against tau times the largest sampled entry of its head.
+    from oracle import ref
+    t0 = time.time()
+    w = synth.make("longtail_gdpa")
+    announce(f"full-size dbias longtail_gdpa: B={w.B} H={w.H} Tq={w.total_q} bias [{w.bias_lo}, {w.bias_hi}]")
+    d = to_dev(w)
+    import recsys_jagged_attention_gdpa_amd as ja
+    g = ja.gdpa_backward(d["q"], d["k"], d["v"], d["dout"], d["q_off"], d["kv_off"], act=w.act,
+                         scale=w.scale, causal=w.causal, bias=d["bias"], bias_kind=w.bias_kind,
+                         bias_lo=w.bias_lo, bias_hi=w.bias_hi, with_dbias=True)
+    torch.cuda.synchronize()
+    db = np64(g[3])
+    del d, g
+    torch.cuda.empty_cache()
+    announce(f"full-size dbias: GPU done at {time.time() - t0:.1f}s")
+    assert np.isfinite(db).all()
+    W = w.bias_hi - w.bias_lo + 1
+    rng = np.random.default_rng(5)
+    for h in (0, int(rng.integers(1, w.H))):
+        positions = [w.bias_lo + 1, -200, -1, 0, 1, 100, w.bias_hi - 1]
+        got, want = [], []
+        for pos in positions:
+            c = pos - w.bias_lo
+            assert 0 < c < W - 1
+            want.append(ref.gdpa_dbias_entry(w.q, w.k, w.v, w.dout, w.q_off, w.kv_off, scale=w.scale,
+                                             act=w.act, causal=w.causal, bias_kind=w.bias_kind,
+                                             bias_table=w.bias_table, bias_lo=w.bias_lo,
+                                             bias_hi=w.bias_hi, h=h, c=c))
+            got.append(db[h, c])
+        got, want = np.array(got), np.array(want)
+        ratio = np.abs(got - want).max() / np.abs(want).max()
+        announce(f"full-size dbias head {h}: entries {positions} worst ratio {ratio:.2e} "
+                 f"({time.time() - t0:.1f}s)")
+        assert ratio <= TAU[w.dtype], (h, got, want)

@@ -104,3 +104,20 @@ def test_oracle_causal_with_fewer_keys_than_queries(mode):
     assert np.all(got["o"][:7] == 0.0)
     if mode == "jfa":
         assert np.all(np.isneginf(got["lse"][:7]))
+
+
+@pytest.mark.parametrize("bias,lo,hi", [("rel", -4, 6), ("keypos", 2, 9), ("rel", 0, 0)])
+def test_oracle_single_table_entry_matches_whole_gradient(bias, lo, hi):
+    # The one-entry routine (used on full-size batches) against the whole-table
+    # gradient, itself pinned to dense autograd above: every entry, both heads.
+    from oracle import ref
+    w = synth.custom(mode="gdpa", lq=[13, 0, 21, 1, 7], lk=[9, 4, 21, 1, 0], H=2, D=16,
+                     dtype=torch.float32, seed=21, act="gelu_tanh", causal=True, bias_kind=bias,
+                     bias_lo=lo, bias_hi=hi, bias_sigma=0.5)
+    whole = oracle_dbias(w)
+    for h in range(2):
+        for c in range(hi - lo + 1):
+            e = ref.gdpa_dbias_entry(w.q, w.k, w.v, w.dout, w.q_off, w.kv_off, scale=w.scale, act=w.act,
+                                     causal=True, bias_kind=bias, bias_table=w.bias_table, bias_lo=lo,
+                                     bias_hi=hi, h=h, c=c)
+            assert abs(e - whole[h, c]) <= 1e-12 * max(np.abs(whole).max(), 1e-30), (h, c)

@@ -20,6 +20,11 @@
  * indices i (query) and j (key):
  *   X[i][j]  = scale * <q_i, k_j> + bias(h, i, j)
  *   valid    = (j < Lk) and (not causal or j <= i + Lk - Lq)
+ *              and, with a window w > 0 (sliding-window attention, named on
+ *              "Meta redesigns AI training infrastructure...", section "Custom
+ *              Kernels and 5D Parallelism..."; the pages give no definition):
+ *              i' - j < w and (causal or j - i' < w), where i' = i + Lk - Lq
+ *              is the query's aligned position
  *   GDPA:  O_i = sum_{valid j} act(X_ij) v_j                 (no normalisation)
  *   JFA:   O_i = sum_{valid j} softmax_j(X_i.) v_j,  LSE_i = log sum_j exp X_ij
  *          (a row with no valid key: O_i = 0, LSE_i = -inf)
@@ -109,6 +114,7 @@ typedef struct {
     double scale;
     int act;
     int causal;
+    int window;
     int bias_kind;
     const float *bias_table;
     int bias_lo, bias_hi;
@@ -128,7 +134,10 @@ static double bias_at(const problem *p, int h, int64_t i, int64_t j) {
 
 static int is_valid(const problem *p, int64_t i, int64_t j, int64_t lq, int64_t lk) {
     if (j < 0 || j >= lk) return 0;
-    return !p->causal || j <= i + lk - lq;
+    const int64_t ia = i + lk - lq;  /* the query's position aligned to the keys */
+    if (p->causal && j > ia) return 0;
+    if (p->window > 0 && (ia - j >= p->window || (!p->causal && j - ia >= p->window))) return 0;
+    return 1;
 }
 
 typedef struct { int64_t qs, lq, ks, lk, o0; } sample;
@@ -265,11 +274,11 @@ static int nthreads_or_default(int nthreads) {
 
 static problem make_problem(const float *q, const float *k, const float *v, const int32_t *q_off,
                             int32_t lq_fixed, const int32_t *kv_off, int B, int H, int D, double scale,
-                            int act, int causal, int bias_kind, const float *bias_table, int bias_lo,
+                            int act, int causal, int window, int bias_kind, const float *bias_table, int bias_lo,
                             int bias_hi) {
     problem p;
     p.q = q; p.k = k; p.v = v; p.q_off = q_off; p.kv_off = kv_off; p.lq_fixed = lq_fixed;
-    p.B = B; p.H = H; p.D = D; p.scale = scale; p.act = act; p.causal = causal;
+    p.B = B; p.H = H; p.D = D; p.scale = scale; p.act = act; p.causal = causal; p.window = window;
     p.bias_kind = bias_table ? bias_kind : BIAS_NONE; p.bias_table = bias_table;
     p.bias_lo = bias_lo; p.bias_hi = bias_hi;
     return p;
@@ -409,9 +418,9 @@ static int run_dbias(const problem *p, int softmax, const float *dout, double *d
 
 int ref_gdpa_fwd(const float *q, const float *k, const float *v, double *o, const int32_t *q_off,
                  int32_t lq_fixed, const int32_t *kv_off, int B, int H, int D, double scale, int act,
-                 int causal, int bias_kind, const float *bias_table, int bias_lo, int bias_hi,
+                 int causal, int window, int bias_kind, const float *bias_table, int bias_lo, int bias_hi,
                  int nthreads) {
-    problem p = make_problem(q, k, v, q_off, lq_fixed, kv_off, B, H, D, scale, act, causal, bias_kind,
+    problem p = make_problem(q, k, v, q_off, lq_fixed, kv_off, B, H, D, scale, act, causal, window, bias_kind,
                              bias_table, bias_lo, bias_hi);
     run_fwd(&p, 0, o, NULL, nthreads);
     return 0;
@@ -420,9 +429,9 @@ int ref_gdpa_fwd(const float *q, const float *k, const float *v, double *o, cons
 /* lse: [total_q_out, H] (token-major, like the outputs). */
 int ref_attn_fwd(const float *q, const float *k, const float *v, double *o, double *lse,
                  const int32_t *q_off, int32_t lq_fixed, const int32_t *kv_off, int B, int H, int D,
-                 double scale, int causal, int bias_kind, const float *bias_table, int bias_lo,
+                 double scale, int causal, int window, int bias_kind, const float *bias_table, int bias_lo,
                  int bias_hi, int nthreads) {
-    problem p = make_problem(q, k, v, q_off, lq_fixed, kv_off, B, H, D, scale, ACT_SILU, causal,
+    problem p = make_problem(q, k, v, q_off, lq_fixed, kv_off, B, H, D, scale, ACT_SILU, causal, window,
                              bias_kind, bias_table, bias_lo, bias_hi);
     run_fwd(&p, 1, o, lse, nthreads);
     return 0;
@@ -430,18 +439,18 @@ int ref_attn_fwd(const float *q, const float *k, const float *v, double *o, doub
 
 int ref_gdpa_bwd(const float *q, const float *k, const float *v, const float *dout, double *dq,
                  double *dk, double *dv, const int32_t *q_off, const int32_t *kv_off, int B, int H,
-                 int D, double scale, int act, int causal, int bias_kind, const float *bias_table,
+                 int D, double scale, int act, int causal, int window, int bias_kind, const float *bias_table,
                  int bias_lo, int bias_hi, int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, bias_kind,
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, bias_kind,
                              bias_table, bias_lo, bias_hi);
     return run_bwd(&p, 0, dout, dq, dk, dv, nthreads);
 }
 
 int ref_attn_bwd(const float *q, const float *k, const float *v, const float *dout, double *dq,
                  double *dk, double *dv, const int32_t *q_off, const int32_t *kv_off, int B, int H,
-                 int D, double scale, int causal, int bias_kind, const float *bias_table, int bias_lo,
+                 int D, double scale, int causal, int window, int bias_kind, const float *bias_table, int bias_lo,
                  int bias_hi, int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, bias_kind,
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, window, bias_kind,
                              bias_table, bias_lo, bias_hi);
     return run_bwd(&p, 1, dout, dq, dk, dv, nthreads);
 }
@@ -449,18 +458,18 @@ int ref_attn_bwd(const float *q, const float *k, const float *v, const float *do
 /* dL/dtable [H][bias_hi - bias_lo + 1] of L = <O, dout> (needs a bias kind). */
 int ref_gdpa_dbias(const float *q, const float *k, const float *v, const float *dout, double *dtable,
                    const int32_t *q_off, const int32_t *kv_off, int B, int H, int D, double scale,
-                   int act, int causal, int bias_kind, const float *bias_table, int bias_lo,
+                   int act, int causal, int window, int bias_kind, const float *bias_table, int bias_lo,
                    int bias_hi, int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, bias_kind,
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, bias_kind,
                              bias_table, bias_lo, bias_hi);
     return run_dbias(&p, 0, dout, dtable, nthreads);
 }
 
 int ref_attn_dbias(const float *q, const float *k, const float *v, const float *dout, double *dtable,
                    const int32_t *q_off, const int32_t *kv_off, int B, int H, int D, double scale,
-                   int causal, int bias_kind, const float *bias_table, int bias_lo, int bias_hi,
+                   int causal, int window, int bias_kind, const float *bias_table, int bias_lo, int bias_hi,
                    int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, bias_kind,
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, window, bias_kind,
                              bias_table, bias_lo, bias_hi);
     return run_dbias(&p, 1, dout, dtable, nthreads);
 }
@@ -471,10 +480,10 @@ int ref_attn_dbias(const float *q, const float *k, const float *v, const float *
  * visited; the end entries (c = 0 or c = hi - lo) scan every pair of a row. */
 int ref_gdpa_dbias_entry(const float *q, const float *k, const float *v, const float *dout,
                          double *out, const int32_t *q_off, const int32_t *kv_off, int B, int H,
-                         int D, double scale, int act, int causal, int bias_kind,
+                         int D, double scale, int act, int causal, int window, int bias_kind,
                          const float *bias_table, int bias_lo, int bias_hi, int h, int c,
                          int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, bias_kind,
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, bias_kind,
                              bias_table, bias_lo, bias_hi);
     const int64_t W = (int64_t)bias_hi - bias_lo + 1;
     if (!q_off || p.bias_kind == BIAS_NONE || h < 0 || h >= H || c < 0 || c >= W) return 1;

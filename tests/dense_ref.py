@@ -66,6 +66,11 @@ def dense(w, *, grads=True):
     mask = (i < lq_t) & (j < lk_t)
     if w.causal:
         mask = mask & (j <= i + lk_t - lq_t)
+    if w.window:
+        ia = i + lk_t - lq_t  # aligned query position
+        mask = mask & (ia - j < w.window)
+        if not w.causal:
+            mask = mask & (j - ia < w.window)
     mask = mask.unsqueeze(1)  # [B, 1, Lq, Lk]
 
     x = w.scale * torch.matmul(qp, kp.transpose(-1, -2))

@@ -5,8 +5,9 @@ from oracle import ref
 
 
 def bias_kw(w):
+    """Bias and sliding-window arguments of the oracle calls."""
     return dict(bias_kind=w.bias_kind, bias_table=w.bias_table, bias_lo=w.bias_lo,
-                bias_hi=w.bias_hi)
+                bias_hi=w.bias_hi, window=w.window)
 
 
 def oracle_fwd(w, nthreads=0):
@@ -55,17 +56,26 @@ def structural_zero_rows(w):
     q_out = np.zeros(w.total_q_out, dtype=bool)
     q_in = np.zeros(w.total_q, dtype=bool)
     k_rows = np.zeros(w.total_k, dtype=bool)
+    big = np.int64(1) << 40
+    win = w.window
     for b in range(w.B):
-        i = np.arange(lq[b])
-        n = np.clip(i + lk[b] - lq[b] + 1, 0, lk[b]) if w.causal else np.full(lq[b], lk[b])
+        # row i sees keys [kb, ke); its aligned position is ia = i + lk - lq
+        ia = np.arange(lq[b]) + lk[b] - lq[b]
+        ke = np.clip(ia + 1, 0, lk[b]) if w.causal else (np.clip(ia + win, 0, lk[b]) if win else
+                                                         np.full(lq[b], lk[b]))
+        kb = np.clip(ia - win + 1, 0, None) if win else np.zeros(lq[b], dtype=np.int64)
+        n = np.maximum(ke - kb, 0)
         o0 = b * w.lq_fixed if w.q_off is None else int(w.q_off[b])
         q_out[o0:o0 + lq[b]] = n == 0
         if w.q_off is not None:
             q_in[o0:o0 + lq[b]] = n == 0
+        # key j is seen by the rows whose aligned position lies in [lo_j, hi_j]
         j = np.arange(lk[b])
-        first = np.maximum(j - (lk[b] - lq[b]), 0) if w.causal else np.zeros(lk[b], dtype=np.int64)
+        lo_j = j if w.causal else (j - win + 1 if win else j - big)
+        hi_j = j + win - 1 if win else j + big
+        cnt = np.minimum(hi_j, lk[b] - 1) - np.maximum(lo_j, lk[b] - lq[b]) + 1
         k0 = int(w.kv_off[b])
-        k_rows[k0:k0 + lk[b]] = (lq[b] - first) <= 0
+        k_rows[k0:k0 + lk[b]] = cnt <= 0
     rep = lambda m: np.repeat(m[:, None], w.H, axis=1)
     return rep(q_out), rep(q_in), rep(k_rows)
 

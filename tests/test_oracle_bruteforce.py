@@ -121,3 +121,47 @@ def test_oracle_single_table_entry_matches_whole_gradient(bias, lo, hi):
                                      causal=True, bias_kind=bias, bias_table=w.bias_table, bias_lo=lo,
                                      bias_hi=hi, h=h, c=c)
             assert abs(e - whole[h, c]) <= 1e-12 * max(np.abs(whole).max(), 1e-30), (h, c)
+
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_oracle_sliding_window_matches_dense(seed):
+    # Sliding windows (causal: aligned distance < w; otherwise |distance| < w) on
+    # random jagged batches with Lq != Lk, bias tables and every activation.
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 5))
+    lq = rng.integers(0, 40, size=B)
+    lk = rng.integers(0, 40, size=B) if seed % 2 else lq.copy()
+    bias = ["none", "rel", "keypos"][seed % 3]
+    w = synth.custom(mode="jfa" if seed % 4 < 2 else "gdpa", lq=lq, lk=lk, H=2, D=16,
+                     dtype=torch.float32, seed=seed, act=["silu", "gelu_tanh", "gelu_erf"][seed % 3],
+                     causal=bool(seed % 3 != 1), window=int(rng.integers(1, 12)), bias_kind=bias,
+                     bias_lo=-6, bias_hi=8, bias_sigma=0.5)
+    want = dense(w)
+    got = oracle_fwd(w)
+    got.update(oracle_bwd(w))
+    for name in ("o", "dq", "dk", "dv"):
+        assert max_rel(got[name], want[name]) <= TOL, name
+    if bias != "none":
+        assert max_rel(oracle_dbias(w), want["dbias"]) <= TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_structural_zero_rows_match_dense_mask(causal):
+    from tests.helpers import structural_zero_rows
+    for window in (0, 1, 3, 50):
+        w = synth.custom(mode="jfa", lq=[7, 0, 12, 3, 9], lk=[4, 6, 12, 9, 0], H=1, D=8,
+                         dtype=torch.float32, seed=1, causal=causal, window=window)
+        q_out, q_in, k_rows = structural_zero_rows(w)
+        for b in range(w.B):
+            lq, lk = int(w.lq[b]), int(w.lk[b])
+            i = np.arange(lq)[:, None] + lk - lq
+            j = np.arange(lk)[None, :]
+            m = np.ones((lq, lk), dtype=bool)
+            if causal:
+                m &= j <= i
+            if window:
+                m &= (i - j < window) & (causal | (j - i < window))
+            q0, k0 = int(w.q_off[b]), int(w.kv_off[b])
+            assert np.array_equal(q_in[q0:q0 + lq, 0], ~m.any(axis=1)), (window, b)
+            assert np.array_equal(k_rows[k0:k0 + lk, 0], ~m.any(axis=0)), (window, b)

@@ -127,13 +127,14 @@ def _loss(w, q, k, v):
     return float((oracle_fwd(w2)["o"] * w.dout.double().numpy()).sum())
 
 
-@pytest.mark.parametrize("mode,act,causal,bias", [
-    ("gdpa", "silu", False, "none"), ("gdpa", "gelu_tanh", True, "rel"),
-    ("gdpa", "gelu_erf", False, "keypos"), ("jfa", "silu", True, "rel"),
-    ("jfa", "silu", False, "keypos")])
-def test_gradients_match_central_differences(mode, act, causal, bias):
+@pytest.mark.parametrize("mode,act,causal,bias,window", [
+    ("gdpa", "silu", False, "none", 0), ("gdpa", "gelu_tanh", True, "rel", 0),
+    ("gdpa", "gelu_erf", False, "keypos", 0), ("jfa", "silu", True, "rel", 0),
+    ("jfa", "silu", False, "keypos", 0), ("jfa", "silu", True, "none", 4),
+    ("gdpa", "gelu_tanh", False, "rel", 3)])
+def test_gradients_match_central_differences(mode, act, causal, bias, window):
     w = _w(mode, 7, act=act, causal=causal, bias_kind=bias, bias_lo=-3 if bias == "rel" else 0,
-           bias_hi=5, dtype=torch.bfloat16)
+           bias_hi=5, dtype=torch.bfloat16, window=window)
     # bf16-valued inputs held in float32, so x +- 2^-14 is exact in float32.
     q, k, v = (t.float() for t in (w.q, w.k, w.v))
     w = synth.Workload(**{**w.__dict__, "q": q, "k": k, "v": v, "dout": w.dout.float()})
@@ -190,6 +191,41 @@ def test_jfa_bias_table_gradient_sums_to_zero():
         g = oracle_dbias(w)
         assert np.abs(g).max() > 1e-3
         assert np.abs(g.sum(axis=1)).max() <= 1e-12 * np.abs(g).sum()
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+def test_window_of_one_sees_only_the_aligned_key(mode):
+    # Causal window 1: row i sees key i + Lk - Lq alone.  JFA: P = 1, so O_i is that
+    # key's value and LSE_i its score; GDPA: O_i = act(X) times that value.
+    w = _w(mode, 5, causal=True, window=1, act="gelu_tanh")
+    o = oracle_fwd(w)
+    lq, lk = w.lq, w.lk
+    for b in range(w.B):
+        q0, k0 = int(w.q_off[b]), int(w.kv_off[b])
+        for i in range(int(lq[b])):
+            j = i + int(lk[b]) - int(lq[b])
+            if j < 0:
+                assert np.all(o["o"][q0 + i] == 0.0)
+                continue
+            for h in range(w.H):
+                x = w.scale * float(np.dot(w.q[q0 + i, h].double().numpy(), w.k[k0 + j, h].double().numpy()))
+                vj = w.v[k0 + j, h].double().numpy()
+                if mode == "jfa":
+                    assert np.allclose(o["o"][q0 + i, h], vj, rtol=1e-13, atol=1e-13)
+                    assert abs(o["lse"][q0 + i, h] - x) <= 1e-12 * max(1.0, abs(x))
+                else:
+                    y, _ = ref.act("gelu_tanh", np.array([x]))
+                    assert np.allclose(o["o"][q0 + i, h], y[0] * vj, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_wider_than_every_sample_changes_nothing(mode, causal):
+    w = _w(mode, 9, causal=causal, bias_kind="rel", bias_lo=-4, bias_hi=4)
+    wide = synth.Workload(**{**w.__dict__, "window": 64})
+    for a, b in ((oracle_fwd(w), oracle_fwd(wide)), (oracle_bwd(w), oracle_bwd(wide))):
+        for k in a:
+            assert np.array_equal(a[k], b[k]), k
 
 
 # ---------------------------------------------------------------- closed forms

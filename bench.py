@@ -42,7 +42,7 @@ KERNEL_SOURCES = ["ja_fwd.hip", "ja_bwd.hip", "ja_plan.hip", "ja_tiles.h", "ja_d
 # Workloads: which roofline bounds them (short K/V streams Q / dO / O through HBM;
 # long sequences are MFMA work).
 BOUND = {"gdpa_xattn_short_kv": "hbm", "pma_gdpa_fwd": "hbm", "jfa_causal_self": "mfma",
-         "longtail_gdpa": "mfma", "tiny_gdpa_fp32": "alu"}
+         "longtail_gdpa": "mfma", "tiny_gdpa_fp32": "alu", "jfa_swa_causal_self": "mfma"}
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (the plain fp32 kernels are ALU loops)
 
 
@@ -55,12 +55,14 @@ def pairs_per_sample(w) -> np.ndarray:
     """Valid (query, key) pairs of each sample (per head)."""
     lq = w.lq.astype(np.int64)
     lk = w.lk.astype(np.int64)
-    if not w.causal:
+    if not w.causal and not w.window:
         return lq * lk
     out = np.zeros(len(lq), dtype=np.int64)
     for n, (a, b) in enumerate(zip(lq, lk)):
-        i = np.arange(a, dtype=np.int64)
-        out[n] = int(np.clip(i + b - a + 1, 0, b).sum())
+        ia = np.arange(a, dtype=np.int64) + b - a  # aligned positions
+        end = np.clip(ia + 1, 0, b) if w.causal else (np.clip(ia + w.window, 0, b) if w.window else b)
+        beg = np.clip(ia - w.window + 1, 0, b) if w.window else 0
+        out[n] = int(np.maximum(end - beg, 0).sum())
     return out
 
 
@@ -155,7 +157,7 @@ class Runner:
             total_k=w.total_k, q_offsets=self.q_off, kv_offsets=self.kv_off,
             lq_fixed=w.lq_fixed, causal=w.causal, scale=w.scale, act=w.act,
             bias_kind=w.bias_kind, bias_table=self.bias, bias_lo=w.bias_lo, bias_hi=w.bias_hi,
-            max_kv_len=self.max_kv_len)
+            max_kv_len=self.max_kv_len, window=w.window)
         rows = w.total_q_out
         self.o = torch.empty((rows, w.H, w.D), dtype=w.dtype, device=dev)
         self.lse = torch.empty((w.H, rows), dtype=torch.float32, device=dev)
@@ -443,7 +445,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "B": w.B, "H": w.H, "D": w.D,
                    "total_q": w.total_q, "total_k": w.total_k, "act": w.act if w.mode == "gdpa" else "softmax",
-                   "causal": w.causal, "bias": w.bias_kind, "jagged_sparsity": round(sparsity, 4),
+                   "causal": w.causal, "window": w.window, "bias": w.bias_kind, "jagged_sparsity": round(sparsity, 4),
                    "useful_pairs": P, "backward": runner.backward, "bias_grad": runner.bias_grad},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),

@@ -26,7 +26,14 @@
  * offsets are int32 [B+1], start at 0, never decrease and end at the row
  * count.  Samples may be empty.  Within a sample, i and j are 0-based local
  * positions and a pair (i, j) is valid iff j < Lk and, with causal masking,
- * j <= i + Lk - Lq (bottom-right alignment; j <= i when Lq == Lk).
+ * j <= i + Lk - Lq (bottom-right alignment; j <= i when Lq == Lk).  A sliding
+ * window w > 0 (window) also requires ia - j < w and, without causal masking,
+ * j - ia < w, where ia = i + Lk - Lq is the row's aligned position: each row
+ * sees the w nearest keys up to its diagonal (causal) or a band of 2w - 1
+ * keys around it.  The pages name sliding-window attention ("Meta redesigns
+ * AI training infrastructure...", section "Custom Kernels and 5D Parallelism
+ * for Trillion-Parameter Scale") without defining it; this is the plain
+ * reading.
  *
  * Shared query block.  With q_offsets == NULL, q holds lq_fixed rows
  * ([lq_fixed, H, D]) that every sample attends with (pooling by learned seed
@@ -112,6 +119,7 @@ typedef struct ja_problem {
                                     library skip launching its long-sequence kernels; a bound
                                     that some sample exceeds gives undefined results, like
                                     invalid offsets.  Negative: JA_ERR_SHAPE. */
+    int32_t window;              /* sliding window w (0 = none, negative: JA_ERR_SHAPE) */
 } ja_problem;
 
 /* Workspace bytes that the given pass of either attention form needs (0 only

@@ -39,7 +39,7 @@ class JaProblem(ctypes.Structure):
         ("q_offsets", ctypes.c_void_p), ("lq_fixed", ctypes.c_int32), ("causal", ctypes.c_int32),
         ("kv_offsets", ctypes.c_void_p), ("scale", ctypes.c_float), ("act", ctypes.c_int32),
         ("bias_kind", ctypes.c_int32), ("bias_lo", ctypes.c_int32), ("bias_hi", ctypes.c_int32),
-        ("bias_table", ctypes.c_void_p), ("max_kv_len", ctypes.c_int32),
+        ("bias_table", ctypes.c_void_p), ("max_kv_len", ctypes.c_int32), ("window", ctypes.c_int32),
     ]
 
 
@@ -105,7 +105,7 @@ def _stream(stream):
 
 def make_problem(*, batch, heads, head_dim, dtype, total_q, total_k, q_offsets, kv_offsets,
                  lq_fixed=0, causal=False, scale=None, act="silu", bias_kind="none",
-                 bias_table=None, bias_lo=0, bias_hi=0, max_kv_len=0) -> JaProblem:
+                 bias_table=None, bias_lo=0, bias_hi=0, max_kv_len=0, window=0) -> JaProblem:
     """Fill a JaProblem.  Offsets and the bias table are device tensors (or raw pointers)."""
     p = JaProblem()
     p.batch, p.heads, p.head_dim = int(batch), int(heads), int(head_dim)
@@ -121,6 +121,7 @@ def make_problem(*, batch, heads, head_dim, dtype, total_q, total_k, q_offsets, 
     p.bias_lo, p.bias_hi = int(bias_lo), int(bias_hi)
     p.bias_table = _ptr(bias_table)
     p.max_kv_len = int(max_kv_len)
+    p.window = int(window)
     return p
 
 

@@ -102,6 +102,7 @@ ja_status check_problem(const ja_problem *p, int pass) {
         return JA_ERR_UNSUPPORTED;
     if (!(p->scale == p->scale)) return JA_ERR_SHAPE;  // NaN scale
     if (p->max_kv_len < 0) return JA_ERR_SHAPE;
+    if (p->window < 0) return JA_ERR_SHAPE;
     // Kernels address a (sample, head) slice with 32-bit byte offsets; bounding
     // every [rows, H, D] tensor below 4 GiB bounds every slice (the sample
     // lengths themselves live on the device).
@@ -136,6 +137,7 @@ ja::AttnParams base_params(const ja_problem &p, const Layout &L, void *ws) {
     a.total_k = p.total_k;
     a.scale = p.scale;
     a.causal = p.causal;
+    a.window = p.window;
     a.bias_kind = p.bias_kind;
     a.bias_lo = p.bias_lo;
     a.bias_hi = p.bias_hi;
@@ -164,6 +166,7 @@ ja::PlanParams plan_of(const ja_problem &p, int kind, int tile_rows, int inner_r
     q.B = p.batch;
     q.H = p.heads;
     q.causal = p.causal;
+    q.window = p.window;
     q.kind = kind;
     q.tile_rows = tile_rows;
     q.inner_rows = inner_rows;

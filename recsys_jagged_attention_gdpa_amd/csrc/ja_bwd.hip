@@ -122,7 +122,8 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
         const int irow = iw + l32;
         const bool row_ok = irow < s.lq;
         const int i_last = (i0 + BM < s.lq ? i0 + BM : s.lq) - 1;
-        const int nkv = (key_end(i_last, s.lq, s.lk, p.causal) + BN - 1) / BN;
+        const int nkv = (key_end(i_last, s.lq, s.lk, p.causal, p.window) + BN - 1) / BN;
+        const int jt_first = key_begin(i0, s.lq, s.lk, p.window) / BN;  // tiles before it see no row of the unit
         const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h), Gs(p.dout, s.qs, s.lq, H, h), dQs(p.dq, s.qs, s.lq, H, h);
         const HeadSlice<D> Ks(p.k, s.ks, s.lk, H, h), Vs(p.v, s.ks, s.lk, H, h);
         const rsrc_t brs = make_rsrc(bz.kind ? bz.table + (int64_t)h * bz.width : nullptr,
@@ -139,7 +140,11 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
             lse2 = buf_load_f32(lr, off) * LOG2E;
             dlt = buf_load_f32(dr, off);
         }
-        const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
+        const int my_kend = key_end(irow, s.lq, s.lk, p.causal, p.window);
+        const int my_kbeg = key_begin(irow, s.lq, s.lk, p.window);
+        // keys every row of the wave sees: [wkb, wke)
+        const int wke = key_end(iw, s.lq, s.lk, p.causal, p.window);
+        const int wkb = key_begin(iw + 31, s.lq, s.lk, p.window);
 
         f32x16 dqacc[NDB];
 #pragma unroll
@@ -159,13 +164,13 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
             if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tile has landed
         };
-        load_tile(0);
-        store_tile(0);
+        load_tile(jt_first);
+        store_tile(jt_first & 1);
         __syncthreads();
         const float sl = MODE == JFA ? p.scale * LOG2E : p.scale;
         const float nl = -lse2;
 
-        for (int jt = 0; jt < nkv; ++jt) {
+        for (int jt = jt_first; jt < nkv; ++jt) {
             const int j0 = jt * BN;
             const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             const lchar *Vt = Kt + TILE_BYTES;
@@ -173,8 +178,9 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
             load_tile(jt + 1);  // past the last tile: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);
 
-            // Wave-uniform: does this tile cross the key end, the diagonal or the query end?
-            const bool masked = (j0 + BN > s.lk) | (p.causal && (j0 + BN - 1 > iw + s.lk - s.lq)) | (iw + 32 > s.lq);
+            // Wave-uniform: does this tile cross the key end, the diagonal, the
+            // window start or the query end?
+            const bool masked = (j0 + BN > wke) | (j0 < wkb) | (iw + 32 > s.lq);
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb) {
                 f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -208,8 +214,10 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
                 if (masked) {
                     // invalid pairs (and rows without a visible key, LSE = -inf) give nothing
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        dx[e] = (row_ok & (j0 + nb * 32 + crow(e, g) < my_kend)) ? dx[e] : 0.0f;
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = j0 + nb * 32 + crow(e, g);
+                        dx[e] = (row_ok & (j < my_kend) & (j >= my_kbeg)) ? dx[e] : 0.0f;
+                    }
                 }
                 bf16x8 dsb[2];
                 pack_operands(dx, dsb[0], dsb[1]);
@@ -282,11 +290,16 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dkacc[db] = dvacc[db] = f32x16{};
 
-        // Query rows that see any key of the unit: i >= jt0 - (lk - lq) when causal.
-        int ia0 = p.causal ? jt0 - (s.lk - s.lq) : 0;
-        ia0 = ia0 < 0 ? 0 : ia0;
+        // Query rows that see any key of the unit, [ia0, ia_end): with ia = i + lk - lq
+        // the aligned position, causal masking needs ia >= jt0, a window w needs
+        // ia < jt0 + BK - 1 + w and (without causal masking) ia > jt0 - w.
         const int shift = s.lk - s.lq;  // causal: key j visible to row i iff j <= i + shift
-        const int nsteps = ia0 < s.lq ? (s.lq - ia0 + BQ - 1) / BQ : 0;
+        const int win = p.window;
+        int ia0 = p.causal ? jt0 - shift : (win ? jt0 - win - shift + 1 : 0);
+        ia0 = ia0 < 0 ? 0 : ia0;
+        int ia_end = win ? jt0 + BK - 1 + win - shift : s.lq;
+        ia_end = ia_end > s.lq ? s.lq : ia_end;
+        const int nsteps = ia0 < ia_end ? (ia_end - ia0 + BQ - 1) / BQ : 0;
 
         // Query / dO rows of step st are copied straight into LDS buffer
         // (st & 1); the step's LSE, delta and bias window go through registers.
@@ -327,7 +340,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
             __builtin_amdgcn_sched_barrier(0);
 
             // Wave-uniform: does this step cross the query end or the diagonal?
-            const bool masked = (ia + BQ > s.lq) | (p.causal && (jw + 31 > ia + shift));
+            const bool masked = (ia + BQ > s.lq) | (p.causal && (jw + 31 > ia + shift)) |
+                                (win && ((jw < key_begin(ia + BQ - 1, s.lq, s.lk, win)) |
+                                         (jw + 32 > key_end(ia, s.lq, s.lk, p.causal, win))));
             // Software pipeline over the step's 32-row blocks: the next block's S
             // and dP products are issued inside the current block's element-wise
             // stage (one basic block), so the scheduler can interleave the matrix
@@ -394,7 +409,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int i = ia + qb * 32 + crow(e, g);
-                        const bool valid = (i < s.lq) & (!p.causal | (jkey <= i + shift));
+                        const int dist = i + shift - jkey;  // aligned distance
+                        const bool valid = (i < s.lq) & (!p.causal | (dist >= 0)) &
+                                           (!win | ((dist < win) & (p.causal | (-dist < win))));
                         pv[e] = valid ? pv[e] : 0.0f;
                         dx[e] = valid ? dx[e] : 0.0f;
                     }
@@ -517,12 +534,14 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
                 sacc = mfma32(lds_read16(Qt, off), lds_read16(Kt, off), sacc);
                 dpacc = mfma32(lds_read16(Gt, off), lds_read16(Vt, off), dpacc);
             }
-            const bool masked = (ia + 32 > s.lq) | (s.lk < 32) | (p.causal != 0);
+            const bool masked = (ia + 32 > s.lq) | (s.lk < 32) | (p.causal != 0) | (p.window != 0);
             float pv[16], dx[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int i = ia + crow(e, g);
-                const bool valid = !masked | ((i < s.lq) & key_ok & (!p.causal | (jkey <= i + shift)));
+                const int dist = i + shift - jkey;  // aligned distance
+                const bool valid = !masked | ((i < s.lq) & key_ok & (!p.causal | (dist >= 0)) &
+                                              (!p.window | ((dist < p.window) & (p.causal | (-dist < p.window)))));
                 pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bv[e], dpacc[e], lse2[e], dlt[e], valid, dx[e]);
             }
             bf16x8 pb[2], dsb[2];

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
         const int irow = iw + l32;
         const bool row_ok = irow < s.lq;
         const int i_last = (i0 + BM < s.lq ? i0 + BM : s.lq) - 1;
-        const int nkv = (key_end(i_last, s.lq, s.lk, p.causal) + BN - 1) / BN;
+        const int nkv = (key_end(i_last, s.lq, s.lk, p.causal, p.window) + BN - 1) / BN;
+        const int jt_first = key_begin(i0, s.lq, s.lk, p.window) / BN;  // tiles before it see no row of the unit
         const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h), Gs(p.dout, s.qs, s.lq, H, h);
         const HeadSlice<D> Ks(p.k, s.ks, s.lk, H, h), Vs(p.v, s.ks, s.lk, H, h);
         const rsrc_t brs = make_rsrc(bz.table + (int64_t)h * W, (uint32_t)W * 4u);
@@ -114,7 +115,11 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
             lse2 = buf_load_f32(lr, off) * LOG2E;
             dlt = buf_load_f32(dr, off);
         }
-        const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
+        const int my_kend = key_end(irow, s.lq, s.lk, p.causal, p.window);
+        const int my_kbeg = key_begin(irow, s.lq, s.lk, p.window);
+        // keys every row of the wave sees: [wkb, wke)
+        const int wke = key_end(iw, s.lq, s.lk, p.causal, p.window);
+        const int wkb = key_begin(iw + 31, s.lq, s.lk, p.window);
         float acc_lo = 0.0f, acc_hi = 0.0f;  // this lane's dX of blocks clamped whole to an end entry
 
         // Key / value tile jt is copied straight into LDS buffer (jt & 1); the
@@ -131,13 +136,13 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
             if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tile has landed
         };
-        load_tile(0);
-        store_tile(0);
+        load_tile(jt_first);
+        store_tile(jt_first & 1);
         __syncthreads();
         const float sl = MODE == JFA ? p.scale * LOG2E : p.scale;
         const float nl = -lse2;
 
-        for (int jt = 0; jt < nkv; ++jt) {
+        for (int jt = jt_first; jt < nkv; ++jt) {
             const int j0 = jt * BN;
             const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             const lchar *Vt = Kt + TILE_BYTES;
@@ -145,8 +150,9 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
             load_tile(jt + 1);  // past the last tile: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);
 
-            // Wave-uniform: does this tile cross the key end, the diagonal or the query end?
-            const bool masked = (j0 + BN > s.lk) | (p.causal && (j0 + BN - 1 > iw + s.lk - s.lq)) | (iw + 32 > s.lq);
+            // Wave-uniform: does this tile cross the key end, the diagonal, the
+            // window start or the query end?
+            const bool masked = (j0 + BN > wke) | (j0 < wkb) | (iw + 32 > s.lq);
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb) {
                 f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -173,8 +179,10 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
                 if (masked) {
                     // invalid pairs (and rows without a visible key, LSE = -inf) give nothing
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        dx[e] = (row_ok & (j0 + nb * 32 + crow(e, g) < my_kend)) ? dx[e] : 0.0f;
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = j0 + nb * 32 + crow(e, g);
+                        dx[e] = (row_ok & (j < my_kend) & (j >= my_kbeg)) ? dx[e] : 0.0f;
+                    }
                 }
 
                 const int jb = j0 + nb * 32;  // first key of the block

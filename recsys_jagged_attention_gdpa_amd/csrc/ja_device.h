@@ -305,11 +305,19 @@ __device__ __forceinline__ Sample load_sample(const int32_t *q_off, int lq_fixed
     return s;
 }
 
-// Keys visible to query row i (exclusive end) under the bottom-right causal rule.
-__device__ __forceinline__ int key_end(int i, int lq, int lk, int causal) {
-    if (!causal) return lk;
-    const int e = i + lk - lq + 1;
+// Keys visible to query row i are [key_begin, key_end) (empty when begin >= end).
+// With ia = i + lk - lq the row's position aligned to the keys (bottom-right):
+// causal masking ends them at ia; a sliding window w > 0 keeps aligned
+// distances ia - j below w, and without causal masking also j - ia below w.
+__device__ __forceinline__ int key_end(int i, int lq, int lk, int causal, int window) {
+    if (!causal && !window) return lk;
+    const int e = i + lk - lq + (causal ? 1 : window);
     return e < 0 ? 0 : (e > lk ? lk : e);
+}
+__device__ __forceinline__ int key_begin(int i, int lq, int lk, int window) {
+    if (!window) return 0;
+    const int b = i + lk - lq - window + 1;
+    return b < 0 ? 0 : (b > lk ? lk : b);
 }
 
 struct BiasArgs {

@@ -79,8 +79,8 @@ __global__ __launch_bounds__(F32_THREADS) void fwd_f32_kernel(const AttnParams p
     float acc[D];
     for (int d = 0; d < D; ++d) acc[d] = 0.0f;
     float m = -INFINITY, l = 0.0f;
-    const int kend = key_end(i, s.lq, s.lk, p.causal);
-    for (int j = 0; j < kend; ++j) {
+    const int kend = key_end(i, s.lq, s.lk, p.causal, p.window);
+    for (int j = key_begin(i, s.lq, s.lk, p.window); j < kend; ++j) {
         const float *kj = K + ((s.ks + j) * p.H + h) * (int64_t)D;
         const float *vj = V + ((s.ks + j) * p.H + h) * (int64_t)D;
         float x = p.scale * dot_f32(qi, kj, D);
@@ -141,8 +141,8 @@ __global__ __launch_bounds__(F32_THREADS) void dq_f32_kernel(const AttnParams p)
     }
     float acc[D];
     for (int d = 0; d < D; ++d) acc[d] = 0.0f;
-    const int kend = key_end(i, s.lq, s.lk, p.causal);
-    for (int j = 0; j < kend; ++j) {
+    const int kend = key_end(i, s.lq, s.lk, p.causal, p.window);
+    for (int j = key_begin(i, s.lq, s.lk, p.window); j < kend; ++j) {
         const float *kj = K + ((s.ks + j) * p.H + h) * (int64_t)D;
         const float *vj = V + ((s.ks + j) * p.H + h) * (int64_t)D;
         float x = p.scale * dot_f32(qi, kj, D);
@@ -178,6 +178,7 @@ __global__ __launch_bounds__(F32_THREADS) void dkdv_f32_kernel(const AttnParams 
     int i_first = p.causal ? j - (s.lk - s.lq) : 0;
     i_first = i_first < 0 ? 0 : i_first;
     for (int i = i_first; i < s.lq; ++i) {
+        if (j < key_begin(i, s.lq, s.lk, p.window) || j >= key_end(i, s.lq, s.lk, p.causal, p.window)) continue;
         const float *qi = Q + ((s.qs + i) * p.H + h) * (int64_t)D;
         const float *gi = G + ((s.qs + i) * p.H + h) * (int64_t)D;
         float x = p.scale * dot_f32(qi, kj, D);
@@ -230,14 +231,15 @@ __global__ __launch_bounds__(F32_THREADS) void dbias_f32_kernel(const AttnParams
             const int64_t r = s.qs + i;
             const float *qi = Q + (r * p.H + h) * (int64_t)D;
             const float *gi = G + (r * p.H + h) * (int64_t)D;
-            const int kend = key_end(i, s.lq, s.lk, p.causal);
+            const int kend = key_end(i, s.lq, s.lk, p.causal, p.window);
+            const int kbeg = key_begin(i, s.lq, s.lk, p.window);
             // keys of row i whose position maps to entry c: [ja, jb)
-            int ja = 0, jb = kend;
+            int ja = kbeg, jb = kend;
             if (bz.kind == BIAS_REL) {  // position i - j
-                if (!last) ja = i - target;              // i - j <= target
+                if (!last) ja = max(ja, i - target);       // i - j <= target
                 if (!first) jb = min(jb, i - target + 1);  // i - j >= target
             } else {                    // position j
-                if (!first) ja = target;
+                if (!first) ja = max(ja, target);
                 if (!last) jb = min(jb, target + 1);
             }
             ja = ja < 0 ? 0 : ja;

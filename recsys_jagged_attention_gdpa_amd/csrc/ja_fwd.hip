@@ -82,8 +82,9 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         const int iw = i0 + wv * 32;           // first row of this wave
         const int irow = iw + l32;             // this lane's query row
         const int i_last = (i0 + BM < s.lq ? i0 + BM : s.lq) - 1;
-        const int kend = key_end(i_last, s.lq, s.lk, p.causal);
+        const int kend = key_end(i_last, s.lq, s.lk, p.causal, p.window);
         const int nkv = (kend + BN - 1) / BN;
+        const int jt_first = key_begin(i0, s.lq, s.lk, p.window) / BN;  // tiles before it see no row of the unit
         const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h), Os(p.out, s.o0, s.lq, H, h);
         const HeadSlice<D> Ks(p.k, s.ks, s.lk, H, h), Vs(p.v, s.ks, s.lk, H, h);
         const bool res = MODE == JFA && p.o_res_out != nullptr;
@@ -115,11 +116,16 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;  // JFA works in log2 units
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tile has landed
         };
-        load_tile(0);
-        store_tile(0);
+        load_tile(jt_first);
+        store_tile(jt_first & 1);
         __syncthreads();
 
-        for (int jt = 0; jt < nkv; ++jt) {
+        // keys of the wave's rows: every row sees [wkb, wke) at least; masking is
+        // needed only where a tile leaves that range
+        const int wke = key_end(iw, s.lq, s.lk, p.causal, p.window);
+        const int wkb = key_begin(iw + 31, s.lq, s.lk, p.window);
+        const int my_kbeg = key_begin(irow, s.lq, s.lk, p.window);
+        for (int jt = jt_first; jt < nkv; ++jt) {
             const int j0 = jt * BN;
             const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             const lchar *Vt = Kt + TILE_BYTES;
@@ -140,13 +146,12 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             }
 
             // Element-wise stage.  A tile needs per-element masking only when it
-            // crosses the key end or (causal) the diagonal of this wave's rows;
-            // that test and the bias kind are wave-uniform, so each variant is
-            // a straight-line loop behind one scalar branch.
-            const bool tail = j0 + BN > s.lk;
-            const bool diag = p.causal && (j0 + BN - 1 > iw + s.lk - s.lq);
-            const bool masked = tail || diag;
-            const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
+            // crosses the key end, (causal) the diagonal or (window) the window
+            // start of this wave's rows; that test and the bias kind are
+            // wave-uniform, so each variant is a straight-line loop behind one
+            // scalar branch.
+            const bool masked = (j0 + BN > wke) || (j0 < wkb);
+            const int my_kend = key_end(irow, s.lq, s.lk, p.causal, p.window);
             bf16x8 pb[NKS], pbl[SPLIT ? NKS : 1];
             // x = scale * s + bias (JFA: in log2 units); without bias only the
             // scale is applied, folded into later arithmetic where possible.
@@ -176,8 +181,10 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                     for (int e = 0; e < 16; ++e) pv[e] = act_fwd<ACT>(sacc[nb][e]);
                     if (masked) {
 #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            pv[e] = (j0 + nb * 32 + crow(e, g) >= my_kend) ? 0.0f : pv[e];
+                        for (int e = 0; e < 16; ++e) {
+                            const int j = j0 + nb * 32 + crow(e, g);
+                            pv[e] = (j >= my_kend) | (j < my_kbeg) ? 0.0f : pv[e];
+                        }
                     }
                     pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
                 }
@@ -186,8 +193,10 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
 #pragma unroll
                     for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            sacc[nb][e] = (j0 + nb * 32 + crow(e, g) >= my_kend) ? -INFINITY : sacc[nb][e];
+                        for (int e = 0; e < 16; ++e) {
+                            const int j = j0 + nb * 32 + crow(e, g);
+                            sacc[nb][e] = (j >= my_kend) | (j < my_kbeg) ? -INFINITY : sacc[nb][e];
+                        }
                 }
                 float tmax = -INFINITY;
 #pragma unroll
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
         const rsrc_t lse_r = make_rsrc(MODE == JFA ? p.lse + (int64_t)h * p.total_q_out + s.o0 : p.lse,
                                        MODE == JFA ? (uint32_t)s.lq * 4u : 0u);
         const int nblk = (s.lq + 31) / 32;
-        const bool masked = s.lk < 32 || p.causal;
+        const bool masked = s.lk < 32 || p.causal || p.window;
         // One 32-row query block, with Q rows in `qreg`; the next block's rows
         // are loaded into `qnext` first, so they are in flight meanwhile.  The
         // wave's LDS tile holds the block's Q rows, then its output rows.
@@ -332,7 +341,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
                 const int off = lds_off<D>(l32, 2 * kk + g);
                 sacc = mfma32(lds_read16(Kt, off), lds_read16(Ot, off), sacc);
             }
-            const int my_kend = key_end(irow, s.lq, s.lk, p.causal);
+            const int my_kend = key_end(irow, s.lq, s.lk, p.causal, p.window);
+            const int my_kbeg = key_begin(irow, s.lq, s.lk, p.window);
             float pv[16];
             float norm = 1.0f, lse_row = 0.0f;
             if constexpr (MODE == GDPA) {
@@ -340,7 +350,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
                 for (int e = 0; e < 16; ++e) {
                     const int j = crow(e, g);
                     const float y = act_fwd<ACT>(__builtin_fmaf(sacc[e], p.scale, bv[e]));
-                    pv[e] = (masked & (j >= my_kend)) ? 0.0f : y;  // bitwise: no per-lane branches
+                    pv[e] = (masked & ((j >= my_kend) | (j < my_kbeg))) ? 0.0f : y;  // bitwise: no per-lane branches
                 }
             } else {
                 float m = -INFINITY;
@@ -348,7 +358,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
                 for (int e = 0; e < 16; ++e) {
                     const int j = crow(e, g);
                     float x = __builtin_fmaf(sacc[e], sl2, bv[e] * LOG2E);
-                    x = (masked & (j >= my_kend)) ? -INFINITY : x;
+                    x = (masked & ((j >= my_kend) | (j < my_kbeg))) ? -INFINITY : x;
                     pv[e] = x;
                     m = fmaxf(m, x);
                 }

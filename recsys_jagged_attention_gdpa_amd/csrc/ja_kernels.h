@@ -46,6 +46,7 @@ struct PlanParams {
     int tile_rows;   // rows per unit tile
     int inner_rows;  // rows per inner-loop step (cost unit)
     int only_short;  // PLAN_SAMPLES: keep samples with lk <= FUSED_MAX_LK; PLAN_KV/Q: skip them (1) or not (0)
+    int window;      // sliding window (0: none)
     int2 *tiles;     // out: (sample, tile) pairs, most expensive first
     int max_tiles;
     PlanCounters *counters;
@@ -68,6 +69,7 @@ struct AttnParams {
     int64_t total_q, total_k;
     float scale;
     int causal;
+    int window;  // sliding window: aligned distances below it are kept (0: none)
     int bias_kind, bias_lo, bias_hi;
     const float *bias;
     const int2 *tiles;

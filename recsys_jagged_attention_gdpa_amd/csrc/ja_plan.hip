@@ -61,16 +61,18 @@ __device__ int tile_cost(const PlanParams &p, const PlanSample &s, int t) {
     if (p.kind == PLAN_Q_TILES) {
         int last = (t + 1) * p.tile_rows;
         last = (last < s.lq ? last : s.lq) - 1;
-        const int kend = key_end(last, s.lq, s.lk, p.causal);
-        return ceil_div(kend, p.inner_rows) + 1;
+        const int kend = key_end(last, s.lq, s.lk, p.causal, p.window);
+        const int kbeg = key_begin(t * p.tile_rows, s.lq, s.lk, p.window) / p.inner_rows * p.inner_rows;
+        return ceil_div(kend > kbeg ? kend - kbeg : 0, p.inner_rows) + 1;
     }
     if (p.kind == PLAN_KV_TILES) {
-        int first_q = 0;
-        if (p.causal) {
-            first_q = t * p.tile_rows - (s.lk - s.lq);
-            first_q = first_q < 0 ? 0 : first_q;
-        }
-        const int nq = s.lq - first_q;
+        // query rows that see some key of the tile (aligned position ia = i + lk - lq)
+        const int shift = s.lk - s.lq, j0 = t * p.tile_rows, w = p.window;
+        int first_q = p.causal ? j0 - shift : (w ? j0 - w - shift + 1 : 0);
+        first_q = first_q < 0 ? 0 : first_q;
+        int end_q = w ? j0 + p.tile_rows - 1 + w - shift : s.lq;
+        end_q = end_q > s.lq ? s.lq : end_q;
+        const int nq = end_q - first_q;
         return ceil_div(nq > 0 ? nq : 0, p.inner_rows) + 1;
     }
     return ceil_div(s.lq, p.inner_rows) + 1;
@@ -99,6 +101,10 @@ __device__ __forceinline__ bool grouped(const PlanParams &p) { return p.kind != 
 // so a sample with many tiles is not walked tile by tile.
 __device__ int64_t sample_cost(const PlanParams &p, const PlanSample &s) {
     const int64_t lq = s.lq, lk = s.lk;
+    if (p.window) {  // an estimate: rows times the keys a full window holds
+        const int64_t span = p.causal ? p.window : 2 * (int64_t)p.window - 1;
+        return lq * (span < lk ? span : lk);
+    }
     if (!p.causal) return lq * lk;
     // row i sees clamp(i + lk - lq + 1, 0, lk) keys
     auto tri = [](int64_t n) { return n * (n + 1) / 2; };  // 1 + ... + n

@@ -139,6 +139,11 @@ CATALOGUE = {
                           q_len=("loguniform", 100, 16384), kv_len="same", qkv_sigma=1.0,
                           act="gelu_erf", causal=False, bias=("rel", -512, 512, math.sqrt(0.1)),
                           backward=True),
+    # The JFA causal self-attention batch with a sliding window of 1024 keys (the
+    # pages report sliding-window attention on long-sequence self-attention).
+    "jfa_swa_causal_self": dict(mode="jfa", B=64, H=8, D=128, dtype="bf16", q_len=("uniform", 1, 8192),
+                                kv_len="same", qkv_sigma=1.0, act=None, causal=True, bias=None,
+                                backward=True, window=1024, same_draw_as="jfa_causal_self"),
 }
 
 
@@ -160,8 +165,8 @@ def make(name: str, seed: Optional[int] = None, *, B: Optional[int] = None,
          max_len: Optional[int] = None, with_dout: Optional[bool] = None) -> Workload:
     """Draw workload ``name``.  ``B`` and ``max_len`` shrink it for parity tests."""
     spec = CATALOGUE[name]
-    if seed is None:
-        seed = 1000 + list(CATALOGUE).index(name) + 1
+    if seed is None:  # a variant of another workload draws the same batch
+        seed = 1000 + list(CATALOGUE).index(spec.get("same_draw_as", name)) + 1
     rng = np.random.default_rng(seed)
     B = spec["B"] if B is None else B
     H, D = spec["H"], spec["D"]
@@ -201,7 +206,7 @@ def make(name: str, seed: Optional[int] = None, *, B: Optional[int] = None,
                     lq_fixed=lq_fixed, kv_off=kv_off, q=q, k=k, v=v, dout=dout,
                     act=spec["act"] or "silu", scale=1.0 / math.sqrt(D), causal=spec["causal"],
                     bias_kind=bias_kind, bias_table=table, bias_lo=lo, bias_hi=hi,
-                    backward=spec["backward"])
+                    backward=spec["backward"], window=spec.get("window", 0))
 
 
 def custom(*, mode="gdpa", lq, lk=None, H=2, D=64, dtype=torch.bfloat16, seed=0, sigma=1.0,

@@ -74,7 +74,7 @@ def test_workspace_size_is_positive_and_aligned():
     (dict(bias_kind=4), 3), (dict(batch=0), 2), (dict(heads=0), 2), (dict(total_q=-1), 2),
     (dict(kv_offsets=None), 1), (dict(bias_kind="rel", bias_table=None), 1),
     (dict(bias_kind="rel", bias_table=0x3000, bias_lo=5, bias_hi=1), 2),
-    (dict(q_offsets=None, lq_fixed=3, total_q=4), 2), (dict(max_kv_len=-1), 2),
+    (dict(q_offsets=None, lq_fixed=3, total_q=4), 2), (dict(max_kv_len=-1), 2), (dict(window=-1), 2),
     # slices are addressed with 32-bit offsets: tensors of 4 GiB or more are refused
     (dict(total_q=1 << 24, heads=64, head_dim=128), 3), (dict(total_k=1 << 24, heads=16, head_dim=128), 3),
     (dict(total_q=1 << 23, heads=1, head_dim=128, dtype=torch.float32), 3),  # exactly 4 GiB

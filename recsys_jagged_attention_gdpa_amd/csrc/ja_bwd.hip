@@ -536,13 +536,19 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
             }
             const bool masked = (ia + 32 > s.lq) | (s.lk < 32) | (p.causal != 0) | (p.window != 0);
             float pv[16], dx[16];
+            if (!masked) {  // wave-uniform: interior blocks carry no per-element tests
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int i = ia + crow(e, g);
-                const int dist = i + shift - jkey;  // aligned distance
-                const bool valid = !masked | ((i < s.lq) & key_ok & (!p.causal | (dist >= 0)) &
-                                              (!p.window | ((dist < p.window) & (p.causal | (-dist < p.window)))));
-                pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bv[e], dpacc[e], lse2[e], dlt[e], valid, dx[e]);
+                for (int e = 0; e < 16; ++e)
+                    pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bv[e], dpacc[e], lse2[e], dlt[e], true, dx[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int i = ia + crow(e, g);
+                    const int dist = i + shift - jkey;  // aligned distance
+                    const bool valid = (i < s.lq) & key_ok & (!p.causal | (dist >= 0)) &
+                                       (!p.window | ((dist < p.window) & (p.causal | (-dist < p.window))));
+                    pv[e] = score_bwd<MODE, ACT>(sacc[e], p.scale, bv[e], dpacc[e], lse2[e], dlt[e], valid, dx[e]);
+                }
             }
             bf16x8 pb[2], dsb[2];
             pack_operands(pv, pb[0], pb[1]);

@@ -345,23 +345,30 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
             const int my_kbeg = key_begin(irow, s.lq, s.lk, p.window);
             float pv[16];
             float norm = 1.0f, lse_row = 0.0f;
+            // masked is unit-uniform: interior units carry no per-element tests
             if constexpr (MODE == GDPA) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = crow(e, g);
-                    const float y = act_fwd<ACT>(__builtin_fmaf(sacc[e], p.scale, bv[e]));
-                    pv[e] = (masked & ((j >= my_kend) | (j < my_kbeg))) ? 0.0f : y;  // bitwise: no per-lane branches
+                for (int e = 0; e < 16; ++e) pv[e] = act_fwd<ACT>(__builtin_fmaf(sacc[e], p.scale, bv[e]));
+                if (masked) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = crow(e, g);
+                        pv[e] = ((j >= my_kend) | (j < my_kbeg)) ? 0.0f : pv[e];
+                    }
                 }
             } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) pv[e] = __builtin_fmaf(sacc[e], sl2, bv[e] * LOG2E);
+                if (masked) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = crow(e, g);
+                        pv[e] = ((j >= my_kend) | (j < my_kbeg)) ? -INFINITY : pv[e];
+                    }
+                }
                 float m = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = crow(e, g);
-                    float x = __builtin_fmaf(sacc[e], sl2, bv[e] * LOG2E);
-                    x = (masked & ((j >= my_kend) | (j < my_kbeg))) ? -INFINITY : x;
-                    pv[e] = x;
-                    m = fmaxf(m, x);
-                }
+                for (int e = 0; e < 16; ++e) m = fmaxf(m, pv[e]);
                 m = fmaxf(m, shfl_xor32(m));
                 const float shift = m == -INFINITY ? 0.0f : m;
                 float l = 0.0f;

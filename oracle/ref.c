@@ -43,6 +43,19 @@
  *   index (REL: clamp(i - j, lo, hi) - lo; KEYPOS: clamp(j, lo, hi) - lo) is c
  *   of dX_ij
  *
+ * Rotary position embedding (optional, rope_base > 0).  The pages name a
+ * rotary embedding fused into their block-attention kernel ("Meta redesigns AI
+ * training infrastructure...", section "Custom Kernels and 5D Parallelism for
+ * Trillion-Parameter Scale") without defining it; this is the rotation of
+ * RoFormer (Su et al.) in its split-half form.  A query or key row at
+ * sample-local position t (query i, key j; row r of a shared query block) is
+ * turned pair by pair before the scores are formed: element d < D/2 and
+ * element d + D/2 rotate by the angle t * rope_base^(-2d/D),
+ *   x'_d = x_d cos a - x_{d+D/2} sin a,   x'_{d+D/2} = x_d sin a + x_{d+D/2} cos a.
+ * X uses the turned rows; V is not turned.  The gradients returned are with
+ * respect to the rows as given, so dQ_i and dK_j are the gradients of the
+ * turned rows turned back (the rotation's transpose is the turn by -a).
+ *
  * Inputs are float32 arrays (bf16 values are exactly representable in
  * float32); all arithmetic is double.  Layout is token-major [T, H, D] with
  * int32 offsets [B+1]; a NULL q_off means one block of lq_fixed query rows
@@ -118,6 +131,8 @@ typedef struct {
     int bias_kind;
     const float *bias_table;
     int bias_lo, bias_hi;
+    double rope_base;            /* 0: no rotary embedding */
+    double *qrot, *krot;         /* turned copies of q and k (rotary embedding only) */
 } problem;
 
 static int64_t clampi(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -157,11 +172,48 @@ static const float *row_of(const problem *p, const float *base, int64_t row, int
     return base + (row * p->H + h) * (int64_t)p->D;
 }
 
+/* Element d of query row `row` (global), head h, as the scores see it: turned
+ * by the rotary embedding when there is one. */
+static double q_at(const problem *p, int64_t row, int h, int d) {
+    const int64_t e = (row * p->H + h) * (int64_t)p->D + d;
+    return p->qrot ? p->qrot[e] : (double)p->q[e];
+}
+static double k_at(const problem *p, int64_t row, int h, int d) {
+    const int64_t e = (row * p->H + h) * (int64_t)p->D + d;
+    return p->krot ? p->krot[e] : (double)p->k[e];
+}
+
+/* Rotary embedding of one row x[0..D) at position t: pair (d, d + D/2) turns
+ * by sign * t * base^(-2d/D) (sign -1: the inverse turn). */
+static void rope_turn(double *x, int D, double base, double t, int sign) {
+    const int half = D / 2;
+    for (int d = 0; d < half; ++d) {
+        const double a = sign * t * pow(base, -2.0 * d / D);
+        const double c = cos(a), sn = sin(a);
+        const double x0 = x[d], x1 = x[d + half];
+        x[d] = x0 * c - x1 * sn;
+        x[d + half] = x0 * sn + x1 * c;
+    }
+}
+
+/* Turned copy of a [rows, H, D] tensor: row r of sample b sits at position
+ * r - off[b]; with off NULL (a shared query block) row r sits at position r. */
+static double *rope_copy(const float *x, const int32_t *off, int B, int64_t rows, int H, int D,
+                         double base) {
+    double *y = (double *)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * H * D);
+    if (!y) return NULL;
+    for (int64_t e = 0; e < rows * H * D; ++e) y[e] = (double)x[e];
+    for (int b = 0; b < (off ? B : 1); ++b) {
+        const int64_t r0 = off ? off[b] : 0, r1 = off ? off[b + 1] : rows;
+        for (int64_t r = r0; r < r1; ++r)
+            for (int h = 0; h < H; ++h) rope_turn(y + (r * H + h) * (int64_t)D, D, base, (double)(r - r0), 1);
+    }
+    return y;
+}
+
 static double score(const problem *p, int h, const sample *s, int64_t i, int64_t j) {
-    const float *qi = row_of(p, p->q, s->qs + i, h);
-    const float *kj = row_of(p, p->k, s->ks + j, h);
     double dot = 0.0;
-    for (int d = 0; d < p->D; ++d) dot += (double)qi[d] * (double)kj[d];
+    for (int d = 0; d < p->D; ++d) dot += q_at(p, s->qs + i, h, d) * k_at(p, s->ks + j, h, d);
     return p->scale * dot + bias_at(p, h, i, j);
 }
 
@@ -274,14 +326,30 @@ static int nthreads_or_default(int nthreads) {
 
 static problem make_problem(const float *q, const float *k, const float *v, const int32_t *q_off,
                             int32_t lq_fixed, const int32_t *kv_off, int B, int H, int D, double scale,
-                            int act, int causal, int window, int bias_kind, const float *bias_table, int bias_lo,
-                            int bias_hi) {
+                            int act, int causal, int window, double rope_base, int bias_kind,
+                            const float *bias_table, int bias_lo, int bias_hi) {
     problem p;
     p.q = q; p.k = k; p.v = v; p.q_off = q_off; p.kv_off = kv_off; p.lq_fixed = lq_fixed;
     p.B = B; p.H = H; p.D = D; p.scale = scale; p.act = act; p.causal = causal; p.window = window;
     p.bias_kind = bias_table ? bias_kind : BIAS_NONE; p.bias_table = bias_table;
     p.bias_lo = bias_lo; p.bias_hi = bias_hi;
+    p.rope_base = rope_base;
+    p.qrot = p.krot = NULL;
     return p;
+}
+
+/* Turned copies of q and k when the problem has a rotary embedding. */
+static int rope_prepare(problem *p) {
+    if (!(p->rope_base > 0.0)) return 0;
+    const int64_t tq = p->q_off ? (int64_t)p->q_off[p->B] : p->lq_fixed;
+    p->qrot = rope_copy(p->q, p->q_off, p->B, tq, p->H, p->D, p->rope_base);
+    p->krot = rope_copy(p->k, p->kv_off, p->B, (int64_t)p->kv_off[p->B], p->H, p->D, p->rope_base);
+    return (p->qrot && p->krot) ? 0 : 2;
+}
+static void rope_release(problem *p) {
+    free(p->qrot);
+    free(p->krot);
+    p->qrot = p->krot = NULL;
 }
 
 static int64_t out_rows(const problem *p) {
@@ -344,9 +412,9 @@ static int run_bwd(const problem *p, int softmax, const float *dout, double *dq,
             double w, dx;
             pair_bwd(p, softmax, h, &s, i, j, doi, sr ? sr[0] : 0.0, sr ? sr[1] : 1.0,
                      sr ? sr[2] : 0.0, &w, &dx);
-            const float *kj = row_of(p, p->k, s.ks + j, h);
-            for (int d = 0; d < D; ++d) dqi[d] += p->scale * dx * (double)kj[d];
+            for (int d = 0; d < D; ++d) dqi[d] += p->scale * dx * k_at(p, s.ks + j, h, d);
         }
+        if (p->qrot) rope_turn(dqi, D, p->rope_base, (double)i, -1);
     }
 #pragma omp parallel for schedule(dynamic, 16) num_threads(nt)
     for (int64_t u = 0; u < tk * H; ++u) {
@@ -361,15 +429,15 @@ static int run_bwd(const problem *p, int softmax, const float *dout, double *dq,
             if (!is_valid(p, i, j, s.lq, s.lk)) continue;
             const double *sr = softmax ? st + 4 * ((s.qs + i) * H + h) : NULL;
             const float *doi = row_of(p, dout, s.qs + i, h);
-            const float *qi = row_of(p, p->q, s.qs + i, h);
             double w, dx;
             pair_bwd(p, softmax, h, &s, i, j, doi, sr ? sr[0] : 0.0, sr ? sr[1] : 1.0,
                      sr ? sr[2] : 0.0, &w, &dx);
             for (int d = 0; d < D; ++d) {
-                dkj[d] += p->scale * dx * (double)qi[d];
+                dkj[d] += p->scale * dx * q_at(p, s.qs + i, h, d);
                 dvj[d] += w * (double)doi[d];
             }
         }
+        if (p->krot) rope_turn(dkj, D, p->rope_base, (double)j, -1);
     }
     free(st);
     return 0;
@@ -414,64 +482,85 @@ static int run_dbias(const problem *p, int softmax, const float *dout, double *d
 /* ------------------------------------------------------------ exported API */
 /* act: 0 SiLU, 1 GELU (tanh form), 2 GELU (erf form).
  * bias_kind: 0 none, 1 REL (query minus key), 2 KEYPOS (key position).
+ * rope_base: 0 for no rotary embedding, else the base of its angles.
  * nthreads <= 0: OpenMP default.  Return 0 on success. */
 
 int ref_gdpa_fwd(const float *q, const float *k, const float *v, double *o, const int32_t *q_off,
                  int32_t lq_fixed, const int32_t *kv_off, int B, int H, int D, double scale, int act,
-                 int causal, int window, int bias_kind, const float *bias_table, int bias_lo, int bias_hi,
-                 int nthreads) {
-    problem p = make_problem(q, k, v, q_off, lq_fixed, kv_off, B, H, D, scale, act, causal, window, bias_kind,
-                             bias_table, bias_lo, bias_hi);
+                 int causal, int window, double rope_base, int bias_kind, const float *bias_table,
+                 int bias_lo, int bias_hi, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, lq_fixed, kv_off, B, H, D, scale, act, causal, window, rope_base,
+                             bias_kind, bias_table, bias_lo, bias_hi);
+    if (rope_prepare(&p)) { rope_release(&p); return 2; }
     run_fwd(&p, 0, o, NULL, nthreads);
+    rope_release(&p);
     return 0;
 }
 
 /* lse: [total_q_out, H] (token-major, like the outputs). */
 int ref_attn_fwd(const float *q, const float *k, const float *v, double *o, double *lse,
                  const int32_t *q_off, int32_t lq_fixed, const int32_t *kv_off, int B, int H, int D,
-                 double scale, int causal, int window, int bias_kind, const float *bias_table, int bias_lo,
-                 int bias_hi, int nthreads) {
+                 double scale, int causal, int window, double rope_base, int bias_kind,
+                 const float *bias_table, int bias_lo, int bias_hi, int nthreads) {
     problem p = make_problem(q, k, v, q_off, lq_fixed, kv_off, B, H, D, scale, ACT_SILU, causal, window,
-                             bias_kind, bias_table, bias_lo, bias_hi);
+                             rope_base, bias_kind, bias_table, bias_lo, bias_hi);
+    if (rope_prepare(&p)) { rope_release(&p); return 2; }
     run_fwd(&p, 1, o, lse, nthreads);
+    rope_release(&p);
     return 0;
 }
 
 int ref_gdpa_bwd(const float *q, const float *k, const float *v, const float *dout, double *dq,
                  double *dk, double *dv, const int32_t *q_off, const int32_t *kv_off, int B, int H,
-                 int D, double scale, int act, int causal, int window, int bias_kind, const float *bias_table,
-                 int bias_lo, int bias_hi, int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, bias_kind,
-                             bias_table, bias_lo, bias_hi);
-    return run_bwd(&p, 0, dout, dq, dk, dv, nthreads);
+                 int D, double scale, int act, int causal, int window, double rope_base, int bias_kind,
+                 const float *bias_table, int bias_lo, int bias_hi, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, rope_base,
+                             bias_kind, bias_table, bias_lo, bias_hi);
+    if (!q_off) return 1;
+    if (rope_prepare(&p)) { rope_release(&p); return 2; }
+    const int rc = run_bwd(&p, 0, dout, dq, dk, dv, nthreads);
+    rope_release(&p);
+    return rc;
 }
 
 int ref_attn_bwd(const float *q, const float *k, const float *v, const float *dout, double *dq,
                  double *dk, double *dv, const int32_t *q_off, const int32_t *kv_off, int B, int H,
-                 int D, double scale, int causal, int window, int bias_kind, const float *bias_table, int bias_lo,
-                 int bias_hi, int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, window, bias_kind,
-                             bias_table, bias_lo, bias_hi);
-    return run_bwd(&p, 1, dout, dq, dk, dv, nthreads);
+                 int D, double scale, int causal, int window, double rope_base, int bias_kind,
+                 const float *bias_table, int bias_lo, int bias_hi, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, window, rope_base,
+                             bias_kind, bias_table, bias_lo, bias_hi);
+    if (!q_off) return 1;
+    if (rope_prepare(&p)) { rope_release(&p); return 2; }
+    const int rc = run_bwd(&p, 1, dout, dq, dk, dv, nthreads);
+    rope_release(&p);
+    return rc;
 }
 
 /* dL/dtable [H][bias_hi - bias_lo + 1] of L = <O, dout> (needs a bias kind). */
 int ref_gdpa_dbias(const float *q, const float *k, const float *v, const float *dout, double *dtable,
                    const int32_t *q_off, const int32_t *kv_off, int B, int H, int D, double scale,
-                   int act, int causal, int window, int bias_kind, const float *bias_table, int bias_lo,
-                   int bias_hi, int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, bias_kind,
-                             bias_table, bias_lo, bias_hi);
-    return run_dbias(&p, 0, dout, dtable, nthreads);
+                   int act, int causal, int window, double rope_base, int bias_kind,
+                   const float *bias_table, int bias_lo, int bias_hi, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, rope_base,
+                             bias_kind, bias_table, bias_lo, bias_hi);
+    if (!q_off) return 1;
+    if (rope_prepare(&p)) { rope_release(&p); return 2; }
+    const int rc = run_dbias(&p, 0, dout, dtable, nthreads);
+    rope_release(&p);
+    return rc;
 }
 
 int ref_attn_dbias(const float *q, const float *k, const float *v, const float *dout, double *dtable,
                    const int32_t *q_off, const int32_t *kv_off, int B, int H, int D, double scale,
-                   int causal, int window, int bias_kind, const float *bias_table, int bias_lo, int bias_hi,
-                   int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, window, bias_kind,
-                             bias_table, bias_lo, bias_hi);
-    return run_dbias(&p, 1, dout, dtable, nthreads);
+                   int causal, int window, double rope_base, int bias_kind, const float *bias_table,
+                   int bias_lo, int bias_hi, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, ACT_SILU, causal, window, rope_base,
+                             bias_kind, bias_table, bias_lo, bias_hi);
+    if (!q_off) return 1;
+    if (rope_prepare(&p)) { rope_release(&p); return 2; }
+    const int rc = run_dbias(&p, 1, dout, dtable, nthreads);
+    rope_release(&p);
+    return rc;
 }
 
 /* One entry c of head h of the GDPA table gradient, summed sample by sample.
@@ -480,16 +569,17 @@ int ref_attn_dbias(const float *q, const float *k, const float *v, const float *
  * visited; the end entries (c = 0 or c = hi - lo) scan every pair of a row. */
 int ref_gdpa_dbias_entry(const float *q, const float *k, const float *v, const float *dout,
                          double *out, const int32_t *q_off, const int32_t *kv_off, int B, int H,
-                         int D, double scale, int act, int causal, int window, int bias_kind,
-                         const float *bias_table, int bias_lo, int bias_hi, int h, int c,
+                         int D, double scale, int act, int causal, int window, double rope_base,
+                         int bias_kind, const float *bias_table, int bias_lo, int bias_hi, int h, int c,
                          int nthreads) {
-    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, bias_kind,
-                             bias_table, bias_lo, bias_hi);
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, rope_base,
+                             bias_kind, bias_table, bias_lo, bias_hi);
     const int64_t W = (int64_t)bias_hi - bias_lo + 1;
     if (!q_off || p.bias_kind == BIAS_NONE || h < 0 || h >= H || c < 0 || c >= W) return 1;
+    if (rope_prepare(&p)) { rope_release(&p); return 2; }
     const int interior = c > 0 && c < W - 1;
     double *per_b = (double *)calloc((size_t)(B > 0 ? B : 1), sizeof(double));
-    if (!per_b) return 2;
+    if (!per_b) { rope_release(&p); return 2; }
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads_or_default(nthreads))
     for (int b = 0; b < B; ++b) {
         sample s = sample_rows(&p, b);
@@ -516,6 +606,7 @@ int ref_gdpa_dbias_entry(const float *q, const float *k, const float *v, const f
     for (int b = 0; b < B; ++b) tot += per_b[b];
     *out = tot;
     free(per_b);
+    rope_release(&p);
     return 0;
 }
 

@@ -53,6 +53,7 @@ class Workload:
     bias_hi: int
     backward: bool  # whether the workload includes a backward pass
     window: int = 0  # sliding window: a query sees keys at aligned distance < window (0: no window)
+    rope_base: float = 0.0  # rotary embedding of q and k by sample-local position (0: none)
 
     @property
     def lq(self) -> np.ndarray:
@@ -206,12 +207,13 @@ def make(name: str, seed: Optional[int] = None, *, B: Optional[int] = None,
                     lq_fixed=lq_fixed, kv_off=kv_off, q=q, k=k, v=v, dout=dout,
                     act=spec["act"] or "silu", scale=1.0 / math.sqrt(D), causal=spec["causal"],
                     bias_kind=bias_kind, bias_table=table, bias_lo=lo, bias_hi=hi,
-                    backward=spec["backward"], window=spec.get("window", 0))
+                    backward=spec["backward"], window=spec.get("window", 0),
+                    rope_base=float(spec.get("rope_base", 0.0)))
 
 
 def custom(*, mode="gdpa", lq, lk=None, H=2, D=64, dtype=torch.bfloat16, seed=0, sigma=1.0,
            act="silu", causal=False, bias_kind="none", bias_lo=0, bias_hi=0, bias_sigma=0.3,
-           shared_q=None, scale=None, with_dout=True, window=0) -> Workload:
+           shared_q=None, scale=None, with_dout=True, window=0, rope_base=0.0) -> Workload:
     """A workload with explicit per-sample lengths (edge cases, small shapes).
 
     ``shared_q`` = n gives one shared block of n query rows (``lq`` is ignored)."""
@@ -236,4 +238,4 @@ def custom(*, mode="gdpa", lq, lk=None, H=2, D=64, dtype=torch.bfloat16, seed=0,
                     lq_fixed=lq_fixed, kv_off=kv_off, q=q, k=k, v=v, dout=dout, act=act,
                     scale=(1.0 / math.sqrt(D)) if scale is None else scale, causal=causal,
                     bias_kind=bias_kind, bias_table=table, bias_lo=bias_lo, bias_hi=bias_hi,
-                    backward=with_dout, window=int(window))
+                    backward=with_dout, window=int(window), rope_base=float(rope_base))

@@ -29,6 +29,19 @@ def _pad(x, off, lens, L):
     return out
 
 
+def _rope(xp, base):
+    """Rotary embedding of padded [B, H, L, D] rows by their padded (sample-local)
+    index t: the halves of the head dimension form complex numbers
+    z_d = x_d + i x_{d + D/2}, multiplied by exp(i t base^(-2d/D))."""
+    D = xp.shape[-1]
+    half = D // 2
+    t = torch.arange(xp.shape[2], dtype=torch.float64).view(1, 1, -1, 1)
+    freq = torch.pow(torch.tensor(float(base), dtype=torch.float64),
+                     -2.0 * torch.arange(half, dtype=torch.float64) / D)
+    z = torch.complex(xp[..., :half], xp[..., half:]) * torch.polar(torch.ones_like(t * freq), t * freq)
+    return torch.cat([z.real, z.imag], dim=-1)
+
+
 def _unpad(xp, off, lens, T):
     H, D = xp.shape[1], xp.shape[3]
     out = torch.zeros(T, H, D, dtype=xp.dtype)
@@ -58,6 +71,8 @@ def dense(w, *, grads=True):
         out_off = w.q_off
     kp = _pad(k, w.kv_off, lk, Lk)
     vp = _pad(v, w.kv_off, lk, Lk)
+    if w.rope_base:
+        qp, kp = _rope(qp, w.rope_base), _rope(kp, w.rope_base)
 
     i = torch.arange(Lq).view(1, Lq, 1)
     j = torch.arange(Lk).view(1, 1, Lk)

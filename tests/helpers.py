@@ -5,9 +5,9 @@ from oracle import ref
 
 
 def bias_kw(w):
-    """Bias and sliding-window arguments of the oracle calls."""
+    """Bias, sliding-window and rotary-embedding arguments of the oracle calls."""
     return dict(bias_kind=w.bias_kind, bias_table=w.bias_table, bias_lo=w.bias_lo,
-                bias_hi=w.bias_hi, window=w.window)
+                bias_hi=w.bias_hi, window=w.window, rope_base=w.rope_base)
 
 
 def oracle_fwd(w, nthreads=0):

@@ -55,6 +55,13 @@
  * X uses the turned rows; V is not turned.  The gradients returned are with
  * respect to the rows as given, so dQ_i and dK_j are the gradients of the
  * turned rows turned back (the rotation's transpose is the turn by -a).
+ * With bf16 operands (rope_bf16 = 1) the turned rows are themselves operands
+ * of bf16 products, so they are bf16 values: the turn is taken in float32 and
+ * each turned element rounded to bf16 (nearest even) -- a quantisation step,
+ * taken here in the same precision as on the GPU: c and s are the float32
+ * roundings of the fp64 cosine and sine, x'_d = fmaf(x_d, c, -(x_{d+D/2} s))
+ * and x'_{d+D/2} = fmaf(x_d, s, x_{d+D/2} c) with float32 products.  The
+ * gradients then follow the rounded rows (the rounding is held fixed).
  *
  * Inputs are float32 arrays (bf16 values are exactly representable in
  * float32); all arithmetic is double.  Layout is token-major [T, H, D] with
@@ -132,6 +139,7 @@ typedef struct {
     const float *bias_table;
     int bias_lo, bias_hi;
     double rope_base;            /* 0: no rotary embedding */
+    int rope_bf16;               /* turned rows rounded to bf16 (bf16 operands) */
     double *qrot, *krot;         /* turned copies of q and k (rotary embedding only) */
 } problem;
 
@@ -196,17 +204,44 @@ static void rope_turn(double *x, int D, double base, double t, int sign) {
     }
 }
 
+/* float32 -> nearest bf16 (ties to even), returned as float32. */
+static float bf16_round(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    u &= 0xffff0000u;
+    memcpy(&x, &u, 4);
+    return x;
+}
+
+/* The turn of one row in float32, each element rounded to bf16. */
+static void rope_turn_bf16(const float *x, double *y, int D, double base, double t) {
+    const int half = D / 2;
+    for (int d = 0; d < half; ++d) {
+        const double a = t * pow(base, -2.0 * d / D);
+        const float c = (float)cos(a), sn = (float)sin(a);
+        const float x0 = x[d], x1 = x[d + half];
+        const float p0 = x1 * sn, p1 = x1 * c;
+        y[d] = bf16_round(fmaf(x0, c, -p0));
+        y[d + half] = bf16_round(fmaf(x0, sn, p1));
+    }
+}
+
 /* Turned copy of a [rows, H, D] tensor: row r of sample b sits at position
  * r - off[b]; with off NULL (a shared query block) row r sits at position r. */
 static double *rope_copy(const float *x, const int32_t *off, int B, int64_t rows, int H, int D,
-                         double base) {
+                         double base, int round_bf16) {
     double *y = (double *)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * H * D);
     if (!y) return NULL;
     for (int64_t e = 0; e < rows * H * D; ++e) y[e] = (double)x[e];
     for (int b = 0; b < (off ? B : 1); ++b) {
         const int64_t r0 = off ? off[b] : 0, r1 = off ? off[b + 1] : rows;
         for (int64_t r = r0; r < r1; ++r)
-            for (int h = 0; h < H; ++h) rope_turn(y + (r * H + h) * (int64_t)D, D, base, (double)(r - r0), 1);
+            for (int h = 0; h < H; ++h) {
+                const int64_t e = (r * H + h) * (int64_t)D;
+                if (round_bf16) rope_turn_bf16(x + e, y + e, D, base, (double)(r - r0));
+                else rope_turn(y + e, D, base, (double)(r - r0), 1);
+            }
     }
     return y;
 }
@@ -333,7 +368,8 @@ static problem make_problem(const float *q, const float *k, const float *v, cons
     p.B = B; p.H = H; p.D = D; p.scale = scale; p.act = act; p.causal = causal; p.window = window;
     p.bias_kind = bias_table ? bias_kind : BIAS_NONE; p.bias_table = bias_table;
     p.bias_lo = bias_lo; p.bias_hi = bias_hi;
-    p.rope_base = rope_base;
+    p.rope_base = fabs(rope_base);
+    p.rope_bf16 = rope_base < 0.0;
     p.qrot = p.krot = NULL;
     return p;
 }
@@ -342,8 +378,9 @@ static problem make_problem(const float *q, const float *k, const float *v, cons
 static int rope_prepare(problem *p) {
     if (!(p->rope_base > 0.0)) return 0;
     const int64_t tq = p->q_off ? (int64_t)p->q_off[p->B] : p->lq_fixed;
-    p->qrot = rope_copy(p->q, p->q_off, p->B, tq, p->H, p->D, p->rope_base);
-    p->krot = rope_copy(p->k, p->kv_off, p->B, (int64_t)p->kv_off[p->B], p->H, p->D, p->rope_base);
+    p->qrot = rope_copy(p->q, p->q_off, p->B, tq, p->H, p->D, p->rope_base, p->rope_bf16);
+    p->krot = rope_copy(p->k, p->kv_off, p->B, (int64_t)p->kv_off[p->B], p->H, p->D, p->rope_base,
+                        p->rope_bf16);
     return (p->qrot && p->krot) ? 0 : 2;
 }
 static void rope_release(problem *p) {
@@ -482,7 +519,8 @@ static int run_dbias(const problem *p, int softmax, const float *dout, double *d
 /* ------------------------------------------------------------ exported API */
 /* act: 0 SiLU, 1 GELU (tanh form), 2 GELU (erf form).
  * bias_kind: 0 none, 1 REL (query minus key), 2 KEYPOS (key position).
- * rope_base: 0 for no rotary embedding, else the base of its angles.
+ * rope_base: 0 for no rotary embedding, else the base of its angles; a negative
+ * value -b means base b with the turned rows rounded to bf16 (rope_bf16).
  * nthreads <= 0: OpenMP default.  Return 0 on success. */
 
 int ref_gdpa_fwd(const float *q, const float *k, const float *v, double *o, const int32_t *q_off,
@@ -607,6 +645,18 @@ int ref_gdpa_dbias_entry(const float *q, const float *k, const float *v, const f
     *out = tot;
     free(per_b);
     rope_release(&p);
+    return 0;
+}
+
+/* The turned copy of a [rows, H, D] tensor (positions from off as above;
+ * rope_base negative: the bf16-rounded variant), exported so the tests can pin
+ * the turn on its own. */
+int ref_rope(const float *x, double *out, const int32_t *off, int B, int64_t rows, int H, int D,
+             double rope_base) {
+    double *y = rope_copy(x, off, B, rows, H, D, fabs(rope_base), rope_base < 0.0);
+    if (!y) return 2;
+    memcpy(out, y, sizeof(double) * (size_t)rows * H * D);
+    free(y);
     return 0;
 }
 

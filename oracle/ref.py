@@ -53,6 +53,8 @@ def _load():
         lib.ref_gdpa_dbias_entry.argtypes = [P, P, P, P, P, P, P, I, I, I, D, I, I, I, D, I, P, I, I,
                                              I, I, I]
         lib.ref_act.argtypes = [I, P, P, P, ctypes.c_int64]
+        lib.ref_rope.argtypes = [P, P, P, I, ctypes.c_int64, I, I, D]
+        lib.ref_rope.restype = ctypes.c_int
         lib.ref_max_threads.argtypes = []
         for f in (lib.ref_gdpa_fwd, lib.ref_attn_fwd, lib.ref_gdpa_bwd, lib.ref_attn_bwd,
                   lib.ref_gdpa_dbias, lib.ref_attn_dbias, lib.ref_gdpa_dbias_entry,
@@ -87,6 +89,13 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
+def _rope_arg(base, bf16):
+    """The C side's rope_base: the base, negated when the turned rows are rounded to bf16."""
+    base = float(base)
+    assert base >= 0.0
+    return -base if (bf16 and base > 0.0) else base
+
+
 class _Args:
     def __init__(self, q, k, v, q_off, kv_off, lq_fixed, bias_kind, bias_table, bias_lo, bias_hi):
         self.q, self.k, self.v = _f32(q), _f32(k), _f32(v)
@@ -112,35 +121,39 @@ class _Args:
 
 
 def gdpa_fwd(q, k, v, q_off, kv_off, *, scale, act, lq_fixed=0, causal=False, window=0,
-             rope_base=0.0, bias_kind="none", bias_table=None, bias_lo=0, bias_hi=0, nthreads=0):
+             rope_base=0.0, rope_bf16=False, bias_kind="none", bias_table=None, bias_lo=0, bias_hi=0,
+             nthreads=0):
     """GDPA forward: O_i = sum_j act(scale q_i.k_j + bias_ij) v_j over valid j (q, k turned
     by the rotary embedding first when rope_base > 0)."""
     a = _Args(q, k, v, q_off, kv_off, lq_fixed, bias_kind, bias_table, bias_lo, bias_hi)
     o = np.empty((a.t_out, a.H, a.D), dtype=np.float64)
     rc = _load().ref_gdpa_fwd(_ptr(a.q), _ptr(a.k), _ptr(a.v), _ptr(o), _ptr(a.q_off), a.lq_fixed,
                               _ptr(a.kv_off), a.B, a.H, a.D, float(scale), ACTS[act], int(causal),
-                              int(window), float(rope_base), a.bias_kind, _ptr(a.bias_table),
+                              int(window), _rope_arg(rope_base, rope_bf16), a.bias_kind,
+                              _ptr(a.bias_table),
                               a.bias_lo, a.bias_hi, int(nthreads))
     assert rc == 0
     return o
 
 
 def attn_fwd(q, k, v, q_off, kv_off, *, scale, lq_fixed=0, causal=False, window=0,
-             rope_base=0.0, bias_kind="none", bias_table=None, bias_lo=0, bias_hi=0, nthreads=0):
+             rope_base=0.0, rope_bf16=False, bias_kind="none", bias_table=None, bias_lo=0, bias_hi=0,
+             nthreads=0):
     """JFA forward: row softmax over valid keys; returns (O, LSE[T, H])."""
     a = _Args(q, k, v, q_off, kv_off, lq_fixed, bias_kind, bias_table, bias_lo, bias_hi)
     o = np.empty((a.t_out, a.H, a.D), dtype=np.float64)
     lse = np.empty((a.t_out, a.H), dtype=np.float64)
     rc = _load().ref_attn_fwd(_ptr(a.q), _ptr(a.k), _ptr(a.v), _ptr(o), _ptr(lse), _ptr(a.q_off),
                               a.lq_fixed, _ptr(a.kv_off), a.B, a.H, a.D, float(scale), int(causal),
-                              int(window), float(rope_base), a.bias_kind, _ptr(a.bias_table),
+                              int(window), _rope_arg(rope_base, rope_bf16), a.bias_kind,
+                              _ptr(a.bias_table),
                               a.bias_lo, a.bias_hi, int(nthreads))
     assert rc == 0
     return o, lse
 
 
 def _bwd(fn, with_act, q, k, v, dout, q_off, kv_off, scale, act, causal, window, rope_base,
-         bias_kind, bias_table, bias_lo, bias_hi, nthreads):
+         rope_bf16, bias_kind, bias_table, bias_lo, bias_hi, nthreads):
     assert q_off is not None, "backward of a shared query block is not part of the oracle"
     a = _Args(q, k, v, q_off, kv_off, 0, bias_kind, bias_table, bias_lo, bias_hi)
     do = _f32(dout)
@@ -152,29 +165,32 @@ def _bwd(fn, with_act, q, k, v, dout, q_off, kv_off, scale, act, causal, window,
             _ptr(a.kv_off), a.B, a.H, a.D, float(scale)]
     if with_act:
         args.append(ACTS[act])
-    args += [int(causal), int(window), float(rope_base), a.bias_kind, _ptr(a.bias_table),
+    args += [int(causal), int(window), _rope_arg(rope_base, rope_bf16), a.bias_kind,
+             _ptr(a.bias_table),
              a.bias_lo, a.bias_hi, int(nthreads)]
     rc = fn(*args)
     assert rc == 0, rc
     return dq, dk, dv
 
 
-def gdpa_bwd(q, k, v, dout, q_off, kv_off, *, scale, act, causal=False, window=0, rope_base=0.0,
+def gdpa_bwd(q, k, v, dout, q_off, kv_off, *, scale, act, causal=False, window=0,
+             rope_base=0.0, rope_bf16=False,
              bias_kind="none", bias_table=None, bias_lo=0, bias_hi=0, nthreads=0):
     """GDPA backward of L = <O, dout>: returns (dQ, dK, dV) in float64."""
     return _bwd(_load().ref_gdpa_bwd, True, q, k, v, dout, q_off, kv_off, scale, act, causal, window,
-                rope_base, bias_kind, bias_table, bias_lo, bias_hi, nthreads)
+                rope_base, rope_bf16, bias_kind, bias_table, bias_lo, bias_hi, nthreads)
 
 
-def attn_bwd(q, k, v, dout, q_off, kv_off, *, scale, causal=False, window=0, rope_base=0.0,
+def attn_bwd(q, k, v, dout, q_off, kv_off, *, scale, causal=False, window=0,
+             rope_base=0.0, rope_bf16=False,
              bias_kind="none", bias_table=None, bias_lo=0, bias_hi=0, nthreads=0):
     """JFA backward of L = <O, dout>: returns (dQ, dK, dV) in float64."""
     return _bwd(_load().ref_attn_bwd, False, q, k, v, dout, q_off, kv_off, scale, None, causal, window,
-                rope_base, bias_kind, bias_table, bias_lo, bias_hi, nthreads)
+                rope_base, rope_bf16, bias_kind, bias_table, bias_lo, bias_hi, nthreads)
 
 
 def _dbias(fn, with_act, q, k, v, dout, q_off, kv_off, scale, act, causal, window, rope_base,
-           bias_kind, bias_table, bias_lo, bias_hi, nthreads):
+           rope_bf16, bias_kind, bias_table, bias_lo, bias_hi, nthreads):
     assert q_off is not None and bias_kind != "none"
     a = _Args(q, k, v, q_off, kv_off, 0, bias_kind, bias_table, bias_lo, bias_hi)
     do = _f32(dout)
@@ -184,41 +200,59 @@ def _dbias(fn, with_act, q, k, v, dout, q_off, kv_off, scale, act, causal, windo
             a.B, a.H, a.D, float(scale)]
     if with_act:
         args.append(ACTS[act])
-    args += [int(causal), int(window), float(rope_base), a.bias_kind, _ptr(a.bias_table),
+    args += [int(causal), int(window), _rope_arg(rope_base, rope_bf16), a.bias_kind,
+             _ptr(a.bias_table),
              a.bias_lo, a.bias_hi, int(nthreads)]
     rc = fn(*args)
     assert rc == 0, rc
     return dt
 
 
-def gdpa_dbias(q, k, v, dout, q_off, kv_off, *, scale, act, causal=False, window=0, rope_base=0.0,
+def gdpa_dbias(q, k, v, dout, q_off, kv_off, *, scale, act, causal=False, window=0,
+               rope_base=0.0, rope_bf16=False,
                bias_kind, bias_table, bias_lo, bias_hi, nthreads=0):
     """GDPA: dL/dtable [H, hi - lo + 1] of L = <O, dout> (float64)."""
     return _dbias(_load().ref_gdpa_dbias, True, q, k, v, dout, q_off, kv_off, scale, act, causal,
-                  window, rope_base, bias_kind, bias_table, bias_lo, bias_hi, nthreads)
+                  window, rope_base, rope_bf16, bias_kind, bias_table, bias_lo, bias_hi, nthreads)
 
 
-def attn_dbias(q, k, v, dout, q_off, kv_off, *, scale, causal=False, window=0, rope_base=0.0,
+def attn_dbias(q, k, v, dout, q_off, kv_off, *, scale, causal=False, window=0,
+               rope_base=0.0, rope_bf16=False,
                bias_kind, bias_table, bias_lo, bias_hi, nthreads=0):
     """JFA: dL/dtable [H, hi - lo + 1] of L = <O, dout> (float64)."""
     return _dbias(_load().ref_attn_dbias, False, q, k, v, dout, q_off, kv_off, scale, None, causal,
-                  window, rope_base, bias_kind, bias_table, bias_lo, bias_hi, nthreads)
+                  window, rope_base, rope_bf16, bias_kind, bias_table, bias_lo, bias_hi, nthreads)
 
 
 def gdpa_dbias_entry(q, k, v, dout, q_off, kv_off, *, scale, act, causal=False, window=0,
-                     rope_base=0.0, bias_kind, bias_table, bias_lo, bias_hi, h, c, nthreads=0):
+                     rope_base=0.0, rope_bf16=False, bias_kind, bias_table, bias_lo, bias_hi, h, c, nthreads=0):
     """One entry (head h, index c) of the GDPA table gradient, in float64."""
     a = _Args(q, k, v, q_off, kv_off, 0, bias_kind, bias_table, bias_lo, bias_hi)
     do = _f32(dout)
     out = np.zeros(1, dtype=np.float64)
     rc = _load().ref_gdpa_dbias_entry(_ptr(a.q), _ptr(a.k), _ptr(a.v), _ptr(do), _ptr(out),
                                       _ptr(a.q_off), _ptr(a.kv_off), a.B, a.H, a.D, float(scale),
-                                      ACTS[act], int(causal), int(window), float(rope_base),
+                                      ACTS[act], int(causal), int(window),
+                                      _rope_arg(rope_base, rope_bf16),
                                       a.bias_kind,
                                       _ptr(a.bias_table),
                                       a.bias_lo, a.bias_hi, int(h), int(c), int(nthreads))
     assert rc == 0, rc
     return float(out[0])
+
+
+def rope(x, off, *, rope_base, rope_bf16=False):
+    """The rotary turn of a [rows, H, D] tensor by sample-local positions (off: int32
+    [B+1], or None for one block whose row r sits at position r), in float64; with
+    rope_bf16 the float32 turn rounded to bf16."""
+    x = _f32(x)
+    o = _i32(off)
+    y = np.empty(x.shape, dtype=np.float64)
+    B = 1 if o is None else len(o) - 1
+    rc = _load().ref_rope(_ptr(x), _ptr(y), _ptr(o), B, x.shape[0], x.shape[1], x.shape[2],
+                          _rope_arg(rope_base, rope_bf16))
+    assert rc == 0, rc
+    return y
 
 
 def act(name, x):

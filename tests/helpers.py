@@ -1,13 +1,16 @@
 """Shared test helpers: run the oracle on a synthetic workload, compare results."""
 import numpy as np
+import torch
 
 from oracle import ref
 
 
 def bias_kw(w):
-    """Bias, sliding-window and rotary-embedding arguments of the oracle calls."""
+    """Bias, sliding-window and rotary-embedding arguments of the oracle calls.  With
+    bf16 operands the turned rows are bf16 values (rounded as the GPU rounds them)."""
     return dict(bias_kind=w.bias_kind, bias_table=w.bias_table, bias_lo=w.bias_lo,
-                bias_hi=w.bias_hi, window=w.window, rope_base=w.rope_base)
+                bias_hi=w.bias_hi, window=w.window, rope_base=w.rope_base,
+                rope_bf16=w.dtype == torch.bfloat16)
 
 
 def oracle_fwd(w, nthreads=0):
@@ -87,12 +90,15 @@ def softmax_grad_floor(w, name):
     are fp32 dot products of length D of size up to D max|dO| max|V|.  Rows that
     cancel keep the absolute rounding of that difference: this floor is 16 fp32
     unit roundoffs (2^-20) of its largest possible size, times scale and max|K|
-    (dQ) or max|Q| (dK)."""
+    (dQ) or max|Q| (dK).  With the rotary embedding a turned element can reach
+    sqrt(2) times the largest input element, and turning the gradient back mixes
+    the errors of a pair (another sqrt(2)): a factor 2."""
     if w.mode != "jfa" or name not in ("dq", "dk") or w.dout is None:
         return 0.0
     other = w.k if name == "dq" else w.q
     mx = lambda t: float(t.float().abs().max()) if t.numel() else 0.0
-    return w.scale * mx(other) * mx(w.dout) * mx(w.v) * w.D * 2.0 ** -20
+    turn = 2.0 if w.rope_base else 1.0
+    return turn * w.scale * mx(other) * mx(w.dout) * mx(w.v) * w.D * 2.0 ** -20
 
 
 def row_check(got, want, tau, what="", floor_frac=1e-6, zero_rows=None, abs_floor=0.0):

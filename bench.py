@@ -42,7 +42,8 @@ KERNEL_SOURCES = ["ja_fwd.hip", "ja_bwd.hip", "ja_plan.hip", "ja_tiles.h", "ja_d
 # Workloads: which roofline bounds them (short K/V streams Q / dO / O through HBM;
 # long sequences are MFMA work).
 BOUND = {"gdpa_xattn_short_kv": "hbm", "pma_gdpa_fwd": "hbm", "jfa_causal_self": "mfma",
-         "longtail_gdpa": "mfma", "tiny_gdpa_fp32": "alu", "jfa_swa_causal_self": "mfma"}
+         "longtail_gdpa": "mfma", "tiny_gdpa_fp32": "alu", "jfa_swa_causal_self": "mfma",
+         "jfa_rope_causal_self": "mfma"}
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (the plain fp32 kernels are ALU loops)
 
 
@@ -106,6 +107,8 @@ def kernel_cost(w, kernel: str) -> tuple[float, float]:
         return e * HD * 2 * tq + 4 * w.H * tq, 2.0 * HD * tq
     if kernel == "bwd_dbias":  # read Q, dO, K, V; recompute S and dP (two GEMMs per pair)
         return e * HD * (2 * tq + 2 * tk), 4.0 * w.D * P
+    if kernel in ("rope", "rope_back"):  # read and write every row of q and k (dq and dk)
+        return e * HD * 2 * (w.q.shape[0] + w.total_k), 0.0
     return 0.0, 0.0
 
 
@@ -157,7 +160,7 @@ class Runner:
             total_k=w.total_k, q_offsets=self.q_off, kv_offsets=self.kv_off,
             lq_fixed=w.lq_fixed, causal=w.causal, scale=w.scale, act=w.act,
             bias_kind=w.bias_kind, bias_table=self.bias, bias_lo=w.bias_lo, bias_hi=w.bias_hi,
-            max_kv_len=self.max_kv_len, window=w.window)
+            max_kv_len=self.max_kv_len, window=w.window, rope_base=w.rope_base)
         rows = w.total_q_out
         self.o = torch.empty((rows, w.H, w.D), dtype=w.dtype, device=dev)
         self.lse = torch.empty((w.H, rows), dtype=torch.float32, device=dev)
@@ -176,19 +179,21 @@ class Runner:
             self.ws_b = torch.empty(_lib.ja_workspace_size(self.prob, pass_b), dtype=torch.uint8, device=dev)
 
     def kernels(self):
+        rope = ["rope"] if self.w.rope_base else []
+        rope_back = ["rope_back"] if (self.w.rope_base and self.backward) else []
         if self.w.dtype == torch.float32:  # plain fp32 kernels: no planner, no short / fused units
-            ks = ["fwd"]
+            ks = rope + ["fwd"]
             if self.backward:
                 ks += (["bwd_delta"] if self.w.mode == "jfa" else []) + ["bwd_q", "bwd_kv"]
                 ks += ["bwd_dbias"] if self.bias_grad else []
-            return ks
+            return ks + rope_back
         long_units = not (0 < self.max_kv_len <= SHORT_KV)  # else those kernels are not launched
-        ks = ["plan", "fwd_short"] + (["fwd"] if long_units else [])
+        ks = rope + ["plan", "fwd_short"] + (["fwd"] if long_units else [])
         if self.backward:
             ks += ["bwd_fused"] + (["bwd_kv", "bwd_q"] if long_units else [])
             ks += ["bwd_delta"] if self.w.mode == "jfa" else []
             ks += ["bwd_dbias"] if self.bias_grad else []
-        return ks
+        return ks + rope_back
 
     def step(self):
         p, w = self.prob, self.w
@@ -242,7 +247,8 @@ def measured_traffic(workload, kernel):
 # Device-side kernel names of the library's kernels, as profilers list them.
 KERNEL_SYMBOLS = {"plan": "plan_kernel", "fwd": "ja::fwd_kernel<", "fwd_short": "fwd_short_kernel",
                   "bwd_fused": "ja::fused_kernel<", "bwd_kv": "dkdv_kernel<", "bwd_q": "dq_kernel<",
-                  "bwd_delta": "delta_kernel<", "bwd_dbias": "dbias_kernel<"}
+                  "bwd_delta": "delta_kernel<", "bwd_dbias": "dbias_kernel<", "rope": "rope_kernel<",
+                  "rope_back": "rope_kernel<"}
 
 
 def write_traffic(workload, kernel, fetch_csv, write_csv, copy_mib, command):
@@ -445,7 +451,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "B": w.B, "H": w.H, "D": w.D,
                    "total_q": w.total_q, "total_k": w.total_k, "act": w.act if w.mode == "gdpa" else "softmax",
-                   "causal": w.causal, "window": w.window, "bias": w.bias_kind, "jagged_sparsity": round(sparsity, 4),
+                   "causal": w.causal, "window": w.window, "rope_base": w.rope_base, "bias": w.bias_kind, "jagged_sparsity": round(sparsity, 4),
                    "useful_pairs": P, "backward": runner.backward, "bias_grad": runner.bias_grad},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),

@@ -40,6 +40,18 @@
  * queries); the output still has one row block per sample:
  * [B * lq_fixed, H, D], sample b at rows b * lq_fixed.  Forward only.
  *
+ * Rotary embedding.  With rope_base > 0 every query and key row is turned
+ * before the scores are formed: element d < D/2 and element d + D/2 of a row at
+ * sample-local position t (query i, key j; row r of a shared query block) turn
+ * by the angle t * rope_base^(-2d/D):
+ *   x'_d = x_d cos a - x_{d+D/2} sin a,   x'_{d+D/2} = x_d sin a + x_{d+D/2} cos a
+ * (RoFormer's rotation in split-half form; values are not turned).  The pages
+ * name a rotary embedding fused into their block-attention kernel ("Meta
+ * redesigns AI training infrastructure...", section "Custom Kernels and 5D
+ * Parallelism for Trillion-Parameter Scale") without defining it.  The turned
+ * rows live in the workspace; the backward entry points return gradients with
+ * respect to the rows as given.
+ *
  * Bias.  An fp32 table [H][bias_hi - bias_lo + 1] on the device, added after
  * the scale, before the activation / softmax:
  *   JA_BIAS_REL     table[h][clamp(i - j, bias_lo, bias_hi) - bias_lo]
@@ -120,12 +132,15 @@ typedef struct ja_problem {
                                     that some sample exceeds gives undefined results, like
                                     invalid offsets.  Negative: JA_ERR_SHAPE. */
     int32_t window;              /* sliding window w (0 = none, negative: JA_ERR_SHAPE) */
+    float rope_base;             /* rotary embedding base (commonly 10000), 0 = none; negative,
+                                    infinite or NaN: JA_ERR_SHAPE */
 } ja_problem;
 
 /* Workspace bytes that the given pass of either attention form needs (0 only
- * for invalid problems).  Depends on B, H, D, total_q, total_k, lq_fixed and
- * dtype (JA_PASS_BWD_DBIAS: also the bias range); the same value serves GDPA
- * and JFA. */
+ * for invalid problems).  Depends on B, H, D, total_q, total_k, lq_fixed,
+ * dtype and whether rope_base > 0 (the turned copies of q and k), and for
+ * JA_PASS_BWD_DBIAS also on the bias range; the same value serves GDPA and
+ * JFA. */
 size_t ja_workspace_size(const ja_problem *p, int pass);
 
 /* GDPA forward.  q [Tq, H, D] (or [lq_fixed, H, D]), k, v [Tk, H, D],
@@ -177,7 +192,9 @@ typedef enum {
     JA_KERNEL_BWD_Q = 4,      /* backward dQ units */
     JA_KERNEL_BWD_DELTA = 5,  /* JFA backward delta preprocess */
     JA_KERNEL_FWD_SHORT = 6,  /* forward attention, samples with <= 32 keys */
-    JA_KERNEL_BWD_DBIAS = 7   /* bias-table gradient (both of its kernels) */
+    JA_KERNEL_BWD_DBIAS = 7,  /* bias-table gradient (both of its kernels) */
+    JA_KERNEL_ROPE = 8,       /* rotary embedding of q and k (one launch) */
+    JA_KERNEL_ROPE_BACK = 9   /* backward: dq and dk turned back (one launch) */
 } ja_kernel_id;
 
 /* From now on, in every call made by the calling thread, record start_event

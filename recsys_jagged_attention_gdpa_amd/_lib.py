@@ -29,7 +29,7 @@ EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_at
            "jagged_attn_bwd", "ja_profile_kernel", "ja_status_string", "ja_last_hip_error",
            "ja_version")
 KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5,
-           "fwd_short": 6, "bwd_dbias": 7}
+           "fwd_short": 6, "bwd_dbias": 7, "rope": 8, "rope_back": 9}
 
 
 class JaProblem(ctypes.Structure):
@@ -40,6 +40,7 @@ class JaProblem(ctypes.Structure):
         ("kv_offsets", ctypes.c_void_p), ("scale", ctypes.c_float), ("act", ctypes.c_int32),
         ("bias_kind", ctypes.c_int32), ("bias_lo", ctypes.c_int32), ("bias_hi", ctypes.c_int32),
         ("bias_table", ctypes.c_void_p), ("max_kv_len", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
     ]
 
 
@@ -105,7 +106,8 @@ def _stream(stream):
 
 def make_problem(*, batch, heads, head_dim, dtype, total_q, total_k, q_offsets, kv_offsets,
                  lq_fixed=0, causal=False, scale=None, act="silu", bias_kind="none",
-                 bias_table=None, bias_lo=0, bias_hi=0, max_kv_len=0, window=0) -> JaProblem:
+                 bias_table=None, bias_lo=0, bias_hi=0, max_kv_len=0, window=0,
+                 rope_base=0.0) -> JaProblem:
     """Fill a JaProblem.  Offsets and the bias table are device tensors (or raw pointers)."""
     p = JaProblem()
     p.batch, p.heads, p.head_dim = int(batch), int(heads), int(head_dim)
@@ -122,6 +124,7 @@ def make_problem(*, batch, heads, head_dim, dtype, total_q, total_k, q_offsets, 
     p.bias_table = _ptr(bias_table)
     p.max_kv_len = int(max_kv_len)
     p.window = int(window)
+    p.rope_base = float(rope_base)
     return p
 
 

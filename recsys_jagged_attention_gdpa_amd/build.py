@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libjagged_attn.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["ja_api.cpp", "ja_plan.hip", "ja_fwd.hip", "ja_bwd.hip", "ja_dbias.hip", "ja_f32.hip"]
+SOURCES = ["ja_api.cpp", "ja_plan.hip", "ja_fwd.hip", "ja_bwd.hip", "ja_dbias.hip", "ja_f32.hip",
+           "ja_rope.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cmath>
 #include <cstdint>
 
 #include "ja_kernels.h"
@@ -42,7 +43,7 @@ int64_t tile_cap(int64_t rows, int B, int tile) { return rows / tile + B + 1; }
 
 struct Layout {
     size_t counters;  // 4 PlanCounters blocks
-    size_t tiles_q, tiles_k, tiles_s, delta, tiles_a, dbias_part, total;
+    size_t tiles_q, tiles_k, tiles_s, delta, tiles_a, dbias_part, rope_q, rope_k, total;
     int64_t cap_q, cap_k, cap_s;
 };
 
@@ -72,6 +73,13 @@ Layout layout_of(const ja_problem &p, int pass) {
         off += align_up((size_t)L.cap_q * sizeof(int2));
         L.dbias_part = off;
         off += align_up((size_t)ja::DBIAS_GRID * p.heads * (size_t)bias_width(p) * sizeof(float));
+    }
+    if (p.rope_base > 0.0f) {  // turned copies of q and k
+        const size_t row = (size_t)p.heads * p.head_dim * (p.dtype == JA_BF16 ? 2 : 4);
+        L.rope_q = off;
+        off += align_up((size_t)(p.total_q > 0 ? p.total_q : 1) * row);
+        L.rope_k = off;
+        off += align_up((size_t)(p.total_k > 0 ? p.total_k : 1) * row);
     }
     L.total = off;
     return L;
@@ -103,6 +111,7 @@ ja_status check_problem(const ja_problem *p, int pass) {
     if (!(p->scale == p->scale)) return JA_ERR_SHAPE;  // NaN scale
     if (p->max_kv_len < 0) return JA_ERR_SHAPE;
     if (p->window < 0) return JA_ERR_SHAPE;
+    if (!(p->rope_base >= 0.0f) || std::isinf(p->rope_base)) return JA_ERR_SHAPE;  // NaN, negative, inf
     // Kernels address a (sample, head) slice with 32-bit byte offsets; bounding
     // every [rows, H, D] tensor below 4 GiB bounds every slice (the sample
     // lengths themselves live on the device).
@@ -177,6 +186,30 @@ ja::PlanParams plan_of(const ja_problem &p, int kind, int tile_rows, int inner_r
     return q;
 }
 
+// Rotary embedding: turn q and k into the workspace copies (sign +1) and point
+// the attention parameters at them, or turn dq and dk back in place (sign -1).
+hipError_t rope_turn(const ja_problem &p, const void *q_src, void *q_dst, const void *k_src, void *k_dst,
+                     float sign, int timer_id, hipStream_t s) {
+    ja::RopeParams r{};
+    r.seg[0] = ja::RopeSeg{q_src, q_dst, p.q_offsets, p.total_q, p.batch};
+    r.seg[1] = ja::RopeSeg{k_src, k_dst, p.kv_offsets, p.total_k, p.batch};
+    r.H = p.heads;
+    r.sign = sign;
+    const double base = (double)p.rope_base;
+    for (int d = 0; d < p.head_dim / 2; ++d) r.inv_freq[d] = std::pow(base, -2.0 * d / p.head_dim);
+    return ja::launch_rope(r, p.head_dim, p.dtype == JA_F32, timer_id, s);
+}
+
+hipError_t rope_inputs(const ja_problem &p, const Layout &L, void *ws, ja::AttnParams &a, hipStream_t s) {
+    if (!(p.rope_base > 0.0f)) return hipSuccess;
+    char *w = static_cast<char *>(ws);
+    void *qr = w + L.rope_q, *kr = w + L.rope_k;
+    const hipError_t e = rope_turn(p, a.q, qr, a.k, kr, 1.0f, ja::K_ROPE, s);
+    a.q = qr;
+    a.k = kr;
+    return e;
+}
+
 ja_status hip_status(hipError_t e) {
     if (e == hipSuccess) return JA_OK;
     g_last_hip_error = (int)e;
@@ -202,6 +235,8 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
     a.out = o;
     a.lse = lse;
     a.o_res_out = p->dtype == JA_BF16 ? o_res : nullptr;
+    hipError_t e = rope_inputs(*p, L, ws, a, s);
+    if (e != hipSuccess) return hip_status(e);
     if (p->dtype == JA_F32) return hip_status(ja::launch_fwd_f32(a, p->head_dim, mode, p->act, s));
     // two unit lists: query tiles of samples with more than 32 keys, and whole
     // (sample, head) units of samples with at most 32 keys
@@ -215,7 +250,7 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
     const bool long_units = !(p->max_kv_len > 0 && p->max_kv_len <= ja::FUSED_MAX_LK);
     ja::PlanParams pp[2] = {plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3),
                             plan_of(*p, ja::PLAN_Q_TILES, q_tile, kv_tile, 1, a.tiles, L.cap_q, a.counters)};
-    hipError_t e = ja::launch_plan(pp, long_units ? 2 : 1, s);
+    e = ja::launch_plan(pp, long_units ? 2 : 1, s);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(ja::launch_fwd_bf16(a, p->head_dim, mode, p->act, cu_count(), few_q, long_units, s));
 }
@@ -246,7 +281,14 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
     a.dk = dk;
     a.dv = dv;
     a.lse = const_cast<float *>(lse);
-    if (p->dtype == JA_F32) return hip_status(ja::launch_bwd_f32(a, p->head_dim, mode, p->act, s));
+    const bool rope = p->rope_base > 0.0f;
+    hipError_t e = rope_inputs(*p, L, ws, a, s);
+    if (e != hipSuccess) return hip_status(e);
+    if (p->dtype == JA_F32) {
+        e = ja::launch_bwd_f32(a, p->head_dim, mode, p->act, s);
+        if (e == hipSuccess && rope) e = rope_turn(*p, dq, dq, dk, dk, -1.0f, ja::K_ROPE_BACK, s);
+        return hip_status(e);
+    }
     const bool long_units = !(p->max_kv_len > 0 && p->max_kv_len <= ja::FUSED_MAX_LK);
     ja::PlanParams pp[ja::PLAN_MAX];
     int n = 0;
@@ -257,10 +299,12 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
     }
     if (dbias)  // query tiles of every sample, short ones included
         pp[n++] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 0, a.tiles4, L.cap_q, a.counters4);
-    hipError_t e = ja::launch_plan(pp, n, s);
+    e = ja::launch_plan(pp, n, s);
     if (e != hipSuccess) return hip_status(e);
     e = ja::launch_bwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), long_units, s);
     if (e == hipSuccess && dbias) e = ja::launch_dbias_bf16(a, p->head_dim, mode, p->act, s);
+    // the kernels produced the gradients of the turned rows: turn them back
+    if (e == hipSuccess && rope) e = rope_turn(*p, dq, dq, dk, dk, -1.0f, ja::K_ROPE_BACK, s);
     return hip_status(e);
 }
 
@@ -271,7 +315,7 @@ const ja::KernelTimer &ja::kernel_timer() { return g_timer; }
 extern "C" {
 
 ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event) {
-    if (kernel_id < JA_KERNEL_PLAN || kernel_id > JA_KERNEL_BWD_DBIAS) return JA_ERR_UNSUPPORTED;
+    if (kernel_id < JA_KERNEL_PLAN || kernel_id > JA_KERNEL_ROPE_BACK) return JA_ERR_UNSUPPORTED;
     if ((start_event == nullptr) != (stop_event == nullptr)) return JA_ERR_NULL;
     g_timer.which = start_event ? kernel_id : -1;
     g_timer.start = static_cast<hipEvent_t>(start_event);
@@ -321,6 +365,6 @@ const char *ja_status_string(int status) {
 
 int ja_last_hip_error(void) { return g_last_hip_error; }
 
-int ja_version(void) { return 100; }
+int ja_version(void) { return 200; }
 
 }  // extern "C"

@@ -126,7 +126,7 @@ hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream);
 // Optional per-kernel event recording around launches (measurement aid).
 enum KernelId {
     K_PLAN = 0, K_FWD = 1, K_BWD_FUSED = 2, K_BWD_KV = 3, K_BWD_Q = 4, K_BWD_DELTA = 5, K_FWD_SHORT = 6,
-    K_BWD_DBIAS = 7
+    K_BWD_DBIAS = 7, K_ROPE = 8, K_ROPE_BACK = 9
 };
 struct KernelTimer {
     int which = -1;
@@ -152,6 +152,25 @@ hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int gr
                            hipStream_t stream);
 // Bias-table gradient (p.dbias, p.dbias_part, p.tiles4 / p.counters4 planned).
 hipError_t launch_dbias_bf16(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
+// Rotary embedding pass: up to two segments (rows of one [rows, H, D] tensor
+// each, with the offsets that give each row its sample-local position, or
+// NULL for a shared block whose row r sits at position r), turned by
+// sign * t * base^(-2d/D) from src into dst (dst may equal src).
+struct RopeSeg {
+    const void *src;
+    void *dst;
+    const int32_t *off;
+    int64_t rows;
+    int B;
+};
+constexpr int ROPE_MAX_HALF = 64;  // D / 2 for the largest head dimension
+struct RopeParams {
+    RopeSeg seg[2];
+    int H;
+    float sign;                       // +1 forward turn, -1 inverse
+    double inv_freq[ROPE_MAX_HALF];   // base^(-2d/D), d < D/2
+};
+hipError_t launch_rope(const RopeParams &p, int D, bool f32, int timer_id, hipStream_t stream);
 hipError_t launch_fwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
 hipError_t launch_bwd_f32(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
 

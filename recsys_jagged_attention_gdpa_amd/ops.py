@@ -10,7 +10,9 @@ max_kv_len (0 = unknown) is an optional upper bound on every sample's key
 count; a bound of at most 32 lets the library skip its long-sequence kernels.
 window (0 = none) keeps the pairs whose aligned distance i + Lk - Lq - j is
 below it (and, without causal masking, above minus it): sliding-window
-attention.
+attention.  rope_base (0 = none) turns q and k by the rotary embedding of
+their sample-local positions before the scores are formed; gradients are with
+respect to the rows as given.
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ from . import _lib
 
 
 def _problem(q, k, q_offsets, kv_offsets, *, causal, scale, act, bias, bias_kind, bias_lo,
-             bias_hi, max_kv_len=0, window=0):
+             bias_hi, max_kv_len=0, window=0, rope_base=0.0):
     B = int(kv_offsets.numel()) - 1
     H, D = int(q.shape[1]), int(q.shape[2])
     return _lib.make_problem(
@@ -28,7 +30,7 @@ def _problem(q, k, q_offsets, kv_offsets, *, causal, scale, act, bias, bias_kind
         total_k=int(k.shape[0]), q_offsets=q_offsets, kv_offsets=kv_offsets,
         lq_fixed=0 if q_offsets is not None else int(q.shape[0]), causal=causal, scale=scale,
         act=act, bias_kind=bias_kind if bias is not None else "none", bias_table=bias,
-        bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len, window=window)
+        bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len, window=window, rope_base=rope_base)
 
 
 def _check_inputs(q, k, v, q_offsets, kv_offsets, bias):
@@ -52,11 +54,12 @@ def _workspace(problem, pass_, device):
 
 
 def gdpa_forward(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False,
-                 bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, window=0):
+                 bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, window=0,
+                 rope_base=0.0):
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act=act, bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len,
-                 window=window)
+                 window=window, rope_base=rope_base)
     rows = q.shape[0] if q_offsets is not None else p.batch * q.shape[0]
     o = torch.empty((rows, q.shape[1], q.shape[2]), dtype=q.dtype, device=q.device)
     ws = _workspace(p, _lib.PASS_FWD, q.device)
@@ -65,12 +68,13 @@ def gdpa_forward(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, caus
 
 
 def attn_forward(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bias=None,
-                 bias_kind="none", bias_lo=0, bias_hi=0, residual=True, max_kv_len=0, window=0):
+                 bias_kind="none", bias_lo=0, bias_hi=0, residual=True, max_kv_len=0, window=0,
+                 rope_base=0.0):
     """Returns (O, LSE[H, T], O_residual); O_residual is None for fp32 or residual=False."""
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act="silu", bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len,
-                 window=window)
+                 window=window, rope_base=rope_base)
     rows = q.shape[0] if q_offsets is not None else p.batch * q.shape[0]
     o = torch.empty((rows, q.shape[1], q.shape[2]), dtype=q.dtype, device=q.device)
     lse = torch.empty((q.shape[1], rows), dtype=torch.float32, device=q.device)
@@ -91,12 +95,12 @@ def _dbias_out(p, bias, with_dbias):
 
 def gdpa_backward(q, k, v, dout, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False,
                   bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, window=0,
-                  with_dbias=False):
+                  rope_base=0.0, with_dbias=False):
     """(dQ, dK, dV), plus the bias table's gradient last when with_dbias."""
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act=act, bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len,
-                 window=window)
+                 window=window, rope_base=rope_base)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     db, pass_ = _dbias_out(p, bias, with_dbias)
     ws = _workspace(p, pass_, q.device)
@@ -106,12 +110,12 @@ def gdpa_backward(q, k, v, dout, q_offsets, kv_offsets, *, act="silu", scale=Non
 
 def attn_backward(q, k, v, o, dout, lse, q_offsets, kv_offsets, *, o_residual=None, scale=None,
                   causal=False, bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0,
-                  window=0, with_dbias=False):
+                  window=0, rope_base=0.0, with_dbias=False):
     """(dQ, dK, dV), plus the bias table's gradient last when with_dbias."""
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act="silu", bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len,
-                 window=window)
+                 window=window, rope_base=rope_base)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     db, pass_ = _dbias_out(p, bias, with_dbias)
     ws = _workspace(p, pass_, q.device)
@@ -122,9 +126,10 @@ def attn_backward(q, k, v, o, dout, lse, q_offsets, kv_offsets, *, o_residual=No
 class _GDPAFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, q_offsets, kv_offsets, act, scale, causal, bias, bias_kind, bias_lo,
-                bias_hi, max_kv_len, window):
+                bias_hi, max_kv_len, window, rope_base):
         kw = dict(act=act, scale=scale, causal=causal, bias=bias, bias_kind=bias_kind,
-                  bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len, window=window)
+                  bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len, window=window,
+                  rope_base=rope_base)
         ctx.kw = kw
         ctx.save_for_backward(q, k, v, q_offsets, kv_offsets)
         return gdpa_forward(q, k, v, q_offsets, kv_offsets, **kw)
@@ -135,15 +140,15 @@ class _GDPAFunction(torch.autograd.Function):
         want_db = ctx.needs_input_grad[8]  # the bias table
         g = gdpa_backward(q, k, v, do, q_offsets, kv_offsets, with_dbias=want_db, **ctx.kw)
         db = g[3] if want_db else None
-        return g[0], g[1], g[2], None, None, None, None, None, db, None, None, None, None, None
+        return g[0], g[1], g[2], None, None, None, None, None, db, None, None, None, None, None, None
 
 
 class _JFAFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, q_offsets, kv_offsets, scale, causal, bias, bias_kind, bias_lo,
-                bias_hi, max_kv_len, window):
+                bias_hi, max_kv_len, window, rope_base):
         kw = dict(scale=scale, causal=causal, bias=bias, bias_kind=bias_kind, bias_lo=bias_lo,
-                  bias_hi=bias_hi, max_kv_len=max_kv_len, window=window)
+                  bias_hi=bias_hi, max_kv_len=max_kv_len, window=window, rope_base=rope_base)
         o, lse, o_res = attn_forward(q, k, v, q_offsets, kv_offsets, **kw)
         ctx.kw = kw
         ctx.save_for_backward(q, k, v, o, lse, o_res, q_offsets, kv_offsets)
@@ -156,20 +161,21 @@ class _JFAFunction(torch.autograd.Function):
         g = attn_backward(q, k, v, o, do, lse, q_offsets, kv_offsets, o_residual=o_res,
                           with_dbias=want_db, **ctx.kw)
         db = g[3] if want_db else None
-        return g[0], g[1], g[2], None, None, None, None, db, None, None, None, None, None
+        return g[0], g[1], g[2], None, None, None, None, db, None, None, None, None, None, None
 
 
 def gdpa(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False, bias=None,
-         bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, window=0):
+         bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, window=0, rope_base=0.0):
     """Jagged GDPA with autograd (backward needs per-sample query offsets; a bias table
     that requires grad gets its gradient)."""
     return _GDPAFunction.apply(q, k, v, q_offsets, kv_offsets, act, scale, causal, bias,
-                               bias_kind, bias_lo, bias_hi, max_kv_len, window)
+                               bias_kind, bias_lo, bias_hi, max_kv_len, window, rope_base)
 
 
 def jagged_attention(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bias=None,
-                     bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, window=0):
+                     bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, window=0,
+                     rope_base=0.0):
     """Jagged flash attention (softmax) with autograd (a bias table that requires grad gets
     its gradient)."""
     return _JFAFunction.apply(q, k, v, q_offsets, kv_offsets, scale, causal, bias, bias_kind,
-                              bias_lo, bias_hi, max_kv_len, window)
+                              bias_lo, bias_hi, max_kv_len, window, rope_base)

@@ -145,6 +145,12 @@ CATALOGUE = {
     "jfa_swa_causal_self": dict(mode="jfa", B=64, H=8, D=128, dtype="bf16", q_len=("uniform", 1, 8192),
                                 kv_len="same", qkv_sigma=1.0, act=None, causal=True, bias=None,
                                 backward=True, window=1024, same_draw_as="jfa_causal_self"),
+    # The same batch with q and k turned by the rotary embedding (base 10000) of
+    # their positions (the pages pair rotary embedding with long-sequence
+    # self-attention).
+    "jfa_rope_causal_self": dict(mode="jfa", B=64, H=8, D=128, dtype="bf16", q_len=("uniform", 1, 8192),
+                                 kv_len="same", qkv_sigma=1.0, act=None, causal=True, bias=None,
+                                 backward=True, rope_base=10000.0, same_draw_as="jfa_causal_self"),
 }
 
 

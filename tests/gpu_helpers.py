@@ -29,9 +29,10 @@ def to_dev(w, device="cuda"):
 
 
 def bias_kw(w, d):
-    """Bias arguments, plus the optional key-count bound when the case sets one."""
+    """Bias, window and rotary arguments, plus the optional key-count bound when the case
+    sets one."""
     return dict(bias=d["bias"], bias_kind=w.bias_kind, bias_lo=w.bias_lo, bias_hi=w.bias_hi,
-                max_kv_len=d.get("max_kv_len", 0), window=w.window)
+                max_kv_len=d.get("max_kv_len", 0), window=w.window, rope_base=w.rope_base)
 
 
 def gpu_fwd(w, d, residual=True):
@@ -75,7 +76,8 @@ def parity(w, *, backward=True, tau=None, label="", max_kv_len=0):
     """Full-tensor parity of the HIP path against the oracle for workload w."""
     tau = tau or TAU[w.dtype]
     announce(f"{label} mode={w.mode} B={w.B} H={w.H} D={w.D} dtype={w.dtype} causal={w.causal} "
-             f"bias={w.bias_kind} act={w.act} window={w.window} Tq={w.total_q} Tk={w.total_k} "
+             f"bias={w.bias_kind} act={w.act} window={w.window} rope={w.rope_base} Tq={w.total_q} "
+             f"Tk={w.total_k} "
              f"max_kv_len={max_kv_len}")
     d = to_dev(w)
     d["max_kv_len"] = max_kv_len

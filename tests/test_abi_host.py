@@ -75,6 +75,7 @@ def test_workspace_size_is_positive_and_aligned():
     (dict(kv_offsets=None), 1), (dict(bias_kind="rel", bias_table=None), 1),
     (dict(bias_kind="rel", bias_table=0x3000, bias_lo=5, bias_hi=1), 2),
     (dict(q_offsets=None, lq_fixed=3, total_q=4), 2), (dict(max_kv_len=-1), 2), (dict(window=-1), 2),
+    (dict(rope_base=-1.0), 2), (dict(rope_base=float("nan")), 2), (dict(rope_base=float("inf")), 2),
     # slices are addressed with 32-bit offsets: tensors of 4 GiB or more are refused
     (dict(total_q=1 << 24, heads=64, head_dim=128), 3), (dict(total_k=1 << 24, heads=16, head_dim=128), 3),
     (dict(total_q=1 << 23, heads=1, head_dim=128, dtype=torch.float32), 3),  # exactly 4 GiB
@@ -109,6 +110,21 @@ def test_null_tensors_and_workspace_errors():
                                None) == 1
     assert lib.jagged_attn_bwd(ctypes.byref(p), P(1), P(2), P(3), None, None, P(4), P(5), P(6), P(7),
                                P(8), None, P(0x100), ws, None) == 1
+
+
+def test_rotary_embedding_needs_workspace_for_turned_copies():
+    lib = _lib.load()
+    plain, rope = _problem(), _problem(rope_base=10000.0)
+    for pass_ in (_lib.PASS_FWD, _lib.PASS_BWD):
+        n0 = lib.ja_workspace_size(ctypes.byref(plain), pass_)
+        n1 = lib.ja_workspace_size(ctypes.byref(rope), pass_)
+        # turned copies of q (10 rows) and k (12 rows), each rounded up to 256 bytes
+        row = 2 * 64 * 2
+        assert n1 - n0 == -(-10 * row // 256) * 256 + -(-12 * row // 256) * 256
+        P = ctypes.c_void_p
+        st = lib.jagged_gdpa_fwd(ctypes.byref(rope), P(0x10), P(0x20), P(0x30), P(0x40), P(0x100),
+                                 ctypes.c_size_t(n0), None)
+        assert st == 4  # the plain workspace is too small once q and k are turned
 
 
 def test_bias_gradient_arguments():

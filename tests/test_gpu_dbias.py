@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 def gpu_dbias(w, d, fwd=None):
     kw = dict(bias=d["bias"], bias_kind=w.bias_kind, bias_lo=w.bias_lo, bias_hi=w.bias_hi,
-              scale=w.scale, causal=w.causal, window=w.window, with_dbias=True)
+              scale=w.scale, causal=w.causal, window=w.window, rope_base=w.rope_base, with_dbias=True)
     if w.mode == "gdpa":
         g = ja.gdpa_backward(d["q"], d["k"], d["v"], d["dout"], d["q_off"], d["kv_off"], act=w.act, **kw)
     else:

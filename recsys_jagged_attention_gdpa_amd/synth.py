@@ -18,6 +18,14 @@ Recipe (shared by every workload):
     workload description means variance s2;
   * bf16 workloads round the float32 draws to bf16 (round to nearest even);
   * offsets are int32 ``[0, cumsum(L)]``.
+
+MXFP8 inputs (tensors named in ``mx``) are given as element codes uint8
+[T, H, D] and scale codes uint8 [T, H, D / 32] (blocks of 32 head-dimension
+elements), drawn after everything else: one scale code per block uniform on
+{125 .. 128}, then the element codes are the FP8 E4M3 casts (torch's
+``float8_e4m3fn``) of the tensor's float32 normal draws divided by the block's
+scale 2^(code - 127), clamped to +-448 first.  This stands in for the upstream
+kernels that quantise their outputs; the attention itself only decodes.
 """
 from __future__ import annotations
 
@@ -54,6 +62,8 @@ class Workload:
     backward: bool  # whether the workload includes a backward pass
     window: int = 0  # sliding window: a query sees keys at aligned distance < window (0: no window)
     rope_base: float = 0.0  # rotary embedding of q and k by sample-local position (0: none)
+    mx: tuple = ()  # names ("q", "k", "v") of tensors given in MXFP8: the tensor holds uint8 codes
+    mx_scales: Optional[dict] = None  # name -> uint8 scale codes [T, H, D / 32]
 
     @property
     def lq(self) -> np.ndarray:
@@ -97,10 +107,19 @@ class Workload:
         else:
             q, q_off = gather(self.q, self.q_off, samples), offs(self.q_off, samples)
             out_off = self.q_off
+        scales = None
+        if self.mx_scales:
+            scales = {}
+            for name, sc in self.mx_scales.items():
+                if name == "q":
+                    scales[name] = sc if self.q_off is None else gather(sc, self.q_off, samples)
+                else:
+                    scales[name] = gather(sc, self.kv_off, samples)
         return dataclasses.replace(
             self, B=len(samples), q_off=q_off, q=q,
             kv_off=offs(self.kv_off, samples), k=gather(self.k, self.kv_off, samples),
-            v=gather(self.v, self.kv_off, samples), dout=gather(self.dout, out_off, samples))
+            v=gather(self.v, self.kv_off, samples), dout=gather(self.dout, out_off, samples),
+            mx_scales=scales)
 
 
 def _normal(rng, shape, sigma, dtype):
@@ -108,6 +127,16 @@ def _normal(rng, shape, sigma, dtype):
     if sigma != 1.0:
         x *= np.float32(sigma)
     return torch.from_numpy(x).to(dtype)
+
+
+def _mx_encode(rng, x: torch.Tensor):
+    """MXFP8 codes of float32 draws x [T, H, D]: (element codes, scale codes)."""
+    T, H, D = x.shape
+    sc = rng.integers(125, 129, size=(T, H, D // 32)).astype(np.uint8)
+    step = torch.from_numpy(np.ldexp(1.0, sc.astype(np.int64) - 127).astype(np.float32))
+    y = (x.float().reshape(T, H, D // 32, 32) / step[..., None]).clamp(-448.0, 448.0)
+    codes = y.reshape(T, H, D).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, torch.from_numpy(sc)
 
 
 def _offsets(lens):
@@ -219,10 +248,12 @@ def make(name: str, seed: Optional[int] = None, *, B: Optional[int] = None,
 
 def custom(*, mode="gdpa", lq, lk=None, H=2, D=64, dtype=torch.bfloat16, seed=0, sigma=1.0,
            act="silu", causal=False, bias_kind="none", bias_lo=0, bias_hi=0, bias_sigma=0.3,
-           shared_q=None, scale=None, with_dout=True, window=0, rope_base=0.0) -> Workload:
+           shared_q=None, scale=None, with_dout=True, window=0, rope_base=0.0, mx=()) -> Workload:
     """A workload with explicit per-sample lengths (edge cases, small shapes).
 
-    ``shared_q`` = n gives one shared block of n query rows (``lq`` is ignored)."""
+    ``shared_q`` = n gives one shared block of n query rows (``lq`` is ignored);
+    ``mx`` names the tensors ("q", "k", "v") given in MXFP8 (``dtype`` is then the
+    type of the others and of the outputs)."""
     rng = np.random.default_rng(seed)
     lk = lq if lk is None else lk
     B = len(lk)
@@ -230,9 +261,11 @@ def custom(*, mode="gdpa", lq, lk=None, H=2, D=64, dtype=torch.bfloat16, seed=0,
     kv_off = _offsets(lk)
     tq = lq_fixed if q_off is None else int(q_off[-1])
     tk = int(kv_off[-1])
-    q = _normal(rng, (tq, H, D), sigma, dtype)
-    k = _normal(rng, (tk, H, D), sigma, dtype)
-    v = _normal(rng, (tk, H, D), sigma, dtype)
+    mx = tuple(mx)
+    assert set(mx) <= {"q", "k", "v"}
+    q = _normal(rng, (tq, H, D), sigma, torch.float32 if "q" in mx else dtype)
+    k = _normal(rng, (tk, H, D), sigma, torch.float32 if "k" in mx else dtype)
+    v = _normal(rng, (tk, H, D), sigma, torch.float32 if "v" in mx else dtype)
     table = None
     if bias_kind != "none":
         table = _normal(rng, (H, bias_hi - bias_lo + 1), bias_sigma, torch.float32)
@@ -240,8 +273,17 @@ def custom(*, mode="gdpa", lq, lk=None, H=2, D=64, dtype=torch.bfloat16, seed=0,
     if with_dout:
         t_out = B * lq_fixed if q_off is None else tq
         dout = _normal(rng, (t_out, H, D), 1.0, dtype)
+    scales = None
+    if mx:
+        scales = {}
+        enc = {"q": q, "k": k, "v": v}
+        for name in ("q", "k", "v"):
+            if name in mx:
+                enc[name], scales[name] = _mx_encode(rng, enc[name])
+        q, k, v = enc["q"], enc["k"], enc["v"]
     return Workload(name="custom", mode=mode, B=B, H=H, D=D, dtype=dtype, q_off=q_off,
                     lq_fixed=lq_fixed, kv_off=kv_off, q=q, k=k, v=v, dout=dout, act=act,
                     scale=(1.0 / math.sqrt(D)) if scale is None else scale, causal=causal,
                     bias_kind=bias_kind, bias_table=table, bias_lo=bias_lo, bias_hi=bias_hi,
-                    backward=with_dout, window=int(window), rope_base=float(rope_base))
+                    backward=with_dout, window=int(window), rope_base=float(rope_base), mx=mx,
+                    mx_scales=scales)

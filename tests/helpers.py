@@ -2,7 +2,7 @@
 import numpy as np
 import torch
 
-from oracle import ref
+from oracle import mx, ref
 
 
 def bias_kw(w):
@@ -13,32 +13,46 @@ def bias_kw(w):
                 rope_bf16=w.dtype == torch.bfloat16)
 
 
+def inputs(w):
+    """q, k, v as the oracle reads them: MXFP8 tensors decoded (exactly) to float32."""
+    out = []
+    for name in ("q", "k", "v"):
+        t = getattr(w, name)
+        if name in w.mx:
+            t = mx.decode_f32(t.numpy(), w.mx_scales[name].numpy())
+        out.append(t)
+    return out
+
+
 def oracle_fwd(w, nthreads=0):
+    q, k, v = inputs(w)
     if w.mode == "gdpa":
-        o = ref.gdpa_fwd(w.q, w.k, w.v, w.q_off, w.kv_off, scale=w.scale, act=w.act,
+        o = ref.gdpa_fwd(q, k, v, w.q_off, w.kv_off, scale=w.scale, act=w.act,
                          lq_fixed=w.lq_fixed, causal=w.causal, nthreads=nthreads, **bias_kw(w))
         return {"o": o}
-    o, lse = ref.attn_fwd(w.q, w.k, w.v, w.q_off, w.kv_off, scale=w.scale, lq_fixed=w.lq_fixed,
+    o, lse = ref.attn_fwd(q, k, v, w.q_off, w.kv_off, scale=w.scale, lq_fixed=w.lq_fixed,
                           causal=w.causal, nthreads=nthreads, **bias_kw(w))
     return {"o": o, "lse": lse}
 
 
 def oracle_bwd(w, nthreads=0):
+    q, k, v = inputs(w)
     if w.mode == "gdpa":
-        dq, dk, dv = ref.gdpa_bwd(w.q, w.k, w.v, w.dout, w.q_off, w.kv_off, scale=w.scale,
+        dq, dk, dv = ref.gdpa_bwd(q, k, v, w.dout, w.q_off, w.kv_off, scale=w.scale,
                                   act=w.act, causal=w.causal, nthreads=nthreads, **bias_kw(w))
     else:
-        dq, dk, dv = ref.attn_bwd(w.q, w.k, w.v, w.dout, w.q_off, w.kv_off, scale=w.scale,
+        dq, dk, dv = ref.attn_bwd(q, k, v, w.dout, w.q_off, w.kv_off, scale=w.scale,
                                   causal=w.causal, nthreads=nthreads, **bias_kw(w))
     return {"dq": dq, "dk": dk, "dv": dv}
 
 
 def oracle_dbias(w, nthreads=0):
     """dL/dtable [H, hi - lo + 1] for a workload with a bias table and per-sample queries."""
+    q, k, v = inputs(w)
     if w.mode == "gdpa":
-        return ref.gdpa_dbias(w.q, w.k, w.v, w.dout, w.q_off, w.kv_off, scale=w.scale, act=w.act,
+        return ref.gdpa_dbias(q, k, v, w.dout, w.q_off, w.kv_off, scale=w.scale, act=w.act,
                               causal=w.causal, nthreads=nthreads, **bias_kw(w))
-    return ref.attn_dbias(w.q, w.k, w.v, w.dout, w.q_off, w.kv_off, scale=w.scale,
+    return ref.attn_dbias(q, k, v, w.dout, w.q_off, w.kv_off, scale=w.scale,
                           causal=w.causal, nthreads=nthreads, **bias_kw(w))
 
 

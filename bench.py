@@ -43,7 +43,7 @@ KERNEL_SOURCES = ["ja_fwd.hip", "ja_bwd.hip", "ja_plan.hip", "ja_tiles.h", "ja_d
 # long sequences are MFMA work).
 BOUND = {"gdpa_xattn_short_kv": "hbm", "pma_gdpa_fwd": "hbm", "jfa_causal_self": "mfma",
          "longtail_gdpa": "mfma", "tiny_gdpa_fp32": "alu", "jfa_swa_causal_self": "mfma",
-         "jfa_rope_causal_self": "mfma"}
+         "jfa_rope_causal_self": "mfma", "pma_gdpa_fwd_mxfp8": "hbm", "gdpa_xattn_short_kv_mxfp8": "hbm"}
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (the plain fp32 kernels are ALU loops)
 
 
@@ -95,7 +95,11 @@ def kernel_cost(w, kernel: str) -> tuple[float, float]:
     tk = int(w.lk.astype(np.int64)[sel].sum())
     q_rows = tq if w.q_off is not None else w.q.shape[0]  # shared queries are read once
     if kernel in ("fwd", "fwd_short"):
-        b = e * HD * (q_rows + tq_out + 2 * tk) + (4 * w.H * tq_out if w.mode == "jfa" else 0)
+        if w.mx:  # codes (1 byte) and a scale code per 32 elements in; bf16 out
+            b = HD * (q_rows + 2 * tk) * (1 + 1 / 32) + 2 * HD * tq_out
+        else:
+            b = e * HD * (q_rows + tq_out + 2 * tk)
+        b += 4 * w.H * tq_out if w.mode == "jfa" else 0
         return b, 4.0 * w.D * P
     if kernel == "bwd_fused":  # read Q, dO, K, V; write dQ, dK, dV; five GEMMs per pair
         return e * HD * (3 * tq + 4 * tk), 10.0 * w.D * P
@@ -149,6 +153,7 @@ class Runner:
         self.k = w.k.to(dev)
         self.v = w.v.to(dev)
         self.dout = None if w.dout is None else w.dout.to(dev)
+        self.sc = {n: t.to(dev) for n, t in (w.mx_scales or {}).items()}
         self.q_off = None if w.q_off is None else torch.from_numpy(w.q_off).to(dev)
         self.kv_off = torch.from_numpy(w.kv_off).to(dev)
         self.bias = None if w.bias_table is None else w.bias_table.to(dev)
@@ -156,13 +161,13 @@ class Runner:
         # lets the library leave out its long-sequence kernels when none can have work
         self.max_kv_len = int(w.lk.max()) if w.B > 0 else 0
         self.prob = _lib.make_problem(
-            batch=w.B, heads=w.H, head_dim=w.D, dtype=w.dtype, total_q=w.q.shape[0],
+            batch=w.B, heads=w.H, head_dim=w.D, dtype=torch.bfloat16 if w.mx else w.dtype, total_q=w.q.shape[0],
             total_k=w.total_k, q_offsets=self.q_off, kv_offsets=self.kv_off,
             lq_fixed=w.lq_fixed, causal=w.causal, scale=w.scale, act=w.act,
             bias_kind=w.bias_kind, bias_table=self.bias, bias_lo=w.bias_lo, bias_hi=w.bias_hi,
             max_kv_len=self.max_kv_len, window=w.window, rope_base=w.rope_base)
         rows = w.total_q_out
-        self.o = torch.empty((rows, w.H, w.D), dtype=w.dtype, device=dev)
+        self.o = torch.empty((rows, w.H, w.D), dtype=torch.bfloat16 if w.mx else w.dtype, device=dev)
         self.lse = torch.empty((w.H, rows), dtype=torch.float32, device=dev)
         self.o_res = torch.empty_like(self.o) if (w.mode == "jfa" and w.dtype == torch.bfloat16) else None
         self.ws_f = torch.empty(_lib.ja_workspace_size(self.prob, _lib.PASS_FWD), dtype=torch.uint8, device=dev)
@@ -197,6 +202,14 @@ class Runner:
 
     def step(self):
         p, w = self.prob, self.w
+        if w.mx:  # MXFP8 forward (no backward)
+            sc = self.sc
+            if w.mode == "gdpa":
+                _lib.jagged_gdpa_fwd_mx(p, self.q, sc["q"], self.k, sc["k"], self.v, sc["v"], self.o, self.ws_f)
+            else:
+                _lib.jagged_attn_fwd_mx(p, self.q, sc["q"], self.k, sc["k"], self.v, sc["v"], self.o, self.lse,
+                                        self.o_res, self.ws_f)
+            return
         if w.mode == "gdpa":
             _lib.jagged_gdpa_fwd(p, self.q, self.k, self.v, self.o, self.ws_f)
             if self.backward:
@@ -447,7 +460,8 @@ def main():
         "metric": "useful (unpadded) TFLOP/s fwd+bwd and % bf16 MFMA peak, sparsity-0.5 jagged",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8-in/bf16" if w.mx else ("bf16" if w.dtype == torch.bfloat16 else "f32"),
         "data": "synthetic",
         "config": {"workload": args.workload, "B": w.B, "H": w.H, "D": w.D,
                    "total_q": w.total_q, "total_k": w.total_k, "act": w.act if w.mode == "gdpa" else "softmax",

@@ -171,6 +171,29 @@ ja_status jagged_attn_fwd(const ja_problem *p, const void *q, const void *k, con
                           float *lse, void *o_residual, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* MXFP8 forward (GDPA and JFA).  The pages report MXFP8-based attention, the
+ * quantisation fused into the upstream projection and normalisation kernels
+ * ("Meta redesigns AI training infrastructure...", sections "Custom Kernels
+ * and 5D Parallelism for Trillion-Parameter Scale" and "Key Numbers"), so q,
+ * k and v arrive quantised in the OCP Microscaling MXFP8 format:
+ *   q, k, v        uint8 [rows, H, D]: FP8 E4M3 codes (bias 7, no infinities,
+ *                  largest finite 448);
+ *   q/k/v_scale    uint8 [rows, H, D / 32]: one E8M0 scale code E per block of
+ *                  32 consecutive head-dimension elements of a row and head,
+ *                  scale 2^(E - 127), E in 1 .. 254 (0 and 255 are not decoded).
+ * The element value is scale times code value; attention is computed exactly
+ * as by jagged_gdpa_fwd / jagged_attn_fwd on those values (they are decoded to
+ * bf16 exactly, accumulation in fp32).  p->dtype must be JA_BF16 (the type of
+ * o and o_residual) and p->rope_base 0, else JA_ERR_UNSUPPORTED; a NULL scale
+ * array of a tensor with rows: JA_ERR_NULL.  Workspace as for the forward
+ * (ja_workspace_size(p, JA_PASS_FWD)).  There is no MXFP8 backward. */
+ja_status jagged_gdpa_fwd_mx(const ja_problem *p, const void *q, const void *q_scale, const void *k,
+                             const void *k_scale, const void *v, const void *v_scale, void *o, void *workspace,
+                             size_t workspace_bytes, void *stream);
+ja_status jagged_attn_fwd_mx(const ja_problem *p, const void *q, const void *q_scale, const void *k,
+                             const void *k_scale, const void *v, const void *v_scale, void *o, float *lse,
+                             void *o_residual, void *workspace, size_t workspace_bytes, void *stream);
+
 /* JFA backward: takes the forward's o and lse; dq, dk, dv written.  The softmax
  * backward needs delta_i = <dO_i, O_i>.  With o_residual NULL it is formed from
  * the bf16 o alone (as FlashAttention does): o's rounding then perturbs every

@@ -26,8 +26,8 @@ BIAS = {"none": 0, "rel": 1, "keypos": 2}
 PASS_FWD, PASS_BWD, PASS_BWD_DBIAS = 0, 1, 2
 
 EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_attn_fwd",
-           "jagged_attn_bwd", "ja_profile_kernel", "ja_status_string", "ja_last_hip_error",
-           "ja_version")
+           "jagged_attn_bwd", "jagged_gdpa_fwd_mx", "jagged_attn_fwd_mx", "ja_profile_kernel",
+           "ja_status_string", "ja_last_hip_error", "ja_version")
 KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5,
            "fwd_short": 6, "bwd_dbias": 7, "rope": 8, "rope_back": 9}
 
@@ -74,7 +74,10 @@ def load(path: str = LIB_PATH):
         lib.jagged_attn_fwd.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.jagged_gdpa_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.jagged_attn_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        for f in (lib.jagged_gdpa_fwd, lib.jagged_attn_fwd, lib.jagged_gdpa_bwd, lib.jagged_attn_bwd):
+        lib.jagged_gdpa_fwd_mx.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.jagged_attn_fwd_mx.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        for f in (lib.jagged_gdpa_fwd, lib.jagged_attn_fwd, lib.jagged_gdpa_bwd, lib.jagged_attn_bwd,
+                  lib.jagged_gdpa_fwd_mx, lib.jagged_attn_fwd_mx):
             f.restype = ctypes.c_int
         lib.ja_profile_kernel.argtypes = [ctypes.c_int, P, P]
         lib.ja_profile_kernel.restype = ctypes.c_int
@@ -162,6 +165,19 @@ def jagged_attn_bwd(problem, q, k, v, o, o_residual, dout, lse, dq, dk, dv, dbia
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_residual), _ptr(dout),
         _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
+
+
+def jagged_gdpa_fwd_mx(problem, q, q_scale, k, k_scale, v, v_scale, o, workspace, stream=None):
+    _check("jagged_gdpa_fwd_mx", load().jagged_gdpa_fwd_mx(
+        ctypes.byref(problem), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(v), _ptr(v_scale),
+        _ptr(o), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def jagged_attn_fwd_mx(problem, q, q_scale, k, k_scale, v, v_scale, o, lse, o_residual, workspace,
+                       stream=None):
+    _check("jagged_attn_fwd_mx", load().jagged_attn_fwd_mx(
+        ctypes.byref(problem), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(v), _ptr(v_scale),
+        _ptr(o), _ptr(lse), _ptr(o_residual), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def ja_profile_kernel(kernel, start_event, stop_event):

@@ -216,13 +216,21 @@ ja_status hip_status(hipError_t e) {
     return JA_ERR_HIP;
 }
 
+// MXFP8 scale codes of q, k, v (all NULL: bf16 / fp32 inputs).
+struct MXScales {
+    const void *q, *k, *v;
+};
+
 ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, const void *v, void *o, float *lse,
-                  void *o_res, void *ws, size_t ws_bytes, void *stream) {
+                  void *o_res, void *ws, size_t ws_bytes, void *stream, const MXScales *mx = nullptr) {
     ja_status st = check_problem(p, JA_PASS_FWD);
     if (st != JA_OK) return st;
+    // MXFP8 inputs: bf16 outputs, no rotary embedding (the turn works on bf16 / fp32 rows)
+    if (mx && (p->dtype != JA_BF16 || p->rope_base > 0.0f)) return JA_ERR_UNSUPPORTED;
     // A tensor with no rows is never touched, so its pointer may be NULL.
     const bool has_q = p->total_q > 0, has_o = total_q_out(*p) > 0, has_k = p->total_k > 0;
     if ((has_q && !q) || (has_k && (!k || !v)) || (has_o && !o)) return JA_ERR_NULL;
+    if (mx && ((has_q && !mx->q) || (has_k && (!mx->k || !mx->v)))) return JA_ERR_NULL;
     if (mode == 1 && has_o && !lse) return JA_ERR_NULL;
     st = check_workspace(p, JA_PASS_FWD, ws, ws_bytes);
     if (st != JA_OK) return st;
@@ -235,6 +243,12 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
     a.out = o;
     a.lse = lse;
     a.o_res_out = p->dtype == JA_BF16 ? o_res : nullptr;
+    if (mx) {
+        a.q_sc = static_cast<const uint8_t *>(mx->q);
+        a.k_sc = static_cast<const uint8_t *>(mx->k);
+        a.v_sc = static_cast<const uint8_t *>(mx->v);
+        a.mx = 1;
+    }
     hipError_t e = rope_inputs(*p, L, ws, a, s);
     if (e != hipSuccess) return hip_status(e);
     if (p->dtype == JA_F32) return hip_status(ja::launch_fwd_f32(a, p->head_dim, mode, p->act, s));
@@ -337,6 +351,20 @@ ja_status jagged_gdpa_fwd(const ja_problem *p, const void *q, const void *k, con
 ja_status jagged_attn_fwd(const ja_problem *p, const void *q, const void *k, const void *v, void *o, float *lse,
                           void *o_residual, void *workspace, size_t workspace_bytes, void *stream) {
     return run_fwd(p, 1, q, k, v, o, lse, o_residual, workspace, workspace_bytes, stream);
+}
+
+ja_status jagged_gdpa_fwd_mx(const ja_problem *p, const void *q, const void *q_scale, const void *k,
+                             const void *k_scale, const void *v, const void *v_scale, void *o, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    const MXScales mx{q_scale, k_scale, v_scale};
+    return run_fwd(p, 0, q, k, v, o, nullptr, nullptr, workspace, workspace_bytes, stream, &mx);
+}
+
+ja_status jagged_attn_fwd_mx(const ja_problem *p, const void *q, const void *q_scale, const void *k,
+                             const void *k_scale, const void *v, const void *v_scale, void *o, float *lse,
+                             void *o_residual, void *workspace, size_t workspace_bytes, void *stream) {
+    const MXScales mx{q_scale, k_scale, v_scale};
+    return run_fwd(p, 1, q, k, v, o, lse, o_residual, workspace, workspace_bytes, stream, &mx);
 }
 
 ja_status jagged_gdpa_bwd(const ja_problem *p, const void *q, const void *k, const void *v, const void *dout, void *dq,

@@ -24,6 +24,8 @@
 // the causal diagonal ("Meta redesigns...", section "Eliminating Compute
 // Waste in Asymmetric Workloads").  Key rows past the sample's end are loaded
 // as zeros.
+#include <type_traits>
+
 #include "ja_device.h"
 #include "ja_kernels.h"
 #include "ja_tiles.h"
@@ -41,7 +43,12 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 units a running softmax max may l
 // bf16(P) plus its bf16 residual, two MFMAs into the same accumulator, so O
 // (and delta = <dO, O> formed from it in backward) is accurate to ~2^-17
 // rather than carrying the 2^-9 rounding of P.
-template <int D, int MODE, int ACT, int WAVES, int BN, bool SPLIT>
+// MX (MXFP8 inputs: E4M3 codes with a scale per 32 head-dimension elements):
+// Q, K and V are read as codes and decoded to bf16 after the load; key / value
+// tiles then come through registers (codes in flight during the current tile,
+// decoded into the LDS tile at its end) instead of the buffer->LDS copy, which
+// moves bytes without decoding them.
+template <int D, int MODE, int ACT, int WAVES, int BN, bool SPLIT, bool MX>
 __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(const AttnParams p) {
     constexpr int NT = WAVES * WAVE;
     constexpr int BM = 32 * WAVES;
@@ -94,7 +101,12 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
 
         // Q rows of this lane, in B-operand layout: chunk 2kk+g of row irow.
         bf16x8 qreg[NKK];
-        load_row_operand<D>(qreg, Qs, irow, g);
+        if constexpr (MX)
+            load_row_operand<D>(qreg, MXSlice<D>(p.q, p.q_sc, s.qs, s.lq, H, h), irow, g);
+        else
+            load_row_operand<D>(qreg, Qs, irow, g);
+        const MXSlice<D> Km(p.k, p.k_sc, s.ks, MX ? s.lk : 0, H, h), Vm(p.v, p.v_sc, s.ks, MX ? s.lk : 0, H, h);
+        MXPairLoader<BN, D, NT> mxl;
 
         f32x16 oacc[NDB];
 #pragma unroll
@@ -107,12 +119,17 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         float bnext = 0.0f;
         auto load_tile = [&](int jt) {
             lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
-            dma_tile<BN, D, NT>(kt, Ks, jt * BN, tid);
-            dma_tile<BN, D, NT>(kt + TILE_BYTES, Vs, jt * BN, tid);
+            if constexpr (MX) {
+                mxl.load(Km, Vm, jt * BN, tid);
+            } else {
+                dma_tile<BN, D, NT>(kt, Ks, jt * BN, tid);
+                dma_tile<BN, D, NT>(kt + TILE_BYTES, Vs, jt * BN, tid);
+            }
             const int bi = bias_stage_rowmajor(bz, i0, BM, jt * BN, BN, tid);
             bnext = buf_load_f32(brs, bi >= 0 ? (uint32_t)bi * 4u : OOB);
         };
         auto store_tile = [&](int buf) {
+            if constexpr (MX) mxl.store(lbase + buf * 2 * TILE_BYTES, lbase + buf * 2 * TILE_BYTES + TILE_BYTES, tid);
             if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;  // JFA works in log2 units
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tile has landed
         };
@@ -270,7 +287,8 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
 // computed.  Loads and stores go through per-sample buffer descriptors, so the
 // loop body has no branches around memory operations and the next block's
 // loads stay in flight across the current block's stores.
-template <int D, int MODE, int ACT, bool SPLIT>
+// MX: MXFP8 inputs, decoded to bf16 when K / V and the Q blocks are written to LDS.
+template <int D, int MODE, int ACT, bool SPLIT, bool MX>
 __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnParams p) {
     constexpr int KV_BYTES = 32 * D * 2;
     constexpr int NKK = D / 16, NDB = D / 32;
@@ -301,12 +319,22 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
         const int h = w % H;
         const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
         const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
-        {
+        if constexpr (MX) {
+            MXPairLoader<32, D, FWD_THREADS> kv;
+            kv.load(MXSlice<D>(p.k, p.k_sc, s.ks, s.lk, H, h), MXSlice<D>(p.v, p.v_sc, s.ks, s.lk, H, h), 0,
+                    threadIdx.x);
+            kv.store(Kt, Vt, threadIdx.x);
+        } else {
             PairLoader<32, D, FWD_THREADS> kv;
             kv.load(static_cast<const bf16 *>(p.k), static_cast<const bf16 *>(p.v), s.ks, H, h, 0, s.lk, threadIdx.x);
             kv.store(Kt, Vt, threadIdx.x);
         }
-        const HeadSlice<D> Qs(p.q, s.qs, s.lq, H, h);
+        using QSlice = std::conditional_t<MX, MXSlice<D>, HeadSlice<D>>;
+        using QTile = std::conditional_t<MX, MXWaveTile<D>, WaveTile<D>>;
+        const QSlice Qs = [&]() {
+            if constexpr (MX) return MXSlice<D>(p.q, p.q_sc, s.qs, s.lq, H, h);
+            else return HeadSlice<D>(p.q, s.qs, s.lq, H, h);
+        }();
         const HeadSlice<D> Os(p.out, s.o0, s.lq, H, h);
         // the residual (JFA, optional) and LSE slices; zero-sized when not written
         const bool res = MODE == JFA && p.o_res_out != nullptr;
@@ -318,7 +346,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
         // One 32-row query block, with Q rows in `qreg`; the next block's rows
         // are loaded into `qnext` first, so they are in flight meanwhile.  The
         // wave's LDS tile holds the block's Q rows, then its output rows.
-        auto block = [&](int blk, const WaveTile<D> &qreg, WaveTile<D> &qnext) -> int {
+        auto block = [&](int blk, const QTile &qreg, QTile &qnext) -> int {
             const int irow = blk * 32 + l32;
             qreg.store(Ot, lane);
             lds_wave_sync();
@@ -406,7 +434,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
         };
 
         int blk = wv;
-        WaveTile<D> qa, qb;
+        QTile qa, qb;
         qa.load(Qs, blk * 32, lane);
         // Enter the loop with nothing outstanding, so the loop's waits cover
         // only the previous block's prefetch, not its stores.
@@ -423,26 +451,30 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
     }
 }
 
-template <int D, int MODE, int ACT, bool SPLIT>
+template <int D, int MODE, int ACT, bool SPLIT, bool MX>
 static hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, bool long_units, hipStream_t stream) {
     const KernelTimer &t = kernel_timer();
     t.begin(K_FWD_SHORT, stream);
-    hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT, SPLIT>), dim3(2 * cus), dim3(FWD_THREADS), 0, stream, p);
+    hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT, SPLIT, MX>), dim3(2 * cus), dim3(FWD_THREADS), 0, stream, p);
     t.end(K_FWD_SHORT, stream);
     if (!long_units) return hipGetLastError();
     t.begin(K_FWD, stream);
     if (few_q)  // every unit is one block of <= 32 shared query rows
-        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, 32, SPLIT>), dim3(8 * cus), dim3(WAVE), 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, 32, SPLIT, MX>), dim3(8 * cus), dim3(WAVE), 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE, SPLIT>), dim3(2 * cus), dim3(4 * WAVE), 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE, SPLIT, MX>), dim3(2 * cus), dim3(4 * WAVE), 0, stream, p);
     t.end(K_FWD, stream);
     return hipGetLastError();
 }
 
 template <int D, int MODE, int ACT>
 static hipError_t launch_fwd_t(const AttnParams &p, int cus, bool few_q, bool long_units, hipStream_t stream) {
-    if (MODE == JFA && p.o_res_out) return launch_fwd_s<D, MODE, ACT, true>(p, cus, few_q, long_units, stream);
-    return launch_fwd_s<D, MODE, ACT, false>(p, cus, few_q, long_units, stream);
+    const bool mx = p.mx != 0;  // MXFP8 inputs
+    if (MODE == JFA && p.o_res_out)
+        return mx ? launch_fwd_s<D, MODE, ACT, true, true>(p, cus, few_q, long_units, stream)
+                  : launch_fwd_s<D, MODE, ACT, true, false>(p, cus, few_q, long_units, stream);
+    return mx ? launch_fwd_s<D, MODE, ACT, false, true>(p, cus, few_q, long_units, stream)
+              : launch_fwd_s<D, MODE, ACT, false, false>(p, cus, few_q, long_units, stream);
 }
 
 template <int D>

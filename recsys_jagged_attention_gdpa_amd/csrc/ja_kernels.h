@@ -82,6 +82,10 @@ struct AttnParams {
     PlanCounters *counters4;
     float *dbias;             // bias gradient output [H][hi - lo + 1], or NULL
     float *dbias_part;        // bias gradient partial rows [DBIAS_GRID][H][hi - lo + 1]
+    // MXFP8 forward: q, k, v hold E4M3 codes and these their E8M0 scale codes
+    // [T, H, D / 32] (all NULL for bf16 / fp32 inputs)
+    const uint8_t *q_sc, *k_sc, *v_sc;
+    int mx;  // 1: q, k, v are MXFP8 (forward only)
 };
 
 // Units of the tile lists (PLAN_Q_TILES, PLAN_KV_TILES) are numbered

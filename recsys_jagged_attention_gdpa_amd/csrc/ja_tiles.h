@@ -325,4 +325,121 @@ __device__ __forceinline__ void pack_operands(const float (&v)[16], bf16x8 &lo, 
     }
 }
 
+// ------------------------------------------------------------------ MXFP8
+// MXFP8 inputs (OCP Microscaling: FP8 E4M3 elements, one E8M0 scale 2^(E-127)
+// per block of 32 consecutive head-dimension elements of a row and head) are
+// read as codes and decoded to bf16 after the load, so the attention arithmetic
+// is the bf16 path's on exactly the decoded values: each chunk of 8 elements
+// lies inside one block, and v_cvt_scalef32_pk_bf16_fp8 turns two codes into
+// two bf16 values times a float32 scale (byte pairs 0-1 / 2-3 by its word
+// select; checked on the hardware against the format's table).  A scale code
+// becomes the float32 with that biased exponent; codes 0 and 255 (2^-127, NaN)
+// are outside what the kernels decode (they read as scales 0 and infinity).
+
+// Codes of one 8-element chunk and its block's scale code.
+struct MXRaw {
+    u32x2 codes;
+    uint32_t scale;
+};
+
+__device__ __forceinline__ u32x4 mx_decode(const MXRaw &r) {
+    const float sc = __builtin_bit_cast(float, r.scale << 23);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.codes[0], sc, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.codes[0], sc, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.codes[1], sc, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.codes[1], sc, true);
+    return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                 __builtin_bit_cast(uint32_t, d)};
+}
+
+// One head of an MXFP8 [T, H, D] tensor (codes) with its [T, H, D / 32] scale
+// codes: rows 0 .. rows-1 from global row `row0`, through bounds-checked
+// descriptors (rows past the slice read as zero codes, i.e. zeros).
+template <int D>
+struct MXSlice {
+    rsrc_t c, s;
+    uint32_t row_bytes, srow_bytes;  // H * D and H * D / 32
+    __device__ __forceinline__ MXSlice(const void *codes, const void *scales, int64_t row0, int rows, int H, int h) {
+        c = make_rsrc(static_cast<const uint8_t *>(codes) + (row0 * H + h) * (int64_t)D, rows_span(rows, H, D, 1));
+        s = make_rsrc(static_cast<const uint8_t *>(scales) + (row0 * H + h) * (int64_t)(D / 32),
+                      rows_span(rows, H, D / 32, 1));
+        row_bytes = (uint32_t)(H * D);
+        srow_bytes = (uint32_t)(H * D / 32);
+    }
+    // chunk ch (elements 8 ch .. 8 ch + 7, in block ch / 4) of row `row`;
+    // valid = false reads zeros (an always out-of-range offset)
+    __device__ __forceinline__ MXRaw raw(int row, int ch, bool valid = true) const {
+        const uint32_t oc = valid ? (uint32_t)row * row_bytes + (uint32_t)ch * 8u : OOB;
+        const uint32_t os = valid ? (uint32_t)row * srow_bytes + (uint32_t)(ch >> 2) : OOB;
+        MXRaw r;
+        r.codes = __builtin_amdgcn_raw_buffer_load_b64(c, (int)oc, 0, 0);
+        r.scale = __builtin_amdgcn_raw_buffer_load_b8(s, (int)os, 0, 0);
+        return r;
+    }
+    __device__ __forceinline__ u32x4 load16(int row, int ch) const { return mx_decode(raw(row, ch)); }
+};
+
+// One lane's row of an MXFP8 slice in MFMA operand layout (chunk 2kk+g for k-step kk).
+template <int D>
+__device__ __forceinline__ void load_row_operand(bf16x8 (&reg)[D / 16], const MXSlice<D> &S, int row, int g) {
+    MXRaw r[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) r[kk] = S.raw(row, 2 * kk + g);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) reg[kk] = __builtin_bit_cast(bf16x8, mx_decode(r[kk]));
+}
+
+// ROWS rows of two MXFP8 slices (K and V) staged by NT threads into bf16 tiles
+// of the swizzled LDS layout: load() issues the reads of the codes, store()
+// decodes and writes, so the loads can stay in flight across other work.
+template <int ROWS, int D, int NT>
+struct MXPairLoader {
+    static constexpr int CHUNKS = ROWS * D / 8;
+    static constexpr int PER_THREAD = (CHUNKS + NT - 1) / NT;
+    MXRaw a[PER_THREAD], b[PER_THREAD];
+    __device__ __forceinline__ void load(const MXSlice<D> &A, const MXSlice<D> &B, int r0, int tid) {
+#pragma unroll
+        for (int it = 0; it < PER_THREAD; ++it) {
+            const int cid = tid + it * NT;
+            const int r = cid / (D / 8), c = cid % (D / 8);
+            // slots past the tile (CHUNKS < NT) read zeros
+            a[it] = A.raw(r0 + r, c, cid < CHUNKS);
+            b[it] = B.raw(r0 + r, c, cid < CHUNKS);
+        }
+    }
+    __device__ __forceinline__ void store(lchar *ta, lchar *tb, int tid) const {
+#pragma unroll
+        for (int it = 0; it < PER_THREAD; ++it) {
+            const int cid = tid + it * NT;
+            const int r = cid / (D / 8), c = cid % (D / 8);
+            if (CHUNKS % NT != 0 && cid >= CHUNKS) continue;
+            lds_write16(ta, lds_off<D>(r, c), mx_decode(a[it]));
+            lds_write16(tb, lds_off<D>(r, c), mx_decode(b[it]));
+        }
+    }
+};
+
+// WaveTile for an MXFP8 slice: 32 rows read as codes by one wave, decoded when
+// written to the LDS tile.
+template <int D>
+struct MXWaveTile {
+    static constexpr int PER_LANE = 32 * D / 8 / WAVE;
+    MXRaw a[PER_LANE];
+    __device__ __forceinline__ void load(const MXSlice<D> &S, int r0, int lane) {
+#pragma unroll
+        for (int it = 0; it < PER_LANE; ++it) {
+            const int cid = lane + it * WAVE;
+            a[it] = S.raw(r0 + cid / (D / 8), cid % (D / 8));
+        }
+    }
+    __device__ __forceinline__ void store(lchar *t, int lane) const {
+#pragma unroll
+        for (int it = 0; it < PER_LANE; ++it) {
+            const int cid = lane + it * WAVE;
+            lds_write16(t, lds_off<D>(cid / (D / 8), cid % (D / 8)), mx_decode(a[it]));
+        }
+    }
+};
+
 }  // namespace ja

@@ -84,6 +84,43 @@ def attn_forward(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bi
     return o, lse, o_res
 
 
+def _check_mx(q, k, v, scales):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        sc = scales[name]
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 3 or t.dtype != torch.uint8:
+            raise ValueError(f"{name} must hold MXFP8 codes: a contiguous 3-D uint8 device tensor")
+        if (sc.dtype != torch.uint8 or not sc.is_cuda or not sc.is_contiguous()
+                or tuple(sc.shape) != (t.shape[0], t.shape[1], t.shape[2] // 32)):
+            raise ValueError(f"{name} scale codes must be a contiguous uint8 [T, H, D/32] device tensor")
+    if k.shape != v.shape or k.shape[1:] != q.shape[1:]:
+        raise ValueError("q, k, v shapes disagree")
+
+
+def mx_forward(mode, q, q_scale, k, k_scale, v, v_scale, q_offsets, kv_offsets, *, act="silu", scale=None,
+               causal=False, bias=None, bias_kind="none", bias_lo=0, bias_hi=0, residual=True,
+               max_kv_len=0, window=0):
+    """Forward on MXFP8 inputs (E4M3 codes uint8 [T, H, D], E8M0 scale codes uint8
+    [T, H, D/32]); bf16 outputs.  mode "gdpa" returns O; "jfa" returns (O, LSE, O_residual)."""
+    _check_mx(q, k, v, {"q": q_scale, "k": k_scale, "v": v_scale})
+    B = int(kv_offsets.numel()) - 1
+    H, D = int(q.shape[1]), int(q.shape[2])
+    p = _lib.make_problem(
+        batch=B, heads=H, head_dim=D, dtype=torch.bfloat16, total_q=int(q.shape[0]), total_k=int(k.shape[0]),
+        q_offsets=q_offsets, kv_offsets=kv_offsets, lq_fixed=0 if q_offsets is not None else int(q.shape[0]),
+        causal=causal, scale=scale, act=act, bias_kind=bias_kind if bias is not None else "none",
+        bias_table=bias, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len, window=window)
+    rows = q.shape[0] if q_offsets is not None else B * q.shape[0]
+    o = torch.empty((rows, H, D), dtype=torch.bfloat16, device=q.device)
+    ws = _workspace(p, _lib.PASS_FWD, q.device)
+    if mode == "gdpa":
+        _lib.jagged_gdpa_fwd_mx(p, q, q_scale, k, k_scale, v, v_scale, o, ws)
+        return o
+    lse = torch.empty((H, rows), dtype=torch.float32, device=q.device)
+    o_res = torch.empty_like(o) if residual else None
+    _lib.jagged_attn_fwd_mx(p, q, q_scale, k, k_scale, v, v_scale, o, lse, o_res, ws)
+    return o, lse, o_res
+
+
 def _dbias_out(p, bias, with_dbias):
     """Bias-gradient output [H, hi - lo + 1] and the workspace pass that goes with it."""
     if not with_dbias:

@@ -139,6 +139,15 @@ def _mx_encode(rng, x: torch.Tensor):
     return codes, torch.from_numpy(sc)
 
 
+def _mx_inputs(rng, mx, q, k, v):
+    """Codes for the tensors named in mx (in the order q, k, v) and their scale codes."""
+    scales, enc = {}, {"q": q, "k": k, "v": v}
+    for name in ("q", "k", "v"):
+        if name in mx:
+            enc[name], scales[name] = _mx_encode(rng, enc[name])
+    return enc["q"], enc["k"], enc["v"], scales
+
+
 def _offsets(lens):
     return np.concatenate([[0], np.cumsum(np.asarray(lens, dtype=np.int64))]).astype(np.int32)
 
@@ -180,6 +189,16 @@ CATALOGUE = {
     "jfa_rope_causal_self": dict(mode="jfa", B=64, H=8, D=128, dtype="bf16", q_len=("uniform", 1, 8192),
                                  kv_len="same", qkv_sigma=1.0, act=None, causal=True, bias=None,
                                  backward=True, rope_base=10000.0, same_draw_as="jfa_causal_self"),
+    # The pooling and cross-attention forwards with MXFP8 queries, keys and values
+    # (the pages report MXFP8-based attention; the quantisation happens upstream).
+    "pma_gdpa_fwd_mxfp8": dict(mode="gdpa", B=2048, H=4, D=64, dtype="bf16", q_len=("shared", 16),
+                               kv_len=("uniform", 1, 4096), qkv_sigma=1.0, act="silu", causal=False,
+                               bias=("keypos", 0, 4095, math.sqrt(0.1)), backward=False, mx=("q", "k", "v"),
+                               same_draw_as="pma_gdpa_fwd"),
+    "gdpa_xattn_short_kv_mxfp8": dict(mode="gdpa", B=1024, H=4, D=128, dtype="bf16",
+                                      q_len=("uniform", 1, 1024), kv_len=("fixed", 32),
+                                      qkv_sigma=math.sqrt(0.5), act="gelu_tanh", causal=False, bias=None,
+                                      backward=False, mx=("q", "k", "v"), same_draw_as="gdpa_xattn_short_kv"),
 }
 
 
@@ -224,9 +243,10 @@ def make(name: str, seed: Optional[int] = None, *, B: Optional[int] = None,
 
     tq = lq_fixed if q_off is None else int(q_off[-1])
     tk = int(kv_off[-1])
-    q = _normal(rng, (tq, H, D), sigma, dtype)
-    k = _normal(rng, (tk, H, D), sigma, dtype)
-    v = _normal(rng, (tk, H, D), sigma, dtype)
+    mx = tuple(spec.get("mx", ()))
+    q = _normal(rng, (tq, H, D), sigma, torch.float32 if "q" in mx else dtype)
+    k = _normal(rng, (tk, H, D), sigma, torch.float32 if "k" in mx else dtype)
+    v = _normal(rng, (tk, H, D), sigma, torch.float32 if "v" in mx else dtype)
 
     bias_kind, table, lo, hi = "none", None, 0, 0
     if spec["bias"] is not None:
@@ -238,12 +258,15 @@ def make(name: str, seed: Optional[int] = None, *, B: Optional[int] = None,
     if backward:
         t_out = B * lq_fixed if q_off is None else tq
         dout = _normal(rng, (t_out, H, D), 1.0, dtype)
+    scales = None
+    if mx:
+        q, k, v, scales = _mx_inputs(rng, mx, q, k, v)
     return Workload(name=name, mode=spec["mode"], B=B, H=H, D=D, dtype=dtype, q_off=q_off,
                     lq_fixed=lq_fixed, kv_off=kv_off, q=q, k=k, v=v, dout=dout,
                     act=spec["act"] or "silu", scale=1.0 / math.sqrt(D), causal=spec["causal"],
                     bias_kind=bias_kind, bias_table=table, bias_lo=lo, bias_hi=hi,
                     backward=spec["backward"], window=spec.get("window", 0),
-                    rope_base=float(spec.get("rope_base", 0.0)))
+                    rope_base=float(spec.get("rope_base", 0.0)), mx=mx, mx_scales=scales)
 
 
 def custom(*, mode="gdpa", lq, lk=None, H=2, D=64, dtype=torch.bfloat16, seed=0, sigma=1.0,
@@ -275,12 +298,7 @@ def custom(*, mode="gdpa", lq, lk=None, H=2, D=64, dtype=torch.bfloat16, seed=0,
         dout = _normal(rng, (t_out, H, D), 1.0, dtype)
     scales = None
     if mx:
-        scales = {}
-        enc = {"q": q, "k": k, "v": v}
-        for name in ("q", "k", "v"):
-            if name in mx:
-                enc[name], scales[name] = _mx_encode(rng, enc[name])
-        q, k, v = enc["q"], enc["k"], enc["v"]
+        q, k, v, scales = _mx_inputs(rng, mx, q, k, v)
     return Workload(name="custom", mode=mode, B=B, H=H, D=D, dtype=dtype, q_off=q_off,
                     lq_fixed=lq_fixed, kv_off=kv_off, q=q, k=k, v=v, dout=dout, act=act,
                     scale=(1.0 / math.sqrt(D)) if scale is None else scale, causal=causal,

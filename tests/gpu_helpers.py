@@ -25,6 +25,8 @@ def to_dev(w, device="cuda"):
     d["kv_off"] = torch.from_numpy(w.kv_off).to(device)
     d["bias"] = None if w.bias_table is None else w.bias_table.to(device).contiguous()
     d["dout"] = None if w.dout is None else w.dout.to(device).contiguous()
+    for name, sc in (w.mx_scales or {}).items():
+        d[name + "_sc"] = sc.to(device).contiguous()
     return d
 
 
@@ -36,6 +38,15 @@ def bias_kw(w, d):
 
 
 def gpu_fwd(w, d, residual=True):
+    if w.mx:
+        assert set(w.mx) == {"q", "k", "v"}, "the MXFP8 forward takes q, k and v in MXFP8"
+        kw = bias_kw(w, d)
+        kw.pop("rope_base")
+        out = ja.mx_forward(w.mode, d["q"], d["q_sc"], d["k"], d["k_sc"], d["v"], d["v_sc"], d["q_off"],
+                            d["kv_off"], act=w.act, scale=w.scale, causal=w.causal, residual=residual, **kw)
+        if w.mode == "gdpa":
+            return {"o": out}
+        return {"o": out[0], "lse": out[1], "o_res": out[2]}
     if w.mode == "gdpa":
         o = ja.gdpa_forward(d["q"], d["k"], d["v"], d["q_off"], d["kv_off"], act=w.act,
                             scale=w.scale, causal=w.causal, **bias_kw(w, d))

@@ -154,3 +154,24 @@ def test_bias_gradient_arguments():
         assert fn(wide, P(0x500), 1 << 30) == 3        # row too long for the gradient pass
         assert fn(rel, P(0x500), n1) == 4              # workspace sized for the plain backward
         assert fn(rel, P(0x500), n2 - 1) == 4
+
+
+def test_mxfp8_forward_arguments():
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    ws = ctypes.c_size_t(1 << 30)
+
+    def gdpa(prob, qs, ks, vs):
+        return lib.jagged_gdpa_fwd_mx(ctypes.byref(prob), P(0x10), qs, P(0x20), ks, P(0x30), vs, P(0x40),
+                                      P(0x100), ws, None)
+
+    def jfa(prob, qs, ks, vs):
+        return lib.jagged_attn_fwd_mx(ctypes.byref(prob), P(0x10), qs, P(0x20), ks, P(0x30), vs, P(0x40),
+                                      P(0x50), None, P(0x100), ws, None)
+
+    for fn in (gdpa, jfa):
+        assert fn(_problem(dtype=torch.float32), P(1), P(2), P(3)) == 3      # bf16 outputs only
+        assert fn(_problem(rope_base=10000.0), P(1), P(2), P(3)) == 3        # no rotary embedding
+        assert fn(_problem(), None, P(2), P(3)) == 1                         # scale codes needed
+        assert fn(_problem(), P(1), P(2), None) == 1
+        assert fn(_problem(head_dim=48), P(1), P(2), P(3)) == 3

@@ -24,14 +24,15 @@ def _single_head(w, b, h):
     s = w.subset([b])
     pick = lambda t: None if t is None else t[:, h:h + 1, :].contiguous()
     tab = None if s.bias_table is None else s.bias_table[h:h + 1].contiguous()
+    scales = None if not s.mx_scales else {n: pick(sc) for n, sc in s.mx_scales.items()}
     return synth.Workload(**{**s.__dict__, "H": 1, "q": pick(s.q), "k": pick(s.k), "v": pick(s.v),
-                             "dout": pick(s.dout), "bias_table": tab})
+                             "dout": pick(s.dout), "bias_table": tab, "mx_scales": scales})
 
 
 # (workload, random slices besides the longest sample)
 CASES = [("tiny_gdpa_fp32", 2), ("gdpa_xattn_short_kv", 3), ("jfa_causal_self", 1),
          ("pma_gdpa_fwd", 3), ("longtail_gdpa", 1), ("jfa_swa_causal_self", 1),
-         ("jfa_rope_causal_self", 1)]
+         ("jfa_rope_causal_self", 1), ("pma_gdpa_fwd_mxfp8", 3), ("gdpa_xattn_short_kv_mxfp8", 3)]
 
 
 @pytest.mark.timeout(900)

@@ -1,0 +1,75 @@
+"""MXFP8 forward on the HIP path against the fp64 oracle.
+
+q, k and v arrive as FP8 E4M3 codes with one E8M0 scale code per block of 32
+head-dimension elements; the oracle decodes them exactly and runs the plain
+fp64 attention.  Same per-row bar as the bf16 path (tau = 2e-2; rows with no
+visible key exactly zero), since the decoded values are exact bf16 values.
+"""
+import pytest
+import torch
+
+from recsys_jagged_attention_gdpa_amd import synth
+from tests.gpu_helpers import announce, gpu_fwd, parity, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# short (<= 32 keys) and long samples, Lq != Lk, empty samples, ragged tails
+LQ = [1, 70, 300, 0, 129, 5, 40, 260, 33]
+LK = [32, 1, 17, 0, 300, 65, 40, 129, 500]
+MX = ("q", "k", "v")
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_mx_forward_matches_oracle(mode, causal, D):
+    w = synth.custom(mode=mode, lq=LQ, lk=LK, H=2, D=D, seed=D + causal, act="gelu_tanh", causal=causal,
+                     with_dout=False, mx=MX)
+    parity(w, backward=False, label=f"mxfp8 {mode} causal={causal} D={D}")
+
+
+@pytest.mark.parametrize("mode,bias,act", [("gdpa", "rel", "gelu_erf"), ("gdpa", "keypos", "silu"),
+                                           ("jfa", "rel", "silu"), ("jfa", "keypos", "silu")])
+def test_mx_forward_with_bias_and_window(mode, bias, act):
+    w = synth.custom(mode=mode, lq=[600, 31, 128, 1, 0], lk=[600, 31, 200, 3, 7], H=3, D=128, seed=5,
+                     act=act, causal=True, window=150, bias_kind=bias, bias_lo=-60 if bias == "rel" else 0,
+                     bias_hi=60 if bias == "rel" else 300, with_dout=False, mx=MX)
+    parity(w, backward=False, label=f"mxfp8 {mode} bias={bias}")
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+@pytest.mark.parametrize("shared", [16, 48])
+def test_mx_forward_shared_queries(mode, shared):
+    # 16 rows: one-wave 32-row units; 48 rows: the 4-wave 128-row units
+    w = synth.custom(mode=mode, lq=None, lk=[700, 0, 1, 31, 33, 257, 4000], H=4, D=64, seed=3,
+                     shared_q=shared, act="silu", bias_kind="keypos", bias_lo=0, bias_hi=4095,
+                     with_dout=False, mx=MX)
+    parity(w, backward=False, label=f"mxfp8 shared-q={shared} {mode}")
+
+
+def test_mx_jfa_without_residual_and_wide_scales():
+    w = synth.custom(mode="jfa", lq=LQ, lk=LK, H=2, D=128, seed=9, with_dout=False, mx=MX)
+    # value scale codes spread over 2^-27 .. 2^+27 (every decoded value stays inside
+    # bf16's normal range); query / key codes over 2^-9 .. 2^0, so the scores, and
+    # with them the LSE bar, stay at ordinary magnitudes
+    gen = torch.Generator().manual_seed(1)
+    rnd = lambda lo, hi, sc: torch.randint(lo, hi, tuple(sc.shape), generator=gen, dtype=torch.int64).to(torch.uint8)
+    scales = {"q": rnd(118, 128, w.mx_scales["q"]), "k": rnd(118, 128, w.mx_scales["k"]),
+              "v": rnd(100, 155, w.mx_scales["v"])}
+    w = synth.Workload(**{**w.__dict__, "mx_scales": scales})
+    parity(w, backward=False, label="mxfp8 jfa wide scales")
+    d = to_dev(w)
+    a = gpu_fwd(w, d, residual=True)
+    b = gpu_fwd(w, d, residual=False)
+    torch.cuda.synchronize()
+    announce("mxfp8 jfa residual on/off: LSE equal")
+    assert torch.equal(a["lse"], b["lse"])
+
+
+def test_mx_forward_is_deterministic():
+    w = synth.custom(mode="gdpa", lq=LQ, lk=LK, H=2, D=128, seed=4, act="gelu_erf", with_dout=False, mx=MX)
+    d = to_dev(w)
+    announce("mxfp8 determinism")
+    a, b = gpu_fwd(w, d), gpu_fwd(w, d)
+    torch.cuda.synchronize()
+    assert torch.equal(a["o"], b["o"])

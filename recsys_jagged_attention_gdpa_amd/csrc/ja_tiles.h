@@ -353,6 +353,18 @@ __device__ __forceinline__ u32x4 mx_decode(const MXRaw &r) {
                  __builtin_bit_cast(uint32_t, d)};
 }
 
+// Codes of two adjacent chunks (16 elements, inside one block) and the block's
+// scale code.
+struct MXRaw2 {
+    u32x4 codes;
+    uint32_t scale;
+};
+
+__device__ __forceinline__ void mx_decode2(const MXRaw2 &r, u32x4 &lo, u32x4 &hi) {
+    lo = mx_decode(MXRaw{u32x2{r.codes[0], r.codes[1]}, r.scale});
+    hi = mx_decode(MXRaw{u32x2{r.codes[2], r.codes[3]}, r.scale});
+}
+
 // One head of an MXFP8 [T, H, D] tensor (codes) with its [T, H, D / 32] scale
 // codes: rows 0 .. rows-1 from global row `row0`, through bounds-checked
 // descriptors (rows past the slice read as zero codes, i.e. zeros).
@@ -378,6 +390,16 @@ struct MXSlice {
         return r;
     }
     __device__ __forceinline__ u32x4 load16(int row, int ch) const { return mx_decode(raw(row, ch)); }
+    // chunks 2 pr and 2 pr + 1 (16 elements, in block pr / 2) of row `row`: one
+    // 16-byte load of codes and one scale byte
+    __device__ __forceinline__ MXRaw2 raw2(int row, int pr, bool valid = true) const {
+        const uint32_t oc = valid ? (uint32_t)row * row_bytes + (uint32_t)pr * 16u : OOB;
+        const uint32_t os = valid ? (uint32_t)row * srow_bytes + (uint32_t)(pr >> 1) : OOB;
+        MXRaw2 r;
+        r.codes = __builtin_amdgcn_raw_buffer_load_b128(c, (int)oc, 0, 0);
+        r.scale = __builtin_amdgcn_raw_buffer_load_b8(s, (int)os, 0, 0);
+        return r;
+    }
 };
 
 // One lane's row of an MXFP8 slice in MFMA operand layout (chunk 2kk+g for k-step kk).
@@ -395,27 +417,33 @@ __device__ __forceinline__ void load_row_operand(bf16x8 (&reg)[D / 16], const MX
 // decodes and writes, so the loads can stay in flight across other work.
 template <int ROWS, int D, int NT>
 struct MXPairLoader {
-    static constexpr int CHUNKS = ROWS * D / 8;
-    static constexpr int PER_THREAD = (CHUNKS + NT - 1) / NT;
-    MXRaw a[PER_THREAD], b[PER_THREAD];
+    static constexpr int PAIRS = ROWS * D / 16;  // 16-code pieces (two chunks)
+    static constexpr int PER_THREAD = (PAIRS + NT - 1) / NT;
+    static_assert(PAIRS % NT == 0 || PAIRS < NT, "tile / thread count mismatch");
+    MXRaw2 a[PER_THREAD], b[PER_THREAD];
     __device__ __forceinline__ void load(const MXSlice<D> &A, const MXSlice<D> &B, int r0, int tid) {
 #pragma unroll
         for (int it = 0; it < PER_THREAD; ++it) {
             const int cid = tid + it * NT;
-            const int r = cid / (D / 8), c = cid % (D / 8);
-            // slots past the tile (CHUNKS < NT) read zeros
-            a[it] = A.raw(r0 + r, c, cid < CHUNKS);
-            b[it] = B.raw(r0 + r, c, cid < CHUNKS);
+            const int r = cid / (D / 16), pr = cid % (D / 16);
+            // slots past the tile (PAIRS < NT) read zeros
+            a[it] = A.raw2(r0 + r, pr, cid < PAIRS);
+            b[it] = B.raw2(r0 + r, pr, cid < PAIRS);
         }
     }
     __device__ __forceinline__ void store(lchar *ta, lchar *tb, int tid) const {
 #pragma unroll
         for (int it = 0; it < PER_THREAD; ++it) {
             const int cid = tid + it * NT;
-            const int r = cid / (D / 8), c = cid % (D / 8);
-            if (CHUNKS % NT != 0 && cid >= CHUNKS) continue;
-            lds_write16(ta, lds_off<D>(r, c), mx_decode(a[it]));
-            lds_write16(tb, lds_off<D>(r, c), mx_decode(b[it]));
+            const int r = cid / (D / 16), pr = cid % (D / 16);
+            if (PAIRS % NT != 0 && cid >= PAIRS) continue;
+            u32x4 lo, hi;
+            mx_decode2(a[it], lo, hi);
+            lds_write16(ta, lds_off<D>(r, 2 * pr), lo);
+            lds_write16(ta, lds_off<D>(r, 2 * pr + 1), hi);
+            mx_decode2(b[it], lo, hi);
+            lds_write16(tb, lds_off<D>(r, 2 * pr), lo);
+            lds_write16(tb, lds_off<D>(r, 2 * pr + 1), hi);
         }
     }
 };
@@ -424,20 +452,25 @@ struct MXPairLoader {
 // written to the LDS tile.
 template <int D>
 struct MXWaveTile {
-    static constexpr int PER_LANE = 32 * D / 8 / WAVE;
-    MXRaw a[PER_LANE];
+    static constexpr int PER_LANE = 32 * D / 16 / WAVE;  // 16-code pieces per lane
+    static_assert((32 * D / 16) % WAVE == 0, "tile / lane count mismatch");
+    MXRaw2 a[PER_LANE];
     __device__ __forceinline__ void load(const MXSlice<D> &S, int r0, int lane) {
 #pragma unroll
         for (int it = 0; it < PER_LANE; ++it) {
             const int cid = lane + it * WAVE;
-            a[it] = S.raw(r0 + cid / (D / 8), cid % (D / 8));
+            a[it] = S.raw2(r0 + cid / (D / 16), cid % (D / 16));
         }
     }
     __device__ __forceinline__ void store(lchar *t, int lane) const {
 #pragma unroll
         for (int it = 0; it < PER_LANE; ++it) {
             const int cid = lane + it * WAVE;
-            lds_write16(t, lds_off<D>(cid / (D / 8), cid % (D / 8)), mx_decode(a[it]));
+            const int r = cid / (D / 16), pr = cid % (D / 16);
+            u32x4 lo, hi;
+            mx_decode2(a[it], lo, hi);
+            lds_write16(t, lds_off<D>(r, 2 * pr), lo);
+            lds_write16(t, lds_off<D>(r, 2 * pr + 1), hi);
         }
     }
 };

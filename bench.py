@@ -43,7 +43,8 @@ KERNEL_SOURCES = ["ja_fwd.hip", "ja_bwd.hip", "ja_plan.hip", "ja_tiles.h", "ja_d
 # long sequences are MFMA work).
 BOUND = {"gdpa_xattn_short_kv": "hbm", "pma_gdpa_fwd": "hbm", "jfa_causal_self": "mfma",
          "longtail_gdpa": "mfma", "tiny_gdpa_fp32": "alu", "jfa_swa_causal_self": "mfma",
-         "jfa_rope_causal_self": "mfma", "pma_gdpa_fwd_mxfp8": "hbm", "gdpa_xattn_short_kv_mxfp8": "hbm"}
+         "jfa_rope_causal_self": "mfma", "pma_gdpa_fwd_mxfp8": "hbm", "gdpa_xattn_short_kv_mxfp8": "hbm",
+         "jfa_causal_self_fwd_mxfp8": "mfma"}
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (the plain fp32 kernels are ALU loops)
 
 

@@ -195,6 +195,9 @@ CATALOGUE = {
                                kv_len=("uniform", 1, 4096), qkv_sigma=1.0, act="silu", causal=False,
                                bias=("keypos", 0, 4095, math.sqrt(0.1)), backward=False, mx=("q", "k", "v"),
                                same_draw_as="pma_gdpa_fwd"),
+    "jfa_causal_self_fwd_mxfp8": dict(mode="jfa", B=64, H=8, D=128, dtype="bf16", q_len=("uniform", 1, 8192),
+                                      kv_len="same", qkv_sigma=1.0, act=None, causal=True, bias=None,
+                                      backward=False, mx=("q", "k", "v"), same_draw_as="jfa_causal_self"),
     "gdpa_xattn_short_kv_mxfp8": dict(mode="gdpa", B=1024, H=4, D=128, dtype="bf16",
                                       q_len=("uniform", 1, 1024), kv_len=("fixed", 32),
                                       qkv_sigma=math.sqrt(0.5), act="gelu_tanh", causal=False, bias=None,

@@ -48,7 +48,7 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 units a running softmax max may l
 // tiles then come through registers (codes in flight during the current tile,
 // decoded into the LDS tile at its end) instead of the buffer->LDS copy, which
 // moves bytes without decoding them.
-// With MX, D = 128 and four waves, S^T = K Q^T runs on the block-scaled fp8
+// With MX and D = 64 or 128, S^T = K Q^T runs on the block-scaled fp8
 // MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) straight from the codes: key tiles
 // reach LDS as codes by buffer->LDS copies (half the bytes, no decoding), query
 // codes stay in registers, and the block scales go in as the MFMA's scale
@@ -105,18 +105,17 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                                      bz.kind ? (uint32_t)bz.width * 4u : 0u);
 
         // Q rows of this lane, in B-operand layout: chunk 2kk+g of row irow.
-        constexpr bool F8S = MX && D == 128 && WAVES == 4;  // S on the fp8 MFMA
-        constexpr int NKS8 = D / 64;                         // 64-code k-steps of the fp8 MFMA
+        constexpr bool F8S = MX && D >= 64;  // S on the fp8 MFMA
+        constexpr int NKS8 = D / 64;          // 64-code k-steps of the fp8 MFMA
         bf16x8 qreg[F8S ? 1 : NKK];
         i32x8 qf[F8S ? NKS8 : 1];  // F8S: query codes, operand layout
         int qsc[F8S ? NKS8 : 1];   // F8S: their block scale codes
         if constexpr (F8S) {
             const MXSlice<D> Qm(p.q, p.q_sc, s.qs, s.lq, H, h);
-            const uint32_t sq = f8_row_scales(Qm, irow);
 #pragma unroll
             for (int ks = 0; ks < NKS8; ++ks) {
-                qf[ks] = f8_row_operand(Qm, irow, ks, g);
-                qsc[ks] = (int)((sq >> (8 * (2 * ks + g))) & 0xffu);
+                qf[ks] = f8_row_operand<D>(Qm, irow, ks, g);
+                qsc[ks] = f8_scale<D>(Qm, irow, 2 * ks + g);
             }
         } else if constexpr (MX) {
             load_row_operand<D>(qreg, MXSlice<D>(p.q, p.q_sc, s.qs, s.lq, H, h), irow, g);
@@ -126,7 +125,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         const MXSlice<D> Km(p.k, p.k_sc, s.ks, MX ? s.lk : 0, H, h), Vm(p.v, p.v_sc, s.ks, MX ? s.lk : 0, H, h);
         MXPairLoader<BN, D, NT> mxl;  // MX: key and value codes, decoded into LDS
         MXTileLoader<BN, D, NT> mxv;  // F8S: value codes only
-        uint32_t ksn[NNB], ksc[NNB];  // F8S: scale codes of the lane's key rows, next / current tile
+        int ksn[NNB][F8S ? NKS8 : 1], ksc[NNB][F8S ? NKS8 : 1];  // F8S: the lane's key-row scale codes, next / current tile
 
         f32x16 oacc[NDB];
 #pragma unroll
@@ -140,10 +139,12 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         auto load_tile = [&](int jt) {
             lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             if constexpr (F8S) {
-                dma_f8_tile<BN, NT>(kt, Km, jt * BN, tid);
+                dma_f8_tile<BN, D, NT>(kt, Km, jt * BN, tid);
                 mxv.load(Vm, jt * BN, tid);
 #pragma unroll
-                for (int nb = 0; nb < NNB; ++nb) ksn[nb] = f8_row_scales(Km, jt * BN + nb * 32 + l32);
+                for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                    for (int ks = 0; ks < NKS8; ++ks) ksn[nb][ks] = f8_scale<D>(Km, jt * BN + nb * 32 + l32, 2 * ks + g);
             } else if constexpr (MX) {
                 mxl.load(Km, Vm, jt * BN, tid);
             } else {
@@ -157,7 +158,9 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             if constexpr (F8S) {
                 mxv.store(lbase + buf * 2 * TILE_BYTES + TILE_BYTES, tid);
 #pragma unroll
-                for (int nb = 0; nb < NNB; ++nb) ksc[nb] = ksn[nb];
+                for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                    for (int ks = 0; ks < NKS8; ++ks) ksc[nb][ks] = ksn[nb][ks];
             } else if constexpr (MX) {
                 mxl.store(lbase + buf * 2 * TILE_BYTES, lbase + buf * 2 * TILE_BYTES + TILE_BYTES, tid);
             }
@@ -189,10 +192,9 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                 if constexpr (F8S) {
 #pragma unroll
                     for (int ks = 0; ks < NKS8; ++ks) {
-                        const i32x8 a = lds_read_f8_operand(Kt, nb * 32 + l32, ks, g);
-                        const int sa = (int)((ksc[nb] >> (8 * (2 * ks + g))) & 0xffu);
-                        sacc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], sacc[nb], 0, 0, 0, sa,
-                                                                                  0, qsc[ks]);
+                        const i32x8 a = lds_read_f8_operand<D>(Kt, nb * 32 + l32, ks, g);
+                        sacc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], sacc[nb], 0, 0, 0,
+                                                                                  ksc[nb][ks], 0, qsc[ks]);
                     }
                 } else {
 #pragma unroll

@@ -485,48 +485,57 @@ struct MXTileLoader {
 // both blocks (any pairing A and B share gives the same sums; here half g takes
 // codes 16 g .. 16 g + 15 of each block); the scale of (row r, block kb) is
 // byte 0 of lane r + 32 kb's scale operand; the accumulator layout is the bf16
-// 32x32 one.  Code tiles in LDS have 128-byte rows (D = 128) whose 16-byte
-// chunks are XOR-swizzled by the row's low three bits, so the operand reads of
-// 8 consecutive rows hit 8 different bank groups.
+// 32x32 one.  Code tiles in LDS have D-byte rows whose 16-byte chunks are
+// XOR-swizzled so that the operand reads of 8 consecutive rows at one chunk
+// hit 8 different bank groups: by the row's low three bits for 128-byte rows,
+// by bits 1-2 for 64-byte rows (two rows share a 128-byte bank line).
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int f8_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+template <int D>
+__device__ __forceinline__ int f8_off(int r, int c) {
+    static_assert(D == 64 || D == 128, "code tiles for D = 64 or 128");
+    if constexpr (D == 128) return r * 128 + ((c ^ (r & 7)) << 4);
+    else return r * 64 + ((c ^ ((r >> 1) & 3)) << 4);
+}
 
-// ROWS rows of 128 codes copied by NT threads straight into a swizzled code
+// ROWS rows of D codes copied by NT threads straight into a swizzled code
 // tile (buffer_load ... lds; lane i of an instruction writes 16 bytes at slot
 // i, so each lane fetches the chunk the swizzle puts there).  Rows past the
 // slice land as zero codes.
-template <int ROWS, int NT>
-__device__ __forceinline__ void dma_f8_tile(lchar *tile, const MXSlice<128> &S, int r0, int tid) {
-    constexpr int CH = 8, SLOTS = ROWS * CH, PER_INSTR = NT / WAVE * WAVE;
+template <int ROWS, int D, int NT>
+__device__ __forceinline__ void dma_f8_tile(lchar *tile, const MXSlice<D> &S, int r0, int tid) {
+    constexpr int CH = D / 16, SLOTS = ROWS * CH, PER_INSTR = NT / WAVE * WAVE;
     static_assert(SLOTS % NT == 0, "tile / thread count mismatch");
     const int wv = tid / WAVE, lane = tid % WAVE;
 #pragma unroll
     for (int it = 0; it < SLOTS / NT; ++it) {
         const int first = it * PER_INSTR + wv * WAVE;
         const int q = first + lane;
-        const int r = q / CH, c = (q % CH) ^ (r & 7);
+        const int r = q / CH;
+        const int c = (f8_off<D>(r, q % CH) - r * D) >> 4;  // the swizzle is an involution
         buf_load16_lds(S.c, tile + first * 16, (uint32_t)(r0 + r) * S.row_bytes + (uint32_t)c * 16u);
     }
 }
 
 // Operand (k-step ks) of row r of a code tile, for lane half g.
+template <int D>
 __device__ __forceinline__ i32x8 lds_read_f8_operand(const lchar *tile, int r, int ks, int g) {
-    const u32x4 lo = __builtin_bit_cast(u32x4, lds_read16(tile, f8_off(r, 4 * ks + g)));
-    const u32x4 hi = __builtin_bit_cast(u32x4, lds_read16(tile, f8_off(r, 4 * ks + 2 + g)));
+    const u32x4 lo = __builtin_bit_cast(u32x4, lds_read16(tile, f8_off<D>(r, 4 * ks + g)));
+    const u32x4 hi = __builtin_bit_cast(u32x4, lds_read16(tile, f8_off<D>(r, 4 * ks + 2 + g)));
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// Operand (k-step ks) of row `row` of an MXFP8 slice (D = 128), for lane half g,
-// and the scale code of its block 2 ks + g.
-__device__ __forceinline__ i32x8 f8_row_operand(const MXSlice<128> &S, int row, int ks, int g) {
+// Operand (k-step ks) of row `row` of an MXFP8 slice, for lane half g.
+template <int D>
+__device__ __forceinline__ i32x8 f8_row_operand(const MXSlice<D> &S, int row, int ks, int g) {
     const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(S.c, (int)((uint32_t)row * S.row_bytes + (uint32_t)(4 * ks + g) * 16u), 0, 0);
     const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(S.c, (int)((uint32_t)row * S.row_bytes + (uint32_t)(4 * ks + 2 + g) * 16u), 0, 0);
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
-// The four scale codes of row `row` (D = 128), byte b = block b.
-__device__ __forceinline__ uint32_t f8_row_scales(const MXSlice<128> &S, int row) {
-    return __builtin_amdgcn_raw_buffer_load_b32(S.s, (int)((uint32_t)row * S.srow_bytes), 0, 0);
+// Scale code of block `blk` of row `row`.
+template <int D>
+__device__ __forceinline__ int f8_scale(const MXSlice<D> &S, int row, int blk) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b8(S.s, (int)((uint32_t)row * S.srow_bytes + (uint32_t)blk), 0, 0);
 }
 
 // WaveTile for an MXFP8 slice: 32 rows read as codes by one wave, decoded when

@@ -32,7 +32,8 @@ def _single_head(w, b, h):
 # (workload, random slices besides the longest sample)
 CASES = [("tiny_gdpa_fp32", 2), ("gdpa_xattn_short_kv", 3), ("jfa_causal_self", 1),
          ("pma_gdpa_fwd", 3), ("longtail_gdpa", 1), ("jfa_swa_causal_self", 1),
-         ("jfa_rope_causal_self", 1), ("pma_gdpa_fwd_mxfp8", 3), ("gdpa_xattn_short_kv_mxfp8", 3)]
+         ("jfa_rope_causal_self", 1), ("pma_gdpa_fwd_mxfp8", 3), ("gdpa_xattn_short_kv_mxfp8", 3),
+         ("jfa_causal_self_fwd_mxfp8", 1)]
 
 
 @pytest.mark.timeout(900)

@@ -330,7 +330,10 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
 // computed.  Loads and stores go through per-sample buffer descriptors, so the
 // loop body has no branches around memory operations and the next block's
 // loads stay in flight across the current block's stores.
-// MX: MXFP8 inputs, decoded to bf16 when K / V and the Q blocks are written to LDS.
+// MX: MXFP8 inputs.  With D = 64 or 128, S^T = K Q^T runs on the block-scaled
+// fp8 MFMA: key codes stay codes in LDS, each Q block is staged as codes in the
+// wave's tile, the block scales go in as the MFMA's scale operands, and only V
+// is decoded to bf16 for the PV product.  With D = 32 all three are decoded.
 template <int D, int MODE, int ACT, bool SPLIT, bool MX>
 __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnParams p) {
     constexpr int KV_BYTES = 32 * D * 2;
@@ -362,7 +365,22 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
         const int h = w % H;
         const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
         const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
-        if constexpr (MX) {
+        constexpr bool F8 = MX && D >= 64;  // S on the fp8 MFMA
+        constexpr int NKS8 = D / 64;
+        int ksc[F8 ? NKS8 : 1];              // F8: scale codes of the lane's key row l % 32
+        if constexpr (F8) {
+            const MXSlice<D> Km(p.k, p.k_sc, s.ks, s.lk, H, h);
+            MXTileLoader<32, D, FWD_THREADS> vl;
+            vl.load(MXSlice<D>(p.v, p.v_sc, s.ks, s.lk, H, h), 0, threadIdx.x);
+            constexpr int KPIECES = 32 * D / 16;  // 16-code pieces of the key tile
+            if (threadIdx.x < KPIECES) {
+                const int r = threadIdx.x / (D / 16), pr = threadIdx.x % (D / 16);
+                lds_write16(Kt, f8_off<D>(r, pr), Km.codes16(r, pr));
+            }
+#pragma unroll
+            for (int ks = 0; ks < NKS8; ++ks) ksc[ks] = f8_scale<D>(Km, l32, 2 * ks + g);
+            vl.store(Vt, threadIdx.x);
+        } else if constexpr (MX) {
             MXPairLoader<32, D, FWD_THREADS> kv;
             kv.load(MXSlice<D>(p.k, p.k_sc, s.ks, s.lk, H, h), MXSlice<D>(p.v, p.v_sc, s.ks, s.lk, H, h), 0,
                     threadIdx.x);
@@ -373,7 +391,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
             kv.store(Kt, Vt, threadIdx.x);
         }
         using QSlice = std::conditional_t<MX, MXSlice<D>, HeadSlice<D>>;
-        using QTile = std::conditional_t<MX, MXWaveTile<D>, WaveTile<D>>;
+        using QTile = std::conditional_t<F8, F8WaveTile<D>, std::conditional_t<MX, MXWaveTile<D>, WaveTile<D>>>;
         const QSlice Qs = [&]() {
             if constexpr (MX) return MXSlice<D>(p.q, p.q_sc, s.qs, s.lq, H, h);
             else return HeadSlice<D>(p.q, s.qs, s.lq, H, h);
@@ -407,10 +425,18 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
             __builtin_amdgcn_sched_barrier(0);  // keep the next block's loads ahead of this block's work
 
             f32x16 sacc = f32x16{};
+            if constexpr (F8) {
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const int off = lds_off<D>(l32, 2 * kk + g);
-                sacc = mfma32(lds_read16(Kt, off), lds_read16(Ot, off), sacc);
+                for (int ks = 0; ks < NKS8; ++ks)
+                    sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        lds_read_f8_operand<D>(Kt, l32, ks, g), lds_read_f8_operand<D>(Ot, l32, ks, g), sacc, 0, 0, 0,
+                        ksc[ks], 0, qreg.sc[ks]);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const int off = lds_off<D>(l32, 2 * kk + g);
+                    sacc = mfma32(lds_read16(Kt, off), lds_read16(Ot, off), sacc);
+                }
             }
             const int my_kend = key_end(irow, s.lq, s.lk, p.causal, p.window);
             const int my_kbeg = key_begin(irow, s.lq, s.lk, p.window);

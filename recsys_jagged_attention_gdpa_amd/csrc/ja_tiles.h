@@ -390,6 +390,10 @@ struct MXSlice {
         return r;
     }
     __device__ __forceinline__ u32x4 load16(int row, int ch) const { return mx_decode(raw(row, ch)); }
+    // 16 codes (chunks 2 pr and 2 pr + 1) of row `row`, no scale
+    __device__ __forceinline__ u32x4 codes16(int row, int pr) const {
+        return __builtin_amdgcn_raw_buffer_load_b128(c, (int)((uint32_t)row * row_bytes + (uint32_t)pr * 16u), 0, 0);
+    }
     // chunks 2 pr and 2 pr + 1 (16 elements, in block pr / 2) of row `row`: one
     // 16-byte load of codes and one scale byte
     __device__ __forceinline__ MXRaw2 raw2(int row, int pr, bool valid = true) const {
@@ -537,6 +541,34 @@ template <int D>
 __device__ __forceinline__ int f8_scale(const MXSlice<D> &S, int row, int blk) {
     return (int)__builtin_amdgcn_raw_buffer_load_b8(S.s, (int)((uint32_t)row * S.srow_bytes + (uint32_t)blk), 0, 0);
 }
+
+// A 32-row block of MXFP8 codes read by one wave (16 codes per lane and load,
+// whole rows per instruction) and written as codes into a swizzled code tile
+// for the fp8 MFMA, with the scale codes of the lane's operand row r0 + l % 32
+// for blocks 2 ks + l / 32.
+template <int D>
+struct F8WaveTile {
+    static constexpr int PER_LANE = 32 * D / 16 / WAVE;
+    static_assert((32 * D / 16) % WAVE == 0, "tile / lane count mismatch");
+    u32x4 a[PER_LANE];
+    int sc[D / 64];
+    __device__ __forceinline__ void load(const MXSlice<D> &S, int r0, int lane) {
+#pragma unroll
+        for (int it = 0; it < PER_LANE; ++it) {
+            const int cid = lane + it * WAVE;
+            a[it] = S.codes16(r0 + cid / (D / 16), cid % (D / 16));
+        }
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks) sc[ks] = f8_scale<D>(S, r0 + (lane & 31), 2 * ks + (lane >> 5));
+    }
+    __device__ __forceinline__ void store(lchar *t, int lane) const {
+#pragma unroll
+        for (int it = 0; it < PER_LANE; ++it) {
+            const int cid = lane + it * WAVE;
+            lds_write16(t, f8_off<D>(cid / (D / 16), cid % (D / 16)), a[it]);
+        }
+    }
+};
 
 // WaveTile for an MXFP8 slice: 32 rows read as codes by one wave, decoded when
 // written to the LDS tile.

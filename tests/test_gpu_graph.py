@@ -111,3 +111,47 @@ def test_captured_step_replays_match_eager(case):
         torch.cuda.synchronize()
         for a, b in zip(step.outputs(), eager2):
             assert torch.equal(a, b), f"replay {rep} on new inputs differs from the eager step"
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+def test_captured_mxfp8_forward_replays_match_eager(mode):
+    w = synth.custom(mode=mode, lq=[1, 70, 300, 0, 129, 5, 260, 33], lk=[32, 1, 17, 0, 300, 65, 129, 500], H=2,
+                     D=128, seed=41, act="gelu_erf", causal=(mode == "jfa"), with_dout=False,
+                     mx=("q", "k", "v"))
+    announce(f"graph capture mxfp8 forward {mode}")
+    d = to_dev(w)
+    p = _lib.make_problem(batch=w.B, heads=w.H, head_dim=w.D, dtype=torch.bfloat16, total_q=w.total_q,
+                          total_k=w.total_k, q_offsets=d["q_off"], kv_offsets=d["kv_off"], causal=w.causal,
+                          scale=w.scale, act=w.act)
+    o = torch.empty((w.total_q, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.H, w.total_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(_lib.ja_workspace_size(p, _lib.PASS_FWD), dtype=torch.uint8, device="cuda")
+
+    def run():
+        if mode == "gdpa":
+            _lib.jagged_gdpa_fwd_mx(p, d["q"], d["q_sc"], d["k"], d["k_sc"], d["v"], d["v_sc"], o, ws)
+        else:
+            _lib.jagged_attn_fwd_mx(p, d["q"], d["q_sc"], d["k"], d["k_sc"], d["v"], d["v_sc"], o, lse, None, ws)
+
+    run()
+    torch.cuda.synchronize()
+    eager = (o.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager[0]), f"replay {rep}: O differs from the eager call"
+        if mode == "jfa":
+            assert torch.equal(lse, eager[1]), f"replay {rep}: LSE differs from the eager call"
+        run()
+        torch.cuda.synchronize()

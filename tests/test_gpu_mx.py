@@ -73,3 +73,21 @@ def test_mx_forward_is_deterministic():
     a, b = gpu_fwd(w, d), gpu_fwd(w, d)
     torch.cuda.synchronize()
     assert torch.equal(a["o"], b["o"])
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+def test_mx_short_only_batch_with_key_bound(mode):
+    # every sample has at most 32 keys: with the bound the long kernels are not launched
+    w = synth.custom(mode=mode, lq=[1, 700, 0, 33, 64], lk=[32, 5, 9, 0, 31], H=2, D=128, seed=13, act="silu",
+                     with_dout=False, mx=MX)
+    parity(w, backward=False, label=f"mxfp8 short-only {mode}", max_kv_len=32)
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+def test_mx_all_empty_samples(mode):
+    # no query rows and no keys at all: nothing is read, the outputs have no rows
+    w = synth.custom(mode=mode, lq=[0, 0, 0], lk=[0, 0, 0], H=2, D=64, seed=1, with_dout=False, mx=MX)
+    parity(w, backward=False, label=f"mxfp8 empty {mode}")
+    # keys but no queries, and queries but no keys (rows exactly zero, LSE -inf)
+    w = synth.custom(mode=mode, lq=[0, 5, 0], lk=[40, 0, 3], H=2, D=64, seed=2, with_dout=False, mx=MX)
+    parity(w, backward=False, label=f"mxfp8 one-sided {mode}")

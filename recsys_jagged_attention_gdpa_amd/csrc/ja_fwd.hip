@@ -132,9 +132,10 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
         float m_run = -INFINITY, l_run = 0.0f;  // JFA running max (log2 units) and partial sum
 
-        // Key / value tile jt is copied straight into LDS buffer (jt & 1); the
-        // bias window it needs goes through a register.  Loads past the sample
-        // read zeros.
+        // Key / value tile jt goes to LDS buffer (jt & 1): bf16 tiles and the
+        // fp8 key codes are copied straight into it, decoded MXFP8 tiles pass
+        // through registers (loaded here, written by store_tile); the bias window
+        // it needs goes through a register.  Loads past the sample read zeros.
         float bnext = 0.0f;
         auto load_tile = [&](int jt) {
             lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;

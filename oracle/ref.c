@@ -56,12 +56,11 @@
  * respect to the rows as given, so dQ_i and dK_j are the gradients of the
  * turned rows turned back (the rotation's transpose is the turn by -a).
  * With bf16 operands (rope_bf16 = 1) the turned rows are themselves operands
- * of bf16 products, so they are bf16 values: the turn is taken in float32 and
- * each turned element rounded to bf16 (nearest even) -- a quantisation step,
- * taken here in the same precision as on the GPU: c and s are the float32
- * roundings of the fp64 cosine and sine, x'_d = fmaf(x_d, c, -(x_{d+D/2} s))
- * and x'_{d+D/2} = fmaf(x_d, s, x_{d+D/2} c) with float32 products.  The
- * gradients then follow the rounded rows (the rounding is held fixed).
+ * of bf16 products, so they are bf16 values: each element of the exact turn
+ * (computed in double) is rounded to the nearest bf16 value, ties to even -- a
+ * quantisation step with a plain definition, taken here straight from the
+ * double, with no intermediate precision.  The gradients then follow the
+ * rounded rows (the rounding is held fixed).
  *
  * Inputs are float32 arrays (bf16 values are exactly representable in
  * float32); all arithmetic is double.  Layout is token-major [T, H, D] with
@@ -204,27 +203,26 @@ static void rope_turn(double *x, int D, double base, double t, int sign) {
     }
 }
 
-/* float32 -> nearest bf16 (ties to even), returned as float32. */
-static float bf16_round(float x) {
-    uint32_t u;
-    memcpy(&u, &x, 4);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    u &= 0xffff0000u;
-    memcpy(&x, &u, 4);
-    return x;
+/* Nearest bf16 value of a double, ties to even: 8 significant bits, the
+ * exponent range of float32 (normal down to 2^-126, below it a fixed step of
+ * 2^-133), magnitudes that round past the largest finite bf16 value become
+ * infinite.  Written from the definition of rounding to a p-bit significand. */
+static double bf16_nearest(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    frexp(x, &e);                /* 2^(e-1) <= |x| < 2^e */
+    int q = e - 8;               /* the bf16 step at |x|: 2^(e-1-7) */
+    if (q < -133) q = -133;
+    const double r = ldexp(nearbyint(ldexp(x, -q)), q);  /* default rounding: to nearest, ties even */
+    const double bf16_max = ldexp(255.0, 120);           /* (2 - 2^-7) 2^127 */
+    return fabs(r) > bf16_max ? copysign(INFINITY, x) : r;
 }
 
-/* The turn of one row in float32, each element rounded to bf16. */
+/* The exact turn of one row (in double), each element rounded to bf16. */
 static void rope_turn_bf16(const float *x, double *y, int D, double base, double t) {
-    const int half = D / 2;
-    for (int d = 0; d < half; ++d) {
-        const double a = t * pow(base, -2.0 * d / D);
-        const float c = (float)cos(a), sn = (float)sin(a);
-        const float x0 = x[d], x1 = x[d + half];
-        const float p0 = x1 * sn, p1 = x1 * c;
-        y[d] = bf16_round(fmaf(x0, c, -p0));
-        y[d + half] = bf16_round(fmaf(x0, sn, p1));
-    }
+    for (int d = 0; d < D; ++d) y[d] = (double)x[d];
+    rope_turn(y, D, base, t, 1);
+    for (int d = 0; d < D; ++d) y[d] = bf16_nearest(y[d]);
 }
 
 /* Turned copy of a [rows, H, D] tensor: row r of sample b sits at position
@@ -335,18 +333,29 @@ static void pair_bwd(const problem *p, int softmax, int h, const sample *s, int6
     }
 }
 
-/* Softmax statistics of query row i (JFA): m, l, and delta_i = sum_j P_ij dP_ij. */
+/* Softmax statistics of query row i (JFA): m, l, and delta_i = sum_j P_ij dP_ij;
+ * with oabs non-NULL also sum_d |dO_id| |O_id| (O_i = sum_j P_ij v_j). */
 static int row_bwd_stats(const problem *p, int h, const sample *s, int64_t i, const float *doi,
-                         double *m, double *l, double *delta) {
+                         double *m, double *l, double *delta, double *oabs) {
     if (!row_stats(p, h, s, i, m, l)) return 0;
-    double dl = 0.0;
+    double dl = 0.0, o[128];
+    for (int d = 0; d < p->D && oabs; ++d) o[d] = 0.0;
     for (int64_t j = 0; j < s->lk; ++j) {
         if (!is_valid(p, i, j, s->lq, s->lk)) continue;
         double w, dx;
         pair_bwd(p, 1, h, s, i, j, doi, *m, *l, 0.0, &w, &dx);  /* dx = P_ij dP_ij here */
         dl += dx;
+        if (oabs) {
+            const float *vj = row_of(p, p->v, s->ks + j, h);
+            for (int d = 0; d < p->D; ++d) o[d] += w * (double)vj[d];
+        }
     }
     *delta = dl;
+    if (oabs) {
+        double a = 0.0;
+        for (int d = 0; d < p->D; ++d) a += fabs((double)doi[d]) * fabs(o[d]);
+        *oabs = a;
+    }
     return 1;
 }
 
@@ -410,14 +419,39 @@ static void run_fwd(const problem *p, int softmax, double *o, double *lse, int n
  * row, summing over its keys; (3) dK and dV per key row, summing over the
  * query rows that see it.  Each output row is written by one iteration, so
  * every phase is parallel over rows and needs no reduction across threads. */
+/* Rounding-noise scale of one gradient row (optional outputs nq, nk), the sum
+ * of two parts:
+ *  - with terms t_d = scale dX_ij x_jd summed over j, max_d sqrt(sum_j t_d^2)
+ *    times dx_unit, the unit roundoff of the dX operands (2^-8 for bf16): the
+ *    error a sum of those terms carries when each dX_ij is rounded before it is
+ *    multiplied;
+ *  - (JFA) scale max_d sum_j P_ij |delta-error_i| |x_jd| with the error of delta
+ *    taken as delta_unit sum_d |dO_id| |O_id| (2^-16 for an output held to 16
+ *    significant bits: a bf16 value plus its bf16 residual), which decides rows
+ *    whose exact dX vanishes (a row with one visible key).
+ * With the rotary embedding the row is turned back afterwards, which mixes
+ * elements d and d + D/2, so pairs are combined. */
+static double noise_of(const double *ss, const double *pd, int D, int turned, double scale, double dx_unit,
+                       double delta_unit) {
+    double mx = 0.0, mp = 0.0;
+    for (int d = 0; d < D; ++d) {
+        const int e = d < D / 2 ? d + D / 2 : d - D / 2;
+        const double v = ss[d] + (turned ? ss[e] : 0.0);
+        const double w = pd[d] + (turned ? pd[e] : 0.0);
+        if (v > mx) mx = v;
+        if (w > mp) mp = w;
+    }
+    return dx_unit * sqrt(mx) + scale * delta_unit * mp;
+}
+
 static int run_bwd(const problem *p, int softmax, const float *dout, double *dq, double *dk,
-                   double *dv, int nthreads) {
+                   double *dv, double *nq, double *nk, double dx_unit, double delta_unit, int nthreads) {
     if (!p->q_off) return 1;
     const int64_t tq = p->q_off[p->B], tk = p->kv_off[p->B];
     const int H = p->H, D = p->D;
-    double *st = NULL; /* per (row, head): m, l, delta, valid */
+    double *st = NULL; /* per (row, head): m, l, delta, valid, sum_d |dO| |O| */
     if (softmax) {
-        st = (double *)malloc(sizeof(double) * 4 * (size_t)(tq > 0 ? tq : 1) * H);
+        st = (double *)malloc(sizeof(double) * 5 * (size_t)(tq > 0 ? tq : 1) * H);
         if (!st) return 2;
     }
     const int nt = nthreads_or_default(nthreads);
@@ -428,8 +462,10 @@ static int run_bwd(const problem *p, int softmax, const float *dout, double *dq,
             const int h = (int)(u % H);
             const int b = sample_of_out_row(p, r);
             sample s = sample_rows(p, b);
-            double *sr = st + 4 * u;
-            sr[3] = row_bwd_stats(p, h, &s, r - s.qs, row_of(p, dout, r, h), &sr[0], &sr[1], &sr[2]);
+            double *sr = st + 5 * u;
+            sr[4] = 0.0;
+            sr[3] = row_bwd_stats(p, h, &s, r - s.qs, row_of(p, dout, r, h), &sr[0], &sr[1], &sr[2],
+                                  (nq || nk) ? &sr[4] : NULL);
         }
     }
 #pragma omp parallel for schedule(dynamic, 16) num_threads(nt)
@@ -440,8 +476,10 @@ static int run_bwd(const problem *p, int softmax, const float *dout, double *dq,
         sample s = sample_rows(p, b);
         const int64_t i = r - s.qs;
         double *dqi = orow(p, dq, r, h);
-        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
-        const double *sr = softmax ? st + 4 * u : NULL;
+        double ss[128], pd[128];
+        for (int d = 0; d < D; ++d) { dqi[d] = 0.0; ss[d] = 0.0; pd[d] = 0.0; }
+        if (nq) nq[u] = 0.0;
+        const double *sr = softmax ? st + 5 * u : NULL;
         if (softmax && sr[3] == 0.0) continue;
         const float *doi = row_of(p, dout, r, h);
         for (int64_t j = 0; j < s.lk; ++j) {
@@ -449,9 +487,16 @@ static int run_bwd(const problem *p, int softmax, const float *dout, double *dq,
             double w, dx;
             pair_bwd(p, softmax, h, &s, i, j, doi, sr ? sr[0] : 0.0, sr ? sr[1] : 1.0,
                      sr ? sr[2] : 0.0, &w, &dx);
-            for (int d = 0; d < D; ++d) dqi[d] += p->scale * dx * k_at(p, s.ks + j, h, d);
+            for (int d = 0; d < D; ++d) {
+                const double kd = k_at(p, s.ks + j, h, d);
+                const double t = p->scale * dx * kd;
+                dqi[d] += t;
+                ss[d] += t * t;
+                if (sr) pd[d] += w * sr[4] * fabs(kd);
+            }
         }
         if (p->qrot) rope_turn(dqi, D, p->rope_base, (double)i, -1);
+        if (nq) nq[u] = noise_of(ss, pd, D, p->qrot != NULL, p->scale, dx_unit, delta_unit);
     }
 #pragma omp parallel for schedule(dynamic, 16) num_threads(nt)
     for (int64_t u = 0; u < tk * H; ++u) {
@@ -461,20 +506,26 @@ static int run_bwd(const problem *p, int softmax, const float *dout, double *dq,
         sample s = sample_rows(p, b);
         const int64_t j = r - s.ks;
         double *dkj = orow(p, dk, r, h), *dvj = orow(p, dv, r, h);
-        for (int d = 0; d < D; ++d) { dkj[d] = 0.0; dvj[d] = 0.0; }
+        double ss[128], pd[128];
+        for (int d = 0; d < D; ++d) { dkj[d] = 0.0; dvj[d] = 0.0; ss[d] = 0.0; pd[d] = 0.0; }
         for (int64_t i = 0; i < s.lq; ++i) {
             if (!is_valid(p, i, j, s.lq, s.lk)) continue;
-            const double *sr = softmax ? st + 4 * ((s.qs + i) * H + h) : NULL;
+            const double *sr = softmax ? st + 5 * ((s.qs + i) * H + h) : NULL;
             const float *doi = row_of(p, dout, s.qs + i, h);
             double w, dx;
             pair_bwd(p, softmax, h, &s, i, j, doi, sr ? sr[0] : 0.0, sr ? sr[1] : 1.0,
                      sr ? sr[2] : 0.0, &w, &dx);
             for (int d = 0; d < D; ++d) {
-                dkj[d] += p->scale * dx * q_at(p, s.qs + i, h, d);
+                const double qd = q_at(p, s.qs + i, h, d);
+                const double t = p->scale * dx * qd;
+                dkj[d] += t;
+                ss[d] += t * t;
+                if (sr) pd[d] += w * sr[4] * fabs(qd);
                 dvj[d] += w * (double)doi[d];
             }
         }
         if (p->krot) rope_turn(dkj, D, p->rope_base, (double)j, -1);
+        if (nk) nk[u] = noise_of(ss, pd, D, p->krot != NULL, p->scale, dx_unit, delta_unit);
     }
     free(st);
     return 0;
@@ -498,7 +549,7 @@ static int run_dbias(const problem *p, int softmax, const float *dout, double *d
         for (int64_t i = 0; i < s.lq; ++i) {
             const float *doi = row_of(p, dout, s.qs + i, h);
             double m = 0.0, l = 1.0, delta = 0.0;
-            if (softmax && !row_bwd_stats(p, h, &s, i, doi, &m, &l, &delta)) continue;
+            if (softmax && !row_bwd_stats(p, h, &s, i, doi, &m, &l, &delta, NULL)) continue;
             for (int64_t j = 0; j < s.lk; ++j) {
                 if (!is_valid(p, i, j, s.lq, s.lk)) continue;
                 double w, dx;
@@ -556,7 +607,7 @@ int ref_gdpa_bwd(const float *q, const float *k, const float *v, const float *do
                              bias_kind, bias_table, bias_lo, bias_hi);
     if (!q_off) return 1;
     if (rope_prepare(&p)) { rope_release(&p); return 2; }
-    const int rc = run_bwd(&p, 0, dout, dq, dk, dv, nthreads);
+    const int rc = run_bwd(&p, 0, dout, dq, dk, dv, NULL, NULL, 0.0, 0.0, nthreads);
     rope_release(&p);
     return rc;
 }
@@ -569,7 +620,24 @@ int ref_attn_bwd(const float *q, const float *k, const float *v, const float *do
                              bias_kind, bias_table, bias_lo, bias_hi);
     if (!q_off) return 1;
     if (rope_prepare(&p)) { rope_release(&p); return 2; }
-    const int rc = run_bwd(&p, 1, dout, dq, dk, dv, nthreads);
+    const int rc = run_bwd(&p, 1, dout, dq, dk, dv, NULL, NULL, 0.0, 0.0, nthreads);
+    rope_release(&p);
+    return rc;
+}
+
+/* As ref_gdpa_bwd / ref_attn_bwd (softmax 0 / 1), also writing the rounding-noise
+ * scale of every dQ row (nq [total_q, H]) and dK row (nk [total_k, H]) for the
+ * given unit roundoffs of dX and of delta (see noise_of). */
+int ref_bwd_noise(int softmax, const float *q, const float *k, const float *v, const float *dout,
+                  double *dq, double *dk, double *dv, double *nq, double *nk, const int32_t *q_off,
+                  const int32_t *kv_off, int B, int H, int D, double scale, int act, int causal,
+                  int window, double rope_base, int bias_kind, const float *bias_table, int bias_lo,
+                  int bias_hi, double dx_unit, double delta_unit, int nthreads) {
+    problem p = make_problem(q, k, v, q_off, 0, kv_off, B, H, D, scale, act, causal, window, rope_base,
+                             bias_kind, bias_table, bias_lo, bias_hi);
+    if (!q_off || D > 128) return 1;
+    if (rope_prepare(&p)) { rope_release(&p); return 2; }
+    const int rc = run_bwd(&p, softmax, dout, dq, dk, dv, nq, nk, dx_unit, delta_unit, nthreads);
     rope_release(&p);
     return rc;
 }

@@ -22,11 +22,14 @@
 // their sine / cosine once, then turns those pairs in every head.
 //
 // Precision.  The turned rows are operands of bf16 products, so they are bf16
-// values: c and s are the float32 roundings of the fp64 cosine and sine of the
-// fp64 angle t * inv_freq[d] (inv_freq = base^(-2d/D), computed on the host in
-// fp64), and x'_d = fma(x_d, c, -(x_{d+D/2} s)), x'_{d+D/2} = fma(x_d, s,
-// x_{d+D/2} c) with float32 products, rounded to nearest even -- a fixed
-// sequence of roundings that a checker can repeat on the CPU.
+// values: each is the bf16 value nearest to the turn (ties to even), with the
+// turn computed in fp64 (cosine and sine of the fp64 angle t * inv_freq[d],
+// inv_freq = base^(-2d/D) computed on the host in fp64) and rounded once,
+// straight from fp64 to bf16.  Rounding through float32 first would round twice
+// and differ from the nearest bf16 value wherever the turn lies within half a
+// float32 step of a bf16 midpoint; a float32 turn would be off by a few float32
+// steps and differ more often still.  fp32 tensors get the fp64 turn rounded
+// once to float32.
 #include "ja_device.h"
 #include "ja_kernels.h"
 
@@ -49,30 +52,49 @@ __device__ __forceinline__ int64_t rope_position(const int32_t *off, int B, int6
     return row - off[lo];
 }
 
+// Nearest bf16 value (ties to even) of a double, as bf16 bits.  Normal range:
+// round the significand to 8 bits in place (add half a step minus one plus the
+// kept part's last bit, clear the 45 dropped bits; a carry moves the exponent),
+// after which the double is exactly a bf16 value and converts to float32 exactly
+// (past the largest bf16 value it becomes infinite).  Below 2^-126 bf16 steps
+// are a fixed 2^-133: round x * 2^133 to an integer instead.
+__device__ __forceinline__ uint32_t bf16_bits_nearest(double x) {
+    float f;
+    if (__builtin_fabs(x) >= 0x1p-126) {
+        uint64_t u = __builtin_bit_cast(uint64_t, x);
+        u += ((1ull << 44) - 1) + ((u >> 45) & 1ull);
+        u &= ~((1ull << 45) - 1);
+        f = (float)__builtin_bit_cast(double, u);
+    } else {
+        f = (float)(__builtin_rint(x * 0x1p133) * 0x1p-133);
+    }
+    return __builtin_bit_cast(uint32_t, f) >> 16;
+}
+
 template <typename T> struct RopeIO;
 template <> struct RopeIO<bf16> {
-    static __device__ __forceinline__ void load(const bf16 *p, float x[ROPE_PAIRS]) {
+    static __device__ __forceinline__ void load(const bf16 *p, double x[ROPE_PAIRS]) {
         const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
-        x[0] = __uint_as_float(w[0] << 16);
-        x[1] = __uint_as_float(w[0] & 0xffff0000u);
-        x[2] = __uint_as_float(w[1] << 16);
-        x[3] = __uint_as_float(w[1] & 0xffff0000u);
+        x[0] = (double)__uint_as_float(w[0] << 16);
+        x[1] = (double)__uint_as_float(w[0] & 0xffff0000u);
+        x[2] = (double)__uint_as_float(w[1] << 16);
+        x[3] = (double)__uint_as_float(w[1] & 0xffff0000u);
     }
-    static __device__ __forceinline__ void store(bf16 *p, const float x[ROPE_PAIRS]) {
+    static __device__ __forceinline__ void store(bf16 *p, const double x[ROPE_PAIRS]) {
         u32x2 w;
-        w[0] = pack2(x[0], x[1]);
-        w[1] = pack2(x[2], x[3]);
+        w[0] = bf16_bits_nearest(x[0]) | (bf16_bits_nearest(x[1]) << 16);
+        w[1] = bf16_bits_nearest(x[2]) | (bf16_bits_nearest(x[3]) << 16);
         *reinterpret_cast<u32x2 *>(p) = w;
     }
 };
 template <> struct RopeIO<float> {
-    static __device__ __forceinline__ void load(const float *p, float x[ROPE_PAIRS]) {
+    static __device__ __forceinline__ void load(const float *p, double x[ROPE_PAIRS]) {
         const f32x4 w = *reinterpret_cast<const f32x4 *>(p);
-        for (int e = 0; e < ROPE_PAIRS; ++e) x[e] = w[e];
+        for (int e = 0; e < ROPE_PAIRS; ++e) x[e] = (double)w[e];
     }
-    static __device__ __forceinline__ void store(float *p, const float x[ROPE_PAIRS]) {
+    static __device__ __forceinline__ void store(float *p, const double x[ROPE_PAIRS]) {
         f32x4 w;
-        for (int e = 0; e < ROPE_PAIRS; ++e) w[e] = x[e];
+        for (int e = 0; e < ROPE_PAIRS; ++e) w[e] = (float)x[e];
         *reinterpret_cast<f32x4 *>(p) = w;
     }
 };
@@ -91,7 +113,7 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_kernel(const RopeParams p) 
     const int d0 = (int)(it % CPR) * ROPE_PAIRS;
     const double t = (double)rope_position(s.off, s.B, row);
 
-    float c[ROPE_PAIRS], sn[ROPE_PAIRS];
+    double c[ROPE_PAIRS], sn[ROPE_PAIRS];
 #pragma unroll
     for (int e = 0; e < ROPE_PAIRS; ++e) {
         // angle t * base^(-2d/D) in fp64: positions reach the tens of thousands,
@@ -99,20 +121,19 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_kernel(const RopeParams p) 
         const double a = t * p.inv_freq[d0 + e];
         double sd, cd;
         sincos(a, &sd, &cd);
-        c[e] = (float)cd;
-        sn[e] = p.sign * (float)sd;  // sign -1: the inverse turn
+        c[e] = cd;
+        sn[e] = p.sign * sd;  // sign -1: the inverse turn
     }
     const T *src = static_cast<const T *>(s.src) + row * p.H * D;
     T *dst = static_cast<T *>(s.dst) + row * p.H * D;
     for (int h = 0; h < p.H; ++h) {
-        float x0[ROPE_PAIRS], x1[ROPE_PAIRS], y0[ROPE_PAIRS], y1[ROPE_PAIRS];
+        double x0[ROPE_PAIRS], x1[ROPE_PAIRS], y0[ROPE_PAIRS], y1[ROPE_PAIRS];
         RopeIO<T>::load(src + h * D + d0, x0);
         RopeIO<T>::load(src + h * D + HALF + d0, x1);
 #pragma unroll
         for (int e = 0; e < ROPE_PAIRS; ++e) {
-            const float p0 = x1[e] * sn[e], p1 = x1[e] * c[e];
-            y0[e] = __builtin_fmaf(x0[e], c[e], -p0);
-            y1[e] = __builtin_fmaf(x0[e], sn[e], p1);
+            y0[e] = x0[e] * c[e] - x1[e] * sn[e];
+            y1[e] = x0[e] * sn[e] + x1[e] * c[e];
         }
         RopeIO<T>::store(dst + h * D + d0, y0);
         RopeIO<T>::store(dst + h * D + HALF + d0, y1);

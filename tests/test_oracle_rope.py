@@ -16,10 +16,10 @@ checks below are fixed by that definition's consequences, not by re-typing it:
   * gradients: central differences of <O, dO>, and padded dense attention in
     complex form with torch autograd;
   * the turn alone keeps every pair's length; its bf16 variant (turned rows of
-    bf16 operands, rounded in float32 as the GPU rounds them) is the nearest-even
-    bf16 rounding of the exact turn wherever the float32 turn does not cross a
-    rounding boundary, and within one bf16 step of it everywhere; attention with
-    that variant equals plain attention of the rounded rows.
+    bf16 operands) is the nearest bf16 value of the exact turn, ties to even,
+    checked against that definition (within half a bf16 step, even on ties, on
+    constructed midpoints and subnormals); attention with that variant equals
+    plain attention of the rounded rows.
 """
 import math
 
@@ -214,25 +214,59 @@ def test_turn_keeps_pair_lengths_and_position_zero(D):
     assert not np.array_equal(y, x)
 
 
+def _bf16_step(x):
+    """The spacing of bf16 values at |x| (8 significant bits; below 2^-126 a fixed
+    2^-133)."""
+    e = np.frexp(np.abs(x))[1]  # 2^(e-1) <= |x| < 2^e
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
 def test_bf16_turn_is_the_rounded_exact_turn():
+    """Each element of the bf16 variant is the bf16 value nearest to the exact turn
+    (ties to even): a bf16 value, within half a bf16 step of the exact turn, and on
+    an exact tie the one with an even last significand bit."""
     w = _jagged(2, D=128)
     ex = ref.rope(w.k, w.kv_off, rope_base=BASE)
     rd = ref.rope(w.k, w.kv_off, rope_base=BASE, rope_bf16=True)
-    # the rounded rows are bf16 values
-    assert np.array_equal(rd, torch.from_numpy(rd).to(torch.bfloat16).double().numpy())
+    # bf16 values: float32 with the low 16 bits clear
+    bits = rd.astype(np.float32).view(np.uint32)
+    assert np.array_equal(rd.astype(np.float32).astype(np.float64), rd)
+    assert not (bits & 0xFFFF).any()
+    step = _bf16_step(ex)
+    err = np.abs(rd - ex)
+    assert (err <= 0.5 * step).all(), float((err / step).max())
+    tie = err == 0.5 * step
+    assert not ((bits[tie] >> 16) & 1).any()
+    # a nearest-value rounding, not a truncation: about half the elements rounded up
+    up = (np.abs(rd) > np.abs(ex)).mean()
+    assert 0.4 < up < 0.6, up
+    # torch's double -> bf16 cast rounds through float32 first, which moves a value by up
+    # to half a float32 step (2^-17 of a bf16 step); away from bf16 midpoints by more than
+    # that the two agree
+    mid = np.abs(err - 0.5 * step) <= 2.0 ** -16 * step
     rne = torch.from_numpy(ex).to(torch.bfloat16).double().numpy()
-    differ = rd != rne
-    # float32 error of the turn (a few units in 2^-24) can only flip the rounding of
-    # values lying that close to a bf16 midpoint
-    assert differ.mean() < 1e-4, differ.mean()
-    ulp = np.ldexp(1.0, np.frexp(np.abs(ex))[1] - 8)  # bf16 step at |ex|
-    # plus the float32 error of the turn itself (two roundings of terms up to the
-    # pair's larger element), which shows where the turn cancels to a tiny value
-    x = w.k.float().numpy().astype(np.float64)
-    h = x.shape[-1] // 2
-    m = np.maximum(np.abs(x[..., :h]), np.abs(x[..., h:]))
-    m = np.concatenate([m, m], axis=-1)
-    assert (np.abs(rd - ex) <= ulp + 2.0 ** -22 * m).all()
+    assert np.array_equal(rd[~mid], rne[~mid])
+
+
+def test_bf16_nearest_on_constructed_values():
+    """Rounding of float32 values placed on and beside bf16 midpoints and in the
+    subnormal range.  Position 0 turns by a zero angle, so one-row samples give the
+    bf16 variant of the rows themselves."""
+    odd = 1.0 + 2.0 ** -7  # a bf16 value whose last significand bit is odd
+    cases = [(1.0 + 2.0 ** -8, 1.0),                    # tie between 1 and odd: to the even 1
+             (odd + 2.0 ** -8, 1.0 + 2.0 ** -6),        # tie between odd and 1 + 2^-6: up, to even
+             (1.0 + 2.0 ** -8 + 2.0 ** -20, odd),       # just above the tie: up
+             (-(1.0 + 2.0 ** -8 - 2.0 ** -20), -1.0),   # just below the tie, negative: to -1
+             (3.0 * 2.0 ** -134, 2.0 ** -132),          # subnormal, 1.5 steps of 2^-133: tie, to even 2
+             (2.0 ** -135, 0.0)]                        # a quarter of the subnormal step: to 0
+    vals = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases])
+    assert np.array_equal(vals.astype(np.float32).astype(np.float64), vals)
+    x = torch.from_numpy(vals.astype(np.float32)).view(-1, 1, 1).repeat(1, 1, 2)
+    off = np.arange(x.shape[0] + 1, dtype=np.int32)  # one-row samples: position 0
+    rd = ref.rope(x, off, rope_base=BASE, rope_bf16=True)
+    assert np.array_equal(rd[:, 0, 0], want), rd[:, 0, 0]
+    assert np.array_equal(rd[:, 0, 1], want), rd[:, 0, 1]
 
 
 @pytest.mark.parametrize("mode", ["gdpa", "jfa"])

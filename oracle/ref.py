@@ -52,6 +52,9 @@ def _load():
         lib.ref_attn_dbias.argtypes = [P, P, P, P, P, P, P, I, I, I, D, I, I, D, I, P, I, I, I]
         lib.ref_gdpa_dbias_entry.argtypes = [P, P, P, P, P, P, P, I, I, I, D, I, I, I, D, I, P, I, I,
                                              I, I, I]
+        lib.ref_bwd_noise.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, I, I, I, D, I, I, I, D, I, P,
+                                      I, I, D, D, I]
+        lib.ref_bwd_noise.restype = ctypes.c_int
         lib.ref_act.argtypes = [I, P, P, P, ctypes.c_int64]
         lib.ref_rope.argtypes = [P, P, P, I, ctypes.c_int64, I, I, D]
         lib.ref_rope.restype = ctypes.c_int
@@ -187,6 +190,33 @@ def attn_bwd(q, k, v, dout, q_off, kv_off, *, scale, causal=False, window=0,
     """JFA backward of L = <O, dout>: returns (dQ, dK, dV) in float64."""
     return _bwd(_load().ref_attn_bwd, False, q, k, v, dout, q_off, kv_off, scale, None, causal, window,
                 rope_base, rope_bf16, bias_kind, bias_table, bias_lo, bias_hi, nthreads)
+
+
+def bwd_noise(mode, q, k, v, dout, q_off, kv_off, *, scale, act="silu", causal=False, window=0,
+              rope_base=0.0, rope_bf16=False, bias_kind="none", bias_table=None, bias_lo=0,
+              bias_hi=0, dx_unit=2.0 ** -8, delta_unit=2.0 ** -16, nthreads=0):
+    """Backward (mode 'gdpa' or 'jfa') plus the rounding-noise scale of every dQ row
+    (nq [total_q, H]) and dK row (nk [total_k, H]): dx_unit max_d sqrt(sum_j t_jd^2)
+    over the terms t_jd = scale dX_ij k_jd (dK: over i, with q_id) of the row's sum,
+    the error that sum carries when each dX is rounded to a unit roundoff of
+    dx_unit, plus (JFA) the error from delta formed with relative error
+    delta_unit.  Returns (dQ, dK, dV, nq, nk)."""
+    assert q_off is not None
+    a = _Args(q, k, v, q_off, kv_off, 0, bias_kind, bias_table, bias_lo, bias_hi)
+    do = _f32(dout)
+    assert do.shape == a.q.shape
+    dq = np.empty(a.q.shape, dtype=np.float64)
+    dk = np.empty(a.k.shape, dtype=np.float64)
+    dv = np.empty(a.v.shape, dtype=np.float64)
+    nq = np.empty(a.q.shape[:2], dtype=np.float64)
+    nk = np.empty(a.k.shape[:2], dtype=np.float64)
+    rc = _load().ref_bwd_noise(int(mode == "jfa"), _ptr(a.q), _ptr(a.k), _ptr(a.v), _ptr(do), _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(nq), _ptr(nk), _ptr(a.q_off), _ptr(a.kv_off),
+                               a.B, a.H, a.D, float(scale), ACTS[act or "silu"], int(causal), int(window),
+                               _rope_arg(rope_base, rope_bf16), a.bias_kind, _ptr(a.bias_table),
+                               a.bias_lo, a.bias_hi, float(dx_unit), float(delta_unit), int(nthreads))
+    assert rc == 0, rc
+    return dq, dk, dv, nq, nk
 
 
 def _dbias(fn, with_act, q, k, v, dout, q_off, kv_off, scale, act, causal, window, rope_base,

@@ -5,7 +5,7 @@ import numpy as np
 import torch
 
 import recsys_jagged_attention_gdpa_amd as ja
-from tests.helpers import (oracle_bwd, oracle_fwd, row_check, softmax_grad_floor,
+from tests.helpers import (oracle_bwd, oracle_fwd, row_check, softmax_cancel_rows,
                            structural_zero_rows)
 
 TAU = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
@@ -74,17 +74,21 @@ def np64(t):
 
 
 def check_lse(got_hq, want_th, what="lse", tol=1e-3):
-    """got [H, T] (GPU layout), want [T, H] (oracle layout)."""
+    """got [H, T] (GPU layout), want [T, H] (oracle layout): the same -inf pattern and
+    |dLSE| <= tol * max(1, |LSE|) elsewhere (relative for large scores: LSE is formed
+    in fp32, whose rounding grows with |LSE|)."""
     g = got_hq.T
     assert np.array_equal(np.isneginf(g), np.isneginf(want_th)), f"{what}: -inf pattern differs"
     fin = np.isfinite(want_th)
     if fin.any():
-        err = np.abs(g[fin] - want_th[fin]).max()
-        assert err <= tol, f"{what}: max |dLSE| {err:.3e} > {tol}"
+        err = np.abs(g[fin] - want_th[fin]) / np.maximum(1.0, np.abs(want_th[fin]))
+        assert err.max() <= tol, f"{what}: max |dLSE| / max(1, |LSE|) {err.max():.3e} > {tol}"
 
 
-def parity(w, *, backward=True, tau=None, label="", max_kv_len=0):
-    """Full-tensor parity of the HIP path against the oracle for workload w."""
+def parity(w, *, backward=True, tau=None, label="", max_kv_len=0, o_floor_frac=1e-6):
+    """Full-tensor parity of the HIP path against the oracle for workload w.  O rows
+    below o_floor_frac times the largest are compared against that floor (and
+    counted)."""
     tau = tau or TAU[w.dtype]
     announce(f"{label} mode={w.mode} B={w.B} H={w.H} D={w.D} dtype={w.dtype} causal={w.causal} "
              f"bias={w.bias_kind} act={w.act} window={w.window} rope={w.rope_base} Tq={w.total_q} "
@@ -96,14 +100,16 @@ def parity(w, *, backward=True, tau=None, label="", max_kv_len=0):
     torch.cuda.synchronize()
     want = oracle_fwd(w)
     zq_out, zq_in, zk = structural_zero_rows(w)
-    rep = {"o": row_check(np64(got["o"]), want["o"], tau, f"{label} O", zero_rows=zq_out)}
+    rep = {"o": row_check(np64(got["o"]), want["o"], tau, f"{label} O", zero_rows=zq_out,
+                          floor_frac=o_floor_frac)}
     if w.mode == "jfa":
         check_lse(np64(got["lse"]), want["lse"], f"{label} LSE")
     if backward and w.dout is not None and w.q_off is not None:
         g = gpu_bwd(w, d, got)
         torch.cuda.synchronize()
-        wb = oracle_bwd(w)
-        for n, z in (("dq", zq_in), ("dk", zk), ("dv", zk)):
-            rep[n] = row_check(np64(g[n]), wb[n], tau, f"{label} {n}", zero_rows=z,
-                               abs_floor=softmax_grad_floor(w, n))
+        wb = oracle_bwd(w, noise=True)
+        cq, ck = softmax_cancel_rows(w)
+        for n, z, nz, c in (("dq", zq_in, wb["nq"], cq), ("dk", zk, wb["nk"], ck), ("dv", zk, None, None)):
+            rep[n] = row_check(np64(g[n]), wb[n], tau, f"{label} {n}", zero_rows=z, noise=nz,
+                               cancel_rows=c)
     return rep

@@ -13,7 +13,7 @@ import torch
 
 from recsys_jagged_attention_gdpa_amd import synth
 from tests.gpu_helpers import TAU, announce, check_lse, gpu_bwd, gpu_fwd, np64, to_dev
-from tests.helpers import (oracle_bwd, oracle_fwd, row_check, softmax_grad_floor,
+from tests.helpers import (oracle_bwd, oracle_fwd, row_check, softmax_cancel_rows,
                            structural_zero_rows)
 
 pytestmark = pytest.mark.gpu
@@ -30,8 +30,8 @@ def _single_head(w, b, h):
 
 
 # (workload, random slices besides the longest sample)
-CASES = [("tiny_gdpa_fp32", 2), ("gdpa_xattn_short_kv", 3), ("jfa_causal_self", 1),
-         ("pma_gdpa_fwd", 3), ("longtail_gdpa", 1), ("jfa_swa_causal_self", 1),
+CASES = [("tiny_gdpa_fp32", 2), ("gdpa_xattn_short_kv", 3), ("jfa_causal_self", 3),
+         ("pma_gdpa_fwd", 3), ("longtail_gdpa", 2), ("jfa_swa_causal_self", 1),
          ("jfa_rope_causal_self", 1), ("pma_gdpa_fwd_mxfp8", 3), ("gdpa_xattn_short_kv_mxfp8", 3),
          ("jfa_causal_self_fwd_mxfp8", 1)]
 
@@ -57,7 +57,9 @@ def test_full_size_sampled_slices(name, n_random):
     rng = np.random.default_rng(77)
     lens = w.lq if w.q_off is not None else w.lk
     longest = int(np.argmax(lens * w.lk))
-    picks = [(longest, int(rng.integers(w.H)))]
+    # the longest sample on two heads, then seeded random (sample, head) slices
+    h0 = int(rng.integers(w.H))
+    picks = [(longest, h0)] + ([(longest, (h0 + 1 + int(rng.integers(w.H - 1))) % w.H)] if w.H > 1 else [])
     for b in rng.choice(w.B, size=min(n_random, w.B), replace=False):
         picks.append((int(b), int(rng.integers(w.H))))
     tau = TAU[w.dtype]
@@ -72,12 +74,14 @@ def test_full_size_sampled_slices(name, n_random):
         if w.mode == "jfa":
             check_lse(np64(out["lse"][h:h + 1, o0:o0 + n]), want["lse"], f"{name} b={b} h={h} LSE")
         if "dq" in out:
-            wb = oracle_bwd(ws)
+            wb = oracle_bwd(ws, noise=True)
+            cq, ck = softmax_cancel_rows(ws)
             k0, k1 = int(w.kv_off[b]), int(w.kv_off[b + 1])
-            for nm, z, rows in (("dq", zq_in, slice(o0, o0 + n)), ("dk", zk, slice(k0, k1)),
-                                ("dv", zk, slice(k0, k1))):
+            for nm, z, rows, nz, c in (("dq", zq_in, slice(o0, o0 + n), wb["nq"], cq),
+                                       ("dk", zk, slice(k0, k1), wb["nk"], ck),
+                                       ("dv", zk, slice(k0, k1), None, None)):
                 row_check(np64(out[nm][rows, h:h + 1]), wb[nm], tau, f"{name} b={b} h={h} {nm}",
-                          zero_rows=z, abs_floor=softmax_grad_floor(ws, nm))
+                          zero_rows=z, noise=nz, cancel_rows=c)
         announce(f"full-size {name}: slice b={b} (Lq={int(ws.lq[0])}, Lk={int(ws.lk[0])}) h={h} "
                  f"ok at {time.time() - t0:.1f}s")
 

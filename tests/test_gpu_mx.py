@@ -47,17 +47,25 @@ def test_mx_forward_shared_queries(mode, shared):
     parity(w, backward=False, label=f"mxfp8 shared-q={shared} {mode}")
 
 
-def test_mx_jfa_without_residual_and_wide_scales():
+@pytest.mark.parametrize("case", ["wide scores", "wide values"])
+def test_mx_jfa_without_residual_and_wide_scales(case):
     w = synth.custom(mode="jfa", lq=LQ, lk=LK, H=2, D=128, seed=9, with_dout=False, mx=MX)
-    # value scale codes spread over 2^-27 .. 2^+27 (every decoded value stays inside
-    # bf16's normal range); query / key codes over 2^-9 .. 2^0, so the scores, and
-    # with them the LSE bar, stay at ordinary magnitudes
     gen = torch.Generator().manual_seed(1)
     rnd = lambda lo, hi, sc: torch.randint(lo, hi, tuple(sc.shape), generator=gen, dtype=torch.int64).to(torch.uint8)
-    scales = {"q": rnd(118, 128, w.mx_scales["q"]), "k": rnd(118, 128, w.mx_scales["k"]),
-              "v": rnd(100, 155, w.mx_scales["v"])}
-    w = synth.Workload(**{**w.__dict__, "mx_scales": scales})
-    parity(w, backward=False, label="mxfp8 jfa wide scales")
+    if case == "wide scores":
+        # every scale code over 2^-20 .. 2^+13 and the score scale times 2^-8: scores,
+        # and with them the LSE, reach magnitudes of 10^4 (the LSE bar is relative)
+        scales = {n: rnd(107, 141, w.mx_scales[n]) for n in MX}
+        w = synth.Workload(**{**w.__dict__, "mx_scales": scales, "scale": w.scale * 2.0 ** -8})
+    else:
+        # value scale codes over 2^-27 .. 2^+27 (every decoded value stays inside bf16's
+        # normal range); query / key codes over 2^-9 .. 2^0
+        scales = {"q": rnd(118, 128, w.mx_scales["q"]), "k": rnd(118, 128, w.mx_scales["k"]),
+                  "v": rnd(100, 155, w.mx_scales["v"])}
+        w = synth.Workload(**{**w.__dict__, "mx_scales": scales})
+    # value scales spread the O rows over 2^33 in magnitude: compare every row on its own
+    # scale (each is a P-weighted average of its sample's values, no cancellation)
+    parity(w, backward=False, label=f"mxfp8 jfa {case}", o_floor_frac=1e-15)
     d = to_dev(w)
     a = gpu_fwd(w, d, residual=True)
     b = gpu_fwd(w, d, residual=False)

@@ -2,8 +2,9 @@
 """Throughput of the jagged attention hot path on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-planning, forward and backward (GDPA cross-attention with 32 keys per sample
-and jagged queries, B=1024, H=4, D=128, by default).  Inputs are resident in
+planning, forward and backward (by default JFA causal self-attention over a
+jagged batch, B=64, H=8, D=128, lengths uniform in 1..8192: the
+sparsity-0.5, MFMA-bound workload the metric names).  Inputs are resident in
 HBM before the timed region.  Prints ONE JSON line on stdout; details go to
 stderr.
 
@@ -12,8 +13,9 @@ stderr.
 Metric: useful (unpadded) TFLOP/s of forward + backward.  Useful work counts
 only valid (query, key) pairs P: forward 4 D P, backward 10 D P (five
 GEMM-sized products per pair).  The dominant kernel is also placed on its
-roofline (HBM bytes or MFMA FLOPs per launch / its average duration, timed with
-HIP events recorded by the library around that kernel's launches).
+roofline (HBM bytes or MFMA FLOPs per launch / its average duration).  Every
+kernel's duration comes from HIP events that the library records around its
+launches during the timed steps, on the stream it runs on.
 """
 from __future__ import annotations
 
@@ -223,20 +225,6 @@ class Runner:
                                      self.dq, self.dk, self.dv, self.db, self.ws_b)
 
 
-def kernel_durations(runner, ev, kernels, reps=3):
-    """Average duration (ms) of each kernel over `reps` steps (events from the library)."""
-    out = {}
-    for kname in kernels:
-        pairs = [(ev.create(), ev.create()) for _ in range(reps)]
-        for a, b in pairs:
-            _lib.ja_profile_kernel(kname, a, b)
-            runner.step()
-        _lib.ja_profile_kernel(kname, None, None)
-        torch.cuda.synchronize()
-        out[kname] = sum(ev.elapsed_ms(a, b) for a, b in pairs) / reps
-    return out
-
-
 # ------------------------------------------------------------------ traffic
 def sources_digest():
     h = hashlib.sha256()
@@ -359,7 +347,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gdpa_xattn_short_kv", choices=sorted(synth.CATALOGUE))
+    ap.add_argument("--workload", default="jfa_causal_self", choices=sorted(synth.CATALOGUE))
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -404,15 +392,6 @@ def main():
         runner.step()
     torch.cuda.synchronize()
 
-    # per-kernel durations (outside the timed region) to find the dominant kernel
-    durs = kernel_durations(runner, ev, runner.kernels())
-    dominant = max(durs, key=durs.get)
-    if args.roofline_kernel:
-        if args.roofline_kernel not in durs:
-            raise SystemExit(f"kernel {args.roofline_kernel} does not run in this workload")
-        dominant = args.roofline_kernel
-    log("[bench] kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in durs.items()))
-
     if args.calibrate_copy_mib:
         # one element-wise kernel that reads n bytes and writes n bytes
         n = args.calibrate_copy_mib * (1 << 20)
@@ -423,18 +402,29 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy kernel: read {n} bytes, wrote {n} bytes")
 
-    # timed region: exactly K steps, dominant kernel timed by events on its own stream
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    # timed region: exactly K steps; the library records an event pair around every
+    # kernel it launches, on the stream it launches it on
+    names = runner.kernels()
+    pairs = [{k: (ev.create(), ev.create()) for k in names} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for a, b in pairs:
-        _lib.ja_profile_kernel(dominant, a, b)
+    for step_pairs in pairs:
+        for k, (a, b) in step_pairs.items():
+            _lib.ja_profile_kernel(k, a, b)
         runner.step()
     torch.cuda.synchronize()
     t_end = time.perf_counter()
-    _lib.ja_profile_kernel(dominant, None, None)
-    dom_ms = sum(ev.elapsed_ms(a, b) for a, b in pairs) / args.steps
+    for k in names:
+        _lib.ja_profile_kernel(k, None, None)
+    durs = {k: sum(ev.elapsed_ms(*sp[k]) for sp in pairs) / args.steps for k in names}
     ev.close()
+    dominant = max(durs, key=durs.get)
+    if args.roofline_kernel:
+        if args.roofline_kernel not in durs:
+            raise SystemExit(f"kernel {args.roofline_kernel} does not run in this workload")
+        dominant = args.roofline_kernel
+    dom_ms = durs[dominant]
+    log("[bench] kernel ms (timed steps): " + ", ".join(f"{k}={v:.4f}" for k, v in durs.items()))
 
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
     P = valid_pairs(w) * w.H

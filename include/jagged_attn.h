@@ -72,7 +72,15 @@
  * Errors.  The return code is the only error channel.  Host-visible arguments
  * are checked before anything is launched; on any error nothing is launched
  * and no output is touched.  Offsets live in device memory and are not read by
- * the host: offsets that break the rules above give undefined results.
+ * the host: offsets that break the rules above (including a max_kv_len bound
+ * that some sample exceeds) give undefined results -- unless the environment
+ * variable JA_CHECK_OFFSETS is set to 1 when the call is made.  Then, before
+ * any other launch, a validation kernel checks them on the device and the call
+ * waits for its verdict (it synchronises `stream`, so this mode is for
+ * debugging, not for graph capture): invalid offsets return JA_ERR_BAD_OFFSETS
+ * with no attention kernel launched and no output touched.  Its flag lives in
+ * the workspace.  A window wider than every sample's aligned distances keeps
+ * every pair: values past total_q + total_k are treated as that width.
  *
  * Asynchrony.  Every entry point enqueues its kernels on `stream` (a
  * hipStream_t, NULL for the default stream) and returns without waiting.
@@ -96,6 +104,8 @@ typedef enum {
     JA_ERR_UNSUPPORTED = 3, /* dtype / head_dim / act / bias kind / shared-query backward, or a
                                [rows, H, D] tensor of 4 GiB or more (split such a batch) */
     JA_ERR_WORKSPACE = 4,   /* workspace NULL, misaligned or smaller than ja_workspace_size */
+    JA_ERR_BAD_OFFSETS = 5, /* offsets break the layout rules; reported only in the opt-in
+                               validation mode (environment JA_CHECK_OFFSETS=1, see Errors) */
     JA_ERR_HIP = 6          /* a HIP launch failed (the HIP error is in ja_last_hip_error) */
 } ja_status;
 
@@ -217,13 +227,15 @@ typedef enum {
     JA_KERNEL_FWD_SHORT = 6,  /* forward attention, samples with <= 32 keys */
     JA_KERNEL_BWD_DBIAS = 7,  /* bias-table gradient (both of its kernels) */
     JA_KERNEL_ROPE = 8,       /* rotary embedding of q and k (one launch) */
-    JA_KERNEL_ROPE_BACK = 9   /* backward: dq and dk turned back (one launch) */
+    JA_KERNEL_ROPE_BACK = 9,  /* backward: dq and dk turned back (one launch) */
+    JA_KERNEL_CHECK_OFFSETS = 10 /* offsets validation (JA_CHECK_OFFSETS=1 only) */
 } ja_kernel_id;
 
 /* From now on, in every call made by the calling thread, record start_event
  * immediately before and stop_event immediately after launching kernel
  * `kernel_id`, on the call's stream (both are hipEvent_t created by the
- * caller).  NULL events switch this off.  Thread-local; never synchronises. */
+ * caller).  Each kernel id has its own pair, so several kernels can be timed in
+ * one call; NULL events switch that id off.  Thread-local; never synchronises. */
 ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event);
 
 /* Human-readable name of a status code (static storage). */

@@ -19,17 +19,18 @@ LIB_PATH = os.path.join(_HERE, "libjagged_attn.so")
 
 JA_OK = 0
 STATUS = {0: "JA_OK", 1: "JA_ERR_NULL", 2: "JA_ERR_SHAPE", 3: "JA_ERR_UNSUPPORTED",
-          4: "JA_ERR_WORKSPACE", 6: "JA_ERR_HIP"}
+          4: "JA_ERR_WORKSPACE", 5: "JA_ERR_BAD_OFFSETS", 6: "JA_ERR_HIP"}
+STATUS_CODES = {v: k for k, v in STATUS.items()}
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 ACTS = {"silu": 0, "gelu_tanh": 1, "gelu_erf": 2}
 BIAS = {"none": 0, "rel": 1, "keypos": 2}
 PASS_FWD, PASS_BWD, PASS_BWD_DBIAS = 0, 1, 2
 
 EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_attn_fwd",
-           "jagged_attn_bwd", "jagged_gdpa_fwd_mx", "jagged_attn_fwd_mx", "ja_profile_kernel",
-           "ja_status_string", "ja_last_hip_error", "ja_version")
+           "jagged_attn_bwd", "jagged_gdpa_fwd_mx", "jagged_attn_fwd_mx",
+           "ja_profile_kernel", "ja_status_string", "ja_last_hip_error", "ja_version")
 KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5,
-           "fwd_short": 6, "bwd_dbias": 7, "rope": 8, "rope_back": 9}
+           "fwd_short": 6, "bwd_dbias": 7, "rope": 8, "rope_back": 9, "check_offsets": 10}
 
 
 class JaProblem(ctypes.Structure):
@@ -182,7 +183,7 @@ def jagged_attn_fwd_mx(problem, q, q_scale, k, k_scale, v, v_scale, o, lse, o_re
 
 def ja_profile_kernel(kernel, start_event, stop_event):
     """Record raw hipEvent_t handles around `kernel` ("fwd", "bwd_fused", ...) in later calls
-    on this thread; pass None, None to stop."""
+    on this thread (each kernel has its own pair); pass None, None to stop for that kernel."""
     kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     _check("ja_profile_kernel", load().ja_profile_kernel(kid, start_event, stop_event))
 

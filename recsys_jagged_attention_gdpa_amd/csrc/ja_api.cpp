@@ -8,6 +8,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 
 #include "ja_kernels.h"
 
@@ -48,6 +49,15 @@ struct Layout {
 };
 
 int64_t bias_width(const ja_problem &p) { return (int64_t)p.bias_hi - p.bias_lo + 1; }
+
+// The sliding window as the kernels take it: a window wider than any sample's
+// aligned distances (at most Lq + Lk <= total_q + total_k) keeps every pair, so
+// larger values are clamped to total_q + total_k + 1, which keeps the kernels'
+// 32-bit index sums (row + key count + window) in range.
+int eff_window(const ja_problem &p) {
+    const int64_t cap = p.total_q + p.total_k + 1;
+    return (int)((int64_t)p.window < cap ? p.window : cap);
+}
 
 Layout layout_of(const ja_problem &p, int pass) {
     Layout L{};
@@ -146,7 +156,7 @@ ja::AttnParams base_params(const ja_problem &p, const Layout &L, void *ws) {
     a.total_k = p.total_k;
     a.scale = p.scale;
     a.causal = p.causal;
-    a.window = p.window;
+    a.window = eff_window(p);
     a.bias_kind = p.bias_kind;
     a.bias_lo = p.bias_lo;
     a.bias_hi = p.bias_hi;
@@ -175,7 +185,7 @@ ja::PlanParams plan_of(const ja_problem &p, int kind, int tile_rows, int inner_r
     q.B = p.batch;
     q.H = p.heads;
     q.causal = p.causal;
-    q.window = p.window;
+    q.window = eff_window(p);
     q.kind = kind;
     q.tile_rows = tile_rows;
     q.inner_rows = inner_rows;
@@ -216,6 +226,27 @@ ja_status hip_status(hipError_t e) {
     return JA_ERR_HIP;
 }
 
+// Opt-in offsets validation (environment JA_CHECK_OFFSETS=1): a device kernel
+// checks the offsets and the call waits for its verdict before launching
+// anything else.  JA_ERR_BAD_OFFSETS when they break the layout rules.
+bool check_offsets_asked() {
+    const char *e = std::getenv("JA_CHECK_OFFSETS");
+    return e && e[0] == '1' && e[1] == '\0';
+}
+
+ja_status check_offsets(const ja_problem &p, const Layout &L, void *ws, hipStream_t s) {
+    if (!check_offsets_asked()) return JA_OK;
+    auto *ctr = reinterpret_cast<ja::PlanCounters *>(static_cast<char *>(ws) + L.counters);
+    ja::OffsetsCheck c{p.q_offsets, p.kv_offsets, p.batch, p.q_offsets ? p.total_q : 0, p.total_k,
+                       p.max_kv_len, &ctr->flag};
+    hipError_t e = ja::launch_check_offsets(c, s);
+    int bad = 1;
+    if (e == hipSuccess) e = hipMemcpyAsync(&bad, &ctr->flag, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e);
+    return bad ? JA_ERR_BAD_OFFSETS : JA_OK;
+}
+
 // MXFP8 scale codes of q, k, v (all NULL: bf16 / fp32 inputs).
 struct MXScales {
     const void *q, *k, *v;
@@ -236,6 +267,8 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
     if (st != JA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Layout L = layout_of(*p, JA_PASS_FWD);
+    st = check_offsets(*p, L, ws, s);
+    if (st != JA_OK) return st;
     ja::AttnParams a = base_params(*p, L, ws);
     a.q = q;
     a.k = k;
@@ -283,6 +316,8 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
     if (st != JA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Layout L = layout_of(*p, pass);
+    st = check_offsets(*p, L, ws, s);
+    if (st != JA_OK) return st;
     ja::AttnParams a = base_params(*p, L, ws);
     a.q = q;
     a.k = k;
@@ -329,11 +364,10 @@ const ja::KernelTimer &ja::kernel_timer() { return g_timer; }
 extern "C" {
 
 ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event) {
-    if (kernel_id < JA_KERNEL_PLAN || kernel_id > JA_KERNEL_ROPE_BACK) return JA_ERR_UNSUPPORTED;
+    if (kernel_id < JA_KERNEL_PLAN || kernel_id >= ja::K_COUNT) return JA_ERR_UNSUPPORTED;
     if ((start_event == nullptr) != (stop_event == nullptr)) return JA_ERR_NULL;
-    g_timer.which = start_event ? kernel_id : -1;
-    g_timer.start = static_cast<hipEvent_t>(start_event);
-    g_timer.stop = static_cast<hipEvent_t>(stop_event);
+    g_timer.start[kernel_id] = static_cast<hipEvent_t>(start_event);
+    g_timer.stop[kernel_id] = static_cast<hipEvent_t>(stop_event);
     return JA_OK;
 }
 
@@ -386,6 +420,7 @@ const char *ja_status_string(int status) {
     case JA_ERR_SHAPE: return "a size or range argument is out of range";
     case JA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, activation, bias kind or pass, or a tensor of 4 GiB or more";
     case JA_ERR_WORKSPACE: return "workspace NULL, not 256-byte aligned, or too small";
+    case JA_ERR_BAD_OFFSETS: return "offsets break the layout rules (found by the JA_CHECK_OFFSETS=1 validation)";
     case JA_ERR_HIP: return "a HIP launch failed";
     default: return "unknown status";
     }

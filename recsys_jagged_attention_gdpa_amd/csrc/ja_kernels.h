@@ -24,7 +24,8 @@ constexpr int XCDS = 8;
 struct PlanCounters {
     int units;   // number of work units (tiles x heads)
     int cursor;  // next unit to hand out (whole-sample lists)
-    int pad[30];
+    int flag;    // offsets validation verdict (first block only)
+    int pad[29];
     // Tile lists: the units are cut into XCDS contiguous slices, slice c
     // handed out by xcursor[c][0] (one 128-byte line per slice).
     int xcursor[XCDS][32];
@@ -127,19 +128,31 @@ struct PlanBatch {
 };
 hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream);
 
+// Opt-in validation of the offsets (device side): *flag = 1 when they break the
+// layout rules (see launch_check_offsets), else 0.
+struct OffsetsCheck {
+    const int32_t *q_off;  // NULL: shared query block, nothing to check
+    const int32_t *kv_off;
+    int B;
+    int64_t total_q, total_k;
+    int max_kv_len;        // 0: no bound
+    int *flag;
+};
+hipError_t launch_check_offsets(const OffsetsCheck &c, hipStream_t stream);
+
 // Optional per-kernel event recording around launches (measurement aid).
 enum KernelId {
     K_PLAN = 0, K_FWD = 1, K_BWD_FUSED = 2, K_BWD_KV = 3, K_BWD_Q = 4, K_BWD_DELTA = 5, K_FWD_SHORT = 6,
-    K_BWD_DBIAS = 7, K_ROPE = 8, K_ROPE_BACK = 9
+    K_BWD_DBIAS = 7, K_ROPE = 8, K_ROPE_BACK = 9, K_CHECK_OFFSETS = 10, K_COUNT = 11
 };
+// One (start, stop) event pair per kernel id; a null pair records nothing.
 struct KernelTimer {
-    int which = -1;
-    hipEvent_t start = nullptr, stop = nullptr;
+    hipEvent_t start[K_COUNT] = {}, stop[K_COUNT] = {};
     void begin(int id, hipStream_t s) const {
-        if (id == which && start) (void)hipEventRecord(start, s);
+        if (start[id]) (void)hipEventRecord(start[id], s);
     }
     void end(int id, hipStream_t s) const {
-        if (id == which && stop) (void)hipEventRecord(stop, s);
+        if (stop[id]) (void)hipEventRecord(stop[id], s);
     }
 };
 const KernelTimer &kernel_timer();

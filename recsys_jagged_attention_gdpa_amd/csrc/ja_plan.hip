@@ -19,8 +19,10 @@
 // atomic cursor, so every workgroup takes the most expensive unit left.
 //
 // One workgroup of 1024 threads; all state in LDS.  The list only orders the
-// work: every output tile is owned by exactly one unit, so results do not
-// depend on the order or on which workgroup runs a unit.
+// work: every output tile is owned by exactly one unit, so the attention
+// results do not depend on the order or on which workgroup runs a unit.  The
+// tile lists are nevertheless a pure function of the offsets (ties in cost keep
+// sample order), since the bias-table gradient's summation order follows them.
 #include "ja_device.h"
 #include "ja_kernels.h"
 
@@ -191,16 +193,47 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanBatch batc
     hist[2 * tid + 1] = excl + a;
     __syncthreads();
 
-    for (int b = tid; b < p.B; b += PLAN_THREADS) {
-        const PlanSample s = plan_sample(p, b);
-        if (grouped(p)) {
-            if (s.ntiles == 0) continue;
-            int pos = atomicAdd(&hist[sample_bucket_of(sample_cost(p, s))], s.ntiles);
-            for_each_tile_desc(p, s, [&](int t) {
-                if (pos < p.max_tiles) p.tiles[pos] = make_int2(b, t);
-                ++pos;
-            });
-        } else {
+    if (grouped(p)) {
+        // Stable placement: within a cost bucket, samples keep their index order,
+        // so the list is a function of the offsets alone.  Samples are taken in
+        // chunks of PLAN_THREADS (one per thread) and the chunk's waves in turn;
+        // inside a wave, lanes sharing a bucket get their positions from a prefix
+        // sum of their tile counts, one distinct bucket at a time.
+        for (int c0 = 0; c0 < p.B; c0 += PLAN_THREADS) {
+            const int b = c0 + tid;
+            const PlanSample s = b < p.B ? plan_sample(p, b) : PlanSample{0, 0, 0};
+            const int bk = s.ntiles > 0 ? sample_bucket_of(sample_cost(p, s)) : -1;
+            int pos = 0;
+            for (int w = 0; w < PLAN_THREADS / WAVE; ++w) {
+                if (wv == w) {
+                    uint64_t todo = __builtin_amdgcn_ballot_w64(bk >= 0);
+                    while (todo) {
+                        const int leader = __builtin_ctzll(todo);
+                        const int key = __shfl(bk, leader, WAVE);
+                        const bool mine = bk == key;
+                        int incl = mine ? s.ntiles : 0;
+                        for (int d = 1; d < WAVE; d <<= 1) {
+                            const int o = __shfl_up(incl, d, WAVE);
+                            if (lane >= d) incl += o;
+                        }
+                        const int base = hist[key];  // read by every lane before the update below
+                        if (mine) pos = base + incl - s.ntiles;
+                        const int total = __shfl(incl, WAVE - 1, WAVE);
+                        if (lane == leader) hist[key] = base + total;
+                        todo &= ~__builtin_amdgcn_ballot_w64(mine);
+                    }
+                }
+                __syncthreads();
+            }
+            if (bk >= 0)
+                for_each_tile_desc(p, s, [&](int t) {
+                    if (pos < p.max_tiles) p.tiles[pos] = make_int2(b, t);
+                    ++pos;
+                });
+        }
+    } else {
+        for (int b = tid; b < p.B; b += PLAN_THREADS) {
+            const PlanSample s = plan_sample(p, b);
             for_each_run(p, s, [&](int t0, int n, int step, int cost) {
                 const int pos = atomicAdd(&hist[bucket_of(cost)], n);
                 for (int k = 0; k < n; ++k)
@@ -214,6 +247,37 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanBatch batc
         p.counters->cursor = 0;
     }
     if (tid < XCDS) p.counters->xcursor[tid][0] = 0;
+}
+
+// Offsets validation (opt-in): q_offsets (when given) and kv_offsets must start
+// at 0, never decrease and end at the row counts; with a key-count bound every
+// sample's key count must respect it.  One workgroup; writes 1 to *flag when
+// anything is wrong, else 0.
+__global__ __launch_bounds__(PLAN_THREADS) void check_offsets_kernel(const OffsetsCheck c) {
+    __shared__ int bad;
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    int mine = 0;
+    if (threadIdx.x == 0) {
+        if (c.q_off && (c.q_off[0] != 0 || (int64_t)c.q_off[c.B] != c.total_q)) mine = 1;
+        if (c.kv_off[0] != 0 || (int64_t)c.kv_off[c.B] != c.total_k) mine = 1;
+    }
+    for (int b = threadIdx.x; b < c.B; b += PLAN_THREADS) {
+        const int lk = c.kv_off[b + 1] - c.kv_off[b];
+        if (lk < 0 || (c.max_kv_len > 0 && lk > c.max_kv_len)) mine = 1;
+        if (c.q_off && c.q_off[b + 1] < c.q_off[b]) mine = 1;
+    }
+    if (mine) bad = 1;  // any writer stores the same value
+    __syncthreads();
+    if (threadIdx.x == 0) *c.flag = bad;
+}
+
+hipError_t launch_check_offsets(const OffsetsCheck &c, hipStream_t stream) {
+    const KernelTimer &t = kernel_timer();
+    t.begin(K_CHECK_OFFSETS, stream);
+    hipLaunchKernelGGL(check_offsets_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, c);
+    t.end(K_CHECK_OFFSETS, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_plan(const PlanParams *lists, int n, hipStream_t stream) {

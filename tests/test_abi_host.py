@@ -30,8 +30,9 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert lib.ja_version() >= 100
-    for code in (0, 1, 2, 3, 4, 6):
+    for code in (0, 1, 2, 3, 4, 5, 6):
         assert lib.ja_status_string(code)
+        assert lib.ja_status_string(code) != lib.ja_status_string(99)
 
 
 def test_problem_struct_layout_matches_header(tmp_path):
@@ -175,3 +176,24 @@ def test_mxfp8_forward_arguments():
         assert fn(_problem(), None, P(2), P(3)) == 1                         # scale codes needed
         assert fn(_problem(), P(1), P(2), None) == 1
         assert fn(_problem(head_dim=48), P(1), P(2), P(3)) == 3
+
+
+def test_offsets_check_mode_keeps_host_errors_first(monkeypatch):
+    # The opt-in device validation (JA_CHECK_OFFSETS=1) runs only after every host-side
+    # check has passed: a bad host argument still returns its own code and launches nothing.
+    monkeypatch.setenv("JA_CHECK_OFFSETS", "1")
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    ws = ctypes.c_size_t(1 << 30)
+    p = _problem(head_dim=48)
+    assert lib.jagged_gdpa_fwd(ctypes.byref(p), P(0x10), P(0x20), P(0x30), P(0x40), P(0x100), ws, None) == 3
+    p = _problem()
+    assert lib.jagged_gdpa_fwd(ctypes.byref(p), None, P(0x20), P(0x30), P(0x40), P(0x100), ws, None) == 1
+    assert lib.jagged_gdpa_fwd(ctypes.byref(p), P(0x10), P(0x20), P(0x30), P(0x40), P(0x104), ws, None) == 4
+    assert "JA_CHECK_OFFSETS" in lib.ja_status_string(5).decode()
+
+
+def test_huge_window_is_accepted_as_unbounded():
+    # A window wider than every sample keeps every pair; INT_MAX is a valid way to say so.
+    for w in (1, 1 << 20, 2**31 - 1):
+        assert _lib.ja_workspace_size(_problem(window=w), _lib.PASS_BWD) > 0

@@ -115,3 +115,20 @@ def test_autograd_bias_gradient():
                             bias=table, bias_kind="keypos", bias_lo=0, bias_hi=90)
     o.backward(d["dout"])
     row_check(np64(table.grad), oracle_dbias(w), TAU[w.dtype], "autograd dbias")
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+def test_bias_gradient_bitwise_run_to_run_with_many_samples(mode):
+    # 320 samples, many sharing a cost (lengths from a small set): the planner must
+    # place equal-cost samples in a fixed order, since the table gradient's fp32
+    # summation order follows the unit list.  Several calls, bitwise equal.
+    rng = np.random.default_rng(21)
+    lens = rng.choice([17, 64, 100, 130, 257], size=320).tolist()
+    w = synth.custom(mode=mode, lq=lens, lk=lens, H=2, D=64, seed=8, act="gelu_erf", causal=mode == "jfa",
+                     bias_kind="rel", bias_lo=-128, bias_hi=128)
+    d = to_dev(w)
+    announce(f"dbias determinism {mode}: B={w.B} Tq={w.total_q}")
+    runs = [gpu_dbias(w, d)[3].clone() for _ in range(4)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        assert torch.equal(runs[0], r)

@@ -42,9 +42,6 @@ def oracle_fwd(w, nthreads=0):
 # bf16 residual; fp32 O for fp32 tensors).
 DX_UNIT = {torch.bfloat16: 2.0 ** -8, torch.float32: 2.0 ** -24}
 DELTA_UNIT = {torch.bfloat16: 2.0 ** -16, torch.float32: 2.0 ** -24}
-# delta formed in fp32 from an output that the reference uses as well (the bf16 O
-# without its residual): only the fp32 arithmetic differs
-DELTA_UNIT_SHARED_OUTPUT = 2.0 ** -24
 
 
 def oracle_bwd(w, nthreads=0, noise=False, delta_unit=None):

@@ -107,7 +107,7 @@ def test_jfa_backward_without_residual_is_exact_backward_of_bf16_output(causal):
     # caller passes.  The GPU must then match, row by row, the exact fp64 backward
     # in which only delta is formed from that same bf16 O.
     from tests.gpu_helpers import gpu_bwd, gpu_fwd, np64, to_dev
-    from tests.helpers import DELTA_UNIT_SHARED_OUTPUT, oracle_bwd, row_check, softmax_cancel_rows
+    from tests.helpers import row_check, softmax_cancel_rows, structural_zero_rows
     w = synth.custom(mode="jfa", lq=[300, 1, 77, 129], lk=[300, 1, 40, 200], H=2, D=128, seed=9,
                      causal=causal)
     d = to_dev(w)
@@ -116,6 +116,9 @@ def test_jfa_backward_without_residual_is_exact_backward_of_bf16_output(causal):
     g = gpu_bwd(w, d, f)
     o_gpu = f["o"].double().cpu()
     want = {n: np.zeros((t, w.H, w.D)) for n, t in (("dq", w.total_q), ("dk", w.total_k), ("dv", w.total_k))}
+    # rounding-noise scales of this interface's own terms (see ref.bwd_noise): bf16 dX
+    # operands, and delta formed in fp32 on the GPU from the bf16 O both sides use
+    noise = {"dq": np.zeros((w.total_q, w.H)), "dk": np.zeros((w.total_k, w.H))}
     for b in range(w.B):
         q0, q1 = int(w.q_off[b]), int(w.q_off[b + 1])
         k0, k1 = int(w.kv_off[b]), int(w.kv_off[b + 1])
@@ -136,12 +139,18 @@ def test_jfa_backward_without_residual_is_exact_backward_of_bf16_output(causal):
         want["dq"][q0:q1] = (w.scale * ds @ k).permute(1, 0, 2).numpy()
         want["dk"][k0:k1] = (w.scale * ds.transpose(-1, -2) @ q).permute(1, 0, 2).numpy()
         want["dv"][k0:k1] = (p.transpose(-1, -2) @ do).permute(1, 0, 2).numpy()
-    # rounding-noise floors of the rows (the same terms as the oracle's backward; delta
-    # comes from the same bf16 O on both sides)
-    nz = oracle_bwd(w, noise=True, delta_unit=DELTA_UNIT_SHARED_OUTPUT)
+        oabs = (do.abs() * o_gpu[q0:q1].permute(1, 0, 2).abs()).sum(-1, keepdim=True)  # [H, lq, 1]
+        u_dx, u_dl = 2.0 ** -8, 2.0 ** -22
+        nq = u_dx * w.scale * ((ds ** 2) @ (k ** 2)).sqrt().amax(-1) + \
+            u_dl * w.scale * oabs[..., 0] * (p @ k.abs()).amax(-1)
+        nk = u_dx * w.scale * ((ds ** 2).transpose(-1, -2) @ (q ** 2)).sqrt().amax(-1) + \
+            u_dl * w.scale * ((p * oabs).transpose(-1, -2) @ q.abs()).amax(-1)
+        noise["dq"][q0:q1] = nq.T.numpy()
+        noise["dk"][k0:k1] = nk.T.numpy()
     cq, ck = softmax_cancel_rows(w)
-    for n, noise, c in (("dq", nz["nq"], cq), ("dk", nz["nk"], ck), ("dv", None, None)):
-        row_check(np64(g[n]), want[n], 2e-2, f"no-residual {n}", noise=noise, cancel_rows=c)
+    _, zq, zk = structural_zero_rows(w)
+    for n, nz, c, z in (("dq", noise["dq"], cq, zq), ("dk", noise["dk"], ck, zk), ("dv", None, None, zk)):
+        row_check(np64(g[n]), want[n], 2e-2, f"no-residual {n}", noise=nz, cancel_rows=c, zero_rows=z)
 
 
 @pytest.mark.parametrize("mode", ["gdpa", "jfa"])

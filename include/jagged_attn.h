@@ -181,6 +181,23 @@ ja_status jagged_attn_fwd(const ja_problem *p, const void *q, const void *k, con
                           float *lse, void *o_residual, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* JFA forward that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics and outputs as
+ * jagged_attn_fwd without the workspace: its plan counters and unit lists live
+ * in a built-in device array of JA_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * held until the process ends (its address is looked up on the first call on
+ * each device).  A problem whose forward workspace (ja_workspace_size(p,
+ * JA_PASS_FWD)) exceeds it returns JA_ERR_WORKSPACE with nothing launched; with a
+ * rotary embedding the turned copies of q and k count towards it.  Every call on
+ * one GPU uses that GPU's array: calls that may overlap on one GPU (different
+ * streams, different host threads) race on it and must be ordered by the caller.
+ * The array needs no clearing: the planner kernel resets what the attention
+ * kernels count from. */
+#define JA_NOALLOC_SCRATCH_BYTES (4u << 20)
+ja_status jagged_attn_fwd_noalloc(const ja_problem *p, const void *q, const void *k, const void *v,
+                                  void *o, float *lse, void *o_residual, void *stream);
+
 /* MXFP8 forward (GDPA and JFA).  The pages report MXFP8-based attention, the
  * quantisation fused into the upstream projection and normalisation kernels
  * ("Meta redesigns AI training infrastructure...", sections "Custom Kernels

@@ -27,8 +27,9 @@ BIAS = {"none": 0, "rel": 1, "keypos": 2}
 PASS_FWD, PASS_BWD, PASS_BWD_DBIAS = 0, 1, 2
 
 EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_attn_fwd",
-           "jagged_attn_bwd", "jagged_gdpa_fwd_mx", "jagged_attn_fwd_mx",
+           "jagged_attn_bwd", "jagged_gdpa_fwd_mx", "jagged_attn_fwd_mx", "jagged_attn_fwd_noalloc",
            "ja_profile_kernel", "ja_status_string", "ja_last_hip_error", "ja_version")
+NOALLOC_SCRATCH_BYTES = 4 << 20  # JA_NOALLOC_SCRATCH_BYTES
 KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5,
            "fwd_short": 6, "bwd_dbias": 7, "rope": 8, "rope_back": 9, "check_offsets": 10}
 
@@ -77,8 +78,9 @@ def load(path: str = LIB_PATH):
         lib.jagged_attn_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.jagged_gdpa_fwd_mx.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.jagged_attn_fwd_mx.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.jagged_attn_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P]
         for f in (lib.jagged_gdpa_fwd, lib.jagged_attn_fwd, lib.jagged_gdpa_bwd, lib.jagged_attn_bwd,
-                  lib.jagged_gdpa_fwd_mx, lib.jagged_attn_fwd_mx):
+                  lib.jagged_gdpa_fwd_mx, lib.jagged_attn_fwd_mx, lib.jagged_attn_fwd_noalloc):
             f.restype = ctypes.c_int
         lib.ja_profile_kernel.argtypes = [ctypes.c_int, P, P]
         lib.ja_profile_kernel.restype = ctypes.c_int
@@ -146,6 +148,12 @@ def jagged_gdpa_fwd(problem, q, k, v, o, workspace, stream=None):
     _check("jagged_gdpa_fwd", load().jagged_gdpa_fwd(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(workspace),
         _nbytes(workspace), _stream(stream)))
+
+
+def jagged_attn_fwd_noalloc(problem, q, k, v, o, lse, o_residual, stream=None):
+    _check("jagged_attn_fwd_noalloc", load().jagged_attn_fwd_noalloc(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o_residual),
+        _stream(stream)))
 
 
 def jagged_attn_fwd(problem, q, k, v, o, lse, o_residual, workspace, stream=None):

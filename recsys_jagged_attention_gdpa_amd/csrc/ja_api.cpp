@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "ja_kernels.h"
 
@@ -357,6 +358,32 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
     return hip_status(e);
 }
 
+// Built-in scratch of the no-allocation forward (jagged_attn_fwd_noalloc): the
+// forward's workspace (plan counters and unit lists) lives in this device array,
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// its device address is looked up once per device and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[JA_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void *g_scratch[MAX_DEVICES];
+
+// Device address of this device's scratch (looked up on the first call on it).
+hipError_t scratch_ptr(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 const ja::KernelTimer &ja::kernel_timer() { return g_timer; }
@@ -392,6 +419,17 @@ ja_status jagged_gdpa_fwd_mx(const ja_problem *p, const void *q, const void *q_s
                              size_t workspace_bytes, void *stream) {
     const MXScales mx{q_scale, k_scale, v_scale};
     return run_fwd(p, 0, q, k, v, o, nullptr, nullptr, workspace, workspace_bytes, stream, &mx);
+}
+
+ja_status jagged_attn_fwd_noalloc(const ja_problem *p, const void *q, const void *k, const void *v, void *o,
+                                  float *lse, void *o_residual, void *stream) {
+    ja_status st = check_problem(p, JA_PASS_FWD);
+    if (st != JA_OK) return st;
+    if (layout_of(*p, JA_PASS_FWD).total > JA_NOALLOC_SCRATCH_BYTES) return JA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const hipError_t e = scratch_ptr(&ws);
+    if (e != hipSuccess) return hip_status(e);
+    return run_fwd(p, 1, q, k, v, o, lse, o_residual, ws, JA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 ja_status jagged_attn_fwd_mx(const ja_problem *p, const void *q, const void *q_scale, const void *k,

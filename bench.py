@@ -361,6 +361,9 @@ def main():
     ap.add_argument("--command", default="", help="the rocprofv3 command the csv files came from")
     ap.add_argument("--bias-grad", action="store_true",
                     help="also compute the bias table's gradient in every backward pass")
+    ap.add_argument("--balance", action="store_true",
+                    help="also report the persistent kernels' per-workgroup busy time (max / mean) "
+                         "in one extra step after the timed ones")
     ap.add_argument("--roofline-kernel", default=None, choices=sorted(KERNEL_SYMBOLS),
                     help="place this kernel on the roofline instead of the slowest one")
     args = ap.parse_args()
@@ -426,6 +429,27 @@ def main():
     dom_ms = durs[dominant]
     log("[bench] kernel ms (timed steps): " + ", ".join(f"{k}={v:.4f}" for k, v in durs.items()))
 
+    balance = None
+    if args.balance:
+        # one more step, outside the timed region, with every persistent kernel's
+        # workgroups stamping their busy cycles
+        persistent = [k for k in ("fwd", "fwd_short", "bwd_kv", "bwd_q", "bwd_fused") if k in names]
+        bufs = {k: torch.zeros(8192, dtype=torch.int64, device="cuda") for k in persistent}
+        for k in persistent:
+            _lib.ja_profile_busy(k, bufs[k])
+        runner.step()
+        torch.cuda.synchronize()
+        for k in persistent:
+            _lib.ja_profile_busy(k, None)
+        balance = {}
+        for k, b in bufs.items():
+            v = b[b > 0].double().cpu().numpy()
+            if v.size:
+                balance[k] = {"workgroups": int(v.size), "max_over_mean": round(float(v.max() / v.mean()), 4),
+                              "min_over_mean": round(float(v.min() / v.mean()), 4),
+                              "mean_cycles": round(float(v.mean()))}
+        log(f"[bench] balance: {balance}")
+
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
     P = valid_pairs(w) * w.H
     useful = (4.0 + (10.0 if runner.backward else 0.0)) * w.D * P
@@ -466,6 +490,8 @@ def main():
         "kernel_ms": {k: round(v, 5) for k, v in durs.items()},
         "cpu_baseline": cpu,
     }
+    if balance is not None:
+        line["balance"] = balance
     print(json.dumps(line), flush=True)
 
 

@@ -255,6 +255,20 @@ typedef enum {
  * one call; NULL events switch that id off.  Thread-local; never synchronises. */
 ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event);
 
+/* Measurement aid for the work scheduler: from now on, in every call made by the
+ * calling thread, each workgroup of kernel `kernel_id` (one of the persistent
+ * attention kernels: JA_KERNEL_FWD, _FWD_SHORT, _BWD_KV, _BWD_Q, _BWD_FUSED) writes
+ * the shader clock cycles from its start to its exit (after its last unit) into
+ * device_buffer[workgroup] (uint64, `capacity` entries; workgroups past it write
+ * nothing).  Busy time max / mean over the workgroups measures the load balance.
+ * The buffer stays owned by the caller and must stay valid while such calls run;
+ * the library never clears it (entries past the launch's grid keep their old
+ * contents).  Other kernel ids are accepted and record nothing.  NULL and 0
+ * switch it off.  Errors: JA_ERR_UNSUPPORTED for an unknown id, JA_ERR_SHAPE when
+ * only one of buffer and capacity is zero, or capacity < 0.  Thread-local; never
+ * synchronises. */
+ja_status ja_profile_busy(int kernel_id, void *device_buffer, int capacity);
+
 /* Human-readable name of a status code (static storage). */
 const char *ja_status_string(int status);
 

@@ -28,7 +28,7 @@ PASS_FWD, PASS_BWD, PASS_BWD_DBIAS = 0, 1, 2
 
 EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_attn_fwd",
            "jagged_attn_bwd", "jagged_gdpa_fwd_mx", "jagged_attn_fwd_mx", "jagged_attn_fwd_noalloc",
-           "ja_profile_kernel", "ja_status_string", "ja_last_hip_error", "ja_version")
+           "ja_profile_kernel", "ja_profile_busy", "ja_status_string", "ja_last_hip_error", "ja_version")
 NOALLOC_SCRATCH_BYTES = 4 << 20  # JA_NOALLOC_SCRATCH_BYTES
 KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5,
            "fwd_short": 6, "bwd_dbias": 7, "rope": 8, "rope_back": 9, "check_offsets": 10}
@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH):
             f.restype = ctypes.c_int
         lib.ja_profile_kernel.argtypes = [ctypes.c_int, P, P]
         lib.ja_profile_kernel.restype = ctypes.c_int
+        lib.ja_profile_busy.argtypes = [ctypes.c_int, P, ctypes.c_int]
+        lib.ja_profile_busy.restype = ctypes.c_int
         lib.ja_status_string.argtypes = [ctypes.c_int]
         lib.ja_status_string.restype = ctypes.c_char_p
         lib.ja_last_hip_error.argtypes = []
@@ -194,6 +196,14 @@ def ja_profile_kernel(kernel, start_event, stop_event):
     on this thread (each kernel has its own pair); pass None, None to stop for that kernel."""
     kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     _check("ja_profile_kernel", load().ja_profile_kernel(kid, start_event, stop_event))
+
+
+def ja_profile_busy(kernel, buffer):
+    """Have every workgroup of `kernel` write its busy cycles into the int64 device tensor
+    `buffer` (one entry per workgroup) in later calls on this thread; None to stop."""
+    kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    cap = 0 if buffer is None else buffer.numel()
+    _check("ja_profile_busy", load().ja_profile_busy(kid, _ptr(buffer), cap))
 
 
 def _nbytes(t):

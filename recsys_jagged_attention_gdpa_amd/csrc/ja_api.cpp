@@ -398,6 +398,14 @@ ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event) 
     return JA_OK;
 }
 
+ja_status ja_profile_busy(int kernel_id, void *device_buffer, int capacity) {
+    if (kernel_id < JA_KERNEL_PLAN || kernel_id >= ja::K_COUNT) return JA_ERR_UNSUPPORTED;
+    if ((device_buffer == nullptr) != (capacity == 0) || capacity < 0) return JA_ERR_SHAPE;
+    g_timer.busy[kernel_id] = static_cast<uint64_t *>(device_buffer);
+    g_timer.busy_cap[kernel_id] = capacity;
+    return JA_OK;
+}
+
 size_t ja_workspace_size(const ja_problem *p, int pass) {
     if (pass != JA_PASS_FWD && pass != JA_PASS_BWD && pass != JA_PASS_BWD_DBIAS) return 0;
     if (check_problem(p, pass) != JA_OK) return 0;

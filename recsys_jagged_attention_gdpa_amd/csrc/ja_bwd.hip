@@ -105,6 +105,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
     if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
+    const uint64_t busy_t0 = busy_start(p.busy);
     const int xcd = xcd_id();
     int slices_done = 0;
     for (;;) {
@@ -233,6 +234,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
         }
         store_row_acc<D>(dQs, irow, dqacc, p.scale, g);
     }
+    busy_end(p.busy, p.busy_cap, busy_t0);
 }
 
 // ----------------------------------------------------------- dK/dV units
@@ -259,6 +261,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
     if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
+    const uint64_t busy_t0 = busy_start(p.busy);
     const int xcd = xcd_id();
     int slices_done = 0;
     for (;;) {
@@ -437,6 +440,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
         store_row_acc<D>(dKs, jkey, dkacc, p.scale, g);
         store_row_acc<D>(dVs, jkey, dvacc, 1.0f, g);
     }
+    busy_end(p.busy, p.busy_cap, busy_t0);
 }
 
 // ------------------------------------------------- fused short-K/V units
@@ -470,6 +474,7 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
     if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
 
+    const uint64_t busy_t0 = busy_start(p.busy);
     for (;;) {
         int w = 0;
         if (lane == 0) w = atomicAdd(&p.counters3->cursor, 1);
@@ -593,6 +598,7 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
         store_tile<D>(dKs, Qt, 0, dkacc, p.scale, lane);
         store_tile<D>(dVs, Gt, 0, dvacc, 1.0f, lane);
     }
+    busy_end(p.busy, p.busy_cap, busy_t0);
 }
 
 // -------------------------------------------------------------- launches
@@ -606,14 +612,14 @@ static hipError_t launch_bwd_t(const AttnParams &p, int grid, bool long_units, h
         t.end(K_BWD_DELTA, st);
     }
     t.begin(K_BWD_FUSED, st);
-    hipLaunchKernelGGL((fused_kernel<D, MODE, ACT>), dim3(2 * grid), dim3(WAVE), 0, st, p);
+    hipLaunchKernelGGL((fused_kernel<D, MODE, ACT>), dim3(2 * grid), dim3(WAVE), 0, st, t.with_busy(p, K_BWD_FUSED));
     t.end(K_BWD_FUSED, st);
     if (!long_units) return hipGetLastError();
     t.begin(K_BWD_KV, st);
-    hipLaunchKernelGGL((dkdv_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, t.with_busy(p, K_BWD_KV));
     t.end(K_BWD_KV, st);
     t.begin(K_BWD_Q, st);
-    hipLaunchKernelGGL((dq_kernel<D, MODE, ACT>), dim3(grid), dim3(BWD_THREADS), 0, st, p);
+    hipLaunchKernelGGL((dq_kernel<D, MODE, ACT>), dim3(grid), dim3(BWD_THREADS), 0, st, t.with_busy(p, K_BWD_Q));
     t.end(K_BWD_Q, st);
     return hipGetLastError();
 }

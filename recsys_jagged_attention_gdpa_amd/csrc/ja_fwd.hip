@@ -78,6 +78,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
     const float sl2 = p.scale * LOG2E;
 
+    const uint64_t busy_t0 = busy_start(p.busy);
     const int xcd = xcd_id();
     int slices_done = 0;
     for (;;) {
@@ -318,6 +319,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             store_row_acc<D>(Os, irow, oacc, norm, g);
         }
     }
+    busy_end(p.busy, p.busy_cap, busy_t0);
 }
 
 // ------------------------------------------------------------------------
@@ -354,6 +356,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
     const float sl2 = p.scale * LOG2E;
 
+    const uint64_t busy_t0 = busy_start(p.busy);
     for (;;) {
         if (threadIdx.x == 0) {
             s_unit = atomicAdd(&p.counters2->cursor, 1);
@@ -519,20 +522,24 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
         }
         __syncthreads();  // K / V of this unit are no longer read
     }
+    busy_end(p.busy, p.busy_cap, busy_t0);
 }
 
 template <int D, int MODE, int ACT, bool SPLIT, bool MX>
 static hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, bool long_units, hipStream_t stream) {
     const KernelTimer &t = kernel_timer();
     t.begin(K_FWD_SHORT, stream);
-    hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT, SPLIT, MX>), dim3(2 * cus), dim3(FWD_THREADS), 0, stream, p);
+    hipLaunchKernelGGL((fwd_short_kernel<D, MODE, ACT, SPLIT, MX>), dim3(2 * cus), dim3(FWD_THREADS), 0, stream,
+                       t.with_busy(p, K_FWD_SHORT));
     t.end(K_FWD_SHORT, stream);
     if (!long_units) return hipGetLastError();
     t.begin(K_FWD, stream);
     if (few_q)  // every unit is one block of <= 32 shared query rows
-        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, 32, SPLIT, MX>), dim3(8 * cus), dim3(WAVE), 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, 32, SPLIT, MX>), dim3(8 * cus), dim3(WAVE), 0, stream,
+                           t.with_busy(p, K_FWD));
     else
-        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE, SPLIT, MX>), dim3(2 * cus), dim3(4 * WAVE), 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE, SPLIT, MX>), dim3(2 * cus), dim3(4 * WAVE), 0, stream,
+                           t.with_busy(p, K_FWD));
     t.end(K_FWD, stream);
     return hipGetLastError();
 }

@@ -87,6 +87,10 @@ struct AttnParams {
     // [T, H, D / 32] (all NULL for bf16 / fp32 inputs)
     const uint8_t *q_sc, *k_sc, *v_sc;
     int mx;  // 1: q, k, v are MXFP8 (forward only)
+    // Measurement aid: when non-NULL, each workgroup of the launch writes the shader
+    // clock cycles from its start to its exit into busy[blockIdx.x] (busy_cap entries)
+    uint64_t *busy;
+    int busy_cap;
 };
 
 // Units of the tile lists (PLAN_Q_TILES, PLAN_KV_TILES) are numbered
@@ -100,6 +104,15 @@ struct UnitRef {
 __device__ __forceinline__ UnitRef tile_unit(const int2 *tiles, int w, int n_units, int H) {
     const int n = n_units / H;
     return UnitRef{tiles[w % n], w / n};
+}
+
+// Busy-time stamps (measurement aid, AttnParams::busy): the shader clock at the
+// workgroup's start, and at its exit the elapsed cycles written by one thread.
+__device__ __forceinline__ uint64_t busy_start(const uint64_t *busy) {
+    return busy ? __builtin_amdgcn_s_memtime() : 0;
+}
+__device__ __forceinline__ void busy_end(uint64_t *busy, int cap, uint64_t t0) {
+    if (busy && threadIdx.x == 0 && (int)blockIdx.x < cap) busy[blockIdx.x] = __builtin_amdgcn_s_memtime() - t0;
 }
 
 // The XCD this workgroup runs on (hardware register XCC_ID).
@@ -146,8 +159,18 @@ enum KernelId {
     K_BWD_DBIAS = 7, K_ROPE = 8, K_ROPE_BACK = 9, K_CHECK_OFFSETS = 10, K_COUNT = 11
 };
 // One (start, stop) event pair per kernel id; a null pair records nothing.
+// busy[id] (with its capacity) receives per-workgroup busy cycles of that kernel.
 struct KernelTimer {
     hipEvent_t start[K_COUNT] = {}, stop[K_COUNT] = {};
+    uint64_t *busy[K_COUNT] = {};
+    int busy_cap[K_COUNT] = {};
+    // the launch parameters of kernel `id`: p with that kernel's busy-time buffer
+    AttnParams with_busy(const AttnParams &p, int id) const {
+        AttnParams q = p;
+        q.busy = busy[id];
+        q.busy_cap = busy_cap[id];
+        return q;
+    }
     void begin(int id, hipStream_t s) const {
         if (start[id]) (void)hipEventRecord(start[id], s);
     }

@@ -197,3 +197,16 @@ def test_huge_window_is_accepted_as_unbounded():
     # A window wider than every sample keeps every pair; INT_MAX is a valid way to say so.
     for w in (1, 1 << 20, 2**31 - 1):
         assert _lib.ja_workspace_size(_problem(window=w), _lib.PASS_BWD) > 0
+
+
+def test_profile_busy_arguments():
+    # Only sets thread-local pointers: nothing is launched or dereferenced.
+    lib = _lib.load()
+    lib.ja_profile_busy.restype = ctypes.c_int
+    lib.ja_profile_busy.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+    assert lib.ja_profile_busy(99, None, 0) == _lib.STATUS_CODES["JA_ERR_UNSUPPORTED"]
+    assert lib.ja_profile_busy(-1, None, 0) == _lib.STATUS_CODES["JA_ERR_UNSUPPORTED"]
+    assert lib.ja_profile_busy(1, None, 8) == _lib.STATUS_CODES["JA_ERR_SHAPE"]
+    assert lib.ja_profile_busy(1, 0x1000, 0) == _lib.STATUS_CODES["JA_ERR_SHAPE"]
+    assert lib.ja_profile_busy(1, 0x1000, -4) == _lib.STATUS_CODES["JA_ERR_SHAPE"]
+    assert lib.ja_profile_busy(1, None, 0) == 0

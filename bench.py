@@ -114,8 +114,10 @@ def kernel_cost(w, kernel: str) -> tuple[float, float]:
         return e * HD * 2 * tq + 4 * w.H * tq, 2.0 * HD * tq
     if kernel == "bwd_dbias":  # read Q, dO, K, V; recompute S and dP (two GEMMs per pair)
         return e * HD * (2 * tq + 2 * tk), 4.0 * w.D * P
-    if kernel in ("rope", "rope_back"):  # read and write every row of q and k (dq and dk)
+    if kernel == "rope":  # read and write every row of q and k
         return e * HD * 2 * (w.q.shape[0] + w.total_k), 0.0
+    if kernel == "rope_back":  # bf16: read and write every row of dk; fp32: of dq and dk
+        return e * HD * 2 * (w.total_k + (w.q.shape[0] if w.dtype == torch.float32 else 0)), 0.0
     return 0.0, 0.0
 
 
@@ -168,7 +170,12 @@ class Runner:
             total_k=w.total_k, q_offsets=self.q_off, kv_offsets=self.kv_off,
             lq_fixed=w.lq_fixed, causal=w.causal, scale=w.scale, act=w.act,
             bias_kind=w.bias_kind, bias_table=self.bias, bias_lo=w.bias_lo, bias_hi=w.bias_hi,
-            max_kv_len=self.max_kv_len, window=w.window, rope_base=w.rope_base)
+            max_kv_len=self.max_kv_len, window=w.window, rope_base=w.rope_base,
+            rope_inputs_turned=w.rope_base > 0)
+        # rotary embedding: q and k turned once per step (the rope call), the turned
+        # rows serving the forward and the backward
+        self.qt = torch.empty_like(self.q) if w.rope_base > 0 else self.q
+        self.kt = torch.empty_like(self.k) if w.rope_base > 0 else self.k
         rows = w.total_q_out
         self.o = torch.empty((rows, w.H, w.D), dtype=torch.bfloat16 if w.mx else w.dtype, device=dev)
         self.lse = torch.empty((w.H, rows), dtype=torch.float32, device=dev)
@@ -188,6 +195,7 @@ class Runner:
 
     def kernels(self):
         rope = ["rope"] if self.w.rope_base else []
+        # the turn back of dk (fp32: dq and dk); the bf16 dQ units turn dq back themselves
         rope_back = ["rope_back"] if (self.w.rope_base and self.backward) else []
         if self.w.dtype == torch.float32:  # plain fp32 kernels: no planner, no short / fused units
             ks = rope + ["fwd"]
@@ -205,6 +213,9 @@ class Runner:
 
     def step(self):
         p, w = self.prob, self.w
+        if w.rope_base > 0:
+            _lib.jagged_rope(p, self.q, self.k, self.qt, self.kt)
+        q, k = self.qt, self.kt
         if w.mx:  # MXFP8 forward (no backward)
             sc = self.sc
             if w.mode == "gdpa":
@@ -214,14 +225,13 @@ class Runner:
                                         self.o_res, self.ws_f)
             return
         if w.mode == "gdpa":
-            _lib.jagged_gdpa_fwd(p, self.q, self.k, self.v, self.o, self.ws_f)
+            _lib.jagged_gdpa_fwd(p, q, k, self.v, self.o, self.ws_f)
             if self.backward:
-                _lib.jagged_gdpa_bwd(p, self.q, self.k, self.v, self.dout, self.dq, self.dk, self.dv, self.db,
-                                     self.ws_b)
+                _lib.jagged_gdpa_bwd(p, q, k, self.v, self.dout, self.dq, self.dk, self.dv, self.db, self.ws_b)
         else:
-            _lib.jagged_attn_fwd(p, self.q, self.k, self.v, self.o, self.lse, self.o_res, self.ws_f)
+            _lib.jagged_attn_fwd(p, q, k, self.v, self.o, self.lse, self.o_res, self.ws_f)
             if self.backward:
-                _lib.jagged_attn_bwd(p, self.q, self.k, self.v, self.o, self.o_res, self.dout, self.lse,
+                _lib.jagged_attn_bwd(p, q, k, self.v, self.o, self.o_res, self.dout, self.lse,
                                      self.dq, self.dk, self.dv, self.db, self.ws_b)
 
 

@@ -48,9 +48,14 @@
  * (RoFormer's rotation in split-half form; values are not turned).  The pages
  * name a rotary embedding fused into their block-attention kernel ("Meta
  * redesigns AI training infrastructure...", section "Custom Kernels and 5D
- * Parallelism for Trillion-Parameter Scale") without defining it.  The turned
- * rows live in the workspace; the backward entry points return gradients with
- * respect to the rows as given.
+ * Parallelism for Trillion-Parameter Scale") without defining it.  Each turned
+ * element is the nearest bf16 (fp32 tensors: float32) value to the turn worked
+ * in fp64.  Either the call turns q and k into workspace copies, or the caller
+ * turns them once with jagged_rope and passes the turned rows to both passes
+ * (rope_inputs_turned = 1).  The backward entry points return gradients with
+ * respect to the rows before the turn: the bf16 backward units turn their dq
+ * rows back in registers before storing them, and a streaming pass turns dk
+ * back (fp32: dq and dk).
  *
  * Bias.  An fp32 table [H][bias_hi - bias_lo + 1] on the device, added after
  * the scale, before the activation / softmax:
@@ -144,11 +149,18 @@ typedef struct ja_problem {
     int32_t window;              /* sliding window w (0 = none, negative: JA_ERR_SHAPE) */
     float rope_base;             /* rotary embedding base (commonly 10000), 0 = none; negative,
                                     infinite or NaN: JA_ERR_SHAPE */
+    int32_t rope_inputs_turned;  /* with rope_base > 0: 1 = q and k are passed already turned
+                                    (jagged_rope's output for this problem), so the call turns
+                                    nothing on the way in and its workspace holds no turned
+                                    copies; a backward still returns dq and dk for the rows
+                                    before the turn.  0 = q and k as they are.  Else
+                                    JA_ERR_SHAPE. */
 } ja_problem;
 
 /* Workspace bytes that the given pass of either attention form needs (0 only
  * for invalid problems).  Depends on B, H, D, total_q, total_k, lq_fixed,
- * dtype and whether rope_base > 0 (the turned copies of q and k), and for
+ * dtype and whether the call turns q and k itself (rope_base > 0 and
+ * rope_inputs_turned 0: room for the turned copies), and for
  * JA_PASS_BWD_DBIAS also on the bias range; the same value serves GDPA and
  * JFA. */
 size_t ja_workspace_size(const ja_problem *p, int pass);
@@ -197,6 +209,18 @@ ja_status jagged_attn_fwd(const ja_problem *p, const void *q, const void *k, con
 #define JA_NOALLOC_SCRATCH_BYTES (4u << 20)
 ja_status jagged_attn_fwd_noalloc(const ja_problem *p, const void *q, const void *k, const void *v,
                                   void *o, float *lse, void *o_residual, void *stream);
+
+/* Rotary embedding on its own: q_turned [Tq, H, D] (or [lq_fixed, H, D]) and
+ * k_turned [Tk, H, D] receive q and k turned as described under "Rotary
+ * embedding" (positions from the problem's offsets), in p->dtype.  The outputs
+ * may be the inputs themselves (turned in place).  Feed them to the attention
+ * calls with rope_inputs_turned = 1: one turn serves a forward and its
+ * backward.  Needs rope_base > 0 (else JA_ERR_SHAPE); otherwise the same
+ * problem checks as a forward.  No workspace; offsets are not validated here
+ * (JA_CHECK_OFFSETS applies to the attention calls).  Asynchronous on the
+ * stream. */
+ja_status jagged_rope(const ja_problem *p, const void *q, const void *k, void *q_turned, void *k_turned,
+                      void *stream);
 
 /* MXFP8 forward (GDPA and JFA).  The pages report MXFP8-based attention, the
  * quantisation fused into the upstream projection and normalisation kernels

@@ -274,7 +274,7 @@ def gdpa_dbias_entry(q, k, v, dout, q_off, kv_off, *, scale, act, causal=False, 
 def rope(x, off, *, rope_base, rope_bf16=False):
     """The rotary turn of a [rows, H, D] tensor by sample-local positions (off: int32
     [B+1], or None for one block whose row r sits at position r), in float64; with
-    rope_bf16 the float32 turn rounded to bf16."""
+    rope_bf16 each turned element rounded to the nearest bf16 value (ties to even)."""
     x = _f32(x)
     o = _i32(off)
     y = np.empty(x.shape, dtype=np.float64)

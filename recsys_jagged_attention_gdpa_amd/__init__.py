@@ -9,6 +9,6 @@ itself.
 from . import _lib  # noqa: F401
 from ._lib import (JaError, JaProblem, ja_workspace_size, jagged_attn_bwd,  # noqa: F401
                    jagged_attn_fwd, jagged_attn_fwd_mx, jagged_gdpa_bwd, jagged_gdpa_fwd,
-                   jagged_gdpa_fwd_mx, make_problem)
+                   jagged_gdpa_fwd_mx, jagged_rope, make_problem)
 from .ops import (attn_backward, attn_forward, gdpa, gdpa_backward, gdpa_forward,  # noqa: F401
-                  jagged_attention, mx_forward)
+                  jagged_attention, mx_forward, rope)

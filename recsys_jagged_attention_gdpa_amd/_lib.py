@@ -28,7 +28,7 @@ PASS_FWD, PASS_BWD, PASS_BWD_DBIAS = 0, 1, 2
 
 EXPORTS = ("ja_workspace_size", "jagged_gdpa_fwd", "jagged_gdpa_bwd", "jagged_attn_fwd",
            "jagged_attn_bwd", "jagged_gdpa_fwd_mx", "jagged_attn_fwd_mx", "jagged_attn_fwd_noalloc",
-           "ja_profile_kernel", "ja_profile_busy", "ja_status_string", "ja_last_hip_error", "ja_version")
+           "jagged_rope", "ja_profile_kernel", "ja_profile_busy", "ja_status_string", "ja_last_hip_error", "ja_version")
 NOALLOC_SCRATCH_BYTES = 4 << 20  # JA_NOALLOC_SCRATCH_BYTES
 KERNELS = {"plan": 0, "fwd": 1, "bwd_fused": 2, "bwd_kv": 3, "bwd_q": 4, "bwd_delta": 5,
            "fwd_short": 6, "bwd_dbias": 7, "rope": 8, "rope_back": 9, "check_offsets": 10}
@@ -42,7 +42,7 @@ class JaProblem(ctypes.Structure):
         ("kv_offsets", ctypes.c_void_p), ("scale", ctypes.c_float), ("act", ctypes.c_int32),
         ("bias_kind", ctypes.c_int32), ("bias_lo", ctypes.c_int32), ("bias_hi", ctypes.c_int32),
         ("bias_table", ctypes.c_void_p), ("max_kv_len", ctypes.c_int32), ("window", ctypes.c_int32),
-        ("rope_base", ctypes.c_float),
+        ("rope_base", ctypes.c_float), ("rope_inputs_turned", ctypes.c_int32),
     ]
 
 
@@ -79,8 +79,10 @@ def load(path: str = LIB_PATH):
         lib.jagged_gdpa_fwd_mx.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.jagged_attn_fwd_mx.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.jagged_attn_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P]
+        lib.jagged_rope.argtypes = [PP, P, P, P, P, P]
         for f in (lib.jagged_gdpa_fwd, lib.jagged_attn_fwd, lib.jagged_gdpa_bwd, lib.jagged_attn_bwd,
-                  lib.jagged_gdpa_fwd_mx, lib.jagged_attn_fwd_mx, lib.jagged_attn_fwd_noalloc):
+                  lib.jagged_gdpa_fwd_mx, lib.jagged_attn_fwd_mx, lib.jagged_attn_fwd_noalloc,
+                  lib.jagged_rope):
             f.restype = ctypes.c_int
         lib.ja_profile_kernel.argtypes = [ctypes.c_int, P, P]
         lib.ja_profile_kernel.restype = ctypes.c_int
@@ -115,7 +117,7 @@ def _stream(stream):
 def make_problem(*, batch, heads, head_dim, dtype, total_q, total_k, q_offsets, kv_offsets,
                  lq_fixed=0, causal=False, scale=None, act="silu", bias_kind="none",
                  bias_table=None, bias_lo=0, bias_hi=0, max_kv_len=0, window=0,
-                 rope_base=0.0) -> JaProblem:
+                 rope_base=0.0, rope_inputs_turned=False) -> JaProblem:
     """Fill a JaProblem.  Offsets and the bias table are device tensors (or raw pointers)."""
     p = JaProblem()
     p.batch, p.heads, p.head_dim = int(batch), int(heads), int(head_dim)
@@ -133,6 +135,7 @@ def make_problem(*, batch, heads, head_dim, dtype, total_q, total_k, q_offsets, 
     p.max_kv_len = int(max_kv_len)
     p.window = int(window)
     p.rope_base = float(rope_base)
+    p.rope_inputs_turned = int(bool(rope_inputs_turned))
     return p
 
 
@@ -156,6 +159,11 @@ def jagged_attn_fwd_noalloc(problem, q, k, v, o, lse, o_residual, stream=None):
     _check("jagged_attn_fwd_noalloc", load().jagged_attn_fwd_noalloc(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o_residual),
         _stream(stream)))
+
+
+def jagged_rope(problem, q, k, q_turned, k_turned, stream=None):
+    _check("jagged_rope", load().jagged_rope(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(q_turned), _ptr(k_turned), _stream(stream)))
 
 
 def jagged_attn_fwd(problem, q, k, v, o, lse, o_residual, workspace, stream=None):

@@ -85,7 +85,7 @@ Layout layout_of(const ja_problem &p, int pass) {
         L.dbias_part = off;
         off += align_up((size_t)ja::DBIAS_GRID * p.heads * (size_t)bias_width(p) * sizeof(float));
     }
-    if (p.rope_base > 0.0f) {  // turned copies of q and k
+    if (p.rope_base > 0.0f && !p.rope_inputs_turned) {  // turned copies of q and k
         const size_t row = (size_t)p.heads * p.head_dim * (p.dtype == JA_BF16 ? 2 : 4);
         L.rope_q = off;
         off += align_up((size_t)(p.total_q > 0 ? p.total_q : 1) * row);
@@ -123,6 +123,7 @@ ja_status check_problem(const ja_problem *p, int pass) {
     if (p->max_kv_len < 0) return JA_ERR_SHAPE;
     if (p->window < 0) return JA_ERR_SHAPE;
     if (!(p->rope_base >= 0.0f) || std::isinf(p->rope_base)) return JA_ERR_SHAPE;  // NaN, negative, inf
+    if (p->rope_inputs_turned != 0 && p->rope_inputs_turned != 1) return JA_ERR_SHAPE;
     // Kernels address a (sample, head) slice with 32-bit byte offsets; bounding
     // every [rows, H, D] tensor below 4 GiB bounds every slice (the sample
     // lengths themselves live on the device).
@@ -198,11 +199,12 @@ ja::PlanParams plan_of(const ja_problem &p, int kind, int tile_rows, int inner_r
 }
 
 // Rotary embedding: turn q and k into the workspace copies (sign +1) and point
-// the attention parameters at them, or turn dq and dk back in place (sign -1).
+// the attention parameters at them, or turn dq and dk back in place (sign -1);
+// with_q false turns the k segment only.
 hipError_t rope_turn(const ja_problem &p, const void *q_src, void *q_dst, const void *k_src, void *k_dst,
-                     float sign, int timer_id, hipStream_t s) {
+                     float sign, int timer_id, hipStream_t s, bool with_q = true) {
     ja::RopeParams r{};
-    r.seg[0] = ja::RopeSeg{q_src, q_dst, p.q_offsets, p.total_q, p.batch};
+    r.seg[0] = ja::RopeSeg{q_src, q_dst, p.q_offsets, with_q ? p.total_q : 0, p.batch};
     r.seg[1] = ja::RopeSeg{k_src, k_dst, p.kv_offsets, p.total_k, p.batch};
     r.H = p.heads;
     r.sign = sign;
@@ -211,8 +213,16 @@ hipError_t rope_turn(const ja_problem &p, const void *q_src, void *q_dst, const 
     return ja::launch_rope(r, p.head_dim, p.dtype == JA_F32, timer_id, s);
 }
 
+// Frequencies of the turn in turns per position, base^(-2d/D) / (2 pi), for the
+// backward units' turn-back.
+void rope_frequencies(const ja_problem &p, ja::AttnParams &a) {
+    const double base = (double)p.rope_base;
+    const double two_pi = 6.283185307179586;  // nearest double to 2 pi
+    for (int d = 0; d < p.head_dim / 2; ++d) a.rope_rev[d] = std::pow(base, -2.0 * d / p.head_dim) / two_pi;
+}
+
 hipError_t rope_inputs(const ja_problem &p, const Layout &L, void *ws, ja::AttnParams &a, hipStream_t s) {
-    if (!(p.rope_base > 0.0f)) return hipSuccess;
+    if (!(p.rope_base > 0.0f) || p.rope_inputs_turned) return hipSuccess;
     char *w = static_cast<char *>(ws);
     void *qr = w + L.rope_q, *kr = w + L.rope_k;
     const hipError_t e = rope_turn(p, a.q, qr, a.k, kr, 1.0f, ja::K_ROPE, s);
@@ -334,7 +344,7 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
     const bool rope = p->rope_base > 0.0f;
     hipError_t e = rope_inputs(*p, L, ws, a, s);
     if (e != hipSuccess) return hip_status(e);
-    if (p->dtype == JA_F32) {
+    if (p->dtype == JA_F32) {  // the scalar kernels leave the turn-back to a pass
         e = ja::launch_bwd_f32(a, p->head_dim, mode, p->act, s);
         if (e == hipSuccess && rope) e = rope_turn(*p, dq, dq, dk, dk, -1.0f, ja::K_ROPE_BACK, s);
         return hip_status(e);
@@ -351,10 +361,14 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
         pp[n++] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 0, a.tiles4, L.cap_q, a.counters4);
     e = ja::launch_plan(pp, n, s);
     if (e != hipSuccess) return hip_status(e);
+    if (rope) {  // the dQ units turn their rows back before storing them
+        a.rope_back = 1;
+        rope_frequencies(*p, a);
+    }
     e = ja::launch_bwd_bf16(a, p->head_dim, mode, p->act, 2 * cu_count(), long_units, s);
     if (e == hipSuccess && dbias) e = ja::launch_dbias_bf16(a, p->head_dim, mode, p->act, s);
-    // the kernels produced the gradients of the turned rows: turn them back
-    if (e == hipSuccess && rope) e = rope_turn(*p, dq, dq, dk, dk, -1.0f, ja::K_ROPE_BACK, s);
+    // dk, the gradient of the turned keys, is turned back by a pass
+    if (e == hipSuccess && rope) e = rope_turn(*p, nullptr, nullptr, dk, dk, -1.0f, ja::K_ROPE_BACK, s, false);
     return hip_status(e);
 }
 
@@ -389,6 +403,15 @@ hipError_t scratch_ptr(void **out) {
 const ja::KernelTimer &ja::kernel_timer() { return g_timer; }
 
 extern "C" {
+
+ja_status jagged_rope(const ja_problem *p, const void *q, const void *k, void *q_turned, void *k_turned,
+                      void *stream) {
+    ja_status st = check_problem(p, JA_PASS_FWD);
+    if (st != JA_OK) return st;
+    if (!(p->rope_base > 0.0f)) return JA_ERR_SHAPE;
+    if ((p->total_q > 0 && (!q || !q_turned)) || (p->total_k > 0 && (!k || !k_turned))) return JA_ERR_NULL;
+    return hip_status(rope_turn(*p, q, q_turned, k, k_turned, 1.0f, ja::K_ROPE, static_cast<hipStream_t>(stream)));
+}
 
 ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event) {
     if (kernel_id < JA_KERNEL_PLAN || kernel_id >= ja::K_COUNT) return JA_ERR_UNSUPPORTED;

@@ -22,6 +22,12 @@
 //     the pages pipeline across the outer loop because the inner loop has
 //     only one or two iterations ("Meta redesigns...", section "Custom Kernels
 //     and 5D Parallelism...").
+// With a rotary embedding the units read turned q and k, so dQ and dK come out
+// as gradients of the turned rows.  The dQ and fused units turn their dQ rows
+// back (the turn's transpose) in registers before the store.  dK is turned back
+// by a streaming pass instead: the dK/dV kernel runs one wave per SIMD at the
+// edge of its register budget, and any epilogue added to it changes how the
+// compiler schedules its main loop (measured: 8 % slower, more than the pass).
 #include "ja_device.h"
 #include "ja_kernels.h"
 #include "ja_tiles.h"
@@ -84,7 +90,7 @@ __device__ __forceinline__ float score_bwd(float s_raw, float scale, float bias,
 }
 
 // ------------------------------------------------------------- dQ units
-template <int D, int MODE, int ACT>
+template <int D, int MODE, int ACT, bool ROPE>
 __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) {
     constexpr int BN = KV_TILE;
     constexpr int BM = Q_TILE;
@@ -232,6 +238,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
             store_tile((jt + 1) & 1);
             __syncthreads();
         }
+        if constexpr (ROPE) rope_back_acc<D>(dqacc, irow, p.rope_rev, g);
         store_row_acc<D>(dQs, irow, dqacc, p.scale, g);
     }
     busy_end(p.busy, p.busy_cap, busy_t0);
@@ -454,7 +461,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
 // registers, dX^T through a small LDS transpose, and the block's complete dQ.
 // Memory accesses go through per-sample buffer descriptors (no branches
 // around them), so the next block's loads stay in flight.
-template <int D, int MODE, int ACT>
+template <int D, int MODE, int ACT, bool ROPE>
 __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
     constexpr int NKK = D / 16, NDB = D / 32;
     constexpr int TILE = 32 * D * 2;           // one 32-row tile
@@ -591,6 +598,7 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
                 for (int ks = 0; ks < 2; ++ks)
                     dqacc[db] = mfma32(lds_read_tr_operand<D>(Kt, ks * 16, db * 32, lane), dtb[ks], dqacc[db]);
             }
+            if constexpr (ROPE) rope_back_acc<D>(dqacc, ia + l32, p.rope_rev, g);
             store_tile<D>(dQs, Qt, ia, dqacc, p.scale, lane);
             lds_wave_sync();  // every LDS read of this block is done before the next stores
         }
@@ -602,7 +610,7 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
 }
 
 // -------------------------------------------------------------- launches
-template <int D, int MODE, int ACT>
+template <int D, int MODE, int ACT, bool ROPE>
 static hipError_t launch_bwd_t(const AttnParams &p, int grid, bool long_units, hipStream_t st) {
     const KernelTimer &t = kernel_timer();
     if (MODE == JFA && p.total_q > 0) {
@@ -612,26 +620,34 @@ static hipError_t launch_bwd_t(const AttnParams &p, int grid, bool long_units, h
         t.end(K_BWD_DELTA, st);
     }
     t.begin(K_BWD_FUSED, st);
-    hipLaunchKernelGGL((fused_kernel<D, MODE, ACT>), dim3(2 * grid), dim3(WAVE), 0, st, t.with_busy(p, K_BWD_FUSED));
+    hipLaunchKernelGGL((fused_kernel<D, MODE, ACT, ROPE>), dim3(2 * grid), dim3(WAVE), 0, st, t.with_busy(p, K_BWD_FUSED));
     t.end(K_BWD_FUSED, st);
     if (!long_units) return hipGetLastError();
     t.begin(K_BWD_KV, st);
     hipLaunchKernelGGL((dkdv_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, t.with_busy(p, K_BWD_KV));
     t.end(K_BWD_KV, st);
     t.begin(K_BWD_Q, st);
-    hipLaunchKernelGGL((dq_kernel<D, MODE, ACT>), dim3(grid), dim3(BWD_THREADS), 0, st, t.with_busy(p, K_BWD_Q));
+    hipLaunchKernelGGL((dq_kernel<D, MODE, ACT, ROPE>), dim3(grid), dim3(BWD_THREADS), 0, st, t.with_busy(p, K_BWD_Q));
     t.end(K_BWD_Q, st);
     return hipGetLastError();
 }
 
+template <int D, bool ROPE>
+static hipError_t launch_bwd_r(const AttnParams &p, int mode, int act, int grid, bool lu, hipStream_t st) {
+    if (mode == JFA) return launch_bwd_t<D, JFA, SILU, ROPE>(p, grid, lu, st);
+    switch (act) {
+    case SILU: return launch_bwd_t<D, GDPA, SILU, ROPE>(p, grid, lu, st);
+    case GELU_TANH: return launch_bwd_t<D, GDPA, GELU_TANH, ROPE>(p, grid, lu, st);
+    default: return launch_bwd_t<D, GDPA, GELU_ERF, ROPE>(p, grid, lu, st);
+    }
+}
+
+// Kernels without the rotary turn-back are their own instantiations, so its
+// registers never weigh on the plain kernels.
 template <int D>
 static hipError_t launch_bwd_d(const AttnParams &p, int mode, int act, int grid, bool lu, hipStream_t st) {
-    if (mode == JFA) return launch_bwd_t<D, JFA, SILU>(p, grid, lu, st);
-    switch (act) {
-    case SILU: return launch_bwd_t<D, GDPA, SILU>(p, grid, lu, st);
-    case GELU_TANH: return launch_bwd_t<D, GDPA, GELU_TANH>(p, grid, lu, st);
-    default: return launch_bwd_t<D, GDPA, GELU_ERF>(p, grid, lu, st);
-    }
+    return p.rope_back ? launch_bwd_r<D, true>(p, mode, act, grid, lu, st)
+                       : launch_bwd_r<D, false>(p, mode, act, grid, lu, st);
 }
 
 hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, bool long_units,

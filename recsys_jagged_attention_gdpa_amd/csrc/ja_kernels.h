@@ -20,6 +20,8 @@ constexpr int DBIAS_MAX_BINS = 4096;  // largest bias table row the gradient pas
 // The chip's accelerator dies (XCDs), each with its own L2.
 constexpr int XCDS = 8;
 
+constexpr int ROPE_MAX_HALF = 64;  // D / 2 for the largest head dimension
+
 // Plan (scheduler) output lives at the start of the workspace.
 struct PlanCounters {
     int units;   // number of work units (tiles x heads)
@@ -91,6 +93,11 @@ struct AttnParams {
     // clock cycles from its start to its exit into busy[blockIdx.x] (busy_cap entries)
     uint64_t *busy;
     int busy_cap;
+    // Backward with a rotary embedding: the dQ rows leave the kernels turned back
+    // (the turn's transpose) by the angle of their row's sample-local position;
+    // rope_rev[d] = base^(-2d/D) / (2 pi), turns per position of pair (d, d + D/2).
+    int rope_back;
+    double rope_rev[ROPE_MAX_HALF];
 };
 
 // Units of the tile lists (PLAN_Q_TILES, PLAN_KV_TILES) are numbered
@@ -203,7 +210,6 @@ struct RopeSeg {
     int64_t rows;
     int B;
 };
-constexpr int ROPE_MAX_HALF = 64;  // D / 2 for the largest head dimension
 struct RopeParams {
     RopeSeg seg[2];
     int H;

@@ -148,6 +148,48 @@ __device__ __forceinline__ void load_row_operand(bf16x8 (&reg)[D / 16], const He
     for (int kk = 0; kk < D / 16; ++kk) reg[kk] = __builtin_bit_cast(bf16x8, S.template load16<CP>(row, 2 * kk + g));
 }
 
+// The rotary turn's transpose on one lane's D^T-layout accumulator set (the
+// gradient of a row at sample-local position t, element e of block db being
+// column db*32 + crow(e, g)): column d < D/2 and its partner d + D/2 sit in the
+// same lane, in block db + D/64 at the same element (D = 32: element e + 8 of
+// the one block).  rev[d] is the pair's frequency in turns per position; the
+// angle t * rev[d] is formed and reduced to [-1/2, 1/2] turn in fp64 (positions
+// reach the hundreds of thousands), its sine and cosine taken by the hardware's
+// fp32 sine and cosine, which take turns (absolute error about 2^-23, far below
+// the bf16 rounding of the gradient that follows).
+template <int D>
+__device__ __forceinline__ void rope_back_acc(f32x16 (&acc)[D / 32], int t, const double *rev, int g) {
+    // (cos, sin) of the angle of pair d at position t
+    auto angle = [&](int d, float &cs, float &sn) {
+        const double r = (double)t * rev[d];
+        const float f = (float)(r - __builtin_rint(r));
+        sn = __builtin_amdgcn_sinf(f);
+        cs = __builtin_amdgcn_cosf(f);
+    };
+    if constexpr (D == 32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float cs, sn;
+            angle(crow(e, g), cs, sn);
+            const float x = acc[0][e], y = acc[0][e + 8];
+            acc[0][e] = cs * x + sn * y;
+            acc[0][e + 8] = cs * y - sn * x;
+        }
+    } else {
+        constexpr int HB = D / 64;
+#pragma unroll
+        for (int db = 0; db < HB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float cs, sn;
+                angle(db * 32 + crow(e, g), cs, sn);
+                const float x = acc[db][e], y = acc[db + HB][e];
+                acc[db][e] = cs * x + sn * y;
+                acc[db + HB][e] = cs * y - sn * x;
+            }
+    }
+}
+
 // Store a D^T-layout accumulator block set (lane owns row `row` of the slice;
 // element e of block db is column db*32 + crow(e, g)) as bf16 times `mul`.
 // Rows past the slice are dropped by the descriptor.

@@ -12,7 +12,9 @@ window (0 = none) keeps the pairs whose aligned distance i + Lk - Lq - j is
 below it (and, without causal masking, above minus it): sliding-window
 attention.  rope_base (0 = none) turns q and k by the rotary embedding of
 their sample-local positions before the scores are formed; gradients are with
-respect to the rows as given.
+respect to the rows as given.  rope() turns q and k once; pass its output with
+rope_inputs_turned=True to a forward and its backward (the autograd functions
+do so), which then turn nothing on the way in.
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ from . import _lib
 
 
 def _problem(q, k, q_offsets, kv_offsets, *, causal, scale, act, bias, bias_kind, bias_lo,
-             bias_hi, max_kv_len=0, window=0, rope_base=0.0):
+             bias_hi, max_kv_len=0, window=0, rope_base=0.0, rope_inputs_turned=False):
     B = int(kv_offsets.numel()) - 1
     H, D = int(q.shape[1]), int(q.shape[2])
     return _lib.make_problem(
@@ -30,7 +32,8 @@ def _problem(q, k, q_offsets, kv_offsets, *, causal, scale, act, bias, bias_kind
         total_k=int(k.shape[0]), q_offsets=q_offsets, kv_offsets=kv_offsets,
         lq_fixed=0 if q_offsets is not None else int(q.shape[0]), causal=causal, scale=scale,
         act=act, bias_kind=bias_kind if bias is not None else "none", bias_table=bias,
-        bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len, window=window, rope_base=rope_base)
+        bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len, window=window, rope_base=rope_base,
+        rope_inputs_turned=rope_inputs_turned)
 
 
 def _check_inputs(q, k, v, q_offsets, kv_offsets, bias):
@@ -55,11 +58,11 @@ def _workspace(problem, pass_, device):
 
 def gdpa_forward(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False,
                  bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, window=0,
-                 rope_base=0.0):
+                 rope_base=0.0, rope_inputs_turned=False):
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act=act, bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len,
-                 window=window, rope_base=rope_base)
+                 window=window, rope_base=rope_base, rope_inputs_turned=rope_inputs_turned)
     rows = q.shape[0] if q_offsets is not None else p.batch * q.shape[0]
     o = torch.empty((rows, q.shape[1], q.shape[2]), dtype=q.dtype, device=q.device)
     ws = _workspace(p, _lib.PASS_FWD, q.device)
@@ -69,12 +72,12 @@ def gdpa_forward(q, k, v, q_offsets, kv_offsets, *, act="silu", scale=None, caus
 
 def attn_forward(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bias=None,
                  bias_kind="none", bias_lo=0, bias_hi=0, residual=True, max_kv_len=0, window=0,
-                 rope_base=0.0):
+                 rope_base=0.0, rope_inputs_turned=False):
     """Returns (O, LSE[H, T], O_residual); O_residual is None for fp32 or residual=False."""
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act="silu", bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len,
-                 window=window, rope_base=rope_base)
+                 window=window, rope_base=rope_base, rope_inputs_turned=rope_inputs_turned)
     rows = q.shape[0] if q_offsets is not None else p.batch * q.shape[0]
     o = torch.empty((rows, q.shape[1], q.shape[2]), dtype=q.dtype, device=q.device)
     lse = torch.empty((q.shape[1], rows), dtype=torch.float32, device=q.device)
@@ -82,6 +85,18 @@ def attn_forward(q, k, v, q_offsets, kv_offsets, *, scale=None, causal=False, bi
     ws = _workspace(p, _lib.PASS_FWD, q.device)
     _lib.jagged_attn_fwd(p, q, k, v, o, lse, o_res, ws)
     return o, lse, o_res
+
+
+def rope(q, k, q_offsets, kv_offsets, *, rope_base, out=None):
+    """q and k turned by the rotary embedding of their sample-local positions (q_offsets
+    None: a shared block, row r at position r), as new tensors or into out = (q_out, k_out)
+    (which may be q and k themselves)."""
+    _check_inputs(q, k, k, q_offsets, kv_offsets, None)
+    p = _problem(q, k, q_offsets, kv_offsets, causal=False, scale=None, act="silu", bias=None,
+                 bias_kind="none", bias_lo=0, bias_hi=0, rope_base=rope_base)
+    qt, kt = out if out is not None else (torch.empty_like(q), torch.empty_like(k))
+    _lib.jagged_rope(p, q, k, qt, kt)
+    return qt, kt
 
 
 def _check_mx(q, k, v, scales):
@@ -132,12 +147,12 @@ def _dbias_out(p, bias, with_dbias):
 
 def gdpa_backward(q, k, v, dout, q_offsets, kv_offsets, *, act="silu", scale=None, causal=False,
                   bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0, window=0,
-                  rope_base=0.0, with_dbias=False):
+                  rope_base=0.0, rope_inputs_turned=False, with_dbias=False):
     """(dQ, dK, dV), plus the bias table's gradient last when with_dbias."""
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act=act, bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len,
-                 window=window, rope_base=rope_base)
+                 window=window, rope_base=rope_base, rope_inputs_turned=rope_inputs_turned)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     db, pass_ = _dbias_out(p, bias, with_dbias)
     ws = _workspace(p, pass_, q.device)
@@ -147,12 +162,12 @@ def gdpa_backward(q, k, v, dout, q_offsets, kv_offsets, *, act="silu", scale=Non
 
 def attn_backward(q, k, v, o, dout, lse, q_offsets, kv_offsets, *, o_residual=None, scale=None,
                   causal=False, bias=None, bias_kind="none", bias_lo=0, bias_hi=0, max_kv_len=0,
-                  window=0, rope_base=0.0, with_dbias=False):
+                  window=0, rope_base=0.0, rope_inputs_turned=False, with_dbias=False):
     """(dQ, dK, dV), plus the bias table's gradient last when with_dbias."""
     _check_inputs(q, k, v, q_offsets, kv_offsets, bias)
     p = _problem(q, k, q_offsets, kv_offsets, causal=causal, scale=scale, act="silu", bias=bias,
                  bias_kind=bias_kind, bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len,
-                 window=window, rope_base=rope_base)
+                 window=window, rope_base=rope_base, rope_inputs_turned=rope_inputs_turned)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     db, pass_ = _dbias_out(p, bias, with_dbias)
     ws = _workspace(p, pass_, q.device)
@@ -166,7 +181,9 @@ class _GDPAFunction(torch.autograd.Function):
                 bias_hi, max_kv_len, window, rope_base):
         kw = dict(act=act, scale=scale, causal=causal, bias=bias, bias_kind=bias_kind,
                   bias_lo=bias_lo, bias_hi=bias_hi, max_kv_len=max_kv_len, window=window,
-                  rope_base=rope_base)
+                  rope_base=rope_base, rope_inputs_turned=rope_base > 0)
+        if rope_base > 0:  # turned once, for the forward and the backward
+            q, k = rope(q, k, q_offsets, kv_offsets, rope_base=rope_base)
         ctx.kw = kw
         ctx.save_for_backward(q, k, v, q_offsets, kv_offsets)
         return gdpa_forward(q, k, v, q_offsets, kv_offsets, **kw)
@@ -185,7 +202,10 @@ class _JFAFunction(torch.autograd.Function):
     def forward(ctx, q, k, v, q_offsets, kv_offsets, scale, causal, bias, bias_kind, bias_lo,
                 bias_hi, max_kv_len, window, rope_base):
         kw = dict(scale=scale, causal=causal, bias=bias, bias_kind=bias_kind, bias_lo=bias_lo,
-                  bias_hi=bias_hi, max_kv_len=max_kv_len, window=window, rope_base=rope_base)
+                  bias_hi=bias_hi, max_kv_len=max_kv_len, window=window, rope_base=rope_base,
+                  rope_inputs_turned=rope_base > 0)
+        if rope_base > 0:  # turned once, for the forward and the backward
+            q, k = rope(q, k, q_offsets, kv_offsets, rope_base=rope_base)
         o, lse, o_res = attn_forward(q, k, v, q_offsets, kv_offsets, **kw)
         ctx.kw = kw
         ctx.save_for_backward(q, k, v, o, lse, o_res, q_offsets, kv_offsets)

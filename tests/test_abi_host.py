@@ -128,6 +128,27 @@ def test_rotary_embedding_needs_workspace_for_turned_copies():
         assert st == 4  # the plain workspace is too small once q and k are turned
 
 
+def test_pre_turned_inputs_need_no_copies_and_rope_call_arguments():
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    plain, turned = _problem(), _problem(rope_base=10000.0, rope_inputs_turned=True)
+    for pass_ in (_lib.PASS_FWD, _lib.PASS_BWD):
+        assert lib.ja_workspace_size(ctypes.byref(turned), pass_) == \
+            lib.ja_workspace_size(ctypes.byref(plain), pass_)
+    bad = _problem(rope_base=10000.0)
+    bad.rope_inputs_turned = 2
+    assert lib.ja_workspace_size(ctypes.byref(bad), 0) == 0
+    # jagged_rope: a turn needs a base, the rows it turns and somewhere to put them;
+    # all of these are refused on the host, before anything is launched
+    assert lib.jagged_rope(ctypes.byref(plain), P(0x10), P(0x20), P(0x30), P(0x40), None) == 2
+    rope = _problem(rope_base=10000.0)
+    assert lib.jagged_rope(ctypes.byref(rope), None, P(0x20), P(0x30), P(0x40), None) == 1
+    assert lib.jagged_rope(ctypes.byref(rope), P(0x10), P(0x20), P(0x30), None, None) == 1
+    assert lib.jagged_rope(ctypes.byref(_problem(rope_base=-2.0)), P(0x10), P(0x20), P(0x30), P(0x40),
+                           None) == 2
+    assert lib.jagged_rope(None, P(0x10), P(0x20), P(0x30), P(0x40), None) == 1
+
+
 def test_bias_gradient_arguments():
     lib = _lib.load()
     P = ctypes.c_void_p

@@ -72,3 +72,92 @@ def test_rope_bias_gradient():
     w = synth.custom(mode="jfa", lq=LQ, lk=LK, H=2, D=128, seed=2, causal=True,
                      bias_kind="rel", bias_lo=-120, bias_hi=40, rope_base=10000.0)
     check_dbias(w, "rope")
+
+
+def _turned_rows_match(got, want64, what):
+    """GPU turned rows against the oracle's: the same value in every element but for
+    at most one in a million, and those one unit in the last place apart (the two
+    sides' fp64 sine and cosine may differ in their last bit)."""
+    g = got.cpu()
+    if g.dtype == torch.bfloat16:
+        w = torch.from_numpy(want64).float().to(torch.bfloat16)  # exact: already bf16 values
+        gi, wi = g.view(torch.int16).int(), w.view(torch.int16).int()
+    else:
+        w = torch.from_numpy(want64).float()  # nearest float32 of the fp64 turn
+        gi, wi = g.view(torch.int32).long(), w.view(torch.int32).long()
+    diff = (gi - wi).abs()
+    n_bad = int((diff != 0).sum())
+    assert n_bad <= max(1, g.numel() // 1_000_000) and int(diff.max()) <= 1, (what, n_bad, int(diff.max()))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rope_call_turns_rows_as_the_oracle(dtype):
+    from oracle import ref
+    import recsys_jagged_attention_gdpa_amd as ja
+    w = synth.custom(mode="jfa", lq=LQ, lk=LK, H=3, D=64, seed=21, dtype=dtype, rope_base=10000.0)
+    announce(f"rope call {dtype}: Tq={w.total_q} Tk={w.total_k}")
+    d = to_dev(w)
+    qt, kt = ja.rope(d["q"], d["k"], d["q_off"], d["kv_off"], rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    bf = dtype == torch.bfloat16
+    _turned_rows_match(qt, ref.rope(w.q, w.q_off, rope_base=w.rope_base, rope_bf16=bf), "q")
+    _turned_rows_match(kt, ref.rope(w.k, w.kv_off, rope_base=w.rope_base, rope_bf16=bf), "k")
+    # in place gives the same rows
+    q2, k2 = d["q"].clone(), d["k"].clone()
+    ja.rope(q2, k2, d["q_off"], d["kv_off"], rope_base=w.rope_base, out=(q2, k2))
+    torch.cuda.synchronize()
+    assert torch.equal(q2, qt) and torch.equal(k2, kt)
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_pre_turned_inputs_give_the_same_results(mode, dtype):
+    """Turning once with the rope call and passing the turned rows to the forward and
+    the backward gives, bit for bit, what the calls that turn q and k themselves give."""
+    import recsys_jagged_attention_gdpa_amd as ja
+    w = synth.custom(mode=mode, lq=LQ, lk=LK, H=2, D=128 if dtype == torch.bfloat16 else 32, seed=8,
+                     dtype=dtype, act="gelu_tanh", causal=True, rope_base=10000.0)
+    announce(f"rope pre-turned {mode} {dtype}")
+    d = to_dev(w)
+    f = gpu_fwd(w, d)
+    g = gpu_bwd(w, d, f)
+    qt, kt = ja.rope(d["q"], d["k"], d["q_off"], d["kv_off"], rope_base=w.rope_base)
+    kw = dict(scale=w.scale, causal=w.causal, rope_base=w.rope_base, rope_inputs_turned=True)
+    if mode == "gdpa":
+        o = ja.gdpa_forward(qt, kt, d["v"], d["q_off"], d["kv_off"], act=w.act, **kw)
+        dq, dk, dv = ja.gdpa_backward(qt, kt, d["v"], d["dout"], d["q_off"], d["kv_off"], act=w.act, **kw)
+        f2 = {"o": o}
+    else:
+        o, lse, o_res = ja.attn_forward(qt, kt, d["v"], d["q_off"], d["kv_off"], **kw)
+        dq, dk, dv = ja.attn_backward(qt, kt, d["v"], o, d["dout"], lse, d["q_off"], d["kv_off"],
+                                      o_residual=o_res, **kw)
+        f2 = {"o": o, "lse": lse, "o_res": o_res}
+    torch.cuda.synchronize()
+    for n, t in f.items():
+        if t is not None:
+            assert torch.equal(f2[n], t), n
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.equal(t, g[n]), n
+
+
+@pytest.mark.parametrize("mode", ["gdpa", "jfa"])
+def test_autograd_turns_once_and_matches_the_direct_calls(mode):
+    import recsys_jagged_attention_gdpa_amd as ja
+    w = synth.custom(mode=mode, lq=LQ, lk=LK, H=2, D=64, seed=15, act="silu", causal=True,
+                     rope_base=10000.0)
+    announce(f"rope autograd {mode}")
+    d = to_dev(w)
+    f = gpu_fwd(w, d)
+    g = gpu_bwd(w, d, f)
+    q, k, v = (d[n].clone().requires_grad_() for n in ("q", "k", "v"))
+    if mode == "gdpa":
+        o = ja.gdpa(q, k, v, d["q_off"], d["kv_off"], act=w.act, scale=w.scale, causal=w.causal,
+                    rope_base=w.rope_base)
+    else:
+        o = ja.jagged_attention(q, k, v, d["q_off"], d["kv_off"], scale=w.scale, causal=w.causal,
+                                rope_base=w.rope_base)
+    o.backward(d["dout"])
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), f["o"])
+    for n, t in (("dq", q.grad), ("dk", k.grad), ("dv", v.grad)):
+        assert torch.equal(t, g[n]), n

@@ -303,7 +303,7 @@ ja_status run_fwd(const ja_problem *p, int mode, const void *q, const void *k, c
     // One shared block of at most 32 query rows (known here, since it is not
     // jagged): one-wave units over 32-row tiles instead of 4-wave 128-row ones.
     const bool few_q = p->q_offsets == nullptr && p->lq_fixed <= ja::FEW_Q_ROWS;
-    const int q_tile = few_q ? ja::FEW_Q_ROWS : ja::Q_TILE, kv_tile = few_q ? 32 : ja::KV_TILE;
+    const int q_tile = few_q ? ja::FEW_Q_ROWS : ja::Q_TILE, kv_tile = few_q ? ja::FEW_Q_KV_TILE : ja::KV_TILE;
     // The caller's bound on key counts may rule out every long-sequence unit.
     const bool long_units = !(p->max_kv_len > 0 && p->max_kv_len <= ja::FUSED_MAX_LK);
     ja::PlanParams pp[2] = {plan_of(*p, ja::PLAN_SAMPLES, 1, 32, 0, a.tiles3, L.cap_s, a.counters3),
@@ -357,8 +357,10 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
         pp[n++] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 1, a.tiles, L.cap_q, a.counters);
         pp[n++] = plan_of(*p, ja::PLAN_KV_TILES, ja::BWD_KV_UNIT, ja::BWD_Q_STEP, 1, a.tiles2, L.cap_k, a.counters2);
     }
-    if (dbias)  // query tiles of every sample, short ones included
-        pp[n++] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 0, a.tiles4, L.cap_q, a.counters4);
+    if (dbias) {  // query tiles of every sample, short ones included; the summation order follows this list
+        pp[n] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 0, a.tiles4, L.cap_q, a.counters4);
+        pp[n++].stable = 1;
+    }
     e = ja::launch_plan(pp, n, s);
     if (e != hipSuccess) return hip_status(e);
     if (rope) {  // the dQ units turn their rows back before storing them

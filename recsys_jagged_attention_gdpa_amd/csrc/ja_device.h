@@ -62,6 +62,7 @@ typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
 typedef __attribute__((address_space(3))) u32x4 lu32x4;
 typedef __attribute__((address_space(3))) s16x4 ls16x4;
 typedef __attribute__((address_space(3))) float lfloat;
+typedef __attribute__((address_space(3))) uint8_t lu8;
 
 __device__ __forceinline__ bf16x8 lds_read16(const lchar *base, int off) {
     return *reinterpret_cast<const lbf16x8 *>(base + off);

@@ -55,17 +55,19 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 units a running softmax max may l
 // operands; only V is decoded to bf16 for the PV product.
 template <int D, int MODE, int ACT, int WAVES, int BN, bool SPLIT, bool MX>
 __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(const AttnParams p) {
+    constexpr bool F8S = MX && D >= 64;  // S and PV on the fp8 MFMA (key and value tiles hold codes)
     constexpr int NT = WAVES * WAVE;
     constexpr int BM = 32 * WAVES;
-    constexpr int TILE_BYTES = BN * D * 2;
+    constexpr int TILE_BYTES = BN * D * (F8S ? 1 : 2);
     constexpr int NKK = D / 16;  // k-steps over the head dimension
     constexpr int NDB = D / 32;  // 32-wide blocks of the head dimension
     constexpr int NNB = BN / 32; // 32-key blocks per tile
     constexpr int NKS = BN / 16; // 16-key k-steps per tile
     constexpr int WIN = BM + BN - 1;  // largest bias window of a (unit, key tile)
-    static_assert(WIN <= NT, "one bias window entry per thread");
+    constexpr int WPT = (WIN + NT - 1) / NT;  // bias window entries per thread
     __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
     __shared__ float s_bias[2][WIN];
+    __shared__ __attribute__((aligned(4))) uint8_t s_vsc[2][F8S ? BN : 4];  // F8S: each value row's scale code S_j
     __shared__ int s_unit;
     lchar *const lbase = (lchar *)smem;
 
@@ -106,7 +108,6 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                                      bz.kind ? (uint32_t)bz.width * 4u : 0u);
 
         // Q rows of this lane, in B-operand layout: chunk 2kk+g of row irow.
-        constexpr bool F8S = MX && D >= 64;  // S on the fp8 MFMA
         constexpr int NKS8 = D / 64;          // 64-code k-steps of the fp8 MFMA
         bf16x8 qreg[F8S ? 1 : NKK];
         i32x8 qf[F8S ? NKS8 : 1];  // F8S: query codes, operand layout
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         }
         const MXSlice<D> Km(p.k, p.k_sc, s.ks, MX ? s.lk : 0, H, h), Vm(p.v, p.v_sc, s.ks, MX ? s.lk : 0, H, h);
         MXPairLoader<BN, D, NT> mxl;  // MX: key and value codes, decoded into LDS
-        MXTileLoader<BN, D, NT> mxv;  // F8S: value codes only
+        F8VLoader<BN, D, NT> mxv;     // F8S: value codes, re-encoded to one scale per key
         int ksn[NNB][F8S ? NKS8 : 1], ksc[NNB][F8S ? NKS8 : 1];  // F8S: the lane's key-row scale codes, next / current tile
 
         f32x16 oacc[NDB];
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         // fp8 key codes are copied straight into it, decoded MXFP8 tiles pass
         // through registers (loaded here, written by store_tile); the bias window
         // it needs goes through a register.  Loads past the sample read zeros.
-        float bnext = 0.0f;
+        float bnext[WPT];
         auto load_tile = [&](int jt) {
             lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             if constexpr (F8S) {
@@ -153,12 +154,15 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                 dma_tile<BN, D, NT>(kt, Ks, jt * BN, tid);
                 dma_tile<BN, D, NT>(kt + TILE_BYTES, Vs, jt * BN, tid);
             }
-            const int bi = bias_stage_rowmajor(bz, i0, BM, jt * BN, BN, tid);
-            bnext = buf_load_f32(brs, bi >= 0 ? (uint32_t)bi * 4u : OOB);
+#pragma unroll
+            for (int r = 0; r < WPT; ++r) {
+                const int bi = bias_stage_rowmajor(bz, i0, BM, jt * BN, BN, tid + r * NT);
+                bnext[r] = buf_load_f32(brs, bi >= 0 ? (uint32_t)bi * 4u : OOB);
+            }
         };
         auto store_tile = [&](int buf) {
             if constexpr (F8S) {
-                mxv.store(lbase + buf * 2 * TILE_BYTES + TILE_BYTES, tid);
+                mxv.store(lbase + buf * 2 * TILE_BYTES + TILE_BYTES, (lu8 *)s_vsc[buf], tid);
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
@@ -166,7 +170,9 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             } else if constexpr (MX) {
                 mxl.store(lbase + buf * 2 * TILE_BYTES, lbase + buf * 2 * TILE_BYTES + TILE_BYTES, tid);
             }
-            if (tid < WIN) s_bias[buf][tid] = MODE == JFA ? bnext * LOG2E : bnext;  // JFA works in log2 units
+#pragma unroll
+            for (int r = 0; r < WPT; ++r)  // JFA works in log2 units
+                if (tid + r * NT < WIN) s_bias[buf][tid + r * NT] = MODE == JFA ? bnext[r] * LOG2E : bnext[r];
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tile has landed
         };
         load_tile(jt_first);
@@ -214,7 +220,9 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             // scalar branch.
             const bool masked = (j0 + BN > wke) || (j0 < wkb);
             const int my_kend = key_end(irow, s.lq, s.lk, p.causal, p.window);
-            bf16x8 pb[NKS], pbl[SPLIT ? NKS : 1];
+            bf16x8 pb[F8S ? 1 : NKS], pbl[SPLIT && !F8S ? NKS : 1];
+            u32x4 pf8[2] = {u32x4{}, u32x4{}};  // F8S: P^T codes of the tile's 32-key blocks
+            int pex[2] = {127, 127};             // F8S: their E8M0 scale codes
             // x = scale * s + bias (JFA: in log2 units); without bias only the
             // scale is applied, folded into later arithmetic where possible.
             if (bz.kind) {
@@ -248,7 +256,11 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                             pv[e] = (j >= my_kend) | (j < my_kbeg) ? 0.0f : pv[e];
                         }
                     }
-                    pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
+                    if constexpr (F8S) {
+                        pex[nb] = encode_p_block(pv, (const lu8 *)s_vsc[jt & 1] + nb * 32, g, pf8[nb]);
+                    } else {
+                        pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
+                    }
                 }
             } else {
                 if (masked) {
@@ -270,7 +282,9 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                 // max exceeds it by more than RESCALE_SLACK (log2 units); otherwise
                 // P is formed against the stale max and stays below 2^RESCALE_SLACK.
                 if (wave_any(tmax > m_run + RESCALE_SLACK)) {
-                    const float m_new = fmaxf(m_run, tmax);
+                    // fp8 P: whole-number maxima, so every rescale is by a power of two
+                    // and P is encoded against a reference the scales absorb exactly
+                    const float m_new = F8S ? ceilf(fmaxf(m_run, tmax)) : fmaxf(m_run, tmax);
                     const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run - m_new);
                     m_run = m_new;
                     l_run *= alpha;
@@ -286,19 +300,33 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                         pv[e] = fast_exp2(__builtin_fmaf(sacc[nb][e], xmul, nm));
                         l_run += pv[e];
                     }
-                    pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
-                    if constexpr (SPLIT) pack_residual_operands(pv, pbl[2 * nb], pbl[2 * nb + 1]);
+                    if constexpr (F8S) {
+                        pex[nb] = encode_p_block(pv, (const lu8 *)s_vsc[jt & 1] + nb * 32, g, pf8[nb]);
+                    } else {
+                        pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
+                        if constexpr (SPLIT) pack_residual_operands(pv, pbl[2 * nb], pbl[2 * nb + 1]);
+                    }
                 }
             }
 
             // O^T += V^T P^T over the tile's keys.
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
+            if constexpr (F8S) {
+                const i32x8 bop = p_f8_operand(pf8[0], pf8[1]);
+                const int scb = g ? pex[1] : pex[0];
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 a = lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane);
-                    oacc[db] = mfma32(a, pb[ks], oacc[db]);
-                    if constexpr (SPLIT) oacc[db] = mfma32(a, pbl[ks % (SPLIT ? NKS : 1)], oacc[db]);
+                    const i32x8 a = lds_read_vt_f8<D, NNB>(Vt, db, lane);
+                    oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, oacc[db], 0, 0, 0, 127, 0, scb);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const bf16x8 a = lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane);
+                        oacc[db] = mfma32(a, pb[ks % (F8S ? 1 : NKS)], oacc[db]);
+                        if constexpr (SPLIT && !F8S) oacc[db] = mfma32(a, pbl[ks % (SPLIT && !F8S ? NKS : 1)], oacc[db]);
+                    }
                 }
             }
 
@@ -343,6 +371,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
     constexpr int NKK = D / 16, NDB = D / 32;
     constexpr int NWAVES = FWD_THREADS / WAVE;
     __shared__ __attribute__((aligned(16))) char smem[(2 + NWAVES) * KV_BYTES];
+    __shared__ __attribute__((aligned(4))) uint8_t s_vsc[32];  // F8: each value row's scale code S_j
     __shared__ int s_unit, s_blk;
     lchar *const Kt = (lchar *)smem;
     lchar *const Vt = Kt + KV_BYTES;
@@ -369,12 +398,12 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
         const int h = w % H;
         const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
         const float *brow = bz.kind ? bz.table + (int64_t)h * bz.width : nullptr;
-        constexpr bool F8 = MX && D >= 64;  // S on the fp8 MFMA
+        constexpr bool F8 = MX && D >= 64;  // S and PV on the fp8 MFMA
         constexpr int NKS8 = D / 64;
         int ksc[F8 ? NKS8 : 1];              // F8: scale codes of the lane's key row l % 32
         if constexpr (F8) {
             const MXSlice<D> Km(p.k, p.k_sc, s.ks, s.lk, H, h);
-            MXTileLoader<32, D, FWD_THREADS> vl;
+            F8VLoader<32, D, FWD_THREADS> vl;
             vl.load(MXSlice<D>(p.v, p.v_sc, s.ks, s.lk, H, h), 0, threadIdx.x);
             constexpr int KPIECES = 32 * D / 16;  // 16-code pieces of the key tile
             if (threadIdx.x < KPIECES) {
@@ -383,7 +412,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
             }
 #pragma unroll
             for (int ks = 0; ks < NKS8; ++ks) ksc[ks] = f8_scale<D>(Km, l32, 2 * ks + g);
-            vl.store(Vt, threadIdx.x);
+            vl.store(Vt, (lu8 *)s_vsc, threadIdx.x);
         } else if constexpr (MX) {
             MXPairLoader<32, D, FWD_THREADS> kv;
             kv.load(MXSlice<D>(p.k, p.k_sc, s.ks, s.lk, H, h), MXSlice<D>(p.v, p.v_sc, s.ks, s.lk, H, h), 0,
@@ -471,7 +500,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
 #pragma unroll
                 for (int e = 0; e < 16; ++e) m = fmaxf(m, pv[e]);
                 m = fmaxf(m, shfl_xor32(m));
-                const float shift = m == -INFINITY ? 0.0f : m;
+                // fp8 P: a whole-number reference, which the block scale absorbs exactly
+                const float shift = m == -INFINITY ? 0.0f : (F8 ? ceilf(m) : m);
                 float l = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -480,11 +510,20 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
                 }
                 l += shfl_xor32(l);
                 norm = l > 0.0f ? 1.0f / l : 0.0f;
-                lse_row = l > 0.0f ? (m + log2f(l)) * LN2 : -INFINITY;
+                lse_row = l > 0.0f ? (shift + log2f(l)) * LN2 : -INFINITY;
             }
             bf16x8 pb[2], pbl[2];
-            pack_operands(pv, pb[0], pb[1]);
-            if constexpr (SPLIT) pack_residual_operands(pv, pbl[0], pbl[1]);
+            i32x8 pf8 = i32x8{};  // F8: P^T codes (one 32-key block) and this lane's scale operand
+            int scb = 127;
+            if constexpr (F8) {
+                u32x4 c0;
+                const int ex = encode_p_block(pv, (const lu8 *)s_vsc, g, c0);
+                pf8 = p_f8_operand(c0, u32x4{});
+                scb = g ? 127 : ex;
+            } else {
+                pack_operands(pv, pb[0], pb[1]);
+                if constexpr (SPLIT) pack_residual_operands(pv, pbl[0], pbl[1]);
+            }
             if constexpr (MODE == JFA) buf_store_f32(lse_r, g == 0 ? (uint32_t)irow * 4u : OOB, lse_row);
             // One 32-wide block of the head dimension at a time, staged as it
             // completes, so only one accumulator block is live.  The optional
@@ -492,11 +531,16 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 f32x16 acc = f32x16{};
+                if constexpr (F8) {
+                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lds_read_vt_f8<D, 1>(Vt, db, lane), pf8, acc,
+                                                                          0, 0, 0, 127, 0, scb);
+                } else {
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 a = lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane);
-                    acc = mfma32(a, pb[ks], acc);
-                    if constexpr (SPLIT) acc = mfma32(a, pbl[ks], acc);
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const bf16x8 a = lds_read_tr_operand<D>(Vt, ks * 16, db * 32, lane);
+                        acc = mfma32(a, pb[ks], acc);
+                        if constexpr (SPLIT) acc = mfma32(a, pbl[ks], acc);
+                    }
                 }
                 stage_acc_block<D>(Ot, acc, db, norm, l32, g);
                 if (MODE == JFA && res) store_resid_block<D>(Rs, irow, acc, db, norm, g);
@@ -535,7 +579,7 @@ static hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, bool lo
     if (!long_units) return hipGetLastError();
     t.begin(K_FWD, stream);
     if (few_q)  // every unit is one block of <= 32 shared query rows
-        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, 32, SPLIT, MX>), dim3(8 * cus), dim3(WAVE), 0, stream,
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, FEW_Q_KV_TILE, SPLIT, MX>), dim3(8 * cus), dim3(WAVE), 0, stream,
                            t.with_busy(p, K_FWD));
     else
         hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE, SPLIT, MX>), dim3(2 * cus), dim3(4 * WAVE), 0, stream,

@@ -50,6 +50,7 @@ struct PlanParams {
     int inner_rows;  // rows per inner-loop step (cost unit)
     int only_short;  // PLAN_SAMPLES: keep samples with lk <= FUSED_MAX_LK; PLAN_KV/Q: skip them (1) or not (0)
     int window;      // sliding window (0: none)
+    int stable;      // tile lists: 1 = ties in cost keep sample order (a function of the offsets alone)
     int2 *tiles;     // out: (sample, tile) pairs, most expensive first
     int max_tiles;
     PlanCounters *counters;
@@ -191,6 +192,7 @@ const KernelTimer &kernel_timer();
 // cus: compute units; few_q: every sample has one shared block of <= 32 query
 // rows (q_offsets NULL, lq_fixed <= FEW_Q_ROWS), planned as 32-row query tiles.
 constexpr int FEW_Q_ROWS = 32;
+constexpr int FEW_Q_KV_TILE = 64;  // key tile of those units
 // long_units: launch the long-sequence kernels (false when no sample has more
 // than FUSED_MAX_LK keys, so only the short-K/V units have work).
 hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, bool long_units,

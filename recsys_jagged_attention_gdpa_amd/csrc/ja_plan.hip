@@ -18,11 +18,14 @@
 // dispatch: the persistent attention kernels pull units in this order from an
 // atomic cursor, so every workgroup takes the most expensive unit left.
 //
-// One workgroup of 1024 threads; all state in LDS.  The list only orders the
-// work: every output tile is owned by exactly one unit, so the attention
-// results do not depend on the order or on which workgroup runs a unit.  The
-// tile lists are nevertheless a pure function of the offsets (ties in cost keep
-// sample order), since the bias-table gradient's summation order follows them.
+// One workgroup of 1024 threads per list; all state in LDS.  The list only
+// orders the work: every output tile is owned by exactly one unit, so the
+// attention results do not depend on the order or on which workgroup runs a
+// unit, and samples of equal cost take their places by LDS atomics.  The list
+// of the bias-table gradient is the exception (PlanParams::stable): its
+// summation order follows the list, so there ties in cost keep sample order, by
+// a stable radix sort of each chunk of samples, and the list is a function of
+// the offsets alone.
 #include "ja_device.h"
 #include "ja_kernels.h"
 
@@ -148,6 +151,74 @@ __device__ void for_each_run(const PlanParams &p, const PlanSample &s, F fn) {
     }
 }
 
+// Exclusive prefix sum of v over the workgroup's threads (in thread order);
+// *total receives the sum.  Every thread must call it (it synchronises).
+__device__ int block_scan_excl(int v, int *wave_tot, int *total) {
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+    int incl = v;
+    for (int d = 1; d < WAVE; d <<= 1) {
+        const int o = __shfl_up(incl, d, WAVE);
+        if (lane >= d) incl += o;
+    }
+    __syncthreads();  // wave_tot free for reuse
+    if (lane == WAVE - 1) wave_tot[wv] = incl;
+    __syncthreads();
+    if (wv == 0) {
+        int x = lane < PLAN_THREADS / WAVE ? wave_tot[lane] : 0;
+        for (int d = 1; d < PLAN_THREADS / WAVE; d <<= 1) {
+            const int o = __shfl_up(x, d, WAVE);
+            if (lane >= d) x += o;
+        }
+        if (lane < PLAN_THREADS / WAVE) wave_tot[lane] = x;  // inclusive over waves
+    }
+    __syncthreads();
+    *total = wave_tot[PLAN_THREADS / WAVE - 1];
+    return incl - v + (wv > 0 ? wave_tot[wv - 1] : 0);
+}
+
+// Stable sort of one key per thread (keys below 4096) by a least-significant-
+// digit radix sort in LDS, three passes of 4 bits: on return key[k], id[k] hold
+// the k-th smallest key and the thread that contributed it, equal keys in
+// thread order.  Each pass ranks a thread's digit within its wave by ballots
+// and across waves and digits by one prefix sum over the (digit, wave) counts.
+struct SortSpace {
+    int key[2][PLAN_THREADS], id[2][PLAN_THREADS];
+    int cnt[16 * (PLAN_THREADS / WAVE)];  // (digit, wave) counts, digit-major, then their offsets
+};
+__device__ void block_sort12(int my_key, SortSpace &sp, int *wave_tot) {
+    constexpr int NW = PLAN_THREADS / WAVE;
+    static_assert(16 * NW <= PLAN_THREADS, "one (digit, wave) count per thread");
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+    const uint64_t lt = lane ? (~0ull >> (WAVE - lane)) : 0ull;  // lanes below this one
+    int k = my_key, me = tid, buf = 0;
+    for (int shift = 0; shift < 12; shift += 4) {
+        const int dig = (k >> shift) & 15;
+        int rank = 0;
+        for (int d = 0; d < 16; ++d) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(dig == d);
+            if (dig == d) rank = __builtin_popcountll(m & lt);
+            if (lane == d) sp.cnt[d * NW + wv] = __builtin_popcountll(m);
+        }
+        __syncthreads();
+        int total;
+        const int c = tid < 16 * NW ? sp.cnt[tid] : 0;
+        const int off = block_scan_excl(c, wave_tot, &total);
+        if (tid < 16 * NW) sp.cnt[tid] = off;
+        __syncthreads();
+        const int dst = sp.cnt[dig * NW + wv] + rank;
+        sp.key[buf][dst] = k;
+        sp.id[buf][dst] = me;
+        __syncthreads();
+        k = sp.key[buf][tid];
+        me = sp.id[buf][tid];
+        buf ^= 1;
+        __syncthreads();  // counts and this buffer are reused by the next pass
+    }
+    sp.key[0][tid] = k;
+    sp.id[0][tid] = me;
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanBatch batch) {
     const PlanParams &p = batch.list[blockIdx.x];
     __shared__ int hist[PLAN_BUCKETS];
@@ -193,43 +264,51 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanBatch batc
     hist[2 * tid + 1] = excl + a;
     __syncthreads();
 
-    if (grouped(p)) {
+    if (grouped(p) && !p.stable) {
+        for (int b = tid; b < p.B; b += PLAN_THREADS) {
+            const PlanSample s = plan_sample(p, b);
+            if (s.ntiles == 0) continue;
+            int pos = atomicAdd(&hist[sample_bucket_of(sample_cost(p, s))], s.ntiles);
+            for_each_tile_desc(p, s, [&](int t) {
+                if (pos < p.max_tiles) p.tiles[pos] = make_int2(b, t);
+                ++pos;
+            });
+        }
+    } else if (grouped(p)) {
         // Stable placement: within a cost bucket, samples keep their index order,
         // so the list is a function of the offsets alone.  Samples are taken in
-        // chunks of PLAN_THREADS (one per thread) and the chunk's waves in turn;
-        // inside a wave, lanes sharing a bucket get their positions from a prefix
-        // sum of their tile counts, one distinct bucket at a time.
+        // chunks of PLAN_THREADS (one per thread): the chunk is sorted by bucket,
+        // stably, and each sample's position is its bucket's running start plus the
+        // tiles of the bucket's earlier samples (a prefix sum in sorted order).
+        __shared__ SortSpace sp;
+        __shared__ int s_nt[PLAN_THREADS];
+        __shared__ int s_seg[PLAN_BUCKETS + 1];
         for (int c0 = 0; c0 < p.B; c0 += PLAN_THREADS) {
             const int b = c0 + tid;
             const PlanSample s = b < p.B ? plan_sample(p, b) : PlanSample{0, 0, 0};
-            const int bk = s.ntiles > 0 ? sample_bucket_of(sample_cost(p, s)) : -1;
-            int pos = 0;
-            for (int w = 0; w < PLAN_THREADS / WAVE; ++w) {
-                if (wv == w) {
-                    uint64_t todo = __builtin_amdgcn_ballot_w64(bk >= 0);
-                    while (todo) {
-                        const int leader = __builtin_ctzll(todo);
-                        const int key = __shfl(bk, leader, WAVE);
-                        const bool mine = bk == key;
-                        int incl = mine ? s.ntiles : 0;
-                        for (int d = 1; d < WAVE; d <<= 1) {
-                            const int o = __shfl_up(incl, d, WAVE);
-                            if (lane >= d) incl += o;
-                        }
-                        const int base = hist[key];  // read by every lane before the update below
-                        if (mine) pos = base + incl - s.ntiles;
-                        const int total = __shfl(incl, WAVE - 1, WAVE);
-                        if (lane == leader) hist[key] = base + total;
-                        todo &= ~__builtin_amdgcn_ballot_w64(mine);
-                    }
-                }
-                __syncthreads();
-            }
-            if (bk >= 0)
-                for_each_tile_desc(p, s, [&](int t) {
-                    if (pos < p.max_tiles) p.tiles[pos] = make_int2(b, t);
+            const int bk = s.ntiles > 0 ? sample_bucket_of(sample_cost(p, s)) : PLAN_BUCKETS;  // none: last
+            s_nt[tid] = s.ntiles;
+            block_sort12(bk, sp, wave_tot);
+            const int key = sp.key[0][tid], src = sp.id[0][tid];
+            const int nt = s_nt[src];
+            int total;
+            const int excl = block_scan_excl(nt, wave_tot, &total);
+            const bool head = tid == 0 || sp.key[0][tid - 1] != key;
+            const bool tail = tid == PLAN_THREADS - 1 || sp.key[0][tid + 1] != key;
+            if (head) s_seg[key] = excl;
+            __syncthreads();
+            const int pos0 = key < PLAN_BUCKETS ? hist[key] + excl - s_seg[key] : 0;
+            __syncthreads();  // every thread has read its bucket's start
+            if (tail && key < PLAN_BUCKETS) hist[key] += excl + nt - s_seg[key];
+            if (key < PLAN_BUCKETS) {
+                const PlanSample t = plan_sample(p, c0 + src);
+                int pos = pos0;
+                for_each_tile_desc(p, t, [&](int tt) {
+                    if (pos < p.max_tiles) p.tiles[pos] = make_int2(c0 + src, tt);
                     ++pos;
                 });
+            }
+            __syncthreads();  // hist, s_nt and the sort space are reused by the next chunk
         }
     } else {
         for (int b = tid; b < p.B; b += PLAN_THREADS) {

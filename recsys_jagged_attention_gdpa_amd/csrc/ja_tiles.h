@@ -612,6 +612,136 @@ struct F8WaveTile {
     }
 };
 
+// ------------------------------------------ fp8 PV product (P in FP8 E4M3)
+// O^T += V^T P^T on the block-scaled fp8 MFMA, 64 keys (two 32-key blocks) per
+// instruction and 32 head-dimension rows per output block.  The MFMA takes one
+// scale per (operand row or column, 32-key block); MXFP8 values carry theirs per
+// (key, 32-element block of the head dimension), which varies along the key
+// axis the product sums over.  So each value row is first re-encoded to one
+// exponent per key: S_j = the largest of the row's block scale codes, every
+// code c of block b becoming the E4M3 value nearest to value(c) * 2^(s_jb - S_j)
+// (exact unless it lands below the normal range).  The value operand then takes
+// unit scales, and P takes the key's scale: P'_ij = P_ij * 2^(S_j - 127), encoded
+// as E4M3 (nearest, ties to even) against one power-of-two scale per (query,
+// 32-key block) that puts the block's largest |P'| in [128, 256).
+
+// Value rows of a tile staged as re-encoded codes: load() issues the reads of
+// 16 codes and the row's scale codes per piece, store() re-encodes them into a
+// code tile (f8_off layout) and writes each row's S_j into s_row[row].
+template <int ROWS, int D, int NT>
+struct F8VLoader {
+    static constexpr int PIECES = ROWS * D / 16;
+    static constexpr int PER_THREAD = (PIECES + NT - 1) / NT;
+    static_assert(PIECES % NT == 0 || PIECES < NT, "tile / thread count mismatch");
+    u32x4 c[PER_THREAD];
+    uint32_t sc[PER_THREAD];  // the row's D / 32 scale codes, byte b for block b
+    __device__ __forceinline__ void load(const MXSlice<D> &S, int r0, int tid) {
+#pragma unroll
+        for (int it = 0; it < PER_THREAD; ++it) {
+            const int q = tid + it * NT;
+            const bool ok = q < PIECES;
+            const int r = r0 + q / (D / 16);
+            const uint32_t oc = ok ? (uint32_t)r * S.row_bytes + (uint32_t)(q % (D / 16)) * 16u : OOB;
+            const uint32_t os = ok ? (uint32_t)r * S.srow_bytes : OOB;
+            c[it] = __builtin_amdgcn_raw_buffer_load_b128(S.c, (int)oc, 0, 0);
+            if constexpr (D == 128) sc[it] = __builtin_amdgcn_raw_buffer_load_b32(S.s, (int)os, 0, 0);
+            else sc[it] = __builtin_amdgcn_raw_buffer_load_b16(S.s, (int)os, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void store(lchar *tile, lu8 *s_row, int tid) const {
+#pragma unroll
+        for (int it = 0; it < PER_THREAD; ++it) {
+            const int q = tid + it * NT;
+            if (PIECES % NT != 0 && q >= PIECES) continue;
+            const int r = q / (D / 16), pc = q % (D / 16);
+            const uint32_t w = sc[it];
+            uint32_t smax = w & 255u, sb = (w >> (8 * (pc >> 1))) & 255u;
+#pragma unroll
+            for (int b = 1; b < D / 32; ++b) smax = max(smax, (w >> (8 * b)) & 255u);
+            u32x4 v = c[it];
+            if (smax - sb >= 20u) {
+                v = u32x4{};  // every |value| * 2^(sb - smax) <= 448 * 2^-20 rounds to zero
+            } else if (sb != smax) {
+                // value(c) * 2^(sb - smax): exact products, then nearest E4M3
+                const float f = __builtin_bit_cast(float, (127u - (smax - sb)) << 23);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    typedef float f32x2 __attribute__((ext_vector_type(2)));
+                    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[k], f, false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[k], f, true);
+                    int o = __builtin_amdgcn_cvt_pk_fp8_f32(lo[0], lo[1], 0, false);
+                    o = __builtin_amdgcn_cvt_pk_fp8_f32(hi[0], hi[1], o, true);
+                    v[k] = (uint32_t)o;
+                }
+            }
+            lds_write16(tile, f8_off<D>(r, pc), v);
+            if (pc == 0) s_row[r] = (uint8_t)smax;
+        }
+    }
+};
+
+// V^T operand (head-dimension block db: row db*32 + l % 32) of the fp8 PV
+// product from a code tile of NKB (1 or 2) 32-key blocks, by transposing reads
+// (ds_read_b64_tr_b8: within each group of 16 lanes, lane i receives byte i % 8
+// of the 8-byte pieces addressed by lanes 2j + i / 8, j = 0 .. 7; checked on the
+// hardware).  Lane half g gets keys crow(e, g), e = 0 .. 15, of each block in
+// byte order e: the order of the P^T operand built from the score accumulator.
+// A missing second block reads as zero codes.
+template <int D, int NKB>
+__device__ __forceinline__ i32x8 lds_read_vt_f8(const lchar *tile, int db, int lane) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) i32x2 li32x2;
+    const int s = lane & 15, G = lane >> 4, g = G >> 1;
+    const int c = 2 * db + (G & 1), half = (s & 1) * 8;
+    i32x8 out = i32x8{};
+#pragma unroll
+    for (int r = 0; r < 2 * NKB; ++r) {
+        const int row = (r >> 1) * 32 + crow(8 * (r & 1) + (s >> 1), g);
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((li32x2 *)(tile + f8_off<D>(row, c) + half));
+        out[2 * r] = v[0];
+        out[2 * r + 1] = v[1];
+    }
+    return out;
+}
+
+// One 32-key block of the P^T operand of the fp8 PV product: a lane's 16 P
+// values (query l % 32, keys crow(e, g) of the block) and the block's per-key
+// scale codes s_row[0 .. 31] give 16 E4M3 codes in byte order e; the return
+// value is the block's E8M0 scale code (the same in both lane halves; unit
+// when every P' of the block is zero).
+__device__ __forceinline__ int encode_p_block(const float (&pv)[16], const lu8 *s_row, int g, u32x4 &codes) {
+    typedef __attribute__((address_space(3))) const uint32_t lcu32;
+    // scale codes of keys crow(4q .. 4q + 3, g), one dword per q
+    auto sk = [&](int q, int t) {
+        const uint32_t w = *(lcu32 *)(s_row + q * 8 + g * 4);
+        return (int)((w >> (8 * t)) & 255u) - 127;
+    };
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, __builtin_fabsf(__builtin_ldexpf(pv[e], sk(e >> 2, e & 3))));
+    m = pair_max(m);  // the block's other 16 keys sit in lane ^ 32
+    // largest |P'| = f * 2^k, f in [0.5, 1): scale 2^(k - 8) puts it in [128, 256)
+    const int e8 = __builtin_amdgcn_frexp_expf(m) - 8 + 127;
+    const int ex = m > 0.0f ? min(max(e8, 1), 254) : 127;
+    const int sh = 127 - ex;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(pv[4 * q], sk(q, 0) + sh),
+                                                __builtin_ldexpf(pv[4 * q + 1], sk(q, 1) + sh), 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(pv[4 * q + 2], sk(q, 2) + sh),
+                                            __builtin_ldexpf(pv[4 * q + 3], sk(q, 3) + sh), w, true);
+        codes[q] = (uint32_t)w;
+    }
+    return ex;
+}
+
+// The P^T operand from its blocks: bytes 0-15 block 0, 16-31 block 1 (zero
+// codes when there is one block); this lane's scale operand is the code of
+// block g.
+__device__ __forceinline__ i32x8 p_f8_operand(const u32x4 &b0, const u32x4 &b1) {
+    return i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+}
+
 // WaveTile for an MXFP8 slice: 32 rows read as codes by one wave, decoded when
 // written to the LDS tile.
 template <int D>

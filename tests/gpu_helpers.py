@@ -5,8 +5,10 @@ import numpy as np
 import torch
 
 import recsys_jagged_attention_gdpa_amd as ja
-from tests.helpers import (oracle_bwd, oracle_fwd, row_check, softmax_cancel_rows,
-                           structural_zero_rows)
+from oracle import mx
+from recsys_jagged_attention_gdpa_amd import synth
+from tests.helpers import (fp8_pv, fp8_pv_check, oracle_bwd, oracle_fwd, oracle_fwd_fp8_pv, row_check,
+                           softmax_cancel_rows, structural_zero_rows)
 
 TAU = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
 
@@ -83,6 +85,48 @@ def check_lse(got_hq, want_th, what="lse", tol=1e-3):
     if fin.any():
         err = np.abs(g[fin] - want_th[fin]) / np.maximum(1.0, np.abs(want_th[fin]))
         assert err.max() <= tol, f"{what}: max |dLSE| / max(1, |LSE|) {err.max():.3e} > {tol}"
+
+
+def mx_parity(w, *, label="", max_kv_len=0, o_floor_frac=1e-6, emulate=True):
+    """Forward parity of an MXFP8 workload: with P in FP8 on the GPU (D = 64 or 128)
+    against the oracle that encodes P the same way (fp8_pv_check), else (D = 32, P
+    in bf16) as parity() against plain attention of the decoded values.
+    emulate=False (JFA only): scores so large that their fp32 rounding moves P by
+    far more than E4M3 midpoints are apart, so the encoding choices are not the
+    oracle's to predict; O is held instead to the encoding's error bound around
+    plain attention, |O - O_plain| <= 2^-4 sum_j P_ij |V_j| / l_i (plain attention
+    of |V|) plus tau of the row."""
+    if not fp8_pv(w):
+        return parity(w, backward=False, label=label, max_kv_len=max_kv_len, o_floor_frac=o_floor_frac)
+    if not emulate:
+        assert w.mode == "jfa", "the |V| bound needs weights of one sign"
+        d = to_dev(w)
+        d["max_kv_len"] = max_kv_len
+        got = gpu_fwd(w, d)
+        torch.cuda.synchronize()
+        want = oracle_fwd(w)
+        absv = torch.from_numpy(np.abs(mx.decode_f32(w.v.numpy(), w.mx_scales["v"].numpy())))
+        env = oracle_fwd(synth.Workload(**{**w.__dict__, "mx": ("q", "k"), "v": absv}))["o"]
+        g, r = np64(got["o"]), want["o"]
+        row_max = np.abs(r).max(axis=-1, keepdims=True)
+        excess = np.abs(g - r) - (2.0 ** -4 * env + TAU[w.dtype] * row_max)
+        announce(f"{label} O within the encoding bound: worst excess {float(excess.max()):.3e}")
+        assert (excess <= 0).all(), float(excess.max())
+        check_lse(np64(got["lse"]), want["lse"], f"{label} LSE")
+        return {}
+    tau = TAU[w.dtype]
+    announce(f"{label} (P in FP8) mode={w.mode} B={w.B} H={w.H} D={w.D} causal={w.causal} bias={w.bias_kind} "
+             f"act={w.act} window={w.window} Tq={w.total_q} Tk={w.total_k} max_kv_len={max_kv_len}")
+    d = to_dev(w)
+    d["max_kv_len"] = max_kv_len
+    got = gpu_fwd(w, d)
+    torch.cuda.synchronize()
+    want = oracle_fwd_fp8_pv(w)
+    zq_out, _, _ = structural_zero_rows(w)
+    rep = {"o": fp8_pv_check(np64(got["o"]), want["o"], want["flip"], tau, f"{label} O", zero_rows=zq_out)}
+    if w.mode == "jfa":
+        check_lse(np64(got["lse"]), want["lse"], f"{label} LSE")
+    return rep
 
 
 def parity(w, *, backward=True, tau=None, label="", max_kv_len=0, o_floor_frac=1e-6):

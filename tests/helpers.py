@@ -37,6 +37,57 @@ def oracle_fwd(w, nthreads=0):
     return {"o": o, "lse": lse}
 
 
+def fp8_pv(w):
+    """Whether the HIP path forms P V with P in FP8: MXFP8 inputs with D = 64 or 128."""
+    return bool(w.mx) and w.D >= 64
+
+
+def oracle_fwd_fp8_pv(w):
+    """The oracle forward with P in FP8 (oracle/mx.py, fwd_fp8_pv) for an MXFP8
+    workload: O, for JFA the LSE, and per row the bound of one encoding step of
+    its largest P term ('flip', [T, H])."""
+    q, k, _ = inputs(w)
+    o, lse, flip = mx.fwd_fp8_pv(w.mode, np.asarray(q), np.asarray(k), w.v.numpy(), w.mx_scales["v"].numpy(),
+                                 w.q_off, w.kv_off, scale=w.scale, act=w.act, lq_fixed=w.lq_fixed,
+                                 causal=w.causal, window=w.window, bias_kind=w.bias_kind,
+                                 bias_table=None if w.bias_table is None else w.bias_table.numpy(),
+                                 bias_lo=w.bias_lo, bias_hi=w.bias_hi)
+    return {"o": o, "lse": lse, "flip": flip} if w.mode == "jfa" else {"o": o, "flip": flip}
+
+
+def fp8_pv_check(got, want, flip, tau, what="", zero_rows=None, max_flip_frac=1e-3):
+    """O rows against the oracle with P in FP8: max_d |got - want| <= tau * max_d |want|
+    on every row but a few.  The GPU encodes P from its fp32 value, so a P element
+    lying within fp32 rounding of an E4M3 midpoint may land one step from the
+    oracle's choice; a row may carry two such steps (flip_r bounds one), and rows
+    that need them are counted: at most max(2, max_flip_frac of the rows).  Rows in
+    zero_rows must be exactly zero."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if want.size == 0:
+        return {"rows": 0, "flipped": 0}
+    g = got.reshape(-1, got.shape[-1])
+    r = want.reshape(-1, want.shape[-1])
+    fl = np.asarray(flip, dtype=np.float64).reshape(-1)
+    assert np.isfinite(g).all(), f"{what}: non-finite values in the GPU result"
+    err = np.abs(g - r).max(axis=1)
+    ref_max = np.abs(r).max(axis=1)
+    zero = np.zeros(len(err), dtype=bool) if zero_rows is None else np.asarray(zero_rows).reshape(-1)
+    assert not (zero & (ref_max != 0)).any(), f"{what}: oracle row expected zero is not"
+    assert not (zero & (np.abs(g).max(axis=1) != 0)).any(), f"{what}: rows expected zero are not"
+    plain = err <= tau * ref_max
+    flipped = ~plain & ~zero
+    ok_flip = err <= tau * ref_max + 2.0 * fl
+    worst = int(np.argmax(np.where(zero, 0.0, err / np.maximum(tau * ref_max + 2.0 * fl, 1e-300))))
+    n_flip = int(flipped.sum())
+    print(f"[fp8-pv check] {what}: rows {len(err)}, rows needing an encoding step {n_flip}", flush=True)
+    assert (ok_flip | zero).all(), (f"{what}: row {worst} err {err[worst]:.3e} ref max {ref_max[worst]:.3e} "
+                                    f"flip {fl[worst]:.3e}")
+    assert n_flip <= max(2, math.ceil(max_flip_frac * len(err))), f"{what}: {n_flip} rows needed an encoding step"
+    return {"rows": len(err), "flipped": n_flip}
+
+
 # Unit roundoffs the kernels work with: dX enters the dQ / dK products as bf16 (fp32
 # for fp32 tensors); JFA's delta comes from O held to 16 bits (bf16 output plus its
 # bf16 residual; fp32 O for fp32 tensors).

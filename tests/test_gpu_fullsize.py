@@ -13,8 +13,8 @@ import torch
 
 from recsys_jagged_attention_gdpa_amd import synth
 from tests.gpu_helpers import TAU, announce, check_lse, gpu_bwd, gpu_fwd, np64, to_dev
-from tests.helpers import (oracle_bwd, oracle_fwd, row_check, softmax_cancel_rows,
-                           structural_zero_rows)
+from tests.helpers import (fp8_pv, fp8_pv_check, oracle_bwd, oracle_fwd, oracle_fwd_fp8_pv, row_check,
+                           softmax_cancel_rows, structural_zero_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,12 +65,17 @@ def test_full_size_sampled_slices(name, n_random):
     tau = TAU[w.dtype]
     for b, h in picks:
         ws = _single_head(w, b, h)
-        want = oracle_fwd(ws)
         o0 = b * w.lq_fixed if w.q_off is None else int(w.q_off[b])
         n = int(ws.total_q_out)
         zq_out, zq_in, zk = structural_zero_rows(ws)
-        row_check(np64(out["o"][o0:o0 + n, h:h + 1]), want["o"], tau, f"{name} b={b} h={h} O",
-                  zero_rows=zq_out)
+        if fp8_pv(ws):  # MXFP8 with P in FP8: the oracle encodes P the same way
+            want = oracle_fwd_fp8_pv(ws)
+            fp8_pv_check(np64(out["o"][o0:o0 + n, h:h + 1]), want["o"], want["flip"], tau,
+                         f"{name} b={b} h={h} O", zero_rows=zq_out)
+        else:
+            want = oracle_fwd(ws)
+            row_check(np64(out["o"][o0:o0 + n, h:h + 1]), want["o"], tau, f"{name} b={b} h={h} O",
+                      zero_rows=zq_out)
         if w.mode == "jfa":
             check_lse(np64(out["lse"][h:h + 1, o0:o0 + n]), want["lse"], f"{name} b={b} h={h} LSE")
         if "dq" in out:

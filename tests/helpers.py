@@ -55,13 +55,16 @@ def oracle_fwd_fp8_pv(w):
     return {"o": o, "lse": lse, "flip": flip} if w.mode == "jfa" else {"o": o, "flip": flip}
 
 
-def fp8_pv_check(got, want, flip, tau, what="", zero_rows=None, max_flip_frac=1e-3):
+def fp8_pv_check(got, want, flip, tau, what="", zero_rows=None, max_flip_frac=5e-3):
     """O rows against the oracle with P in FP8: max_d |got - want| <= tau * max_d |want|
     on every row but a few.  The GPU encodes P from its fp32 value, so a P element
-    lying within fp32 rounding of an E4M3 midpoint may land one step from the
+    lying within that value's error of an E4M3 midpoint may land one step from the
     oracle's choice; a row may carry two such steps (flip_r bounds one), and rows
-    that need them are counted: at most max(2, max_flip_frac of the rows).  Rows in
-    zero_rows must be exactly zero."""
+    that need them are counted.  The fp32 activation (hardware exp2 and reciprocal)
+    is good to ~1e-6 relative and E4M3 midpoints are 2^-4 to 2^-3 apart, so about
+    one element in 10^4 to 10^5 can land on the other side: at most max(4,
+    max_flip_frac of the rows) rows may need a step (a planted error shows in far
+    more rows, or beyond two steps).  Rows in zero_rows must be exactly zero."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
@@ -84,7 +87,7 @@ def fp8_pv_check(got, want, flip, tau, what="", zero_rows=None, max_flip_frac=1e
     print(f"[fp8-pv check] {what}: rows {len(err)}, rows needing an encoding step {n_flip}", flush=True)
     assert (ok_flip | zero).all(), (f"{what}: row {worst} err {err[worst]:.3e} ref max {ref_max[worst]:.3e} "
                                     f"flip {fl[worst]:.3e}")
-    assert n_flip <= max(2, math.ceil(max_flip_frac * len(err))), f"{what}: {n_flip} rows needed an encoding step"
+    assert n_flip <= max(4, math.ceil(max_flip_frac * len(err))), f"{what}: {n_flip} rows needed an encoding step"
     return {"rows": len(err), "flipped": n_flip}
 
 

@@ -443,7 +443,7 @@ def main():
     if args.balance:
         # one more step, outside the timed region, with every persistent kernel's
         # workgroups stamping their busy cycles
-        persistent = [k for k in ("fwd", "fwd_short", "bwd_kv", "bwd_q", "bwd_fused") if k in names]
+        persistent = [k for k in ("fwd", "fwd_short", "bwd_kv", "bwd_q", "bwd_fused", "bwd_dbias") if k in names]
         bufs = {k: torch.zeros(8192, dtype=torch.int64, device="cuda") for k in persistent}
         for k in persistent:
             _lib.ja_profile_busy(k, bufs[k])

@@ -281,7 +281,8 @@ ja_status ja_profile_kernel(int kernel_id, void *start_event, void *stop_event);
 
 /* Measurement aid for the work scheduler: from now on, in every call made by the
  * calling thread, each workgroup of kernel `kernel_id` (one of the persistent
- * attention kernels: JA_KERNEL_FWD, _FWD_SHORT, _BWD_KV, _BWD_Q, _BWD_FUSED) writes
+ * attention kernels: JA_KERNEL_FWD, _FWD_SHORT, _BWD_KV, _BWD_Q, _BWD_FUSED, and the
+ * first kernel of JA_KERNEL_BWD_DBIAS) writes
  * the shader clock cycles from its start to its exit (after its last unit) into
  * device_buffer[workgroup] (uint64, `capacity` entries; workgroups past it write
  * nothing).  Busy time max / mean over the workgroups measures the load balance.

@@ -9,7 +9,7 @@
 // there, so this is the plain derivative of that additive term.
 //
 // One pass over (sample, 128-query tile, head) units recomputes S = QK^T and
-// dP = dO V^T per 64-key tile on the matrix cores (as the dQ units do) and
+// dP = dO V^T per 32-key tile on the matrix cores (as the dQ units do) and
 // forms dX; each wave then stages its 32 x 32 blocks of dX in LDS and sums
 // them along diagonals (REL) or columns (KEYPOS) into its own row of per-entry
 // sums in LDS.  Blocks whose positions all clamp to one end of the table (far
@@ -38,9 +38,14 @@ __device__ __forceinline__ float wave_sum_fixed(float v) {
     return v;
 }
 
+// Key tiles of 32 rows keep a workgroup's LDS (tiles, staging blocks and the
+// four per-wave rows of W sums, sized at launch) within half the CU's for
+// tables of up to ~1,300 entries, so two workgroups share a CU.
+constexpr int DBIAS_BN = 32;
+
 template <int D, int MODE, int ACT>
-__global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParams p) {
-    constexpr int BN = KV_TILE;
+__global__ __launch_bounds__(DBIAS_THREADS, 2) void dbias_kernel(const AttnParams p) {
+    constexpr int BN = DBIAS_BN;
     constexpr int BM = Q_TILE;
     constexpr int TILE_BYTES = BN * D * 2;
     constexpr int NKK = D / 16, NNB = BN / 32;
@@ -48,7 +53,7 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
     static_assert(WIN <= DBIAS_THREADS, "one bias window entry per thread");
     __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
     __shared__ float s_bias[2][WIN];
-    __shared__ float s_bins[4][DBIAS_MAX_BINS];
+    extern __shared__ float s_bins[];  // four rows of W sums, one per wave (dynamic: 16 W bytes)
     __shared__ float s_scr[4][32 * SCR_STRIDE];
     lchar *const lbase = (lchar *)smem;
 
@@ -59,9 +64,9 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
     const int W = bz.width;
     const int n_units = p.counters4->units;
-    float *bins = s_bins[wv];
+    float *bins = s_bins + wv * W;
     float *scr = s_scr[wv];
-    for (int c = tid; c < 4 * DBIAS_MAX_BINS; c += DBIAS_THREADS) (&s_bins[0][0])[c] = 0.0f;
+    for (int c = tid; c < 4 * W; c += DBIAS_THREADS) s_bins[c] = 0.0f;
 
     // Partial row (workgroup, head hh) of the output sums.
     auto part_row = [&](int hh) { return p.dbias_part + ((int64_t)blockIdx.x * H + hh) * W; };
@@ -72,8 +77,8 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
         if (hh >= 0) {
             float *row = part_row(hh);
             for (int c = tid; c < W; c += DBIAS_THREADS) {
-                row[c] = ((s_bins[0][c] + s_bins[1][c]) + s_bins[2][c]) + s_bins[3][c];
-                s_bins[0][c] = s_bins[1][c] = s_bins[2][c] = s_bins[3][c] = 0.0f;
+                row[c] = ((s_bins[c] + s_bins[W + c]) + s_bins[2 * W + c]) + s_bins[3 * W + c];
+                s_bins[c] = s_bins[W + c] = s_bins[2 * W + c] = s_bins[3 * W + c] = 0.0f;
             }
         }
         for (int z = hh + 1; z < h_next; ++z) {
@@ -83,6 +88,7 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
         __syncthreads();
     };
 
+    const uint64_t busy_t0 = busy_start(p.busy);
     int h_cur = -1;
     for (int w = blockIdx.x; w < n_units; w += gridDim.x) {
         const UnitRef u = tile_unit(p.tiles4, w, n_units, H);
@@ -251,6 +257,7 @@ __global__ __launch_bounds__(DBIAS_THREADS, 1) void dbias_kernel(const AttnParam
         }
     }
     flush(h_cur, H);
+    busy_end(p.busy, p.busy_cap, busy_t0);
 }
 
 // dbias[h][c] = sum over workgroups g (in order) of partial row (g, h), entry c.
@@ -269,7 +276,8 @@ static hipError_t launch_dbias_t(const AttnParams &p, hipStream_t st) {
     const int64_t n = (int64_t)p.H * W;
     const KernelTimer &t = kernel_timer();
     t.begin(K_BWD_DBIAS, st);
-    hipLaunchKernelGGL((dbias_kernel<D, MODE, ACT>), dim3(DBIAS_GRID), dim3(DBIAS_THREADS), 0, st, p);
+    hipLaunchKernelGGL((dbias_kernel<D, MODE, ACT>), dim3(DBIAS_GRID), dim3(DBIAS_THREADS),
+                       (size_t)4 * W * sizeof(float), st, t.with_busy(p, K_BWD_DBIAS));
     hipLaunchKernelGGL(dbias_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        (const float *)p.dbias_part, p.dbias, p.H, W, DBIAS_GRID);
     t.end(K_BWD_DBIAS, st);

@@ -14,7 +14,7 @@ constexpr int KV_TILE = 64;
 constexpr int BWD_KV_UNIT = 128;   // keys owned by one dK/dV unit
 constexpr int BWD_Q_STEP = 128;    // queries per inner step of a dK/dV unit
 constexpr int FUSED_MAX_LK = 32;   // samples with at most this many keys use the fused backward unit
-constexpr int DBIAS_GRID = 256;    // workgroups of the bias-gradient pass (fixed: fixes the summation order)
+constexpr int DBIAS_GRID = 512;    // workgroups of the bias-gradient pass (fixed: fixes the summation order)
 constexpr int DBIAS_MAX_BINS = 4096;  // largest bias table row the gradient pass takes
 
 // The chip's accelerator dies (XCDs), each with its own L2.

@@ -107,11 +107,12 @@ struct PairSliceLoader {
 template <int ROWS, int D, int NT>
 __device__ __forceinline__ void dma_tile(lchar *tile, const HeadSlice<D> &S, int r0, int tid) {
     constexpr int CH = D / 8, SLOTS = ROWS * CH, PER_INSTR = NT / WAVE * WAVE;
-    static_assert(SLOTS % NT == 0, "tile / thread count mismatch");
+    static_assert(SLOTS % NT == 0 || (SLOTS < NT && SLOTS % WAVE == 0), "tile / thread count mismatch");
     const int wv = tid / WAVE, lane = tid % WAVE;
 #pragma unroll
-    for (int it = 0; it < SLOTS / NT; ++it) {
+    for (int it = 0; it < (SLOTS >= NT ? SLOTS / NT : 1); ++it) {
         const int first = it * PER_INSTR + wv * WAVE;  // first slot of this wave's instruction
+        if (SLOTS < NT && first >= SLOTS) break;       // a small tile: only the first waves copy
         const int q = first + lane;
         const int r = q / CH, c = (q % CH) ^ swz<D>(r);
         buf_load16_lds(S.r, tile + first * 16, (uint32_t)(r0 + r) * S.row_bytes + (uint32_t)c * 16u);

@@ -192,11 +192,6 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             load_tile(jt + 1);  // past the last tile: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);
 
-            // The matrix-core stages run at raised wave priority, so when the two
-            // waves sharing a SIMD are in different stages the one issuing MFMAs
-            // goes first and the other's element-wise work fills the MFMA latency
-            // (measured: forward -2 % on the JFA workload).
-            __builtin_amdgcn_s_setprio(1);
             // S^T block per 32 keys: lane holds query irow, keys crow(e, g).
             f32x16 sacc[NNB];
 #pragma unroll
@@ -218,7 +213,6 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                 }
             }
 
-            __builtin_amdgcn_s_setprio(0);
             // Element-wise stage.  A tile needs per-element masking only when it
             // crosses the key end, (causal) the diagonal or (window) the window
             // start of this wave's rows; that test and the bias kind are
@@ -315,7 +309,6 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                 }
             }
 
-            __builtin_amdgcn_s_setprio(1);
             // O^T += V^T P^T over the tile's keys.
             if constexpr (F8S) {
                 const i32x8 bop = p_f8_operand(pf8[0], pf8[1]);
@@ -337,7 +330,6 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                 }
             }
 
-            __builtin_amdgcn_s_setprio(0);
             store_tile((jt + 1) & 1);
             __syncthreads();
         }

@@ -197,21 +197,25 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
                     sacc = mfma32(lds_read16(Kt, off), qreg[kk], sacc);
                     dpacc = mfma32(lds_read16(Vt, off), greg[kk], dpacc);
                 }
+                // JFA: the exponent x + bias - LSE (log2 units); without a bias the
+                // scale and -LSE fold into one FMA
                 if (bz.kind) {
                     // raw window: entry (i0 + BM - 1 - irow) + (j - j0) (REL) or j - j0 (KEYPOS)
                     const int bbase = (bz.kind == BIAS_REL ? BM - 1 - wv * 32 - l32 : 0) + g * 4 + nb * 32;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
+                    for (int e = 0; e < 16; ++e) {
                         sacc[e] = __builtin_fmaf(sacc[e], sl, bwin[bbase + (e >> 2) * 8 + (e & 3)]);
+                        if constexpr (MODE == JFA) sacc[e] += nl;
+                    }
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) sacc[e] *= sl;
+                    for (int e = 0; e < 16; ++e) sacc[e] = MODE == JFA ? __builtin_fmaf(sacc[e], sl, nl) : sacc[e] * sl;
                 }
                 float dx[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     if constexpr (MODE == JFA) {
-                        dx[e] = fast_exp2(sacc[e] + nl) * (dpacc[e] - dlt);
+                        dx[e] = fast_exp2(sacc[e]) * (dpacc[e] - dlt);
                     } else {
                         float y, dy;
                         act_fwd_grad<ACT>(sacc[e], y, dy);
@@ -378,6 +382,12 @@ __device__ __forceinline__ void dkdv_step(bool masked, int kind, const lchar *Qt
 #pragma unroll
             for (int e = 0; e < 16; ++e) bv[e] = b;
         }
+        if constexpr (MODE == JFA) {
+            // -LSE joins the addend, so P = exp2(fma(s, sl2, addend)); without a bias
+            // the addend is -LSE itself
+#pragma unroll
+            for (int e = 0; e < 16; ++e) bv[e] = kind == BIAS_NONE ? nlv[e >> 2][e & 3] : bv[e] + nlv[e >> 2][e & 3];
+        }
         bf16x8 qa[PFA], ga[PFA], tg[PFB], tq[PFB];
         if (nextA) {
 #pragma unroll
@@ -411,7 +421,7 @@ __device__ __forceinline__ void dkdv_step(bool masked, int kind, const lchar *Qt
             for (int e = k * EPS; e < (k + 1) * EPS; ++e) {
                 const float x = __builtin_fmaf(sa[e], sl, bv[e]);
                 if constexpr (MODE == JFA) {
-                    pv[e] = fast_exp2(x + nlv[e >> 2][e & 3]);
+                    pv[e] = fast_exp2(x);
                     dx[e] = pv[e] * (da[e] - dlv[e >> 2][e & 3]);
                 } else {
                     float dy;

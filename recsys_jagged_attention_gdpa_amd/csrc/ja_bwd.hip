@@ -248,236 +248,6 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
     busy_end(p.busy, p.busy_cap, busy_t0);
 }
 
-// dK/dV step tiles: the query rows and the dO rows of a step interleaved in LDS
-// groups of 1 KB (512 / D rows of one tensor per group, the two tensors
-// alternating), so one address register reaches the same rows of both tensors
-// (dO at +1 KB) and every block of the step through the read's immediate offset.
-template <int D>
-__device__ __forceinline__ int il_off(int r, int c) {
-    constexpr int RPG = 512 / D;
-    return (r / RPG) * 2048 + (r % RPG) * (2 * D) + ((c ^ swz<D>(r)) << 4);
-}
-template <int ROWS, int D, int NT>
-__device__ __forceinline__ void dma_tile_il(lchar *tile, const HeadSlice<D> &S, int r0, int tid) {
-    constexpr int CH = D / 8, SLOTS = ROWS * CH;
-    static_assert(SLOTS % NT == 0, "tile / thread count mismatch");
-    const int wv = __builtin_amdgcn_readfirstlane(tid / WAVE), lane = tid % WAVE;
-#pragma unroll
-    for (int it = 0; it < SLOTS / NT; ++it) {
-        const int first = it * NT + wv * WAVE;  // first slot of this wave's instruction: one 1 KB group
-        const int q = first + lane;
-        const int r = q / CH, c = (q % CH) ^ swz<D>(r);
-        buf_load16_lds(S.r, tile + (first / WAVE) * 2048, (uint32_t)(r0 + r) * S.row_bytes + (uint32_t)c * 16u);
-    }
-}
-
-// One 128-row query step of a dK/dV unit for one wave (32 keys), software
-// pipelined over the step's four 32-row blocks: while the element-wise stage
-// of block qb runs on the vector ALU, the matrix cores compute S and dP of
-// block qb + 1 and the dV / dK products of block qb - 1, whose operands are
-// read from LDS a slot ahead.  Each slot holds two S/dP products, two dV/dK
-// products and 16 / NKK scores of the element-wise stage; the fences keep the
-// slots in order so that the vector work of a slot issues while its products
-// run.
-template <int D, int MODE, int ACT>
-__device__ __forceinline__ void dkdv_step(bool masked, int kind, const lchar *Qt, const float *bwin, const float *nlw,
-                                          const float *dlw, const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
-                                          f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32], float sl, int ia, int shift,
-                                          int jkey, int wv, int l32, int g, int lane, int lq, int causal, int win) {
-    constexpr int BQ = BWD_Q_STEP, BK = BWD_KV_UNIT;
-    constexpr int NKK = D / 16, NDB = D / 32, NB = BQ / 32;
-    constexpr int EPS = 16 / NKK;  // scores of the element-wise stage per slot
-    constexpr int PFA = 2, PFB = 2;  // operand reads run this many slots ahead (a ring of registers)
-    constexpr int RPG = 512 / D;             // rows per 1 KB group
-    constexpr int BLK = 32 / RPG * 2048;     // bytes from one 32-row block to the next
-    constexpr int GO = 1024;                 // dO rows sit 1 KB after the query rows
-    static_assert(2 * NDB == NKK, "a slot pairs one S/dP step with one (ks, db) dV/dK step");
-    // Per-lane addresses of this step's tile: the rows of k-step kk (row reads) and
-    // of column block db (transposing reads, rows x and x + 8 of a 16-row half);
-    // blocks, halves and the dO tensor are immediate offsets from these.  The
-    // empty asm statements make each address opaque, so it is formed once per
-    // step from the buffer base: left visible, the compiler keeps one register per
-    // (block, operand) address across the whole loop and adds the base per read.
-    const lchar *ar[NKK];
-    const lchar *at[2 * NDB];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        ar[kk] = Qt + il_off<D>(l32, 2 * kk + g);
-        asm("" : "+v"(ar[kk]));
-    }
-    {
-        const int l16 = lane & 15, G = lane >> 4;
-        const int x = g * 4 + (l16 >> 2);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const int dcol = db * 32 + ((G & 1) << 4) + ((l16 & 3) << 2);
-            const int c = dcol >> 3, within = (dcol & 7) << 1;
-            at[2 * db] = Qt + il_off<D>(x, c) + within;
-            at[2 * db + 1] = Qt + il_off<D>(x + 8, c) + within;
-            asm("" : "+v"(at[2 * db]));
-            asm("" : "+v"(at[2 * db + 1]));
-        }
-    }
-    // masking: this lane's first query row of the step and its aligned distance
-    // (opaque for the same reason: one register each, not one per score)
-    int i0 = ia + g * 4, d0 = ia + g * 4 + shift - jkey;
-    asm("" : "+v"(i0));
-    asm("" : "+v"(d0));
-    auto rowread = [&](int qb, int kk, int t) { return lds_read16(ar[kk], qb * BLK + t * GO); };
-    // transposed operand (ks, db) of block qb: rows qb*32 + ks*16 .. +15
-    auto trread = [&](int qb, int k, int t) {
-        const int ks = k / NDB, db = k % NDB;
-        const int o = (qb * 32 + ks * 16) / RPG * 2048 + t * GO;
-        const bf16x4 lo = lds_read_tr(at[2 * db], o), hi = lds_read_tr(at[2 * db + 1], o);
-        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-
-    // S and dP of block 0
-    f32x16 sa = f32x16{}, da = f32x16{};
-    {
-        bf16x8 qa[PFA], ga[PFA];
-#pragma unroll
-        for (int k = 0; k < PFA; ++k) {
-            qa[k] = rowread(0, k, 0);
-            ga[k] = rowread(0, k, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < NKK; ++k) {
-            sa = mfma32(qa[k % PFA], kreg[k], sa);
-            da = mfma32(ga[k % PFA], vreg[k], da);
-            if (k + PFA < NKK) {
-                qa[k % PFA] = rowread(0, k + PFA, 0);
-                ga[k % PFA] = rowread(0, k + PFA, 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    bf16x8 pp[2], pd[2];  // packed P and dX of the previous block
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-        const bool nextA = qb + 1 < NB, prevB = qb > 0;
-        // the element-wise stage reads S and dP from vector registers, which frees
-        // their accumulation registers for the next block's products
-        asm("" : "+v"(sa));
-        asm("" : "+v"(da));
-        f32x4 nlv[4], dlv[4];
-        if constexpr (MODE == JFA) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int il = qb * 32 + r4 * 8 + g * 4;  // rows crow(4 r4 .. 4 r4 + 3, g)
-                nlv[r4] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>((const lchar *)&nlw[il]);
-                dlv[r4] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>((const lchar *)&dlw[il]);
-            }
-        }
-        // additive bias of this block's scores (zero without a bias)
-        float bv[16];
-        if (kind == BIAS_REL) {
-            // raw window: entry (jt0 + BK - 1 - jkey) + (i - ia)
-            const int bbase = BK - 1 - wv * 32 - l32 + g * 4 + qb * 32;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) bv[e] = bwin[bbase + (e >> 2) * 8 + (e & 3)];
-        } else {
-            const float b = kind == BIAS_KEYPOS ? bwin[wv * 32 + l32] : 0.0f;  // entry jkey - jt0 for every row
-#pragma unroll
-            for (int e = 0; e < 16; ++e) bv[e] = b;
-        }
-        if constexpr (MODE == JFA) {
-            // -LSE joins the addend, so P = exp2(fma(s, sl2, addend)); without a bias
-            // the addend is -LSE itself
-#pragma unroll
-            for (int e = 0; e < 16; ++e) bv[e] = kind == BIAS_NONE ? nlv[e >> 2][e & 3] : bv[e] + nlv[e >> 2][e & 3];
-        }
-        bf16x8 qa[PFA], ga[PFA], tg[PFB], tq[PFB];
-        if (nextA) {
-#pragma unroll
-            for (int k = 0; k < PFA; ++k) {
-                qa[k] = rowread(qb + 1, k, 0);
-                ga[k] = rowread(qb + 1, k, 1);
-            }
-        }
-        if (prevB) {
-#pragma unroll
-            for (int k = 0; k < PFB; ++k) {
-                tg[k] = trread(qb - 1, k, 1);
-                tq[k] = trread(qb - 1, k, 0);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 sn = f32x16{}, dn = f32x16{};
-        float pv[16], dx[16];
-#pragma unroll
-        for (int k = 0; k < NKK; ++k) {
-            if (nextA) {
-                sn = mfma32(qa[k % PFA], kreg[k], sn);
-                dn = mfma32(ga[k % PFA], vreg[k], dn);
-            }
-            if (prevB) {
-                const int ks = k / NDB, db = k % NDB;
-                dvacc[db] = mfma32(tg[k % PFB], pp[ks], dvacc[db]);
-                dkacc[db] = mfma32(tq[k % PFB], pd[ks], dkacc[db]);
-            }
-#pragma unroll
-            for (int e = k * EPS; e < (k + 1) * EPS; ++e) {
-                const float x = __builtin_fmaf(sa[e], sl, bv[e]);
-                if constexpr (MODE == JFA) {
-                    pv[e] = fast_exp2(x);
-                    dx[e] = pv[e] * (da[e] - dlv[e >> 2][e & 3]);
-                } else {
-                    float dy;
-                    act_fwd_grad<ACT>(x, pv[e], dy);
-                    dx[e] = da[e] * dy;
-                }
-            }
-            if (masked) {
-#pragma unroll
-                for (int e = k * EPS; e < (k + 1) * EPS; ++e) {
-                    const int i = i0 + (qb * 32 + crow(e, 0));
-                    const int dist = d0 + (qb * 32 + crow(e, 0));  // aligned distance
-                    const bool valid = (i < lq) & (!causal | (dist >= 0)) &
-                                       (!win | ((dist < win) & (causal | (-dist < win))));
-                    pv[e] = valid ? pv[e] : 0.0f;
-                    dx[e] = valid ? dx[e] : 0.0f;
-                }
-            }
-            if (nextA && k + PFA < NKK) {
-                qa[k % PFA] = rowread(qb + 1, k + PFA, 0);
-                ga[k % PFA] = rowread(qb + 1, k + PFA, 1);
-            }
-            if (prevB && k + PFB < NKK) {
-                tg[k % PFB] = trread(qb - 1, k + PFB, 1);
-                tq[k % PFB] = trread(qb - 1, k + PFB, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        pack_operands(pv, pp[0], pp[1]);
-        pack_operands(dx, pd[0], pd[1]);
-        sa = sn;
-        da = dn;
-    }
-    // dV and dK of the last block
-    {
-        bf16x8 tg[PFB], tq[PFB];
-#pragma unroll
-        for (int k = 0; k < PFB; ++k) {
-            tg[k] = trread(NB - 1, k, 1);
-            tq[k] = trread(NB - 1, k, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < NKK; ++k) {
-            const int ks = k / NDB, db = k % NDB;
-            dvacc[db] = mfma32(tg[k % PFB], pp[ks], dvacc[db]);
-            dkacc[db] = mfma32(tq[k % PFB], pd[ks], dkacc[db]);
-            if (k + PFB < NKK) {
-                tg[k % PFB] = trread(NB - 1, k + PFB, 1);
-                tq[k % PFB] = trread(NB - 1, k + PFB, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-}
-
 // ----------------------------------------------------------- dK/dV units
 template <int D, int MODE, int ACT>
 __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p) {
@@ -496,7 +266,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
 
     const int H = p.H;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int n_units = p.counters2->units;
     if (n_units == 0) return;
@@ -530,14 +300,6 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
         bf16x8 kreg[NKK], vreg[NKK];
         load_row_operand<D>(kreg, Ks, jkey, g);
         load_row_operand<D>(vreg, Vs, jkey, g);
-        // K and V feed only the matrix cores (as B operands, which may come from the
-        // accumulation registers): keeping them there leaves the vector registers to
-        // the element-wise stage and the operand reads in flight
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            asm volatile("" : "+a"(kreg[kk]));
-            asm volatile("" : "+a"(vreg[kk]));
-        }
         f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dkacc[db] = dvacc[db] = f32x16{};
@@ -560,8 +322,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
         auto load_step = [&](int st) {
             const int ia = ia0 + st * BQ;
             lchar *qt = lbase + (st & 1) * 2 * TILE_BYTES;
-            dma_tile_il<BQ, D, BWD_THREADS>(qt, Qs, ia, tid);
-            dma_tile_il<BQ, D, BWD_THREADS>(qt + 1024, Gs, ia, tid);
+            dma_tile<BQ, D, BWD_THREADS>(qt, Qs, ia, tid);
+            dma_tile<BQ, D, BWD_THREADS>(qt + TILE_BYTES, Gs, ia, tid);
             const int bi = bias_stage_keymajor(bz, ia, BQ, jt0, BK, tid);
             bnext = buf_load_f32(brs, bi >= 0 ? (uint32_t)bi * 4u : OOB);
             if constexpr (MODE == JFA) {
@@ -585,10 +347,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
 
         for (int st = 0; st < nsteps; ++st) {
             const int ia = ia0 + st * BQ;
-            const lchar *Qt = lbase + (st & 1) * 2 * TILE_BYTES;  // query rows; dO rows interleaved
+            const lchar *Qt = lbase + (st & 1) * 2 * TILE_BYTES;
+            const lchar *Gt = Qt + TILE_BYTES;
             const float *bwin = s_bias[st & 1];
-            const float *nlw = s_lse[st & 1];
-            const float *dlw = s_dlt[st & 1];
             load_step(st + 1);  // past the last step: zeros, no traffic
             __builtin_amdgcn_sched_barrier(0);
 
@@ -596,8 +357,95 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void dkdv_kernel(const AttnParams p
             const bool masked = (ia + BQ > s.lq) | (p.causal && (jw + 31 > ia + shift)) |
                                 (win && ((jw < key_begin(ia + BQ - 1, s.lq, s.lk, win)) |
                                          (jw + 32 > key_end(ia, s.lq, s.lk, p.causal, win))));
-            dkdv_step<D, MODE, ACT>(masked, bz.kind, Qt, bwin, nlw, dlw, kreg, vreg, dkacc, dvacc, sl, ia, shift, jkey,
-                                    wv, l32, g, lane, s.lq, p.causal, win);
+            // Software pipeline over the step's 32-row blocks: the next block's S
+            // and dP products are issued inside the current block's element-wise
+            // stage (one basic block), so the scheduler can interleave the matrix
+            // and vector work of this single wave per SIMD.
+            f32x16 sa = f32x16{}, da = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int off = lds_off<D>(l32, 2 * kk + g);
+                sa = mfma32(lds_read16(Qt, off), kreg[kk], sa);
+                da = mfma32(lds_read16(Gt, off), vreg[kk], da);
+            }
+#pragma unroll
+            for (int qb = 0; qb < BQ / 32; ++qb) {
+                // x = s * sl + bias; invalid pairs are zeroed after the element-wise
+                // stage (rows without any visible key have LSE = -inf, so their
+                // exponent is not finite and must not be used).
+                if (bz.kind == BIAS_REL) {
+                    // raw window: entry (jt0 + BK - 1 - jkey) + (i - ia)
+                    const int bbase = BK - 1 - wv * 32 - l32 + g * 4 + qb * 32;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) sa[e] = __builtin_fmaf(sa[e], sl, bwin[bbase + (e >> 2) * 8 + (e & 3)]);
+                } else if (bz.kind == BIAS_KEYPOS) {
+                    const float b = bwin[wv * 32 + l32];  // entry jkey - jt0, the same for every row
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) sa[e] = __builtin_fmaf(sa[e], sl, b);
+                } else if constexpr (MODE == GDPA) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) sa[e] *= sl;
+                }
+                f32x16 sn = f32x16{}, dn = f32x16{};
+                if (qb + 1 < BQ / 32) {
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) {
+                        const int off = lds_off<D>((qb + 1) * 32 + l32, 2 * kk + g);
+                        sn = mfma32(lds_read16(Qt, off), kreg[kk], sn);
+                        dn = mfma32(lds_read16(Gt, off), vreg[kk], dn);
+                    }
+                }
+                float pv[16], dx[16];
+                if constexpr (MODE == JFA) {
+                    // with a bias S already holds x; without one the scale folds into the FMA
+                    const float xm = bz.kind ? 1.0f : sl;
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int il = qb * 32 + r4 * 8 + g * 4;  // rows crow(4 r4 .. 4 r4 + 3, g)
+                        const f32x4 nl = *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>(
+                            (const lchar *)&s_lse[st & 1][il]);
+                        const f32x4 dl = *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>(
+                            (const lchar *)&s_dlt[st & 1][il]);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int e = r4 * 4 + t;
+                            pv[e] = fast_exp2(__builtin_fmaf(sa[e], xm, nl[t]));
+                            dx[e] = pv[e] * (da[e] - dl[t]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        float dy;
+                        act_fwd_grad<ACT>(sa[e], pv[e], dy);
+                        dx[e] = da[e] * dy;
+                    }
+                }
+                if (masked) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int i = ia + qb * 32 + crow(e, g);
+                        const int dist = i + shift - jkey;  // aligned distance
+                        const bool valid = (i < s.lq) & (!p.causal | (dist >= 0)) &
+                                           (!win | ((dist < win) & (p.causal | (-dist < win))));
+                        pv[e] = valid ? pv[e] : 0.0f;
+                        dx[e] = valid ? dx[e] : 0.0f;
+                    }
+                }
+                bf16x8 pb[2], dsb[2];
+                pack_operands(pv, pb[0], pb[1]);
+                pack_operands(dx, dsb[0], dsb[1]);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        dvacc[db] = mfma32(lds_read_tr_operand<D>(Gt, qb * 32 + ks * 16, db * 32, lane), pb[ks], dvacc[db]);
+                        dkacc[db] = mfma32(lds_read_tr_operand<D>(Qt, qb * 32 + ks * 16, db * 32, lane), dsb[ks], dkacc[db]);
+                    }
+                }
+                sa = sn;
+                da = dn;
+            }
             store_step((st + 1) & 1);
             __syncthreads();
         }

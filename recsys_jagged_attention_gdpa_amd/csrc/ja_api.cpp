@@ -45,7 +45,7 @@ int64_t tile_cap(int64_t rows, int B, int tile) { return rows / tile + B + 1; }
 
 struct Layout {
     size_t counters;  // 4 PlanCounters blocks
-    size_t tiles_q, tiles_k, tiles_s, delta, tiles_a, dbias_part, rope_q, rope_k, total;
+    size_t tiles_q, tiles_k, tiles_s, delta, tiles_a, dbias_part, dbias_slots, dbias_chunks, rope_q, rope_k, total;
     int64_t cap_q, cap_k, cap_s;
 };
 
@@ -84,6 +84,11 @@ Layout layout_of(const ja_problem &p, int pass) {
         off += align_up((size_t)L.cap_q * sizeof(int2));
         L.dbias_part = off;
         off += align_up((size_t)ja::DBIAS_GRID * p.heads * (size_t)bias_width(p) * sizeof(float));
+        // the dQ units' partial rows: one per (unit, wave), and their chunk sums
+        L.dbias_slots = off;
+        off += align_up((size_t)L.cap_q * p.heads * 4 * (size_t)bias_width(p) * sizeof(float));
+        L.dbias_chunks = off;
+        off += align_up((size_t)ja::DBIAS_SLOT_CHUNKS * p.heads * (size_t)bias_width(p) * sizeof(float));
     }
     if (p.rope_base > 0.0f && !p.rope_inputs_turned) {  // turned copies of q and k
         const size_t row = (size_t)p.heads * p.head_dim * (p.dtype == JA_BF16 ? 2 : 4);
@@ -357,8 +362,18 @@ ja_status run_bwd(const ja_problem *p, int mode, const void *q, const void *k, c
         pp[n++] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 1, a.tiles, L.cap_q, a.counters);
         pp[n++] = plan_of(*p, ja::PLAN_KV_TILES, ja::BWD_KV_UNIT, ja::BWD_Q_STEP, 1, a.tiles2, L.cap_k, a.counters2);
     }
-    if (dbias) {  // query tiles of every sample, short ones included; the summation order follows this list
-        pp[n] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, 0, a.tiles4, L.cap_q, a.counters4);
+    if (dbias) {
+        // The dQ units fold the sums of their samples in (partial rows in unit
+        // order, so their list must be a function of the offsets alone); the
+        // separate pass takes the samples of the fused short-K/V units, or every
+        // sample when no long unit runs.  Its summation order follows its list.
+        if (long_units) {
+            pp[1].stable = 1;
+            a.dbias_slots = reinterpret_cast<float *>(static_cast<char *>(ws) + L.dbias_slots);
+            a.dbias_chunks = reinterpret_cast<float *>(static_cast<char *>(ws) + L.dbias_chunks);
+        }
+        pp[n] = plan_of(*p, ja::PLAN_Q_TILES, ja::Q_TILE, ja::KV_TILE, long_units ? 2 : 0, a.tiles4, L.cap_q,
+                        a.counters4);
         pp[n++].stable = 1;
     }
     e = ja::launch_plan(pp, n, s);

@@ -28,6 +28,7 @@
 // by a streaming pass instead: the dK/dV kernel runs one wave per SIMD at the
 // edge of its register budget, and any epilogue added to it changes how the
 // compiler schedules its main loop (measured: 8 % slower, more than the pass).
+#include "ja_dbias_fold.h"
 #include "ja_device.h"
 #include "ja_kernels.h"
 #include "ja_tiles.h"
@@ -90,7 +91,9 @@ __device__ __forceinline__ float score_bwd(float s_raw, float scale, float bias,
 }
 
 // ------------------------------------------------------------- dQ units
-template <int D, int MODE, int ACT, bool ROPE>
+// DB: also the bias-table gradient's partial sums (p.dbias_slots: one row of
+// W entries per (unit, wave)), from the dX blocks the unit forms anyway.
+template <int D, int MODE, int ACT, bool ROPE, bool DB>
 __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) {
     constexpr int BN = KV_TILE;
     constexpr int BM = Q_TILE;
@@ -100,6 +103,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
     static_assert(WIN <= BWD_THREADS, "one bias window entry per thread");
     __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
     __shared__ float s_bias[2][WIN];
+    __shared__ float s_fold[DB ? BWD_THREADS / WAVE : 1][DB ? DBF_FLOATS : 1];
     __shared__ int s_unit;
     lchar *const lbase = (lchar *)smem;
 
@@ -110,6 +114,8 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
     const int n_units = p.counters->units;
     if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
+    DbiasFold fold;
+    if constexpr (DB) fold.init(s_fold[wv], bz.kind, bz.lo, bz.hi, lane);
 
     const uint64_t busy_t0 = busy_start(p.busy);
     const int xcd = xcd_id();
@@ -156,6 +162,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
         f32x16 dqacc[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
+        if constexpr (DB) fold.begin(p.dbias_slots, (int64_t)w * (BWD_THREADS / WAVE) + wv);
 
         // Key / value tile jt is copied straight into LDS buffer (jt & 1); the
         // bias window (JFA: in log2 units) goes through a register.
@@ -230,6 +237,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
                         dx[e] = (row_ok & (j < my_kend) & (j >= my_kbeg)) ? dx[e] : 0.0f;
                     }
                 }
+                if constexpr (DB) fold.block(dx, iw, j0 + nb * 32, lane);
                 bf16x8 dsb[2];
                 pack_operands(dx, dsb[0], dsb[1]);
                 // dQ^T += K^T dX^T over this block's 32 keys
@@ -242,6 +250,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void dq_kernel(const AttnParams p) 
             store_tile((jt + 1) & 1);
             __syncthreads();
         }
+        if constexpr (DB) fold.finish(iw, jt_first * BN, (nkv > jt_first ? nkv : jt_first) * BN, lane);
         if constexpr (ROPE) rope_back_acc<D>(dqacc, irow, p.rope_rev, g);
         store_row_acc<D>(dQs, irow, dqacc, p.scale, g);
     }
@@ -618,6 +627,7 @@ __global__ __launch_bounds__(WAVE, 1) void fused_kernel(const AttnParams p) {
 // -------------------------------------------------------------- launches
 template <int D, int MODE, int ACT, bool ROPE>
 static hipError_t launch_bwd_t(const AttnParams &p, int grid, bool long_units, hipStream_t st) {
+    const bool db = p.dbias_slots != nullptr;
     const KernelTimer &t = kernel_timer();
     if (MODE == JFA && p.total_q > 0) {
         const int64_t threads = p.total_q * p.H * (D / 8);
@@ -633,7 +643,12 @@ static hipError_t launch_bwd_t(const AttnParams &p, int grid, bool long_units, h
     hipLaunchKernelGGL((dkdv_kernel<D, MODE, ACT>), dim3(grid / 2), dim3(BWD_THREADS), 0, st, t.with_busy(p, K_BWD_KV));
     t.end(K_BWD_KV, st);
     t.begin(K_BWD_Q, st);
-    hipLaunchKernelGGL((dq_kernel<D, MODE, ACT, ROPE>), dim3(grid), dim3(BWD_THREADS), 0, st, t.with_busy(p, K_BWD_Q));
+    if (db)
+        hipLaunchKernelGGL((dq_kernel<D, MODE, ACT, ROPE, true>), dim3(grid), dim3(BWD_THREADS), 0, st,
+                           t.with_busy(p, K_BWD_Q));
+    else
+        hipLaunchKernelGGL((dq_kernel<D, MODE, ACT, ROPE, false>), dim3(grid), dim3(BWD_THREADS), 0, st,
+                           t.with_busy(p, K_BWD_Q));
     t.end(K_BWD_Q, st);
     return hipGetLastError();
 }

@@ -22,6 +22,13 @@
 // run; when its head changes it adds its four wave rows in a fixed order and
 // writes one partial row per (workgroup, head).  A second kernel adds the G
 // partial rows of each head in workgroup order.  No atomics.
+//
+// When the dQ units fold the sums in (samples with more than FUSED_MAX_LK
+// keys, whose dX the dQ units form anyway), this pass only takes the samples
+// of the fused short-K/V units, and the reduction also adds the dQ units'
+// partial rows: first per chunk of units (unit order within a chunk, the four
+// waves of a unit in order), then the chunks in order.
+#include "ja_dbias_fold.h"
 #include "ja_device.h"
 #include "ja_kernels.h"
 #include "ja_tiles.h"
@@ -30,13 +37,6 @@ namespace ja {
 
 constexpr int DBIAS_THREADS = 256;
 constexpr int SCR_STRIDE = 33;  // floats per row of a wave's 32 x 32 staging block (odd: no bank conflicts)
-
-// Sum of v over the 64 lanes, the same butterfly order on every call.
-__device__ __forceinline__ float wave_sum_fixed(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
 
 // Key tiles of 32 rows keep a workgroup's LDS (tiles, staging blocks and the
 // four per-wave rows of W sums, sized at launch) within half the CU's for
@@ -260,13 +260,44 @@ __global__ __launch_bounds__(DBIAS_THREADS, 2) void dbias_kernel(const AttnParam
     busy_end(p.busy, p.busy_cap, busy_t0);
 }
 
-// dbias[h][c] = sum over workgroups g (in order) of partial row (g, h), entry c.
-__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *part, float *out, int H, int W, int G) {
+// Partial rows of the dQ units (DbiasFold): chunks[ch][h][c] = sum over the
+// units u of chunk ch of head h (in order) of the rows of u's four waves (in
+// order), entry c.  The units of head h are h n .. h n + n - 1 (head-major
+// numbering, n = units / H); chunk ch holds n ch / CH .. n (ch + 1) / CH - 1.
+// Block (c-group of 64 entries, h, ch); its four waves take one wave index each.
+__global__ __launch_bounds__(256) void dbias_slots_kernel(const float *slots, float *chunks,
+                                                          const PlanCounters *ctr, int H, int W) {
+    constexpr int WV = 4;  // waves per dQ unit
+    const int c = blockIdx.x * 64 + (threadIdx.x & 63), wv = threadIdx.x >> 6;
+    const int h = blockIdx.y, ch = blockIdx.z;
+    const int n = ctr->units / H;
+    const int u0 = (int)((int64_t)n * ch / DBIAS_SLOT_CHUNKS), u1 = (int)((int64_t)n * (ch + 1) / DBIAS_SLOT_CHUNKS);
+    float s = 0.0f;
+    if (c < W)
+        for (int u = u0; u < u1; ++u) s += slots[(((int64_t)h * n + u) * WV + wv) * W + c];
+    __shared__ float red[WV][64];
+    red[wv][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (wv == 0 && c < W) {
+        const int l = threadIdx.x;
+        chunks[((int64_t)ch * H + h) * W + c] = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+    }
+}
+
+// dbias[h][c] = sum over workgroups g (in order) of partial row (g, h), entry c,
+// plus (when the dQ units fold the sums in) the chunk sums in chunk order.
+__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *part, const float *chunks, float *out,
+                                                           int H, int W, int G) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)H * W) return;
     const int h = (int)(idx / W), c = (int)(idx % W);
     float s = 0.0f;
     for (int gi = 0; gi < G; ++gi) s += part[((int64_t)gi * H + h) * W + c];
+    if (chunks) {
+        float f = 0.0f;
+        for (int ch = 0; ch < DBIAS_SLOT_CHUNKS; ++ch) f += chunks[((int64_t)ch * H + h) * W + c];
+        s += f;
+    }
     out[idx] = s;
 }
 
@@ -278,8 +309,13 @@ static hipError_t launch_dbias_t(const AttnParams &p, hipStream_t st) {
     t.begin(K_BWD_DBIAS, st);
     hipLaunchKernelGGL((dbias_kernel<D, MODE, ACT>), dim3(DBIAS_GRID), dim3(DBIAS_THREADS),
                        (size_t)4 * W * sizeof(float), st, t.with_busy(p, K_BWD_DBIAS));
+    if (p.dbias_slots)
+        hipLaunchKernelGGL(dbias_slots_kernel, dim3((unsigned)((W + 63) / 64), (unsigned)p.H, DBIAS_SLOT_CHUNKS),
+                           dim3(256), 0, st, (const float *)p.dbias_slots, p.dbias_chunks,
+                           (const PlanCounters *)p.counters, p.H, W);
     hipLaunchKernelGGL(dbias_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       (const float *)p.dbias_part, p.dbias, p.H, W, DBIAS_GRID);
+                       (const float *)p.dbias_part, (const float *)(p.dbias_slots ? p.dbias_chunks : nullptr),
+                       p.dbias, p.H, W, DBIAS_GRID);
     t.end(K_BWD_DBIAS, st);
     return hipGetLastError();
 }

@@ -16,6 +16,7 @@ constexpr int BWD_Q_STEP = 128;    // queries per inner step of a dK/dV unit
 constexpr int FUSED_MAX_LK = 32;   // samples with at most this many keys use the fused backward unit
 constexpr int DBIAS_GRID = 512;    // workgroups of the bias-gradient pass (fixed: fixes the summation order)
 constexpr int DBIAS_MAX_BINS = 4096;  // largest bias table row the gradient pass takes
+constexpr int DBIAS_SLOT_CHUNKS = 64;  // chunks of dQ units whose partial rows are added first (fixed order)
 
 // The chip's accelerator dies (XCDs), each with its own L2.
 constexpr int XCDS = 8;
@@ -48,7 +49,8 @@ struct PlanParams {
     int kind;
     int tile_rows;   // rows per unit tile
     int inner_rows;  // rows per inner-loop step (cost unit)
-    int only_short;  // PLAN_SAMPLES: keep samples with lk <= FUSED_MAX_LK; PLAN_KV/Q: skip them (1) or not (0)
+    int only_short;  // PLAN_SAMPLES: keep samples with lk <= FUSED_MAX_LK; PLAN_KV/Q: skip them (1), not (0),
+                     // or keep only them (2)
     int window;      // sliding window (0: none)
     int stable;      // tile lists: 1 = ties in cost keep sample order (a function of the offsets alone)
     int2 *tiles;     // out: (sample, tile) pairs, most expensive first
@@ -86,6 +88,11 @@ struct AttnParams {
     PlanCounters *counters4;
     float *dbias;             // bias gradient output [H][hi - lo + 1], or NULL
     float *dbias_part;        // bias gradient partial rows [DBIAS_GRID][H][hi - lo + 1]
+    // Bias gradient folded into the dQ units (NULL: not folded): one row of W
+    // partial sums per (dQ unit, wave), and their sums per chunk of units
+    // [DBIAS_SLOT_CHUNKS][H][W]
+    float *dbias_slots;
+    float *dbias_chunks;
     // MXFP8 forward: q, k, v hold E4M3 codes and these their E8M0 scale codes
     // [T, H, D / 32] (all NULL for bf16 / fp32 inputs)
     const uint8_t *q_sc, *k_sc, *v_sc;

@@ -40,8 +40,8 @@ struct PlanSample {
     int lq, lk, ntiles;
 };
 
-__device__ __forceinline__ bool skipped_as_short(const PlanParams &p, int lk) {
-    return p.only_short && lk <= FUSED_MAX_LK;
+__device__ __forceinline__ bool skipped_by_length(const PlanParams &p, int lk) {
+    return p.only_short == 2 ? lk > FUSED_MAX_LK : (p.only_short && lk <= FUSED_MAX_LK);
 }
 
 __device__ PlanSample plan_sample(const PlanParams &p, int b) {
@@ -51,9 +51,9 @@ __device__ PlanSample plan_sample(const PlanParams &p, int b) {
     s.lq = s.lq < 0 ? 0 : s.lq;
     s.lk = s.lk < 0 ? 0 : s.lk;
     if (p.kind == PLAN_Q_TILES) {
-        s.ntiles = skipped_as_short(p, s.lk) ? 0 : ceil_div(s.lq, p.tile_rows);
+        s.ntiles = skipped_by_length(p, s.lk) ? 0 : ceil_div(s.lq, p.tile_rows);
     } else if (p.kind == PLAN_KV_TILES) {
-        s.ntiles = skipped_as_short(p, s.lk) ? 0 : ceil_div(s.lk, p.tile_rows);
+        s.ntiles = skipped_by_length(p, s.lk) ? 0 : ceil_div(s.lk, p.tile_rows);
     } else {
         s.ntiles = (s.lk <= FUSED_MAX_LK && (s.lq > 0 || s.lk > 0)) ? 1 : 0;
     }

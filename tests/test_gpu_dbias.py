@@ -66,6 +66,14 @@ def test_bias_gradient_dims_and_acts(mode, act, D):
     check_dbias(w, f"{mode} {act} D={D}")
 
 
+@pytest.mark.parametrize("bias,lo,hi", [("rel", -1, 0), ("keypos", 3, 4)])
+def test_bias_gradient_two_entries(bias, lo, hi):
+    # Two entries: every position clamps to one of the two ends.
+    w = synth.custom(mode="gdpa", lq=LQ, lk=LK, H=2, D=64, seed=5, act="gelu_tanh", causal=False,
+                     bias_kind=bias, bias_lo=lo, bias_hi=hi)
+    check_dbias(w, f"two entries {bias}")
+
+
 @pytest.mark.parametrize("mode", ["gdpa", "jfa"])
 def test_bias_gradient_fp32(mode):
     w = synth.custom(mode=mode, lq=[9, 0, 23, 1, 17], lk=[9, 5, 23, 1, 0], H=2, D=32, dtype=torch.float32,

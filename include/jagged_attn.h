@@ -178,7 +178,10 @@ ja_status jagged_gdpa_fwd(const ja_problem *p, const void *q, const void *k, con
  * valid pairs (i, j) of every sample that read it (REL: clamp(i - j), KEYPOS:
  * clamp(j)), the bias being additive in X.  Needs a bias kind and a table
  * row of at most 4096 entries (else JA_ERR_UNSUPPORTED), and a workspace of
- * ja_workspace_size(p, JA_PASS_BWD_DBIAS) bytes (else JA_ERR_WORKSPACE).
+ * ja_workspace_size(p, JA_PASS_BWD_DBIAS) bytes (else JA_ERR_WORKSPACE); that
+ * workspace holds a row of table sums per 32 query rows and head (about
+ * H * (total_q / 32 + 4 B) * (bias_hi - bias_lo + 1) * 4 bytes), so the sums
+ * stay deterministic bit for bit.
  * The custom biases are listed on "GEM Training: How Meta Doubled the
  * Efficiency...", section "What happened". */
 ja_status jagged_gdpa_bwd(const ja_problem *p, const void *q, const void *k, const void *v,

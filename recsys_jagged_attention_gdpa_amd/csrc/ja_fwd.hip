@@ -53,9 +53,38 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 units a running softmax max may l
 // reach LDS as codes by buffer->LDS copies (half the bytes, no decoding), query
 // codes stay in registers, and the block scales go in as the MFMA's scale
 // operands; only V is decoded to bf16 for the PV product.
+//
+// WAVES = 1 (one block of at most 32 shared query rows, pooling by learned
+// seed queries): the waves of a workgroup are independent units, one head each
+// of the same sample (head groups of few_q_heads()), each with its own LDS
+// tiles and no barrier inside its loop.  The heads of a sample share the cache lines
+// of their key and value rows (64-byte rows of fp8 codes fill half a line), so
+// running them side by side on one CU fetches each line from HBM once.
+// End of a tile step: the tiles that every thread of the unit copied are in
+// LDS.  A unit of one wave only orders its own LDS accesses (its DMA has
+// landed: store_tile waited for it); a multi-wave unit needs the barrier.
+template <bool ONE_WAVE>
+__device__ __forceinline__ void unit_sync() {
+    if constexpr (ONE_WAVE) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    } else {
+        __syncthreads();
+    }
+}
+
+// Heads per workgroup of the one-wave units: FEW_Q_HEADS, or fewer where that
+// many copies of a unit's LDS tiles would not fit.
+template <int D, int BN, bool MX>
+constexpr int few_q_heads() {
+    constexpr int tiles = 4 * BN * D * ((MX && D >= 64) ? 1 : 2);  // a unit's double-buffered key / value tiles
+    return 4 * tiles <= 136 * 1024 ? FEW_Q_HEADS : 2 * tiles <= 136 * 1024 ? 2 : 1;
+}
+
 template <int D, int MODE, int ACT, int WAVES, int BN, bool SPLIT, bool MX>
-__global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(const AttnParams p) {
+__global__ __launch_bounds__((WAVES == 1 ? few_q_heads<D, BN, MX>() : WAVES) * WAVE, 2) void fwd_kernel(const AttnParams p) {
     constexpr bool F8S = MX && D >= 64;  // S and PV on the fp8 MFMA (key and value tiles hold codes)
+    constexpr bool IW = WAVES == 1;      // independent waves, one unit each
+    constexpr int WGW = IW ? few_q_heads<D, BN, MX>() : 1;  // waves (units) per workgroup
     constexpr int NT = WAVES * WAVE;
     constexpr int BM = 32 * WAVES;
     constexpr int TILE_BYTES = BN * D * (F8S ? 1 : 2);
@@ -65,17 +94,25 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
     constexpr int NKS = BN / 16; // 16-key k-steps per tile
     constexpr int WIN = BM + BN - 1;  // largest bias window of a (unit, key tile)
     constexpr int WPT = (WIN + NT - 1) / NT;  // bias window entries per thread
-    __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
-    __shared__ float s_bias[2][WIN];
-    __shared__ __attribute__((aligned(4))) uint8_t s_vsc[2][F8S ? BN : 4];  // F8S: each value row's scale code S_j
+    __shared__ __attribute__((aligned(16))) char smem[WGW][4 * TILE_BYTES];
+    __shared__ float s_bias_w[WGW][2][WIN];
+    __shared__ __attribute__((aligned(16))) float s_vsc_w[WGW][2][F8S ? BN : 4];  // F8S: each value row's factor 2^(S_j - 127)
     __shared__ int s_unit;
-    lchar *const lbase = (lchar *)smem;
 
     const int H = p.H;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
+    // the wave index as a scalar: with independent waves it selects the head,
+    // so everything addressed through it (descriptors included) stays uniform
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
-    const int n_units = p.counters->units;
+    const int ut = IW ? lane : tid;  // thread index within the unit
+    const int uw = IW ? 0 : wv;      // wave index within the unit
+    lchar *const lbase = (lchar *)smem[IW ? wv : 0];
+    float(*const s_bias)[WIN] = s_bias_w[IW ? wv : 0];
+    float(*const s_vsc)[F8S ? BN : 4] = s_vsc_w[IW ? wv : 0];
+    // IW: units are (list entry, group of WGW heads)
+    const int hg = (p.H + WGW - 1) / WGW;
+    const int n_units = IW ? p.counters->units / p.H * hg : p.counters->units;
     if (n_units == 0) return;
     const BiasArgs bz{p.bias, p.bias_kind, p.bias_lo, p.bias_hi, p.bias_hi - p.bias_lo + 1};
     const float sl2 = p.scale * LOG2E;
@@ -89,12 +126,13 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         const int w = s_unit;
         __syncthreads();
         if (w < 0) break;
-        const UnitRef u = tile_unit(p.tiles, w, n_units, H);
+        const UnitRef u = IW ? UnitRef{p.tiles[w / hg], (w % hg) * WGW + wv} : tile_unit(p.tiles, w, n_units, H);
         const int2 tile = u.tile;
         const int h = u.h;
+        if (IW && h >= H) continue;            // a wave past the last head of the group
         const Sample s = load_sample(p.q_off, p.lq_fixed, p.kv_off, tile.x);
         const int i0 = tile.y * BM;            // first query row of the unit (sample-local)
-        const int iw = i0 + wv * 32;           // first row of this wave
+        const int iw = i0 + uw * 32;           // first row of this wave
         const int irow = iw + l32;             // this lane's query row
         const int i_last = (i0 + BM < s.lq ? i0 + BM : s.lq) - 1;
         const int kend = key_end(i_last, s.lq, s.lk, p.causal, p.window);
@@ -127,7 +165,9 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         const MXSlice<D> Km(p.k, p.k_sc, s.ks, MX ? s.lk : 0, H, h), Vm(p.v, p.v_sc, s.ks, MX ? s.lk : 0, H, h);
         MXPairLoader<BN, D, NT> mxl;  // MX: key and value codes, decoded into LDS
         F8VLoader<BN, D, NT> mxv;     // F8S: value codes, re-encoded to one scale per key
-        int ksn[NNB][F8S ? NKS8 : 1], ksc[NNB][F8S ? NKS8 : 1];  // F8S: the lane's key-row scale codes, next / current tile
+        uint32_t kwn = 0;                 // F8S: scale word of key row lane of the next tile
+        int ksc[NNB][F8S ? NKS8 : 1];     // F8S: the lane's key-row scale codes, current tile
+        static_assert(!F8S || BN <= WAVE, "one key row per lane");
 
         f32x16 oacc[NDB];
 #pragma unroll
@@ -142,42 +182,41 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
         auto load_tile = [&](int jt) {
             lchar *kt = lbase + (jt & 1) * 2 * TILE_BYTES;
             if constexpr (F8S) {
-                dma_f8_tile<BN, D, NT>(kt, Km, jt * BN, tid);
-                mxv.load(Vm, jt * BN, tid);
-#pragma unroll
-                for (int nb = 0; nb < NNB; ++nb)
-#pragma unroll
-                    for (int ks = 0; ks < NKS8; ++ks) ksn[nb][ks] = f8_scale<D>(Km, jt * BN + nb * 32 + l32, 2 * ks + g);
+                dma_f8_tile<BN, D, NT>(kt, Km, jt * BN, ut);
+                mxv.load(Vm, jt * BN, ut);
+                kwn = f8_scale_word<D>(Km, jt * BN + lane, lane < BN);
             } else if constexpr (MX) {
-                mxl.load(Km, Vm, jt * BN, tid);
+                mxl.load(Km, Vm, jt * BN, ut);
             } else {
-                dma_tile<BN, D, NT>(kt, Ks, jt * BN, tid);
-                dma_tile<BN, D, NT>(kt + TILE_BYTES, Vs, jt * BN, tid);
+                dma_tile<BN, D, NT>(kt, Ks, jt * BN, ut);
+                dma_tile<BN, D, NT>(kt + TILE_BYTES, Vs, jt * BN, ut);
             }
 #pragma unroll
             for (int r = 0; r < WPT; ++r) {
-                const int bi = bias_stage_rowmajor(bz, i0, BM, jt * BN, BN, tid + r * NT);
+                const int bi = bias_stage_rowmajor(bz, i0, BM, jt * BN, BN, ut + r * NT);
                 bnext[r] = buf_load_f32(brs, bi >= 0 ? (uint32_t)bi * 4u : OOB);
             }
         };
         auto store_tile = [&](int buf) {
             if constexpr (F8S) {
-                mxv.store(lbase + buf * 2 * TILE_BYTES + TILE_BYTES, (lu8 *)s_vsc[buf], tid);
+                mxv.store(lbase + buf * 2 * TILE_BYTES + TILE_BYTES, (lfloat *)s_vsc[buf], ut);
 #pragma unroll
-                for (int nb = 0; nb < NNB; ++nb)
+                for (int nb = 0; nb < NNB; ++nb) {
+                    const uint32_t w = lane_word(kwn, nb * 32 + l32);  // key row nb * 32 + l32
 #pragma unroll
-                    for (int ks = 0; ks < NKS8; ++ks) ksc[nb][ks] = ksn[nb][ks];
+                    for (int ks = 0; ks < NKS8; ++ks) ksc[nb][ks] = (int)((w >> (8 * (2 * ks + g))) & 255u);
+                }
             } else if constexpr (MX) {
-                mxl.store(lbase + buf * 2 * TILE_BYTES, lbase + buf * 2 * TILE_BYTES + TILE_BYTES, tid);
+                mxl.store(lbase + buf * 2 * TILE_BYTES, lbase + buf * 2 * TILE_BYTES + TILE_BYTES, ut);
             }
 #pragma unroll
             for (int r = 0; r < WPT; ++r)  // JFA works in log2 units
-                if (tid + r * NT < WIN) s_bias[buf][tid + r * NT] = MODE == JFA ? bnext[r] * LOG2E : bnext[r];
+                if (ut + r * NT < WIN) s_bias[buf][ut + r * NT] = MODE == JFA ? bnext[r] * LOG2E : bnext[r];
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's part of the tile has landed
         };
         load_tile(jt_first);
         store_tile(jt_first & 1);
-        __syncthreads();
+        unit_sync<IW>();
 
         // keys of the wave's rows: every row sees [wkb, wke) at least; masking is
         // needed only where a tile leaves that range
@@ -227,7 +266,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             // scale is applied, folded into later arithmetic where possible.
             if (bz.kind) {
                 // raw window: entry (i0 + BM - 1 - irow) + (j - j0) (REL) or j - j0 (KEYPOS)
-                const int bbase = (bz.kind == BIAS_REL ? BM - 1 - wv * 32 - l32 : 0) + g * 4;
+                const int bbase = (bz.kind == BIAS_REL ? BM - 1 - uw * 32 - l32 : 0) + g * 4;
 #pragma unroll
                 for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
@@ -257,7 +296,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                         }
                     }
                     if constexpr (F8S) {
-                        pex[nb] = encode_p_block(pv, (const lu8 *)s_vsc[jt & 1] + nb * 32, g, pf8[nb]);
+                        pex[nb] = encode_p_block(pv, (const lfloat *)s_vsc[jt & 1] + nb * 32, g, pf8[nb]);
                     } else {
                         pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
                     }
@@ -301,7 +340,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
                         l_run += pv[e];
                     }
                     if constexpr (F8S) {
-                        pex[nb] = encode_p_block(pv, (const lu8 *)s_vsc[jt & 1] + nb * 32, g, pf8[nb]);
+                        pex[nb] = encode_p_block(pv, (const lfloat *)s_vsc[jt & 1] + nb * 32, g, pf8[nb]);
                     } else {
                         pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
                         if constexpr (SPLIT) pack_residual_operands(pv, pbl[2 * nb], pbl[2 * nb + 1]);
@@ -331,7 +370,7 @@ __global__ __launch_bounds__(WAVES * WAVE, WAVES == 4 ? 2 : 8) void fwd_kernel(c
             }
 
             store_tile((jt + 1) & 1);
-            __syncthreads();
+            unit_sync<IW>();
         }
 
         // Epilogue: lane owns query row irow; d = db*32 + crow(e, g).
@@ -371,7 +410,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
     constexpr int NKK = D / 16, NDB = D / 32;
     constexpr int NWAVES = FWD_THREADS / WAVE;
     __shared__ __attribute__((aligned(16))) char smem[(2 + NWAVES) * KV_BYTES];
-    __shared__ __attribute__((aligned(4))) uint8_t s_vsc[32];  // F8: each value row's scale code S_j
+    __shared__ __attribute__((aligned(16))) float s_vsc[32];  // F8: each value row's factor 2^(S_j - 127)
     __shared__ int s_unit, s_blk;
     lchar *const Kt = (lchar *)smem;
     lchar *const Vt = Kt + KV_BYTES;
@@ -412,7 +451,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
             }
 #pragma unroll
             for (int ks = 0; ks < NKS8; ++ks) ksc[ks] = f8_scale<D>(Km, l32, 2 * ks + g);
-            vl.store(Vt, (lu8 *)s_vsc, threadIdx.x);
+            vl.store(Vt, (lfloat *)s_vsc, threadIdx.x);
         } else if constexpr (MX) {
             MXPairLoader<32, D, FWD_THREADS> kv;
             kv.load(MXSlice<D>(p.k, p.k_sc, s.ks, s.lk, H, h), MXSlice<D>(p.v, p.v_sc, s.ks, s.lk, H, h), 0,
@@ -517,7 +556,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
             int scb = 127;
             if constexpr (F8) {
                 u32x4 c0;
-                const int ex = encode_p_block(pv, (const lu8 *)s_vsc, g, c0);
+                const int ex = encode_p_block(pv, (const lfloat *)s_vsc, g, c0);
                 pf8 = p_f8_operand(c0, u32x4{});
                 scb = g ? 127 : ex;
             } else {
@@ -579,8 +618,9 @@ static hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, bool lo
     if (!long_units) return hipGetLastError();
     t.begin(K_FWD, stream);
     if (few_q)  // every unit is one block of <= 32 shared query rows
-        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, FEW_Q_KV_TILE, SPLIT, MX>), dim3(8 * cus), dim3(WAVE), 0, stream,
-                           t.with_busy(p, K_FWD));
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, FEW_Q_KV_TILE, SPLIT, MX>),
+                           dim3(8 / few_q_heads<D, FEW_Q_KV_TILE, MX>() * cus),
+                           dim3(few_q_heads<D, FEW_Q_KV_TILE, MX>() * WAVE), 0, stream, t.with_busy(p, K_FWD));
     else
         hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE, SPLIT, MX>), dim3(2 * cus), dim3(4 * WAVE), 0, stream,
                            t.with_busy(p, K_FWD));

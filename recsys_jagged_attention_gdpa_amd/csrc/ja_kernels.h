@@ -200,6 +200,7 @@ const KernelTimer &kernel_timer();
 // rows (q_offsets NULL, lq_fixed <= FEW_Q_ROWS), planned as 32-row query tiles.
 constexpr int FEW_Q_ROWS = 32;
 constexpr int FEW_Q_KV_TILE = 64;  // key tile of those units
+constexpr int FEW_Q_HEADS = 4;     // heads of one sample per workgroup (a wave each) in those units
 // long_units: launch the long-sequence kernels (false when no sample has more
 // than FUSED_MAX_LK keys, so only the short-K/V units have work).
 hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, bool long_units,

@@ -626,36 +626,61 @@ struct F8WaveTile {
 // as E4M3 (nearest, ties to even) against one power-of-two scale per (query,
 // 32-key block) that puts the block's largest |P'| in [128, 256).
 
+// A row's D / 32 scale codes as one word (byte b: block b), read once per row:
+// lane j of a wave loads the word of row rows[j] and lanes that need it take
+// it from there by a cross-lane read, instead of every lane issuing a one- or
+// two-byte load of its own (many small loads per tile were measured to cost
+// the pooling forward 16 % of its time).
+template <int D>
+__device__ __forceinline__ uint32_t f8_scale_word(const MXSlice<D> &S, int row, bool ok) {
+    const uint32_t os = ok ? (uint32_t)row * S.srow_bytes : OOB;
+    if constexpr (D == 128) return __builtin_amdgcn_raw_buffer_load_b32(S.s, (int)os, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b16(S.s, (int)os, 0, 0);
+}
+__device__ __forceinline__ uint32_t lane_word(uint32_t w, int src_lane) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)w);
+}
+
+// 2^(S - 127) for an E8M0 code S as a float (2^-127, code 0, is a subnormal).
+__device__ __forceinline__ float v_factor(uint32_t code) {
+    return __builtin_bit_cast(float, code ? code << 23 : 0x00400000u);
+}
+
 // Value rows of a tile staged as re-encoded codes: load() issues the reads of
-// 16 codes and the row's scale codes per piece, store() re-encodes them into a
-// code tile (f8_off layout) and writes each row's S_j into s_row[row].
+// 16 codes per piece and of the rows' scale words, store() re-encodes them into
+// a code tile (f8_off layout) and writes each row's factor 2^(S_j - 127) into
+// s_row[row].
 template <int ROWS, int D, int NT>
 struct F8VLoader {
     static constexpr int PIECES = ROWS * D / 16;
     static constexpr int PER_THREAD = (PIECES + NT - 1) / NT;
+    static constexpr int CPR = D / 16;        // pieces per row
+    static constexpr int RPW = WAVE / CPR;    // rows one wave's pieces of one step cover
     static_assert(PIECES % NT == 0 || PIECES < NT, "tile / thread count mismatch");
+    static_assert(PER_THREAD * RPW <= WAVE, "one scale word per lane");
     u32x4 c[PER_THREAD];
-    uint32_t sc[PER_THREAD];  // the row's D / 32 scale codes, byte b for block b
+    uint32_t wrow;  // lane j < PER_THREAD * RPW: the scale word of step j / RPW's row j % RPW for this wave
     __device__ __forceinline__ void load(const MXSlice<D> &S, int r0, int tid) {
 #pragma unroll
         for (int it = 0; it < PER_THREAD; ++it) {
             const int q = tid + it * NT;
             const bool ok = q < PIECES;
-            const int r = r0 + q / (D / 16);
-            const uint32_t oc = ok ? (uint32_t)r * S.row_bytes + (uint32_t)(q % (D / 16)) * 16u : OOB;
-            const uint32_t os = ok ? (uint32_t)r * S.srow_bytes : OOB;
+            const int r = r0 + q / CPR;
+            const uint32_t oc = ok ? (uint32_t)r * S.row_bytes + (uint32_t)(q % CPR) * 16u : OOB;
             c[it] = __builtin_amdgcn_raw_buffer_load_b128(S.c, (int)oc, 0, 0);
-            if constexpr (D == 128) sc[it] = __builtin_amdgcn_raw_buffer_load_b32(S.s, (int)os, 0, 0);
-            else sc[it] = __builtin_amdgcn_raw_buffer_load_b16(S.s, (int)os, 0, 0);
         }
+        const int wv = tid / WAVE, lane = tid % WAVE;
+        const int q0 = wv * WAVE + (lane / RPW) * NT;  // first piece of that step for this wave
+        wrow = f8_scale_word<D>(S, r0 + q0 / CPR + lane % RPW, lane < PER_THREAD * RPW && q0 < PIECES);
     }
-    __device__ __forceinline__ void store(lchar *tile, lu8 *s_row, int tid) const {
+    __device__ __forceinline__ void store(lchar *tile, lfloat *s_row, int tid) const {
 #pragma unroll
         for (int it = 0; it < PER_THREAD; ++it) {
             const int q = tid + it * NT;
+            // every lane takes part in the cross-lane read, then idle lanes skip
+            const uint32_t w = lane_word(wrow, it * RPW + (tid % WAVE) / CPR);
             if (PIECES % NT != 0 && q >= PIECES) continue;
-            const int r = q / (D / 16), pc = q % (D / 16);
-            const uint32_t w = sc[it];
+            const int r = q / CPR, pc = q % CPR;
             uint32_t smax = w & 255u, sb = (w >> (8 * (pc >> 1))) & 255u;
 #pragma unroll
             for (int b = 1; b < D / 32; ++b) smax = max(smax, (w >> (8 * b)) & 255u);
@@ -676,7 +701,7 @@ struct F8VLoader {
                 }
             }
             lds_write16(tile, f8_off<D>(r, pc), v);
-            if (pc == 0) s_row[r] = (uint8_t)smax;
+            if (pc == 0) s_row[r] = v_factor(smax);
         }
     }
 };
@@ -707,30 +732,33 @@ __device__ __forceinline__ i32x8 lds_read_vt_f8(const lchar *tile, int db, int l
 
 // One 32-key block of the P^T operand of the fp8 PV product: a lane's 16 P
 // values (query l % 32, keys crow(e, g) of the block) and the block's per-key
-// scale codes s_row[0 .. 31] give 16 E4M3 codes in byte order e; the return
-// value is the block's E8M0 scale code (the same in both lane halves; unit
-// when every P' of the block is zero).
-__device__ __forceinline__ int encode_p_block(const float (&pv)[16], const lu8 *s_row, int g, u32x4 &codes) {
-    typedef __attribute__((address_space(3))) const uint32_t lcu32;
-    // scale codes of keys crow(4q .. 4q + 3, g), one dword per q
-    auto sk = [&](int q, int t) {
-        const uint32_t w = *(lcu32 *)(s_row + q * 8 + g * 4);
-        return (int)((w >> (8 * t)) & 255u) - 127;
-    };
+// factors f[0 .. 31] = 2^(S_j - 127) (v_factor) give 16 E4M3 codes in byte
+// order e; the return value is the block's E8M0 scale code (the same in both
+// lane halves; unit when every P' of the block is zero).  P' = P f_j is the
+// exact product (a power-of-two factor; it rounds only where P' falls below
+// the fp32 normal range, far below anything the block's scale keeps).
+__device__ __forceinline__ int encode_p_block(const float (&pv)[16], const lfloat *f, int g, u32x4 &codes) {
+    typedef __attribute__((address_space(3))) const f32x4 lcf32x4;
+    float pp[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // factors of keys crow(4q .. 4q + 3, g): 4 consecutive entries
+        const f32x4 fq = *(lcf32x4 *)(f + q * 8 + g * 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pp[4 * q + t] = pv[4 * q + t] * fq[t];
+    }
     float m = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) m = fmaxf(m, __builtin_fabsf(__builtin_ldexpf(pv[e], sk(e >> 2, e & 3))));
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, __builtin_fabsf(pp[e]));
     m = pair_max(m);  // the block's other 16 keys sit in lane ^ 32
     // largest |P'| = f * 2^k, f in [0.5, 1): scale 2^(k - 8) puts it in [128, 256)
     const int e8 = __builtin_amdgcn_frexp_expf(m) - 8 + 127;
     const int ex = m > 0.0f ? min(max(e8, 1), 254) : 127;
-    const int sh = 127 - ex;
+    // 2^(127 - ex) as a float: ex <= 247 for a finite m, so the power is normal
+    const float sc = __builtin_bit_cast(float, (uint32_t)(254 - ex) << 23);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(pv[4 * q], sk(q, 0) + sh),
-                                                __builtin_ldexpf(pv[4 * q + 1], sk(q, 1) + sh), 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(pv[4 * q + 2], sk(q, 2) + sh),
-                                            __builtin_ldexpf(pv[4 * q + 3], sk(q, 3) + sh), w, true);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(pp[4 * q] * sc, pp[4 * q + 1] * sc, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pp[4 * q + 2] * sc, pp[4 * q + 3] * sc, w, true);
         codes[q] = (uint32_t)w;
     }
     return ex;

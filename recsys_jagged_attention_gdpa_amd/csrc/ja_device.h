@@ -271,6 +271,28 @@ __device__ __forceinline__ float pair_sum(float v) {
     return a + b;
 }
 
+// v_permlane16_swap_b32: rows of 16 lanes 1 and 3 of a trade places with rows
+// 0 and 2 of b, so a becomes (a0, b0, a2, b2) and b (a1, b1, a3, b3) (checked
+// on the hardware).  The builtin, so that the compiler places the wait states a
+// matrix-core result needs before this read (inline assembly is opaque to that).
+__device__ __forceinline__ void row_swap16(uint32_t &a, uint32_t &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ void row_swap16(float &a, float &b) {
+    uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
+    row_swap16(x, y);
+    a = __builtin_bit_cast(float, x);
+    b = __builtin_bit_cast(float, y);
+}
+// The same with both registers holding one vector-ALU result (the builtin's two
+// results may be folded into one when its inputs are equal; the s_nop covers
+// the VALU-write -> permlane-read hazard).
+__device__ __forceinline__ void row_swap16_same(int &a, int &b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
 // True on every lane when the predicate holds on any lane (a wave-uniform test).
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

@@ -80,8 +80,14 @@ constexpr int few_q_heads() {
     return 4 * tiles <= 136 * 1024 ? FEW_Q_HEADS : 2 * tiles <= 136 * 1024 ? 2 : 1;
 }
 
-template <int D, int MODE, int ACT, int WAVES, int BN, bool SPLIT, bool MX>
+// HQ (GDPA one-wave units of at most 16 query rows): half the 32 lanes of a
+// score block would hold padding rows, so after the S product the real rows of
+// the tile's two 32-key blocks are packed into one block's registers
+// (v_permlane16_swap), the element-wise stage and the P encoding run once on
+// them, and the P operands are unpacked again for the PV product.
+template <int D, int MODE, int ACT, int WAVES, int BN, bool SPLIT, bool MX, bool HQ = false>
 __global__ __launch_bounds__((WAVES == 1 ? few_q_heads<D, BN, MX>() : WAVES) * WAVE, 2) void fwd_kernel(const AttnParams p) {
+    static_assert(!HQ || (WAVES == 1 && MODE == GDPA && BN == 64), "packed rows: GDPA one-wave units, two key blocks");
     constexpr bool F8S = MX && D >= 64;  // S and PV on the fp8 MFMA (key and value tiles hold codes)
     constexpr bool IW = WAVES == 1;      // independent waves, one unit each
     constexpr int WGW = IW ? few_q_heads<D, BN, MX>() : 1;  // waves (units) per workgroup
@@ -222,7 +228,11 @@ __global__ __launch_bounds__((WAVES == 1 ? few_q_heads<D, BN, MX>() : WAVES) * W
         // needed only where a tile leaves that range
         const int wke = key_end(iw, s.lq, s.lk, p.causal, p.window);
         const int wkb = key_begin(iw + 31, s.lq, s.lk, p.window);
-        const int my_kbeg = key_begin(irow, s.lq, s.lk, p.window);
+        // HQ: lanes 16 .. 31 of each half hold rows 0 .. 15 of the second key block
+        const int qlane = HQ ? (lane & 15) : l32;
+        const int nbo = HQ ? ((lane >> 4) & 1) * 32 : 0;  // HQ: key offset of this lane's block
+        const int erow = iw + qlane;                     // query row of this lane's values
+        const int my_kbeg = key_begin(erow, s.lq, s.lk, p.window);
         for (int jt = jt_first; jt < nkv; ++jt) {
             const int j0 = jt * BN;
             const lchar *Kt = lbase + (jt & 1) * 2 * TILE_BYTES;
@@ -258,7 +268,17 @@ __global__ __launch_bounds__((WAVES == 1 ? few_q_heads<D, BN, MX>() : WAVES) * W
             // wave-uniform, so each variant is a straight-line loop behind one
             // scalar branch.
             const bool masked = (j0 + BN > wke) || (j0 < wkb);
-            const int my_kend = key_end(irow, s.lq, s.lk, p.causal, p.window);
+            const int my_kend = key_end(erow, s.lq, s.lk, p.causal, p.window);
+            constexpr int NBE = HQ ? 1 : NNB;  // score blocks the element-wise stage runs on
+            if constexpr (HQ) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float x = sacc[0][e], y = sacc[1][e];
+                    row_swap16(x, y);
+                    sacc[0][e] = x;
+                    sacc[1][e] = y;
+                }
+            }
             bf16x8 pb[F8S ? 1 : NKS], pbl[SPLIT && !F8S ? NKS : 1];
             u32x4 pf8[2] = {u32x4{}, u32x4{}};  // F8S: P^T codes of the tile's 32-key blocks
             int pex[2] = {127, 127};             // F8S: their E8M0 scale codes
@@ -266,9 +286,9 @@ __global__ __launch_bounds__((WAVES == 1 ? few_q_heads<D, BN, MX>() : WAVES) * W
             // scale is applied, folded into later arithmetic where possible.
             if (bz.kind) {
                 // raw window: entry (i0 + BM - 1 - irow) + (j - j0) (REL) or j - j0 (KEYPOS)
-                const int bbase = (bz.kind == BIAS_REL ? BM - 1 - uw * 32 - l32 : 0) + g * 4;
+                const int bbase = (bz.kind == BIAS_REL ? BM - 1 - uw * 32 - qlane : 0) + g * 4 + nbo;
 #pragma unroll
-                for (int nb = 0; nb < NNB; ++nb)
+                for (int nb = 0; nb < NBE; ++nb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const float b = bwin[bbase + nb * 32 + (e >> 2) * 8 + (e & 3)];
@@ -279,26 +299,60 @@ __global__ __launch_bounds__((WAVES == 1 ? few_q_heads<D, BN, MX>() : WAVES) * W
             if constexpr (MODE == GDPA) {
                 if (!bz.kind) {
 #pragma unroll
-                    for (int nb = 0; nb < NNB; ++nb)
+                    for (int nb = 0; nb < NBE; ++nb)
 #pragma unroll
                         for (int e = 0; e < 16; ++e) sacc[nb][e] *= p.scale;
                 }
 #pragma unroll
-                for (int nb = 0; nb < NNB; ++nb) {
+                for (int nb = 0; nb < NBE; ++nb) {
                     float pv[16];
 #pragma unroll
                     for (int e = 0; e < 16; ++e) pv[e] = act_fwd<ACT>(sacc[nb][e]);
                     if (masked) {
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
-                            const int j = j0 + nb * 32 + crow(e, g);
+                            const int j = j0 + nb * 32 + nbo + crow(e, g);
                             pv[e] = (j >= my_kend) | (j < my_kbeg) ? 0.0f : pv[e];
                         }
                     }
                     if constexpr (F8S) {
-                        pex[nb] = encode_p_block(pv, (const lfloat *)s_vsc[jt & 1] + nb * 32, g, pf8[nb]);
+                        pex[nb] = encode_p_block(pv, (const lfloat *)s_vsc[jt & 1] + nb * 32 + nbo, g, pf8[nb]);
                     } else {
                         pack_operands(pv, pb[2 * nb], pb[2 * nb + 1]);
+                    }
+                }
+                if constexpr (HQ) {
+                    // back to one operand per key block: rows 0 and 2 (queries 0 .. 15)
+                    // of block 1 come from rows 1 and 3 of the packed registers
+                    if constexpr (F8S) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            uint32_t x = pf8[0][k], y = 0u;
+                            row_swap16(x, y);
+                            pf8[0][k] = x;
+                            pf8[1][k] = y;
+                        }
+                        // scale codes: ea takes block 0's code into every row, eb block 1's
+                        // (the block-1 code of query q sits in row 3 and reaches row 2)
+                        int ea = pex[0], eb = pex[0];
+                        row_swap16_same(ea, eb);
+                        pex[0] = ea;
+                        pex[1] = eb;
+                    } else {
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            const u32x4 a = __builtin_bit_cast(u32x4, pb[h2]);
+                            u32x4 lo, hi;
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                uint32_t x = a[k], y = 0u;
+                                row_swap16(x, y);
+                                lo[k] = x;
+                                hi[k] = y;
+                            }
+                            pb[h2] = __builtin_bit_cast(bf16x8, lo);
+                            pb[2 + h2] = __builtin_bit_cast(bf16x8, hi);
+                        }
                     }
                 }
             } else {
@@ -617,10 +671,13 @@ static hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, bool lo
     t.end(K_FWD_SHORT, stream);
     if (!long_units) return hipGetLastError();
     t.begin(K_FWD, stream);
-    if (few_q)  // every unit is one block of <= 32 shared query rows
-        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, FEW_Q_KV_TILE, SPLIT, MX>),
-                           dim3(8 / few_q_heads<D, FEW_Q_KV_TILE, MX>() * cus),
-                           dim3(few_q_heads<D, FEW_Q_KV_TILE, MX>() * WAVE), 0, stream, t.with_busy(p, K_FWD));
+    constexpr int FQH = few_q_heads<D, FEW_Q_KV_TILE, MX>();
+    if (few_q && MODE == GDPA && p.lq_fixed <= 16)  // at most 16 shared query rows: packed rows
+        hipLaunchKernelGGL((fwd_kernel<D, GDPA, ACT, 1, FEW_Q_KV_TILE, false, MX, true>), dim3(8 / FQH * cus),
+                           dim3(FQH * WAVE), 0, stream, t.with_busy(p, K_FWD));
+    else if (few_q)  // every unit is one block of <= 32 shared query rows
+        hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, FEW_Q_KV_TILE, SPLIT, MX>), dim3(8 / FQH * cus),
+                           dim3(FQH * WAVE), 0, stream, t.with_busy(p, K_FWD));
     else
         hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE, SPLIT, MX>), dim3(2 * cus), dim3(4 * WAVE), 0, stream,
                            t.with_busy(p, K_FWD));

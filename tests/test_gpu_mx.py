@@ -42,10 +42,11 @@ def test_mx_forward_with_bias_and_window(mode, bias, act):
 
 
 @pytest.mark.parametrize("mode", ["gdpa", "jfa"])
-@pytest.mark.parametrize("shared", [16, 48])
-def test_mx_forward_shared_queries(mode, shared):
-    # 16 rows: one-wave 32-row units; 48 rows: the 4-wave 128-row units
-    w = synth.custom(mode=mode, lq=None, lk=[700, 0, 1, 31, 33, 257, 4000], H=4, D=64, seed=3,
+@pytest.mark.parametrize("shared,D", [(16, 64), (48, 64), (11, 128), (24, 64)])
+def test_mx_forward_shared_queries(mode, shared, D):
+    # 16 rows or fewer: one-wave 32-row units (GDPA: rows of two key blocks packed
+    # into one block's lanes); 24: one-wave units unpacked; 48: the 4-wave units
+    w = synth.custom(mode=mode, lq=None, lk=[700, 0, 1, 31, 33, 257, 4000], H=4, D=D, seed=3,
                      shared_q=shared, act="silu", bias_kind="keypos", bias_lo=0, bias_hi=4095,
                      with_dout=False, mx=MX)
     mx_parity(w, label=f"mxfp8 shared-q={shared} {mode}")

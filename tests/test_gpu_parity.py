@@ -154,10 +154,12 @@ def test_jfa_backward_without_residual_is_exact_backward_of_bf16_output(causal):
 
 
 @pytest.mark.parametrize("mode", ["gdpa", "jfa"])
-@pytest.mark.parametrize("rows,D,causal", [(1, 32, False), (32, 128, False), (33, 64, False), (20, 128, True)])
+@pytest.mark.parametrize("rows,D,causal", [(1, 32, False), (32, 128, False), (33, 64, False), (20, 128, True),
+                                           (16, 64, True), (9, 128, False)])
 def test_shared_query_block_sizes(mode, rows, D, causal):
-    # Up to 32 shared rows run as one-wave units over 32-row tiles; 33 rows take
-    # the 4-wave path.  Samples with <= 32 keys go to the short-K/V units.
+    # Up to 32 shared rows run as one-wave units over 32-row tiles (GDPA with at
+    # most 16: the two key blocks' rows packed into one block's lanes); 33 rows
+    # take the 4-wave path.  Samples with <= 32 keys go to the short-K/V units.
     w = synth.custom(mode=mode, lq=None, lk=[700, 0, 1, 31, 32, 33, 96, 257], H=2, D=D, seed=rows + D,
                      shared_q=rows, act="gelu_erf", causal=causal, bias_kind="rel", bias_lo=-50,
                      bias_hi=40, bias_sigma=0.3, with_dout=False)

@@ -35,31 +35,6 @@ namespace ja {
 constexpr int FWD_THREADS = 256;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units a running softmax max may lag the true max
 
-// WAVES waves per workgroup, each owning 32 query rows of the unit's tile
-// (BM = 32 WAVES rows), key tiles of BN rows.  The usual shape is 4 waves x
-// 64-key tiles; with one block of at most 32 shared query rows (pooling by
-// learned seed queries) a 1-wave, 32-key shape does no work on padding rows.
-// SPLIT (JFA with the rounding residual requested): P enters the PV product as
-// bf16(P) plus its bf16 residual, two MFMAs into the same accumulator, so O
-// (and delta = <dO, O> formed from it in backward) is accurate to ~2^-17
-// rather than carrying the 2^-9 rounding of P.
-// MX (MXFP8 inputs: E4M3 codes with a scale per 32 head-dimension elements):
-// Q, K and V are read as codes and decoded to bf16 after the load; key / value
-// tiles then come through registers (codes in flight during the current tile,
-// decoded into the LDS tile at its end) instead of the buffer->LDS copy, which
-// moves bytes without decoding them.
-// With MX and D = 64 or 128, S^T = K Q^T runs on the block-scaled fp8
-// MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) straight from the codes: key tiles
-// reach LDS as codes by buffer->LDS copies (half the bytes, no decoding), query
-// codes stay in registers, and the block scales go in as the MFMA's scale
-// operands; only V is decoded to bf16 for the PV product.
-//
-// WAVES = 1 (one block of at most 32 shared query rows, pooling by learned
-// seed queries): the waves of a workgroup are independent units, one head each
-// of the same sample (head groups of few_q_heads()), each with its own LDS
-// tiles and no barrier inside its loop.  The heads of a sample share the cache lines
-// of their key and value rows (64-byte rows of fp8 codes fill half a line), so
-// running them side by side on one CU fetches each line from HBM once.
 // End of a tile step: the tiles that every thread of the unit copied are in
 // LDS.  A unit of one wave only orders its own LDS accesses (its DMA has
 // landed: store_tile waited for it); a multi-wave unit needs the barrier.
@@ -80,6 +55,30 @@ constexpr int few_q_heads() {
     return 4 * tiles <= 136 * 1024 ? FEW_Q_HEADS : 2 * tiles <= 136 * 1024 ? 2 : 1;
 }
 
+// WAVES waves per workgroup, each owning 32 query rows of the unit's tile
+// (BM = 32 WAVES rows), key tiles of BN rows.  The usual shape is 4 waves x
+// 64-key tiles.
+// SPLIT (JFA with the rounding residual requested): P enters the PV product as
+// bf16(P) plus its bf16 residual, two MFMAs into the same accumulator, so O
+// (and delta = <dO, O> formed from it in backward) is accurate to ~2^-17
+// rather than carrying the 2^-9 rounding of P.
+// MX (MXFP8 inputs: E4M3 codes with a scale per 32 head-dimension elements):
+// with D = 64 or 128, S^T = K Q^T and O^T = V'^T P'^T run on the block-scaled
+// fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) straight from the codes: key
+// tiles reach LDS as codes by buffer->LDS copies, query codes stay in
+// registers, value rows come through registers and are re-encoded to one
+// scale per key on their way into the code tile, and P is encoded as E4M3 per
+// 32-key block with that key's scale folded in; the block scales go in as the
+// MFMA's scale operands.  With D = 32 the codes are decoded to bf16 after the
+// load (key / value tiles through registers) and the bf16 products run.
+//
+// WAVES = 1 (one block of at most 32 shared query rows, pooling by learned
+// seed queries): a unit is one wave over a 32-row query tile, and the waves of
+// a workgroup are independent units, one head each of the same sample (head
+// groups of few_q_heads()), each with its own LDS tiles and no barrier inside
+// its loop.  The heads of a sample share the cache lines of their key and
+// value rows (64-byte rows of fp8 codes fill half a line), so running them side
+// by side on one CU fetches each line from HBM once.
 // HQ (GDPA one-wave units of at most 16 query rows): half the 32 lanes of a
 // score block would hold padding rows, so after the S product the real rows of
 // the tile's two 32-key blocks are packed into one block's registers

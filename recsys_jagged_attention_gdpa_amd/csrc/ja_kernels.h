@@ -205,6 +205,9 @@ constexpr int FEW_Q_HEADS = 4;     // heads of one sample per workgroup (a wave 
 // than FUSED_MAX_LK keys, so only the short-K/V units have work).
 hipError_t launch_fwd_bf16(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, bool long_units,
                            hipStream_t stream);
+// The same for MXFP8 inputs (p.mx set); launch_fwd_bf16 forwards to it.
+hipError_t launch_fwd_mx(const AttnParams &p, int D, int mode, int act, int cus, bool few_q, bool long_units,
+                         hipStream_t stream);
 hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, bool long_units,
                            hipStream_t stream);
 // Bias-table gradient (p.dbias, p.dbias_part, p.tiles4 / p.counters4 planned).

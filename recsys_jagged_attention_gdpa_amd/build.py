@@ -20,12 +20,20 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libjagged_attn.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["ja_api.cpp", "ja_plan.hip", "ja_fwd.hip", "ja_fwd_mx.hip", "ja_bwd.hip", "ja_dbias.hip", "ja_f32.hip",
-           "ja_rope.hip"]
-# Per-unit compiler options: the bf16 forward kernels take the latency-hiding
-# ("max-ilp") instruction scheduler, measured 3.5 % faster on the JFA forward
-# (the MXFP8 forward, 2 % slower with it, is its own unit for that reason).
-EXTRA = {"ja_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+SOURCES = ["ja_api.cpp", "ja_plan.hip", "ja_fwd.hip", "ja_fwd_mx.hip", "ja_bwd.hip", "ja_bwd_kv.hip", "ja_dbias.hip",
+           "ja_f32.hip", "ja_rope.hip"]
+# Per-unit compiler options (instruction schedulers), each measured against the
+# default on the kernels of its unit:
+#   * bf16 forward: latency-hiding "max-ilp", JFA forward 3.5 % faster (the
+#     MXFP8 forward, 2 % slower with it, is its own unit for that reason);
+#   * dK/dV: iterative latency-hiding, 6 % faster with the GELU-erf
+#     activation, 0.5 % with the softmax;
+#   * delta, fused short-K/V and dQ units: iterative occupancy-first, dQ 1-2 %
+#     faster (the iterative latency-hiding one made dQ 2.8x slower).
+_SCHED = "-amdgpu-sched-strategy="
+EXTRA = {"ja_fwd.hip": ["-mllvm", _SCHED + "max-ilp"],
+         "ja_bwd_kv.hip": ["-mllvm", _SCHED + "iterative-ilp"],
+         "ja_bwd.hip": ["-mllvm", _SCHED + "iterative-maxocc"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
@@ -50,7 +58,7 @@ def build(jobs: int = 0, verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

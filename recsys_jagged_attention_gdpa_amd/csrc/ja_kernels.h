@@ -210,6 +210,8 @@ hipError_t launch_fwd_mx(const AttnParams &p, int D, int mode, int act, int cus,
                          hipStream_t stream);
 hipError_t launch_bwd_bf16(const AttnParams &p, int D, int mode, int act, int grid, bool long_units,
                            hipStream_t stream);
+// The dK/dV units alone; launch_bwd_bf16 calls it between the fused and the dQ units.
+hipError_t launch_bwd_kv(const AttnParams &p, int D, int mode, int act, int grid, hipStream_t stream);
 // Bias-table gradient (p.dbias, p.dbias_part, p.tiles4 / p.counters4 planned).
 hipError_t launch_dbias_bf16(const AttnParams &p, int D, int mode, int act, hipStream_t stream);
 // Rotary embedding pass: up to two segments (rows of one [rows, H, D] tensor

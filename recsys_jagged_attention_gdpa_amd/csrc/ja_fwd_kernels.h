@@ -313,7 +313,7 @@ __global__ __launch_bounds__((WAVES == 1 ? few_q_heads<D, BN, MX>() : WAVES) * W
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             const int j = j0 + nb * 32 + nbo + crow(e, g);
-                            pv[e] = (j >= my_kend) | (j < my_kbeg) ? 0.0f : pv[e];
+                            pv[e] = ((j >= my_kend) | (j < my_kbeg)) ? 0.0f : pv[e];
                         }
                     }
                     if constexpr (F8S) {
@@ -363,7 +363,7 @@ __global__ __launch_bounds__((WAVES == 1 ? few_q_heads<D, BN, MX>() : WAVES) * W
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             const int j = j0 + nb * 32 + crow(e, g);
-                            sacc[nb][e] = (j >= my_kend) | (j < my_kbeg) ? -INFINITY : sacc[nb][e];
+                            sacc[nb][e] = ((j >= my_kend) | (j < my_kbeg)) ? -INFINITY : sacc[nb][e];
                         }
                 }
                 float tmax = -INFINITY;

@@ -38,9 +38,9 @@ from recsys_jagged_attention_gdpa_amd import _lib, synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-KERNEL_SOURCES = ["ja_fwd.hip", "ja_fwd_mx.hip", "ja_fwd_kernels.h", "ja_bwd.hip", "ja_bwd_kv.hip", "ja_bwd_kernels.h",
-                  "ja_dbias_fold.h", "ja_plan.hip", "ja_tiles.h", "ja_device.h", "ja_kernels.h",
-                  "../build.py"]  # build.py: compiler options
+KERNEL_SOURCES = ["ja_fwd.hip", "ja_fwd_gdpa.hip", "ja_fwd_mx.hip", "ja_fwd_kernels.h", "ja_bwd.hip",
+                  "ja_bwd_kv.hip", "ja_bwd_kernels.h", "ja_dbias_fold.h", "ja_plan.hip", "ja_tiles.h",
+                  "ja_device.h", "ja_kernels.h", "../build.py"]  # build.py: compiler options
 
 # Workloads: which roofline bounds them (short K/V streams Q / dO / O through HBM;
 # long sequences are MFMA work).

@@ -20,18 +20,22 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libjagged_attn.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["ja_api.cpp", "ja_plan.hip", "ja_fwd.hip", "ja_fwd_mx.hip", "ja_bwd.hip", "ja_bwd_kv.hip", "ja_dbias.hip",
-           "ja_f32.hip", "ja_rope.hip"]
+SOURCES = ["ja_api.cpp", "ja_plan.hip", "ja_fwd.hip", "ja_fwd_gdpa.hip", "ja_fwd_mx.hip", "ja_bwd.hip", "ja_bwd_kv.hip",
+           "ja_dbias.hip", "ja_f32.hip", "ja_rope.hip"]
 # Per-unit compiler options (instruction schedulers), each measured against the
 # default on the kernels of its unit:
 #   * bf16 forward: latency-hiding "max-ilp", JFA forward 3.5 % faster (the
 #     MXFP8 forward, 2 % slower with it, is its own unit for that reason);
+#   * the bf16 GDPA long-sequence forward: iterative latency-hiding, GELU-erf
+#     long-tail forward 2 % faster (the short-K/V forward, 3 % slower with it,
+#     stays in the max-ilp unit);
 #   * dK/dV: iterative latency-hiding, 6 % faster with the GELU-erf
 #     activation, 0.5 % with the softmax;
 #   * delta, fused short-K/V and dQ units: iterative occupancy-first, dQ 1-2 %
 #     faster (the iterative latency-hiding one made dQ 2.8x slower).
 _SCHED = "-amdgpu-sched-strategy="
 EXTRA = {"ja_fwd.hip": ["-mllvm", _SCHED + "max-ilp"],
+         "ja_fwd_gdpa.hip": ["-mllvm", _SCHED + "iterative-ilp"],
          "ja_bwd_kv.hip": ["-mllvm", _SCHED + "iterative-ilp"],
          "ja_bwd.hip": ["-mllvm", _SCHED + "iterative-maxocc"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,5 +1,6 @@
 // Forward launches for bf16 inputs (the kernels are in
-// ja_fwd_kernels.h); MXFP8 inputs go to ja_fwd_mx.hip.  The two translation
+// ja_fwd_kernels.h); MXFP8 inputs go to ja_fwd_mx.hip and the GDPA
+// long-sequence kernel is launched from ja_fwd_gdpa.hip.  The translation
 // units are compiled apart so that each can take the instruction scheduling
 // that suits its kernels (the build gives this one the compiler's
 // latency-hiding "max-ilp" scheduler: the JFA forward measured 3.5 % faster

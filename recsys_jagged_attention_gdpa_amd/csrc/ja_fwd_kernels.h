@@ -663,6 +663,12 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_short_kernel(const AttnPar
     busy_end(p.busy, p.busy_cap, busy_t0);
 }
 
+// The bf16 GDPA units of the long-sequence kernel are launched from a
+// translation unit of their own (ja_fwd_gdpa.hip), which the build compiles
+// with its own instruction scheduler; it instantiates every (D, ACT).
+template <int D, int ACT>
+hipError_t launch_fwd_gdpa_long(const AttnParams &p, int cus, hipStream_t stream);
+
 template <int D, int MODE, int ACT, bool SPLIT, bool MX>
 inline hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, bool long_units, hipStream_t stream) {
     const KernelTimer &t = kernel_timer();
@@ -679,6 +685,8 @@ inline hipError_t launch_fwd_s(const AttnParams &p, int cus, bool few_q, bool lo
     else if (few_q)  // every unit is one block of <= 32 shared query rows
         hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 1, FEW_Q_KV_TILE, SPLIT, MX>), dim3(8 / FQH * cus),
                            dim3(FQH * WAVE), 0, stream, t.with_busy(p, K_FWD));
+    else if constexpr (MODE == GDPA && !MX)
+        (void)launch_fwd_gdpa_long<D, ACT>(p, cus, stream);
     else
         hipLaunchKernelGGL((fwd_kernel<D, MODE, ACT, 4, KV_TILE, SPLIT, MX>), dim3(2 * cus), dim3(4 * WAVE), 0, stream,
                            t.with_busy(p, K_FWD));

@@ -40,7 +40,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = ["ja_fwd.hip", "ja_fwd_gdpa.hip", "ja_fwd_mx.hip", "ja_fwd_kernels.h", "ja_bwd.hip",
                   "ja_bwd_kv.hip", "ja_bwd_kernels.h", "ja_dbias_fold.h", "ja_plan.hip", "ja_tiles.h",
-                  "ja_device.h", "ja_kernels.h", "../build.py"]  # build.py: compiler options
+                  "ja_device.h", "ja_kernels.h"]
 
 # Workloads: which roofline bounds them (short K/V streams Q / dO / O through HBM;
 # long sequences are MFMA work).
@@ -238,10 +238,13 @@ class Runner:
 
 # ------------------------------------------------------------------ traffic
 def sources_digest():
+    """Digest of the measured kernels' sources and of the compiler configuration."""
+    from recsys_jagged_attention_gdpa_amd import build as _build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "recsys_jagged_attention_gdpa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(repr(_build.compile_config()).encode())
     return h.hexdigest()[:16]
 
 

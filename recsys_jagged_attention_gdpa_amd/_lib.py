@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
+import warnings
 
 import torch
 
@@ -58,8 +59,23 @@ _lib = None
 _lock = threading.Lock()
 
 
+def stale_reason(path: str = LIB_PATH):
+    """Why the library at `path` may not match the sources next to it (None when
+    its build stamp, written by build.py, equals the current sources' digest)."""
+    from . import build as _build
+    stamp = path + ".sources"
+    if not os.path.exists(stamp):
+        return f"{stamp} is missing (library built without a source stamp)"
+    with open(stamp) as fh:
+        built = fh.read().strip()
+    if built != _build.sources_digest():
+        return "the C/HIP sources or compiler options changed since the library was built"
+    return None
+
+
 def load(path: str = LIB_PATH):
-    """Load the shared library (once).  Raises if it has not been built."""
+    """Load the shared library (once).  Raises if it has not been built; warns
+    when it was built from other sources than the ones in the tree."""
     global _lib
     with _lock:
         if _lib is not None:
@@ -67,6 +83,10 @@ def load(path: str = LIB_PATH):
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m recsys_jagged_attention_gdpa_amd.build`")
+        why = stale_reason(path)
+        if why is not None:
+            warnings.warn(f"{path}: {why}; rebuild with `python -m recsys_jagged_attention_gdpa_amd.build`",
+                          RuntimeWarning, stacklevel=2)
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         PP = ctypes.POINTER(JaProblem)

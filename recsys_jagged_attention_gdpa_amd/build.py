@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -56,6 +57,28 @@ def _compile(src: str) -> str:
     return obj
 
 
+def sources_digest() -> str:
+    """sha256 over the C/HIP sources, the public headers and the compiler options."""
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith((".hip", ".cpp", ".h"))]
+    files += [os.path.join(INCLUDE, f) for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h")]
+    for f in files:
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(repr(compile_config()).encode())
+    return h.hexdigest()
+
+
+def compile_config():
+    """What decides the compiled code besides the sources: units, options, target
+    (directory paths left out, so the value does not depend on where the tree sits)."""
+    return (SOURCES, [a for a in COMMON if not os.path.isabs(a)], sorted(EXTRA.items()), ARCH)
+
+
+STAMP = LIB + ".sources"  # digest of the sources the library was built from
+
+
 def build(jobs: int = 0, verbose: bool = True) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
@@ -67,6 +90,8 @@ def build(jobs: int = 0, verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    with open(STAMP, "w") as fh:
+        fh.write(sources_digest() + "\n")
     if verbose:
         print(f"built {LIB}")
     return LIB

@@ -35,6 +35,16 @@ def test_library_exports_every_declared_symbol():
         assert lib.ja_status_string(code) != lib.ja_status_string(99)
 
 
+def test_library_build_stamp_matches_sources(tmp_path):
+    # the library in the tree was built from the sources in the tree
+    assert _lib.stale_reason() is None, _lib.stale_reason()
+    fake = tmp_path / "libjagged_attn.so"
+    fake.write_bytes(b"")
+    assert "missing" in _lib.stale_reason(str(fake))
+    (tmp_path / "libjagged_attn.so.sources").write_text("0" * 64 + "\n")
+    assert "changed" in _lib.stale_reason(str(fake))
+
+
 def test_problem_struct_layout_matches_header(tmp_path):
     # Compile the header with the host C compiler and compare every field's
     # offset and the struct size with the binding's ctypes mirror.
